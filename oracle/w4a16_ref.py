@@ -1,0 +1,216 @@
+"""The W4A16 oracle: unpack, dequantise to FP16, matmul, round to FP16.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use this module.  It shares no code
+with the HIP library and imports nothing from it.
+
+Notation (the pages' own): ``A`` are the FP16 activations, tokens x
+in-features (``M x K``); ``B`` the INT4 weights, in-features x out-features
+(``K x N``), stored as codes ``q`` in 0..15 with one FP16 scale per group of
+``group`` consecutive in-features per output column; ``C = A . dequant(B)``
+is the FP16 output (``M x N``).
+
+Readings of what the pages leave open (each one is also listed with the
+design notes):
+
+1. Zero point.  The pages say the codes come from a GPTQ-style quantiser and
+   are turned back into real magnitudes by the group scale; they give no zero
+   point.  The reading taken is the symmetric one, ``w = (q - 8) * s``.
+2. Canonical packing.  Eight codes per 32-bit word along K; code ``k = 8j + i``
+   of column ``n`` is bits ``4i .. 4i+3`` of word ``Bq[j][n]`` (least
+   significant nibble first).  The pages only say the kernel's own layout is
+   permuted; this is the plain order a quantiser hands over.
+3. Scale layout: ``S[K/group][N]`` row-major; ``group`` divides K; ``group ==
+   K`` is one scale per output column.
+4. Dequantisation rounds once: ``fp16_rne(f32(q - 8) * f32(s))``.  The float32
+   product of a 4-bit integer and an 11-bit significand is exact, so this is
+   the exact product rounded to FP16 once.
+5. Accumulation: the pages allow FP16 or FP32 registers; the workload fixes
+   FP32.  The oracle accumulates in float64 (``gemm``), which is closer to the
+   exact sum than any FP32 order; ``gemm_f32`` is the FP32-accumulated twin
+   used to show that the FP32 rounding order sits far inside the tolerance.
+6. Output: the accumulated value rounded once to FP16 (round-to-nearest-even,
+   overflow to infinity).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Reading 1: symmetric codes, zero point 8.
+ZERO_POINT = 8
+
+# Version of the permuted layout that ``repack``/``unrepack`` describe.
+LAYOUT_VERSION = 1
+
+# Position of code i (0..7, along K) of one fragment inside its 32-bit word in
+# the permuted layout: codes 2r and 2r+1 go to nibbles r and r+4, so that one
+# shift by 4r and one mask keep the pair (2r, 2r+1) in the two 16-bit halves.
+_NIBBLE_OF_CODE = (0, 4, 1, 5, 2, 6, 3, 7)
+
+
+def _check_words(Bq: np.ndarray) -> None:
+    if Bq.dtype != np.uint32 or Bq.ndim != 2:
+        raise TypeError("Bq must be a 2-D uint32 array [K/8][N]")
+
+
+# ---------------------------------------------------------------------------
+# Packing (reading 2).  "Quant Marlin kernel" explainer, "The architecture:
+# every piece explained", top row: eight 4-bit values in each 32-bit word.
+# ---------------------------------------------------------------------------
+
+def unpack_codes(Bq: np.ndarray) -> np.ndarray:
+    """Codes ``q[K][N]`` (uint8, 0..15) from canonical words ``Bq[K/8][N]``.
+
+    ``q[8j + i][n] = (Bq[j][n] >> 4i) & 0xF``.
+    """
+    _check_words(Bq)
+    K8, N = Bq.shape
+    q = np.empty((K8, 8, N), dtype=np.uint8)
+    for i in range(8):
+        q[:, i, :] = (Bq >> np.uint32(4 * i)) & np.uint32(0xF)
+    return q.reshape(K8 * 8, N)
+
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Canonical words ``Bq[K/8][N]`` from codes ``q[K][N]`` (0..15)."""
+    q = np.asarray(q)
+    if q.ndim != 2 or q.shape[0] % 8:
+        raise ValueError("q must be [K][N] with K a multiple of 8")
+    if q.size and (q.min() < 0 or q.max() > 15):
+        raise ValueError("codes must lie in 0..15")
+    K, N = q.shape
+    q8 = q.astype(np.uint32).reshape(K // 8, 8, N)
+    Bq = np.zeros((K // 8, N), dtype=np.uint32)
+    for i in range(8):
+        Bq |= q8[:, i, :] << np.uint32(4 * i)
+    return Bq
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation (readings 1, 3, 4).  "Quant Marlin kernel" explainer, middle
+# row: unpack the INT4 codes to FP16 and multiply by the group scale; "End-to-
+# end flow": multiply by the relevant group scale to recover FP16 magnitudes.
+# ---------------------------------------------------------------------------
+
+def dequant(Bq: np.ndarray, S: np.ndarray, group: int) -> np.ndarray:
+    """FP16 weights ``W[K][N] = fp16_rne(f32(q - 8) * f32(S[k // group][n]))``."""
+    _check_words(Bq)
+    q = unpack_codes(Bq)
+    K, N = q.shape
+    S = np.asarray(S)
+    if S.dtype != np.float16 or S.shape != (K // group, N) or K % group:
+        raise ValueError("S must be float16 [K/group][N] with group | K")
+    centred = q.astype(np.float32) - np.float32(ZERO_POINT)
+    scale_per_k = np.repeat(S.astype(np.float32), group, axis=0)
+    return (centred * scale_per_k).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# The matmul (readings 5, 6).  "Quant Marlin kernel" explainer, middle row:
+# FP16 weights times FP16 activations with FP16/FP32 accumulation; bottom
+# rows: FP16 activations in, FP16 output out.
+# ---------------------------------------------------------------------------
+
+def _check_a(A: np.ndarray, K: int) -> None:
+    if A.dtype != np.float16 or A.ndim != 2 or A.shape[1] != K:
+        raise ValueError("A must be float16 [M][K]")
+
+
+def gemm(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int,
+         chunk: int = 4096):
+    """``(C16, C64)``: the float64-accumulated product and its FP16 rounding.
+
+    ``C64[m][n] = sum_k f64(A[m][k]) * f64(W[k][n])`` with ``W = dequant(...)``;
+    ``C16 = fp16_rne(C64)``.  Columns are taken ``chunk`` at a time only to
+    bound memory; each output element is the same full sum over K.
+    """
+    _check_words(Bq)
+    K = Bq.shape[0] * 8
+    N = Bq.shape[1]
+    _check_a(A, K)
+    A64 = A.astype(np.float64)
+    C64 = np.empty((A.shape[0], N), dtype=np.float64)
+    for n0 in range(0, N, chunk):
+        n1 = min(N, n0 + chunk)
+        W = dequant(np.ascontiguousarray(Bq[:, n0:n1]),
+                    np.ascontiguousarray(S[:, n0:n1]), group)
+        C64[:, n0:n1] = A64 @ W.astype(np.float64)
+    return C64.astype(np.float16), C64
+
+
+def gemm_f32(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int):
+    """FP32-accumulated twin: ``fp16_rne(f32(A) @ f32(W))`` (BLAS order)."""
+    K = Bq.shape[0] * 8
+    _check_a(A, K)
+    W = dequant(Bq, S, group)
+    C32 = A.astype(np.float32) @ W.astype(np.float32)
+    return C32.astype(np.float16), C32
+
+
+def gemm_columns(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int,
+                 cols) -> np.ndarray:
+    """Float64 ``C64[:, cols]``, dequantising only the listed columns.
+
+    Used to check sampled outputs of shapes too large for the whole product.
+    """
+    cols = np.asarray(cols, dtype=np.int64)
+    K = Bq.shape[0] * 8
+    _check_a(A, K)
+    W = dequant(np.ascontiguousarray(Bq[:, cols]),
+                np.ascontiguousarray(S[:, cols]), group)
+    return A.astype(np.float64) @ W.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# The permuted layout.  "Low-Precision Quantization Kernels in Production"
+# (llms.blog), section 1, mechanism 1, and the "Quant Marlin kernel"
+# explainer's note on the permuted weight layout: codes are reordered once,
+# offline, so that one wide load hands every lane exactly the operand
+# fragment the matrix instruction expects.  The order below is this
+# library's own, for the 16x16x32 FP16 matrix instruction of gfx950 (lane l
+# supplies column l % 16 and eight consecutive K values 8 * (l // 16) .. +7 of
+# a 32-deep K step).  Layout version 1:
+#
+#   code q[k][n] lives in word
+#       ((n16 * (K / 128) + kb) * 64 + lane) * 4 + j
+#   with n16 = n // 16, kb = k // 128, j = (k % 128) // 32,
+#        lane = (n % 16) + 16 * ((k % 32) // 8),
+#   at nibble _NIBBLE_OF_CODE[k % 8].
+#
+# So one 16-byte load per lane covers that lane's column over one whole
+# 128-deep block of K (four 32-deep steps), and a wave's 64 lanes read 1 KiB of
+# contiguous memory.
+# ---------------------------------------------------------------------------
+
+def _check_layout_shape(K: int, N: int) -> None:
+    if K % 128 or N % 16 or K <= 0 or N <= 0:
+        raise ValueError(f"layout needs K % 128 == 0 and N % 16 == 0 "
+                         f"(K={K}, N={N})")
+
+
+def repack(Bq: np.ndarray) -> np.ndarray:
+    """Permuted words (flat uint32, ``K*N/8`` of them) from canonical ``Bq``."""
+    _check_words(Bq)
+    K = Bq.shape[0] * 8
+    N = Bq.shape[1]
+    _check_layout_shape(K, N)
+    q = unpack_codes(Bq)                       # [K][N], k = 128kb+32j+8lg+i
+    q6 = q.reshape(K // 128, 4, 4, 8, N // 16, 16)   # kb, j, lg, i, n16, nl
+    frag = q6.transpose(4, 0, 2, 5, 1, 3)            # n16, kb, lg, nl, j, i
+    frag = frag.astype(np.uint32)
+    words = np.zeros(frag.shape[:-1], dtype=np.uint32)
+    for i in range(8):
+        words |= frag[..., i] << np.uint32(4 * _NIBBLE_OF_CODE[i])
+    return words.reshape(-1)                   # (n16, kb, lane, j) row-major
+
+
+def unrepack(Bp: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Canonical ``Bq[K/8][N]`` from permuted words (inverse of ``repack``)."""
+    _check_layout_shape(K, N)
+    Bp = np.asarray(Bp, dtype=np.uint32).reshape(N // 16, K // 128, 4, 16, 4)
+    frag = np.empty(Bp.shape + (8,), dtype=np.uint8)
+    for i in range(8):
+        frag[..., i] = (Bp >> np.uint32(4 * _NIBBLE_OF_CODE[i])) & np.uint32(0xF)
+    q6 = frag.transpose(1, 4, 2, 5, 0, 3)            # kb, j, lg, i, n16, nl
+    return pack_codes(q6.reshape(K, N))

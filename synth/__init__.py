@@ -1,0 +1,53 @@
+"""Seeded synthetic inputs for the W4A16 matmul.
+
+This module only draws random numbers. It holds none of the method's
+arithmetic (no packing, no dequantisation, no products), so that both the
+oracle-side tests and the GPU path can take their inputs from it without
+sharing any computation.
+
+Recipe (the same for every shape):
+
+* ``numpy.random.default_rng(seed)`` (PCG64), draws taken in this order:
+  activations, then weight words, then scales.
+* Activations ``A``: ``standard_normal`` in float32, rounded to float16
+  (round-to-nearest-even), shape ``[M][K]`` row-major.
+* Weight words ``Bq``: uniform ``uint32`` words, shape ``[K/8][N]``.  A word
+  holds eight 4-bit codes along K, so uniform words are exactly eight
+  independent codes uniform on 0..15.
+* Scales ``S``: ``uniform(0.005, 0.02)`` in float64, rounded to float16,
+  shape ``[K/group][N]`` row-major.
+
+The value distributions are the ones the workload description gives: a
+Gaussian activation, uniform codes, and small positive scales, one per group
+of 128 (or one per column when the group is the whole of K).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+SCALE_LO = 0.005
+SCALE_HI = 0.02
+
+
+def make_inputs(M: int, K: int, N: int, group: int = 128, seed: int = 0):
+    """Return ``(A, Bq, S)`` as numpy arrays (float16, uint32, float16)."""
+    if K % 8 or group <= 0 or K % group:
+        raise ValueError(f"bad shape K={K} group={group}")
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K), dtype=np.float32).astype(np.float16)
+    Bq = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+    S = rng.uniform(SCALE_LO, SCALE_HI, size=(K // group, N)).astype(np.float16)
+    return A, Bq, S
+
+
+def make_activations(M: int, K: int, seed: int = 0):
+    """Activations alone, ``standard_normal`` float32 rounded to float16."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((M, K), dtype=np.float32).astype(np.float16)
+
+
+def make_words(K: int, N: int, seed: int = 0):
+    """Uniform ``uint32`` weight words alone, shape ``[K/8][N]``."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)

@@ -1,0 +1,365 @@
+"""Pins for the CPU oracle: checks against facts other than the oracle itself.
+
+Each test fixes the oracle to something the pages or the mathematics decide:
+hand-worked fixtures, an exhaustive comparison with an independent rounding
+routine, brute force with exact rational sums, closed forms and invariants.
+No GPU is used here.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import w4a16_ref as ref
+from synth import make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fp16_struct(x: float) -> float:
+    """Round a double to float16 with Python's own IEEE half packer (RNE)."""
+    try:
+        return struct.unpack("<e", struct.pack("<e", x))[0]
+    except OverflowError:
+        return math.copysign(math.inf, x)
+
+
+def _fp16_exact(fr: Fraction) -> float:
+    """Round an exact rational to float16, ties to even, by integer arithmetic."""
+    if fr == 0:
+        return 0.0
+    sign = -1.0 if fr < 0 else 1.0
+    a = abs(fr)
+    # Exponent e with 2**e <= a < 2**(e+1); float16 normal range e in [-14, 15].
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -14)                    # subnormals share the 2**-14 exponent
+    quantum = Fraction(2) ** (e - 10)  # 11 significant bits
+    units = a / quantum
+    fl = units.numerator // units.denominator
+    rem = units - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    value = fl * quantum
+    if value >= 65520 or value > 65504:
+        return sign * math.inf
+    return sign * float(value)
+
+
+# ---------------------------------------------------------------------------
+# Packing
+# ---------------------------------------------------------------------------
+
+def test_nibble_order_golden():
+    """Hand-worked words pin the least-significant-first order along K."""
+    rows = []
+    with open(os.path.join(GOLDEN, "nibble_order.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                rows.append((int(line[0], 16), [int(v) for v in line[1:]]))
+    assert len(rows) >= 5
+    Bq = np.array([[w for w, _ in rows]], dtype=np.uint32)   # K=8, N=len(rows)
+    q = oracle.unpack_codes(Bq)
+    for n, (_, codes) in enumerate(rows):
+        assert q[:, n].tolist() == codes
+    assert np.array_equal(oracle.pack_codes(q), Bq)
+
+
+def test_pack_unpack_exhaustive_positions():
+    """Every value at every nibble position, alone in its word."""
+    words = [v << (4 * i) for i in range(8) for v in range(16)]
+    Bq = np.array([words], dtype=np.uint32)
+    q = oracle.unpack_codes(Bq)
+    for col, (i, v) in enumerate((i, v) for i in range(8) for v in range(16)):
+        expect = [0] * 8
+        expect[i] = v
+        assert q[:, col].tolist() == expect
+    assert np.array_equal(oracle.pack_codes(q), Bq)
+
+
+def test_pack_unpack_random_roundtrip():
+    rng = np.random.default_rng(7)
+    Bq = rng.integers(0, 2**32, size=(64, 48), dtype=np.uint32)
+    assert np.array_equal(oracle.pack_codes(oracle.unpack_codes(Bq)), Bq)
+    q = rng.integers(0, 16, size=(256, 40))
+    assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(q)), q)
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation: exhaustive over (code, scale) against an independent
+# rounding routine.
+# ---------------------------------------------------------------------------
+
+def _all_finite_nonzero_fp16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    keep = np.isfinite(vals) & (vals != 0)
+    return vals[keep]
+
+
+def test_dequant_exhaustive_codes_times_every_fp16_scale():
+    """16 codes x all 63,486 finite nonzero FP16 scales of both signs.
+
+    The expected value is the double product ``(q - 8) * s`` (exact: a 4-bit
+    integer times an 11-bit significand) rounded once by Python's IEEE half
+    packer, a routine that shares nothing with numpy's float16 cast.
+    """
+    scales = _all_finite_nonzero_fp16()
+    assert scales.size == 63486
+    K = 128                                 # one group; code of row k is k % 16
+    q = np.tile(np.arange(16, dtype=np.uint8), K // 16)[:, None]
+    q = np.repeat(q, scales.size, axis=1)
+    Bq = oracle.pack_codes(q)
+    S = scales[None, :]
+    W = oracle.dequant(Bq, S, K)
+    got = W[:16, :].astype(np.float64)      # rows 0..15 carry codes 0..15
+    svals = scales.astype(np.float64).tolist()
+    for code in range(16):
+        expect = np.array([_fp16_struct((code - 8) * s) for s in svals])
+        row = got[code]
+        same = (row == expect) | (np.isnan(row) & np.isnan(expect))
+        assert same.all(), f"code {code}: {np.count_nonzero(~same)} mismatches"
+        # the sign of a zero result follows the sign of the scale
+        if code == 8:
+            assert np.array_equal(np.signbit(W[8, :]), np.signbit(scales))
+
+
+def test_dequant_special_cases():
+    s = np.array([[0.01, 0.0123, 3.0, 1000.0]], dtype=np.float16)
+    for code, factor in [(8, 0), (0, -8), (9, 1), (7, -1), (10, 2), (6, -2),
+                         (12, 4), (4, -4)]:
+        Bq = oracle.pack_codes(np.full((128, 4), code))
+        W = oracle.dequant(Bq, np.repeat(s, 1, axis=0), 128)
+        # multiplying by a power of two (or zero) is exact in float16
+        assert np.array_equal(W[0].astype(np.float64),
+                              factor * s[0].astype(np.float64))
+
+
+def test_dequant_group_index():
+    """Scale row ``k // group``: a different scale per group lands per group."""
+    K, N, g = 512, 16, 128
+    q = np.full((K, N), 9)                  # w = +1 * s
+    S = np.array([[1.0], [2.0], [4.0], [8.0]], dtype=np.float16) * \
+        np.arange(1, N + 1, dtype=np.float16)[None, :]
+    W = oracle.dequant(oracle.pack_codes(q), S.astype(np.float16), g)
+    for k in range(K):
+        assert np.array_equal(W[k], S[k // g])
+
+
+# ---------------------------------------------------------------------------
+# The matmul: brute force with exact rational sums on tiny shapes.
+# ---------------------------------------------------------------------------
+
+def _brute_force(A, Bq, S, group):
+    """Exact C (Fractions) from first principles, in pure Python."""
+    M, K = A.shape
+    N = Bq.shape[1]
+    w = [[0.0] * N for _ in range(K)]
+    for k in range(K):
+        for n in range(N):
+            code = (int(Bq[k // 8, n]) >> (4 * (k % 8))) & 0xF
+            w[k][n] = _fp16_struct((code - 8) * float(S[k // group, n]))
+    C = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        a = [Fraction(float(x)) for x in A[m]]
+        for n in range(N):
+            C[m][n] = sum((a[k] * Fraction(w[k][n]) for k in range(K)), Fraction(0))
+    return C
+
+
+@pytest.mark.parametrize("M,K,N,group,seed", [
+    (1, 128, 16, 128, 0), (3, 256, 32, 128, 1), (4, 256, 24, 256, 2),
+    (2, 384, 8, 128, 3),
+])
+def test_gemm_brute_force(M, K, N, group, seed):
+    A, Bq, S = make_inputs(M, K, N, group, seed)
+    C16, C64 = oracle.gemm(A, Bq, S, group)
+    exact = _brute_force(A, Bq, S, group)
+    absum = np.abs(A.astype(np.float64)) @ np.abs(oracle.dequant(Bq, S, group).astype(np.float64))
+    for m in range(M):
+        for n in range(N):
+            e = float(exact[m][n])
+            assert abs(C64[m, n] - e) <= 1e-13 * absum[m, n] + 1e-300
+            # C16 is the exact sum rounded once to float16
+            assert float(C16[m, n]) == _fp16_exact(exact[m][n])
+    C16_32, _ = oracle.gemm_f32(A, Bq, S, group)
+    diff = np.abs(C16_32.astype(np.float64) - C16.astype(np.float64))
+    assert diff.max() <= 5e-3 * np.abs(C64).max() + 2.0**-10
+
+
+def test_gemm_closed_forms():
+    """Values worked out by hand.
+
+    All-ones activations over one group of 128 with every code 9 give
+    ``C = 128 * fp16(s)``; code 7 gives the negative; code 8 gives 0.
+    """
+    s = np.float16(0.01)
+    S = np.full((1, 16), s, dtype=np.float16)
+    A = np.ones((2, 128), dtype=np.float16)
+    for word, expect in [(0x99999999, 128 * float(s)), (0x77777777, -128 * float(s)),
+                         (0x88888888, 0.0)]:
+        Bq = np.full((16, 16), word, dtype=np.uint32)
+        C16, C64 = oracle.gemm(A, Bq, S, 128)
+        assert np.all(C64 == expect)
+        assert np.all(C16.astype(np.float64) == expect)
+    # 128 * fp16(0.01) is exact: fp16(0.01) = 1311 * 2**-17
+    assert 128 * float(s) == 1311 * 2.0**-10
+
+
+def test_gemm_all_codes_eight_is_zero():
+    A, _, S = make_inputs(5, 512, 64, 128, seed=11)
+    Bq = np.full((64, 64), 0x88888888, dtype=np.uint32)
+    C16, C64 = oracle.gemm(A, Bq, S, 128)
+    assert not np.any(C64) and not np.any(C16.astype(np.float64))
+
+
+def test_gemm_one_hot_rows_select_weight_rows():
+    """``A[m] = 2**p * e_k`` gives ``C[m] = 2**p * W[k]`` bit for bit."""
+    K, N = 384, 48
+    _, Bq, S = make_inputs(1, K, N, 128, seed=5)
+    W = oracle.dequant(Bq, S, 128)
+    ks = [0, 1, 7, 8, 127, 128, 200, 383]
+    ps = [0, 0, 1, -1, 2, 0, -3, 0]
+    A = np.zeros((len(ks), K), dtype=np.float16)
+    for m, (k, p) in enumerate(zip(ks, ps)):
+        A[m, k] = np.float16(2.0**p)
+    C16, _ = oracle.gemm(A, Bq, S, 128)
+    for m, (k, p) in enumerate(zip(ks, ps)):
+        assert np.array_equal(C16[m], (W[k].astype(np.float64) * 2.0**p).astype(np.float16))
+
+
+def test_gemm_linear_in_activations():
+    """With integer activations every product and sum is exact in float64."""
+    rng = np.random.default_rng(3)
+    K, N = 256, 32
+    _, Bq, S = make_inputs(1, K, N, 128, seed=9)
+    A1 = rng.integers(-4, 5, size=(3, K)).astype(np.float16)
+    A2 = rng.integers(-4, 5, size=(3, K)).astype(np.float16)
+    _, C1 = oracle.gemm(A1, Bq, S, 128)
+    _, C2 = oracle.gemm(A2, Bq, S, 128)
+    _, C12 = oracle.gemm((A1 + A2).astype(np.float16), Bq, S, 128)
+    assert np.array_equal(C12, C1 + C2)
+    _, Cn = oracle.gemm((-A1).astype(np.float16), Bq, S, 128)
+    assert np.array_equal(Cn, -C1)
+
+
+def test_group_k_equals_replicated_group_128():
+    K, N = 512, 32
+    A, Bq, _ = make_inputs(4, K, N, 128, seed=21)
+    Sk = np.random.default_rng(1).uniform(0.005, 0.02, (1, N)).astype(np.float16)
+    _, Ck = oracle.gemm(A, Bq, Sk, K)
+    _, C128 = oracle.gemm(A, Bq, np.repeat(Sk, K // 128, axis=0), 128)
+    assert np.array_equal(Ck, C128)
+
+
+def test_gemm_rectangular_orientation():
+    """``A[M][K] . W[K][N]`` and not a transposed product: M != K != N."""
+    A, Bq, S = make_inputs(3, 256, 40, 128, seed=4)
+    C16, C64 = oracle.gemm(A, Bq, S, 128)
+    assert C64.shape == (3, 40)
+    exact = _brute_force(A[:1, :], Bq[:, :5], S[:, :5], 128)
+    assert np.allclose(C64[0, :5], [float(x) for x in exact[0]], rtol=1e-12, atol=0)
+
+
+def test_gemm_columns_matches_full():
+    A, Bq, S = make_inputs(6, 1024, 96, 128, seed=8)
+    _, C64 = oracle.gemm(A, Bq, S, 128, chunk=32)
+    cols = [0, 5, 31, 32, 64, 95]
+    assert np.array_equal(oracle.gemm_columns(A, Bq, S, 128, cols), C64[:, cols])
+
+
+# ---------------------------------------------------------------------------
+# The permuted layout.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (640, 48)])
+def test_repack_is_a_bijection(K, N):
+    rng = np.random.default_rng(K + N)
+    Bq = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+    Bp = oracle.repack(Bq)
+    assert Bp.dtype == np.uint32 and Bp.size == K * N // 8
+    assert np.array_equal(oracle.unrepack(Bp, K, N), Bq)
+    # a permutation of nibbles: the multiset of codes is unchanged
+    assert np.array_equal(np.sort(oracle.unpack_codes(Bq).ravel()),
+                          np.sort(oracle.unpack_codes(Bp.reshape(-1, 1)).ravel()))
+
+
+def _mfma16x16x32_model(a_frag, b_frag):
+    """The 16x16x32 FP16 matrix instruction, from its operand definition.
+
+    ``a_frag[l]`` holds A[row l % 16][k = 8 * (l // 16) + i], i = 0..7;
+    ``b_frag[l]`` holds B[k = 8 * (l // 16) + i][col l % 16].  Returns the
+    16 x 16 product in float64.
+    """
+    Am = np.zeros((16, 32))
+    Bm = np.zeros((32, 16))
+    for l in range(64):
+        for i in range(8):
+            Am[l % 16, 8 * (l // 16) + i] = a_frag[l][i]
+            Bm[8 * (l // 16) + i, l % 16] = b_frag[l][i]
+    return Am @ Bm
+
+
+def test_repack_feeds_the_matrix_instruction():
+    """Consume the permuted words the way a wave does and recover ``A . W``.
+
+    Each lane reads four consecutive words per 16-column block and 128-deep
+    block of K, splits each word into four 16-bit pairs by shifting by 4r and
+    masking ``0x000F000F`` (pair r = codes 2r, 2r+1), and feeds them to the
+    instruction model above, 32 K at a time.
+    """
+    M, K, N = 16, 256, 32
+    A, Bq, S = make_inputs(M, K, N, 128, seed=13)
+    Bp = oracle.repack(Bq).reshape(N // 16, K // 128, 64, 4)
+    Af = A.astype(np.float64)
+    C = np.zeros((M, N))
+    for n16 in range(N // 16):
+        for kb in range(K // 128):
+            for j in range(4):
+                k0 = 128 * kb + 32 * j
+                a_frag = [[Af[l % 16, k0 + 8 * (l // 16) + i] for i in range(8)]
+                          for l in range(64)]
+                b_frag = []
+                for l in range(64):
+                    word = int(Bp[n16, kb, l, j])
+                    s = float(S[kb, 16 * n16 + l % 16])
+                    vals = []
+                    for r in range(4):
+                        pair = (word >> (4 * r)) & 0x000F000F
+                        for code in (pair & 0xF, pair >> 16):
+                            vals.append(_fp16_struct((code - 8) * s))
+                    b_frag.append(vals)
+                C[:, 16 * n16:16 * n16 + 16] += _mfma16x16x32_model(a_frag, b_frag)
+    _, C64 = oracle.gemm(A, Bq, S, 128)
+    assert np.allclose(C, C64, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting against the pages' closed form.
+# ---------------------------------------------------------------------------
+
+def test_ideal_speedup_matches_byte_accounting():
+    from weight_only_int4_gemm_amd import roofline
+    vals = {}
+    with open(os.path.join(GOLDEN, "ideal_speedup.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                vals[line[0]] = float(line[1])
+    g = int(vals["group"])
+    K, N = 18432, 73728                     # the page's 72k x 18k layer
+    w4 = roofline.weight_bytes(K, N, g)
+    f16 = 2 * K * N
+    ratio = f16 / w4
+    assert math.floor(ratio * 100) / 100 == vals["ideal_speedup"]
+    # decode-sized activations barely move the ratio
+    assert abs(roofline.algorithmic_bytes(1, K, N, g) / w4 - 1) < 1e-3
