@@ -1,0 +1,172 @@
+/*
+ * w4a16.h -- C interface of libw4a16, a W4A16 matrix multiply for gfx950.
+ *
+ *   C[M x N] = A[M x K] . dequant(B)[K x N]
+ *
+ * A holds FP16 activations (tokens x in-features), B holds 4-bit weight codes
+ * q in 0..15 (in-features x out-features) with one FP16 scale s per group of
+ * `group` consecutive in-features per output column, the weight is
+ * w = (q - 8) * s, products accumulate in FP32 and C is FP16.
+ *
+ * What the operation is comes from the "Quant Marlin kernel" explainer
+ * (aicassindra.com): section "The architecture: every piece explained"
+ * (top row: eight 4-bit codes per 32-bit word, one FP16 scale per group,
+ * commonly 128; middle row: unpack to FP16, multiply by the group scale,
+ * matrix-multiply with FP32 accumulation, split-K with a global reduction;
+ * bottom rows: FP16 in, FP16 out, the permuted layout computed once offline)
+ * and section "End-to-end flow" (tokens x in-features times in-features x
+ * out-features).  The zero point 8, the nibble order and the scale layout
+ * are this library's readings where the pages leave them open.
+ *
+ * Conventions for every entry point:
+ *  - FP16 values are passed as uint16_t bit patterns, so callers need no HIP
+ *    or half-precision headers.  `stream` is a hipStream_t (NULL = the null
+ *    stream of the current device).
+ *  - Pointers marked "device" must point to memory of the current HIP device
+ *    and be 16-byte aligned.  The caller owns and allocates every buffer;
+ *    the library allocates nothing and keeps only a per-device cache of the
+ *    compute-unit count.
+ *  - Work is enqueued on `stream` and the call returns without waiting for
+ *    it.  Nothing is allocated and nothing is synchronised, so calls can be
+ *    captured into a HIP graph.
+ *  - Arguments are checked before anything is launched; on error nothing is
+ *    launched and a negative W4A16_ERR_* code is returned.  W4A16_ERR_LAUNCH
+ *    reports a failed kernel launch (hipGetLastError).  The library never
+ *    prints, aborts or throws.
+ *  - Buffers passed to one call must not overlap, except where stated.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w4a16_status {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = -1,      /* a required pointer is NULL                  */
+    W4A16_ERR_SHAPE = -2,     /* M, K or N out of range or not a multiple    */
+    W4A16_ERR_GROUP = -3,     /* group not a multiple of 128 dividing K      */
+    W4A16_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned            */
+    W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed       */
+    W4A16_ERR_LAUNCH = -6,    /* the kernel launch failed                    */
+    W4A16_ERR_DEVICE = -7     /* no usable current HIP device                */
+};
+
+/* Version of the permuted layout written by w4a16_repack.  Callers that
+ * store permuted weights should store this number with them: weights
+ * permuted for one layout cannot be fed to another without repacking. */
+int w4a16_layout_version(void);
+
+/* Static, NUL-terminated name of a status code ("W4A16_OK", ...). */
+const char* w4a16_status_string(int status);
+
+/* Bytes of the permuted weights for a K x N matrix: K * N / 2. */
+size_t w4a16_packed_bytes(int K, int N);
+
+/* Writes into buf (at most len bytes, NUL-terminated) a one-line
+ * description of how w4a16_gemm would run this shape on the current device:
+ * the kernel variant, grid, splits and workspace bytes, for example
+ *   "gemm_kernel<1,4,4> grid=64x1x4 block=256 splits=4 workspace=1048832".
+ * Returns W4A16_OK, W4A16_ERR_NULL (buf NULL or len 0), W4A16_ERR_SHAPE /
+ * W4A16_ERR_GROUP (a shape w4a16_gemm rejects, or M or N zero) or
+ * W4A16_ERR_DEVICE.  Launches nothing. */
+int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len);
+
+/*
+ * w4a16_repack -- offline permutation of canonical codes into the layout
+ * the GEMM reads.
+ *
+ * The pages: weights are pre-permuted once, offline, so that one wide load
+ * hands every thread exactly the operand fragment of the matrix instruction
+ * ("Quant Marlin kernel" explainer, the paragraph on the permuted weight
+ * layout; "Low-Precision Quantization Kernels in Production", section 1,
+ * mechanism 1).  The order here is this library's own, for the gfx950
+ * 16x16x32 FP16 matrix instruction.
+ *
+ * Bq      (device, read)  canonical codes, uint32[K/8][N] row-major; code k
+ *                         of column n is bits 4*(k%8) .. 4*(k%8)+3 of word
+ *                         Bq[k/8][n] (least significant nibble first).
+ * Bpacked (device, write) w4a16_packed_bytes(K, N) bytes, layout version 1:
+ *                         code (k, n) is in word
+ *                           ((n/16 * K/128 + k/128) * 64 + lane) * 4 + (k%128)/32
+ *                         with lane = n%16 + 16*((k%32)/8), at nibble
+ *                         {0,4,1,5,2,6,3,7}[k%8].  Callers treat it as opaque.
+ * K, N    K a positive multiple of 128, N a positive multiple of 16.
+ * Errors: NULL pointer, bad shape, misalignment, Bq and Bpacked overlapping
+ *         (W4A16_ERR_SHAPE).
+ */
+int w4a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N,
+                 void* stream);
+
+/*
+ * w4a16_workspace_bytes -- bytes of split-K workspace w4a16_gemm needs for
+ * this shape (FP32 partial tiles plus one arrival counter per output tile).
+ * 0 means the call needs no workspace.  Returns 0 for shapes w4a16_gemm
+ * rejects.
+ *
+ * Contract: the caller allocates at least this many bytes and fills them
+ * with zeros once, after allocating.  Every call leaves the counters at zero
+ * again, so one workspace serves any number of later calls of any shape
+ * whose requirement it covers, as long as those calls are ordered (same
+ * stream, or synchronised).  Two calls running at the same time must not
+ * share a workspace.
+ */
+size_t w4a16_workspace_bytes(int M, int K, int N, int group);
+
+/*
+ * w4a16_gemm -- C = A . dequant(Bpacked, scales).
+ *
+ * Split-K and its reduction: the pages split the in-feature dimension over
+ * several workgroups, each computing a partial sum, combined by a global
+ * reduction ("Quant Marlin kernel" explainer, middle row and "End-to-end
+ * flow"); the combination here is deterministic ("Low-Precision Quantization
+ * Kernels in Production", section 3, mechanism 1): FP32 partials are added
+ * in a fixed order, so equal inputs give bit-identical C on every run.
+ *
+ * A         (device, read)  FP16 [M][K] row-major.
+ * Bpacked   (device, read)  output of w4a16_repack for (K, N).
+ * scales    (device, read)  FP16 [K/group][N] row-major.
+ * C         (device, write) FP16 [M][N] row-major.  Rows are written only
+ *                           for m < M; A is read only for m < M.
+ * M         >= 0; M == 0 returns W4A16_OK and launches nothing.
+ * K         positive multiple of 128.
+ * N         multiple of 16, >= 0; N == 0 returns W4A16_OK.
+ * group     multiple of 128 that divides K (128 = per-128 groups; K = one
+ *           scale per output column).
+ * workspace (device, read/write) see w4a16_workspace_bytes; may be NULL
+ *           only when that returns 0 for this shape.
+ * Numerics: each weight is rounded once to FP16 from the exact (q-8)*s,
+ *           products accumulate in FP32, C is rounded once to FP16
+ *           (round to nearest even; overflow gives +-inf).
+ * Errors:   W4A16_ERR_NULL, _SHAPE, _GROUP, _ALIGN, _WORKSPACE, _DEVICE,
+ *           _LAUNCH.  C must not overlap A, Bpacked, scales or workspace.
+ */
+int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked,
+               const uint16_t* scales, uint16_t* C, int M, int K, int N,
+               int group, void* workspace, void* stream);
+
+/*
+ * w4a16_dequant_debug -- W = dequant(Bpacked, scales), written out.
+ *
+ * Uses the same device unpack-and-scale routine as w4a16_gemm, so it shows
+ * bit for bit the FP16 weights the GEMM multiplies ("Quant Marlin kernel"
+ * explainer, middle row: codes to FP16, times the group scale).
+ *
+ * Bpacked (device, read)  output of w4a16_repack for (K, N).
+ * scales  (device, read)  FP16 [K/group][N].
+ * W       (device, write) FP16 [K][N] row-major,
+ *                         W[k][n] = fp16_rne((q[k][n] - 8) * s[k/group][n]).
+ * Errors: as w4a16_gemm.
+ */
+int w4a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales,
+                        uint16_t* W, int K, int N, int group, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

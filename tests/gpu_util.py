@@ -1,0 +1,53 @@
+"""Helpers for the GPU tests: move seeded inputs to the device and run the
+library through its C interface."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import weight_only_int4_gemm_amd as w4
+
+
+def say(*args):
+    """Name the case before a GPU step, flushed, so a failure can be placed."""
+    print("[gpu]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x: np.ndarray):
+    import torch
+    if x.dtype == np.uint32:
+        x = x.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host_u32(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def host_f16(t) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def repack_on_device(Bq_d, K: int, N: int):
+    Bp = w4.alloc_packed(K, N)
+    w4.w4a16_repack(Bq_d, Bp, K, N)
+    return Bp
+
+
+def run_gemm(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int,
+             workspace=None, Bp=None):
+    """C (numpy float16) = the library's product on the given host inputs."""
+    import torch
+    M, K = A.shape
+    N = Bq.shape[1]
+    if Bp is None:
+        Bp = repack_on_device(dev(Bq), K, N)
+    A_d, S_d = dev(A), dev(S)
+    C_d = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    ws = workspace if workspace is not None else w4.alloc_workspace(M, K, N, group)
+    w4.w4a16_gemm(A_d, Bp, S_d, C_d, M, K, N, group, ws)
+    torch.cuda.synchronize()
+    return host_f16(C_d)

@@ -1,0 +1,135 @@
+"""The C interface on the CPU: the library loads, exports what the header
+declares, and rejects bad arguments before touching the device.
+
+Only host logic is called here (argument checks that return before any HIP
+call, and pure helpers); no kernel runs.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_int4_gemm_amd as w4
+from weight_only_int4_gemm_amd import roofline
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN = 0, -1, -2, -3, -4
+
+# Fake, 16-byte aligned addresses: the checks below return before any of
+# them is dereferenced or handed to the runtime.
+P_A, P_B, P_S, P_C, P_W = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w4.load()
+
+
+def test_header_declares_the_interface():
+    names = _declared_functions()
+    assert names == sorted(w4.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_binding_has_the_same_names():
+    for name in _declared_functions():
+        assert callable(getattr(w4, name)), name
+
+
+def test_pure_helpers(lib):
+    assert w4.w4a16_layout_version() == 1
+    assert w4.w4a16_status_string(0) == "W4A16_OK"
+    assert w4.w4a16_status_string(-5) == "W4A16_ERR_WORKSPACE"
+    assert w4.w4a16_status_string(123) == "W4A16_ERR_UNKNOWN"
+    assert w4.w4a16_packed_bytes(4096, 4096) == 4096 * 4096 // 2
+    assert w4.w4a16_packed_bytes(0, 16) == 0
+
+
+def test_layout_version_matches_the_oracle_description():
+    import oracle
+    assert w4.w4a16_layout_version() == oracle.LAYOUT_VERSION
+
+
+@pytest.mark.parametrize("K,N,group,expect", [
+    (100, 64, 128, ERR_SHAPE),      # K not a multiple of 128
+    (0, 64, 128, ERR_SHAPE),
+    (-128, 64, 128, ERR_SHAPE),
+    (256, 24, 128, ERR_SHAPE),      # N not a multiple of 16
+    (256, -16, 128, ERR_SHAPE),
+    (256, 64, 64, ERR_GROUP),       # group not a multiple of 128
+    (384, 64, 256, ERR_GROUP),      # group does not divide K
+    (256, 64, 0, ERR_GROUP),
+])
+def test_gemm_rejects_bad_shapes(lib, K, N, group, expect):
+    rc = lib.w4a16_gemm(P_A, P_B, P_S, P_C, 4, K, N, group, None, None)
+    assert rc == expect
+
+
+def test_gemm_rejects_bad_pointers(lib):
+    assert lib.w4a16_gemm(None, P_B, P_S, P_C, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert lib.w4a16_gemm(P_A, None, P_S, P_C, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert lib.w4a16_gemm(P_A, P_B, None, P_C, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert lib.w4a16_gemm(P_A, P_B, P_S, None, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert lib.w4a16_gemm(P_A + 8, P_B, P_S, P_C, 4, 256, 64, 128, None, None) == ERR_ALIGN
+    assert lib.w4a16_gemm(P_A, P_B, P_S, P_C + 2, 4, 256, 64, 128, None, None) == ERR_ALIGN
+    assert lib.w4a16_gemm(P_A, P_B, P_S, P_C, -1, 256, 64, 128, None, None) == ERR_SHAPE
+    # C overlapping an input
+    assert lib.w4a16_gemm(P_A, P_B, P_S, P_A, 4, 256, 64, 128, None, None) == ERR_SHAPE
+
+
+def test_gemm_empty_output_is_a_no_op(lib):
+    # M == 0 or N == 0: nothing to compute, nothing launched, NULLs allowed
+    assert lib.w4a16_gemm(None, None, None, None, 0, 256, 64, 128, None, None) == OK
+    assert lib.w4a16_gemm(None, None, None, None, 5, 256, 0, 128, None, None) == OK
+
+
+def test_repack_and_dequant_reject_bad_arguments(lib):
+    assert lib.w4a16_repack(None, P_B, 256, 64, None) == ERR_NULL
+    assert lib.w4a16_repack(P_A, P_B, 200, 64, None) == ERR_SHAPE
+    assert lib.w4a16_repack(P_A, P_B, 256, 8, None) == ERR_SHAPE
+    assert lib.w4a16_repack(P_A + 4, P_B, 256, 64, None) == ERR_ALIGN
+    assert lib.w4a16_repack(P_A, P_A + 16, 256, 64, None) == ERR_SHAPE   # overlap
+    assert lib.w4a16_dequant_debug(None, P_S, P_W, 256, 64, 128, None) == ERR_NULL
+    assert lib.w4a16_dequant_debug(P_B, P_S, P_W, 256, 64, 96, None) == ERR_GROUP
+    assert lib.w4a16_dequant_debug(P_B, P_S, P_W, 256, 0, 128, None) == ERR_SHAPE
+    assert lib.w4a16_dequant_debug(P_B, P_S + 2, P_W, 256, 64, 128, None) == ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setenv("W4A16_LIBRARY", str(tmp_path / "missing.so"))
+    mod = importlib.reload(w4)
+    try:
+        with pytest.raises(w4.LibraryNotBuilt):
+            mod.load()
+    finally:
+        monkeypatch.delenv("W4A16_LIBRARY")
+        importlib.reload(w4)
+
+
+def test_roofline_accounting():
+    # configs: 4096 x 4096, group 128, M = 16 moves 8.91 MB
+    assert roofline.algorithmic_bytes(16, 4096, 4096, 128) == 8388608 + 262144 + 131072 + 131072
+    assert roofline.flops(16, 4096, 4096) == 2 * 16 * 4096 * 4096
+    assert roofline.bound(16, 4096, 4096, 128) == "hbm"
+    assert roofline.bound(1024, 8192, 28672, 128) == "mfma"
+    # the ridge between the two peaks sits near M = 80 for weight-dominated shapes
+    assert roofline.bound(64, 18432, 73728, 128) == "hbm"
+    assert roofline.bound(128, 18432, 73728, 128) == "mfma"

@@ -1,1 +1,203 @@
-"""MI355X-native W4A16 matmul (placeholder, filled in below)."""
+"""MI355X-native W4A16 matmul: Python binding of libw4a16.so.
+
+The binding only marshals arguments: every step of the computation runs in
+the library's HIP kernels.  torch provides device memory and the current
+stream.  The functions carry the C interface's names (include/w4a16.h):
+
+    w4a16_repack(Bq, Bpacked, K, N, stream=None)
+    w4a16_gemm(A, Bpacked, scales, C, M, K, N, group, workspace, stream=None)
+    w4a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
+    w4a16_workspace_bytes(M, K, N, group)
+    w4a16_packed_bytes(K, N)
+    w4a16_layout_version()
+    w4a16_status_string(status)
+
+A missing library is an error (``LibraryNotBuilt``); there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "W4A16Error", "LibraryNotBuilt", "library_path", "load",
+    "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
+    "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
+    "w4a16_status_string", "w4a16_describe", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libw4a16.so"
+
+# Status codes of include/w4a16.h.
+W4A16_OK = 0
+
+EXPORTED_SYMBOLS = (
+    "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
+    "w4a16_workspace_bytes", "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
+    "w4a16_describe",
+)
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, fn: str, status: int, name: str):
+        super().__init__(f"{fn} failed: {name} ({status})")
+        self.status = status
+        self.name = name
+
+
+def library_path() -> str:
+    return os.environ.get("W4A16_LIBRARY", os.path.join(_PKG, _LIB_NAME))
+
+
+_lib = None
+
+
+def load():
+    """Load libw4a16.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise LibraryNotBuilt(
+            f"{path} not found; build it with `python -m weight_only_int4_gemm_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.w4a16_layout_version.argtypes = []
+    lib.w4a16_layout_version.restype = i
+    lib.w4a16_status_string.argtypes = [i]
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    lib.w4a16_packed_bytes.argtypes = [i, i]
+    lib.w4a16_packed_bytes.restype = sz
+    lib.w4a16_workspace_bytes.argtypes = [i, i, i, i]
+    lib.w4a16_workspace_bytes.restype = sz
+    lib.w4a16_repack.argtypes = [vp, vp, i, i, vp]
+    lib.w4a16_repack.restype = i
+    lib.w4a16_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp]
+    lib.w4a16_gemm.restype = i
+    lib.w4a16_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.w4a16_dequant_debug.restype = i
+    lib.w4a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
+    lib.w4a16_describe.restype = i
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    """Device address of a tensor (or None / a raw int address)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != W4A16_OK:
+        raise W4A16Error(fn, status, w4a16_status_string(status))
+
+
+def _expect(t, dtype, what):
+    if t is None or isinstance(t, int):
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a device tensor")
+
+
+# ---------------------------------------------------------------------------
+# the C interface, name for name
+# ---------------------------------------------------------------------------
+
+def w4a16_layout_version() -> int:
+    return load().w4a16_layout_version()
+
+
+def w4a16_status_string(status: int) -> str:
+    return load().w4a16_status_string(int(status)).decode()
+
+
+def w4a16_packed_bytes(K: int, N: int) -> int:
+    return load().w4a16_packed_bytes(int(K), int(N))
+
+
+def w4a16_workspace_bytes(M: int, K: int, N: int, group: int) -> int:
+    return load().w4a16_workspace_bytes(int(M), int(K), int(N), int(group))
+
+
+def w4a16_describe(M: int, K: int, N: int, group: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check("w4a16_describe", load().w4a16_describe(int(M), int(K), int(N), int(group), buf, 256))
+    return buf.value.decode()
+
+
+def w4a16_repack(Bq, Bpacked, K: int, N: int, stream=None) -> None:
+    import torch
+    _expect(Bq, torch.int32, "Bq")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _check("w4a16_repack", load().w4a16_repack(_ptr(Bq), _ptr(Bpacked), int(K), int(N),
+                                               _stream(stream)))
+
+
+def w4a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
+               workspace=None, stream=None) -> None:
+    import torch
+    _expect(A, torch.float16, "A")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(C, torch.float16, "C")
+    _check("w4a16_gemm", load().w4a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
+                                           int(M), int(K), int(N), int(group),
+                                           _ptr(workspace), _stream(stream)))
+
+
+def w4a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,
+                        stream=None) -> None:
+    import torch
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(W, torch.float16, "W")
+    _check("w4a16_dequant_debug",
+           load().w4a16_dequant_debug(_ptr(Bpacked), _ptr(scales), _ptr(W), int(K), int(N),
+                                      int(group), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# allocation conveniences (torch owns the memory; the library allocates none)
+# ---------------------------------------------------------------------------
+
+def alloc_workspace(M: int, K: int, N: int, group: int, device=None):
+    """A zero-filled workspace of ``w4a16_workspace_bytes`` bytes, or None."""
+    import torch
+    nbytes = w4a16_workspace_bytes(M, K, N, group)
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+def alloc_packed(K: int, N: int, device=None):
+    """An int32 tensor of ``w4a16_packed_bytes(K, N)`` bytes for repacked codes."""
+    import torch
+    return torch.empty(K * N // 8, dtype=torch.int32, device=device or "cuda")

@@ -1,0 +1,226 @@
+// The C interface (include/w4a16.h): argument checks, the work plan and the
+// launches.  Nothing here allocates, prints or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/w4a16.h"
+#include "internal.hpp"
+#include "layout.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not yet queried
+
+// Compute units of the current device, cached per device.  Returns <= 0 on
+// failure.
+int current_cus(int* device_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (device_out) *device_out = dev;
+  if (dev >= kMaxDevices) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return -1;
+    return cus;
+  }
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Shapes every entry point that reads permuted weights accepts.
+int check_kn(int K, int N, bool allow_empty_n) {
+  if (K <= 0 || K % kBlockK) return W4A16_ERR_SHAPE;
+  if (N < 0 || N % kBlockN || (!allow_empty_n && N == 0)) return W4A16_ERR_SHAPE;
+  // the packed buffer is addressed in 32-bit words by 64-bit offsets; keep
+  // K*N within what the row-major FP16 W and the scales can index
+  if ((int64_t)K * N > ((int64_t)1 << 40)) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+int check_group(int K, int group) {
+  if (group <= 0 || group % kBlockK || K % group) return W4A16_ERR_GROUP;
+  return W4A16_OK;
+}
+
+// Test and tuning override: W4A16_FORCE_PLAN="mb,nb,wk,splits" replaces the
+// heuristic's choice when it names a compiled variant (a field <= 0 keeps
+// the heuristic's value).  It feeds the same kernels; w4a16_workspace_bytes
+// sees it too, so sizes stay consistent within a process.
+void apply_forced_plan(Plan* p, int KB) {
+  const char* env = std::getenv("W4A16_FORCE_PLAN");
+  if (!env || !*env) return;
+  int mb = 0, nb = 0, wk = 0, splits = 0;
+  if (std::sscanf(env, "%d,%d,%d,%d", &mb, &nb, &wk, &splits) != 4) return;
+  Plan q = *p;
+  if (mb > 0) q.mb = mb;
+  if (nb > 0) q.nb = nb;
+  if (wk > 0) q.wk = wk;
+  if (splits > 0) q.splits = splits > KB ? KB : splits;
+  if (!plan_is_compiled(q.mb, q.nb, q.wk)) return;
+  *p = q;
+}
+
+}  // namespace
+
+Plan make_plan(int M, int K, int N, int group, int cus) {
+  (void)group;
+  Plan p{};
+  p.mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  p.nb = 4;
+  p.wk = 4;
+  const int n16 = N / kBlockN;
+  p.tiles_n = (n16 + p.nb - 1) / p.nb;
+  p.tiles_m = (M + 16 * p.mb - 1) / (16 * p.mb);
+  const int KB = K / kBlockK;
+  const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
+  // Aim for two workgroups per compute unit, keeping at least two 128-deep
+  // K blocks per wave.
+  const int64_t target = 2 * (int64_t)(cus > 0 ? cus : 256);
+  int64_t want = (target + tiles - 1) / tiles;
+  int64_t cap = KB / (2 * p.wk);
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want > 64) want = 64;
+  p.splits = (int)(want < 1 ? 1 : want);
+  apply_forced_plan(&p, KB);
+  p.tiles_n = (n16 + p.nb - 1) / p.nb;
+  p.tiles_m = (M + 16 * p.mb - 1) / (16 * p.mb);
+  const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
+  p.workspace_bytes = 0;
+  if (p.splits > 1) {
+    p.workspace_bytes = counters_bytes((int)ftiles) +
+                        (size_t)ftiles * p.splits * (16 * p.mb) * (16 * p.nb) * sizeof(float);
+  }
+  return p;
+}
+
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+int w4a16_layout_version(void) { return kLayoutVersion; }
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "W4A16_OK";
+    case W4A16_ERR_NULL: return "W4A16_ERR_NULL";
+    case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE";
+    case W4A16_ERR_GROUP: return "W4A16_ERR_GROUP";
+    case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN";
+    case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE";
+    case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH";
+    case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE";
+    default: return "W4A16_ERR_UNKNOWN";
+  }
+}
+
+size_t w4a16_packed_bytes(int K, int N) {
+  if (K <= 0 || N <= 0) return 0;
+  return (size_t)K * (size_t)N / 2;
+}
+
+size_t w4a16_workspace_bytes(int M, int K, int N, int group) {
+  if (M <= 0 || N == 0) return 0;
+  if (check_kn(K, N, false) != W4A16_OK || check_group(K, group) != W4A16_OK) return 0;
+  const int cus = current_cus(nullptr);
+  if (cus <= 0) return 0;
+  return make_plan(M, K, N, group, cus).workspace_bytes;
+}
+
+int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
+  if (!buf || len == 0) return W4A16_ERR_NULL;
+  buf[0] = 0;
+  if (M <= 0 || N == 0) return W4A16_ERR_SHAPE;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  const int cus = current_cus(nullptr);
+  if (cus <= 0) return W4A16_ERR_DEVICE;
+  const Plan p = make_plan(M, K, N, group, cus);
+  std::snprintf(buf, len, "gemm_kernel<%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                p.mb, p.nb, p.wk, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk, p.splits,
+                p.workspace_bytes);
+  return W4A16_OK;
+}
+
+int w4a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N, void* stream) {
+  if (!Bq || !Bpacked) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bq) || !aligned16(Bpacked)) return W4A16_ERR_ALIGN;
+  const size_t bytes = w4a16_packed_bytes(K, N);
+  if (overlap(Bq, bytes, Bpacked, bytes)) return W4A16_ERR_SHAPE;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  if (launch_repack(Bq, Bpacked, K, N, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+int w4a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_t* W,
+                        int K, int N, int group, void* stream) {
+  if (!Bpacked || !scales || !W) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bpacked) || !aligned16(scales) || !aligned16(W)) return W4A16_ERR_ALIGN;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  if (launch_dequant(Bpacked, scales, W, K, N, group, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+               uint16_t* C, int M, int K, int N, int group, void* workspace,
+               void* stream) {
+  if (M < 0) return W4A16_ERR_SHAPE;
+  int rc = check_kn(K, N, true);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  if (M == 0 || N == 0) return W4A16_OK;  // empty output: nothing to do
+  if (!A || !Bpacked || !scales || !C) return W4A16_ERR_NULL;
+  if (!aligned16(A) || !aligned16(Bpacked) || !aligned16(scales) || !aligned16(C))
+    return W4A16_ERR_ALIGN;
+  const size_t cbytes = (size_t)M * N * 2;
+  if (overlap(C, cbytes, A, (size_t)M * K * 2) ||
+      overlap(C, cbytes, Bpacked, w4a16_packed_bytes(K, N)) ||
+      overlap(C, cbytes, scales, (size_t)(K / group) * N * 2))
+    return W4A16_ERR_SHAPE;
+  const int cus = current_cus(nullptr);
+  if (cus <= 0) return W4A16_ERR_DEVICE;
+  const Plan plan = make_plan(M, K, N, group, cus);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace) return W4A16_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+    if (overlap(C, cbytes, workspace, plan.workspace_bytes)) return W4A16_ERR_SHAPE;
+  }
+  if (launch_gemm(plan, A, Bpacked, scales, C, M, K, N, group, workspace,
+                  static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+}  // extern "C"

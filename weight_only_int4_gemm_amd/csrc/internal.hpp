@@ -1,0 +1,41 @@
+// Declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// How one w4a16_gemm call is cut into work.
+//  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
+//  nb     16-column blocks per wave (the workgroup's N tile is 16 * nb)
+//  wk     waves per workgroup, each taking every wk-th 128-deep K block of
+//         the workgroup's K range; their sums are added in wave order
+//  splits K ranges per output tile, one workgroup each; their FP32 partials
+//         go through the workspace and are added in split order
+struct Plan {
+  int mb, nb, wk, splits;
+  int tiles_n, tiles_m;
+  size_t workspace_bytes;  // 0 when splits == 1
+};
+
+Plan make_plan(int M, int K, int N, int group, int cus);
+bool plan_is_compiled(int mb, int nb, int wk);
+
+hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
+                         hipStream_t stream);
+hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
+                          int K, int N, int group, hipStream_t stream);
+hipError_t launch_gemm(const Plan& plan, const uint16_t* A, const uint32_t* Bp,
+                       const uint16_t* S, uint16_t* C, int M, int K, int N,
+                       int group, void* workspace, hipStream_t stream);
+
+// Workspace layout for a plan with splits > 1: one 32-bit arrival counter
+// per output tile (padded to 256 bytes), then FP32 partial tiles
+// [tile][split][16*mb rows][16*nb cols].
+inline size_t counters_bytes(int tiles) {
+  return ((size_t)tiles * 4 + 255) / 256 * 256;
+}
+
+}  // namespace w4a16

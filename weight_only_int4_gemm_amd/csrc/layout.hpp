@@ -1,0 +1,49 @@
+// Index arithmetic of the permuted weight layout (version 1).
+//
+// The unit of the layout is a "fragment block": 16 output columns by 128
+// in-features, 2048 codes, 1 KiB, 256 words.  Lane l (0..63) of a wave owns
+// the four consecutive words 4l .. 4l+3 of a block.  Word j of lane l feeds
+// the B operand of the j-th 32-deep step of the gfx950 16x16x32 FP16 matrix
+// instruction: column l % 16, in-features 32j + 8*(l/16) + i for i = 0..7.
+//
+// Blocks are ordered column-block major, then along K:
+//     block(n16, kb) = n16 * (K / 128) + kb
+// so the blocks one column block streams along K are contiguous.
+//
+// Inside a word, code i of the fragment (i = 0..7 along K) sits at nibble
+// kNibbleOfCode[i] = {0,4,1,5,2,6,3,7}[i]: shifting the word right by 4r and
+// masking 0x000F000F leaves codes 2r and 2r+1 in the low and high 16-bit
+// halves, the order the matrix instruction takes its FP16 pairs in.
+#pragma once
+
+#include <stdint.h>
+
+namespace w4a16 {
+
+constexpr int kLayoutVersion = 1;
+constexpr int kBlockK = 128;        // in-features per fragment block
+constexpr int kBlockN = 16;         // output columns per fragment block
+constexpr int kWordsPerLane = 4;    // one 16-byte load per lane per block
+constexpr int kWordsPerBlock = 256;
+
+__host__ __device__ inline int nibble_of_code(int i) {
+  // {0,4,1,5,2,6,3,7}: even codes to nibbles 0..3, odd codes to nibbles 4..7
+  return (i >> 1) + ((i & 1) << 2);
+}
+
+// Word offset of fragment block (n16, kb).
+__host__ __device__ inline int64_t block_word_offset(int n16, int kb, int K) {
+  return ((int64_t)n16 * (K / kBlockK) + kb) * kWordsPerBlock;
+}
+
+// Word offset (within the whole buffer) that holds the eight codes
+// k0 .. k0+7 of column n, for k0 a multiple of 8.
+__host__ __device__ inline int64_t packed_word_of(int k0, int n, int K) {
+  const int n16 = n / kBlockN;
+  const int kb = k0 / kBlockK;
+  const int j = (k0 % kBlockK) / 32;
+  const int lane = (n % kBlockN) + kBlockN * ((k0 % 32) / 8);
+  return block_word_offset(n16, kb, K) + lane * kWordsPerLane + j;
+}
+
+}  // namespace w4a16
