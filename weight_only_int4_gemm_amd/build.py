@@ -31,6 +31,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # no packed FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep the kernels' per-lane arrays (register slots, pointers) out of LDS;
+    # once the loops are unrolled they are plain registers
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-I", os.path.join(ROOT, "include"),
 ]
 

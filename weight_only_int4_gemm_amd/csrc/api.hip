@@ -49,9 +49,11 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 int check_kn(int K, int N, bool allow_empty_n) {
   if (K <= 0 || K % kBlockK) return W4A16_ERR_SHAPE;
   if (N < 0 || N % kBlockN || (!allow_empty_n && N == 0)) return W4A16_ERR_SHAPE;
-  // the packed buffer is addressed in 32-bit words by 64-bit offsets; keep
-  // K*N within what the row-major FP16 W and the scales can index
-  if ((int64_t)K * N > ((int64_t)1 << 40)) return W4A16_ERR_SHAPE;
+  // the kernels index one column block's K blocks, and divide a K-block
+  // index by the group, in 32-bit arithmetic: K < 2^23 keeps both exact
+  if (K >= (1 << 23)) return W4A16_ERR_SHAPE;
+  // scale offsets (row * N + column) are 32-bit as well
+  if ((int64_t)(K / kBlockK) * N >= ((int64_t)1 << 31)) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
 
@@ -60,39 +62,68 @@ int check_group(int K, int group) {
   return W4A16_OK;
 }
 
-// Test and tuning override: W4A16_FORCE_PLAN="mb,nb,wk,splits" replaces the
-// heuristic's choice when it names a compiled variant (a field <= 0 keeps
-// the heuristic's value).  It feeds the same kernels; w4a16_workspace_bytes
-// sees it too, so sizes stay consistent within a process.
+// Test and tuning override: W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth]"
+// replaces the heuristic's choice when it names a compiled variant (a field
+// <= 0 keeps the heuristic's value).  It feeds the same kernels;
+// w4a16_workspace_bytes sees it too, so sizes stay consistent within a
+// process.
 void apply_forced_plan(Plan* p, int KB) {
   const char* env = std::getenv("W4A16_FORCE_PLAN");
   if (!env || !*env) return;
-  int mb = 0, nb = 0, wk = 0, splits = 0;
-  if (std::sscanf(env, "%d,%d,%d,%d", &mb, &nb, &wk, &splits) != 4) return;
+  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0;
+  if (std::sscanf(env, "%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth) < 4) return;
   Plan q = *p;
   if (mb > 0) q.mb = mb;
   if (nb > 0) q.nb = nb;
   if (wk > 0) q.wk = wk;
   if (splits > 0) q.splits = splits > KB ? KB : splits;
-  if (!plan_is_compiled(q.mb, q.nb, q.wk)) return;
+  if (depth > 0) q.depth = depth;
+  if (!plan_is_compiled(q.mb, q.nb, q.wk, q.depth)) {
+    // keep the forced tile but take the first compiled depth for it
+    for (int d : {4, 2, 1}) {
+      if (plan_is_compiled(q.mb, q.nb, q.wk, d)) {
+        q.depth = d;
+        break;
+      }
+    }
+    if (!plan_is_compiled(q.mb, q.nb, q.wk, q.depth)) return;
+  }
   *p = q;
 }
 
 }  // namespace
 
+// The heuristic.  Small batches (M <= 32) stream the weights: one or two
+// 16-row blocks per wave, narrow column tiles so that there are enough
+// workgroups, eight waves per workgroup splitting K, and up to four K blocks
+// in flight per wave.  Larger batches take 64 or 128 rows per wave, so each
+// weight is unpacked once for many rows.  K is split across workgroups only
+// as far as needed to give every compute unit about two workgroups, keeping
+// at least two K blocks per wave.
 Plan make_plan(int M, int K, int N, int group, int cus) {
   (void)group;
   Plan p{};
-  p.mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  p.nb = 4;
-  p.wk = 4;
   const int n16 = N / kBlockN;
+  const int KB = K / kBlockK;
+  if (M <= 16) {
+    p.mb = 1;
+    p.nb = M <= 4 ? 1 : 2;
+    p.wk = 8;
+    p.depth = 4;
+  } else if (M <= 32) {
+    p.mb = 2;
+    p.nb = 2;
+    p.wk = 4;
+    p.depth = 2;
+  } else {
+    p.mb = M <= 64 ? 4 : 8;
+    p.nb = 4;
+    p.wk = 4;
+    p.depth = 1;
+  }
   p.tiles_n = (n16 + p.nb - 1) / p.nb;
   p.tiles_m = (M + 16 * p.mb - 1) / (16 * p.mb);
-  const int KB = K / kBlockK;
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-  // Aim for two workgroups per compute unit, keeping at least two 128-deep
-  // K blocks per wave.
   const int64_t target = 2 * (int64_t)(cus > 0 ? cus : 256);
   int64_t want = (target + tiles - 1) / tiles;
   int64_t cap = KB / (2 * p.wk);
@@ -158,9 +189,10 @@ int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan p = make_plan(M, K, N, group, cus);
-  std::snprintf(buf, len, "gemm_kernel<%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
-                p.mb, p.nb, p.wk, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk, p.splits,
-                p.workspace_bytes);
+  std::snprintf(buf, len,
+                "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
+                p.splits, p.workspace_bytes);
   return W4A16_OK;
 }
 

@@ -8,18 +8,28 @@
 //  * the WK waves of a workgroup share its tile and its K range and take its
 //    128-deep K blocks round-robin; their FP32 sums are added in wave order
 //    through LDS;
-//  * with splits > 1 each workgroup stores its FP32 partial tile in the
+//  * with splits > 1 each workgroup publishes its FP32 partial tile in the
 //    workspace, and the last of a tile's workgroups to arrive (an atomic
 //    counter per tile) adds the partials in split order 0, 1, ..., writes
 //    the FP16 tile and sets the counter back to zero.  The order of every
 //    addition is fixed, so results are bit-identical from run to run.
+//
+// The hand-off between workgroups uses device-scope relaxed atomic stores
+// and loads for the partials (they write through to, and read from, the
+// device coherence point, whichever XCD's L2 a workgroup runs behind), a
+// wait for those stores to complete before the arrival count, and no
+// device-wide fence: a device-scope fence writes back and invalidates the
+// whole L2 of the XCD, which, done by hundreds of workgroups in flight,
+// throws away the weights and activations other workgroups are streaming.
 //
 // Per 128-deep K block a wave issues, for each of its NB column blocks, one
 // 16-byte load per lane of permuted codes (the lane's own operand fragments
 // for four 32-deep steps) and one scale load; it unpacks each word in
 // registers (unpack.hpp) and issues 16x16x32 FP16 matrix instructions against
 // activation fragments read straight from global memory (16 bytes per lane
-// per 16-row block and 32-deep step).
+// per 16-row block and 32-deep step).  Loads run one step ahead of the
+// matrix instructions: the codes of the next K block and the activations of
+// the next 32-deep step are in flight while the current ones are consumed.
 #include "internal.hpp"
 #include "layout.hpp"
 #include "unpack.hpp"
@@ -27,12 +37,20 @@
 namespace w4a16 {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-template <int MB, int NB, int WK>
+template <int MB, int NB>
+struct Slot {
+  uint4 b[NB];         // permuted codes: one 128-deep K block per column block
+  half2_t s[NB];       // the group scale of this lane's column, in both halves
+  half8_t a[MB][4];    // activation fragments, four 32-deep steps
+};
+
+template <int MB, int NB, int WK, int D>
 __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
-    int group, int splits, unsigned* __restrict__ counters,
+    int group_blocks, uint32_t group_magic, int splits, unsigned* __restrict__ counters,
     float* __restrict__ partials) {
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
@@ -41,16 +59,18 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile_n = blockIdx.x;
   const int tile_m = blockIdx.y;
   const int split = blockIdx.z;
   const int KB = K / kBlockK;
-  const int N16 = N / kBlockN;
   const int kb0 = (int)((int64_t)KB * split / splits);
   const int kb1 = (int)((int64_t)KB * (split + 1) / splits);
   const int l16 = lane & 15;
   const int lk = (lane >> 4) * 8;
+  const int n16_0 = tile_n * NB;
+  // column blocks of this tile inside N (ragged N: the rest are skipped)
+  const int nvalid = N / kBlockN - n16_0 < NB ? N / kBlockN - n16_0 : NB;
 
   float4_t acc[MB][NB];
 #pragma unroll
@@ -58,64 +78,88 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Activation rows of this lane (row l16 of each 16-row block); rows >= M
-  // are never read and contribute zeros.
+  // Activation row of this lane in each 16-row block.  Rows >= M read row
+  // M - 1 instead: their sums land in accumulator rows that are never
+  // stored, so no load needs a mask.
   const _Float16* arow[MB];
-  bool aok[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int r = tile_m * TM + mb * 16 + l16;
-    aok[mb] = r < M;
-    arow[mb] = A + (int64_t)(aok[mb] ? r : 0) * K + lk;
+    arow[mb] = A + (int64_t)(r < M ? r : M - 1) * K + lk;
   }
-  // Column blocks of this wave; blocks past N (ragged N) are skipped.
   const uint32_t* bcol[NB];
   const _Float16* scol[NB];
-  bool bok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int n16 = tile_n * NB + nb;
-    bok[nb] = n16 < N16;
-    bcol[nb] = Bp + block_word_offset(bok[nb] ? n16 : 0, 0, K) + lane * kWordsPerLane;
-    scol[nb] = S + (bok[nb] ? n16 * kBlockN + l16 : 0);
+    const int n16 = n16_0 + (nb < nvalid ? nb : nvalid - 1);
+    bcol[nb] = Bp + block_word_offset(n16, 0, K) + lane * kWordsPerLane;
+    scol[nb] = S + n16 * kBlockN + l16;
   }
 
-  for (int kb = kb0 + wave; kb < kb1; kb += WK) {
-    uint4 bw[NB];
-    half2_t s2[NB];
-    const int64_t srow = (int64_t)(kb * kBlockK / group) * N;
+  // Scale row of K block kb: kb / group_blocks (group_magic = 0: a shift).
+  auto scale_row = [&](int kb) -> int {
+    return group_magic ? (int)__umulhi((uint32_t)kb, group_magic) : kb >> group_blocks;
+  };
+  auto load = [&](Slot<MB, NB>& sl, int kb) {
+    const int srow = scale_row(kb) * N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (bok[nb]) {
-        bw[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + (int64_t)kb * kWordsPerBlock);
-        const _Float16 s = scol[nb][srow];
-        s2[nb] = half2_t{s, s};
-      } else {
-        bw[nb] = uint4{0u, 0u, 0u, 0u};
-        s2[nb] = half2_t{(_Float16)0.f, (_Float16)0.f};
-      }
+      sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + kb * kWordsPerBlock);
+      const _Float16 sc = scol[nb][srow];
+      sl.s[nb] = half2_t{sc, sc};
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half8_t a[MB];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (aok[mb]) {
-          a[mb] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
-        } else {
-          a[mb] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-      }
+      for (int j = 0; j < 4; ++j)
+        sl.a[mb][j] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
+  };
+  auto compute = [&](const Slot<MB, NB>& sl) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if (!bok[nb]) continue;
-        const uint32_t w = j == 0 ? bw[nb].x : j == 1 ? bw[nb].y : j == 2 ? bw[nb].z : bw[nb].w;
-        const half8_t b = unpack_scale(w, s2[nb]);
+        // (column blocks past N recompute the last valid block; the store
+        // drops them -- a branch here would stall the load pipeline)
+        const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
+                         : j == 2 ? sl.b[nb].z : sl.b[nb].w;
+        const half8_t b = unpack_scale(w, sl.s[nb]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], b, acc[mb][nb], 0, 0, 0);
-        }
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sl.a[mb][j], b, acc[mb][nb], 0, 0, 0);
       }
+    }
+  };
+
+  // This wave's K blocks are first, first + WK, ...; D of them are in flight
+  // (a ring of D register slots), the next load issued as soon as a slot has
+  // been consumed.  Loads past the last block re-read the last block, which
+  // keeps every load unconditional.
+  const int first = kb0 + wave;
+  const int nblk = first < kb1 ? (kb1 - first + WK - 1) / WK : 0;
+  if (nblk > 0) {
+    const int last = first + (nblk - 1) * WK;
+    Slot<MB, NB> slot[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int kb = first + u * WK;
+      load(slot[u], kb < last ? kb : last);
+    }
+    // Full rounds: straight-line code, so the wait before each slot's use
+    // counts exactly the D - 1 slots of loads issued after it.
+    int t = 0;
+    for (; t + D <= nblk; t += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        compute(slot[u]);
+        const int kb = first + (t + u + D) * WK;
+        load(slot[u], kb < last ? kb : last);
+      }
+    }
+    // The last, partial round: compute only.
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u) {
+      if (t + u < nblk) compute(slot[u]);
     }
   }
 
@@ -148,7 +192,6 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
       const int gr = row0 + r, gc = col0 + c;
       if (gr < M && gc < N) {
         const float4_t x = *reinterpret_cast<const float4_t*>(&red[r * LDT + c]);
-        typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
         const half4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
         *reinterpret_cast<half4_t*>(C + (int64_t)gr * N + gc) = h;
       }
@@ -156,44 +199,50 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     return;
   }
 
-  // Split-K: publish this workgroup's partial tile, then count arrivals.
+  // Split-K: publish this workgroup's partial tile (only rows < M), wait for
+  // the stores to complete, then count the arrival.
   const int tile = tile_m * gridDim.x + tile_n;
   constexpr int TE = TM * TN;
+  const int rows = M - row0 < TM ? M - row0 : TM;
   float* mine = partials + ((int64_t)tile * splits + split) * TE;
-  for (int v = threadIdx.x; v < TM * VPR; v += blockDim.x) {
-    const int r = v / VPR, c = (v % VPR) * VEC;
-    *reinterpret_cast<float4_t*>(mine + r * TN + c) =
-        *reinterpret_cast<const float4_t*>(&red[r * LDT + c]);
+  for (int v = threadIdx.x; v < rows * TN; v += blockDim.x) {
+    const int r = v / TN, c = v % TN;
+    __hip_atomic_store(mine + v, red[r * LDT + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev =
+        __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (unsigned)(splits - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   const float* base = partials + (int64_t)tile * splits * TE;
-  for (int v = threadIdx.x; v < TM * VPR; v += blockDim.x) {
+  for (int v = threadIdx.x; v < rows * VPR; v += blockDim.x) {
     const int r = v / VPR, c = (v % VPR) * VEC;
-    const int gr = row0 + r, gc = col0 + c;
-    if (gr < M && gc < N) {
-      float4_t x = *reinterpret_cast<const float4_t*>(base + r * TN + c);
+    const int gc = col0 + c;
+    if (gc < N) {
+      float x[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        x[e] = __hip_atomic_load(base + r * TN + c + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int s = 1; s < splits; ++s) {
-        x += *reinterpret_cast<const float4_t*>(base + (int64_t)s * TE + r * TN + c);
+        const float* p = base + (int64_t)s * TE + r * TN + c;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          x[e] += __hip_atomic_load(p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
       const half4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-      *reinterpret_cast<half4_t*>(C + (int64_t)gr * N + gc) = h;
+      *reinterpret_cast<half4_t*>(C + (int64_t)(row0 + r) * N + gc) = h;
     }
   }
-  if (threadIdx.x == 0) counters[tile] = 0u;  // ready for the next call
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK>
+template <int MB, int NB, int WK, int D>
 static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                              const uint16_t* S, uint16_t* C, int M, int K, int N,
                              int group, void* workspace, hipStream_t stream) {
@@ -204,27 +253,46 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  hipLaunchKernelGGL((gemm_kernel<MB, NB, WK>), dim3(p.tiles_n, p.tiles_m, p.splits),
+  // Scale row of K block kb is kb / gb, gb = group / 128: a shift when gb is
+  // a power of two, else a multiply-high by ceil(2^32 / gb), exact for
+  // kb, gb < 2^16.
+  const uint32_t gb = (uint32_t)(group / kBlockK);
+  int gshift = 0;
+  uint32_t gmagic = 0;
+  if ((gb & (gb - 1)) == 0) {
+    while ((1u << gshift) < gb) ++gshift;
+  } else {
+    gmagic = (uint32_t)((((uint64_t)1 << 32) + gb - 1) / gb);
+  }
+  hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D>), dim3(p.tiles_n, p.tiles_m, p.splits),
                      dim3(64 * WK), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
                      reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
-                     M, K, N, group, p.splits, counters, partials);
+                     M, K, N, gshift, gmagic, p.splits, counters, partials);
   return hipGetLastError();
 }
 
-bool plan_is_compiled(int mb, int nb, int wk) {
-  return nb == 4 && wk == 4 && (mb == 1 || mb == 2 || mb == 4 || mb == 8);
+// Compiled variants (MB, NB, WK, D).
+#define W4A16_VARIANTS(X)                                                        \
+  X(1, 1, 4, 2) X(1, 1, 4, 4) X(1, 1, 8, 2) X(1, 1, 8, 4)                        \
+  X(1, 2, 4, 2) X(1, 2, 4, 4) X(1, 2, 8, 2) X(1, 2, 8, 4)                        \
+  X(1, 4, 4, 2) X(1, 4, 8, 2)                                                    \
+  X(2, 2, 4, 2) X(2, 4, 4, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) X(8, 2, 4, 1) X(8, 4, 4, 1)
+
+bool plan_is_compiled(int mb, int nb, int wk, int depth) {
+#define W4A16_MATCH(MB_, NB_, WK_, D_) \
+  if (mb == MB_ && nb == NB_ && wk == WK_ && depth == D_) return true;
+  W4A16_VARIANTS(W4A16_MATCH)
+#undef W4A16_MATCH
+  return false;
 }
 
 hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N, int group,
                        void* workspace, hipStream_t stream) {
-#define W4A16_CASE(MB_, NB_, WK_)                                                   \
-  if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_)                                    \
-    return launch_one<MB_, NB_, WK_>(p, A, Bp, S, C, M, K, N, group, workspace, stream);
-  W4A16_CASE(1, 4, 4)
-  W4A16_CASE(2, 4, 4)
-  W4A16_CASE(4, 4, 4)
-  W4A16_CASE(8, 4, 4)
+#define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \
+    return launch_one<MB_, NB_, WK_, D_>(p, A, Bp, S, C, M, K, N, group, workspace, stream);
+  W4A16_VARIANTS(W4A16_CASE)
 #undef W4A16_CASE
   return hipErrorInvalidValue;
 }

@@ -14,14 +14,15 @@ namespace w4a16 {
 //         the workgroup's K range; their sums are added in wave order
 //  splits K ranges per output tile, one workgroup each; their FP32 partials
 //         go through the workspace and are added in split order
+//  depth  K blocks each wave keeps in flight (register slots)
 struct Plan {
-  int mb, nb, wk, splits;
+  int mb, nb, wk, splits, depth;
   int tiles_n, tiles_m;
   size_t workspace_bytes;  // 0 when splits == 1
 };
 
 Plan make_plan(int M, int K, int N, int group, int cus);
-bool plan_is_compiled(int mb, int nb, int wk);
+bool plan_is_compiled(int mb, int nb, int wk, int depth);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);

@@ -8,18 +8,27 @@
 // middle row), a handful of instructions per group of weights ("Why
 // architecture matters here").
 //
-// The trick used here: OR-ing a 4-bit code q into the low mantissa bits of
-// the FP16 value 1024 (0x6400, whose mantissa unit is exactly 1) gives the
-// FP16 value 1024 + q with no conversion instruction.  One shift and one
-// and-or per pair of codes build two such values in the halves of a 32-bit
-// register.  Subtracting 1032 in FP16 is exact (the result is an integer in
-// -8..7), and the FP16 multiply by the scale rounds the exact product once,
-// round-to-nearest-even.  So every weight equals fp16_rne((q - 8) * s)
+// The trick used here: OR-ing a 4-bit code into the mantissa of a suitable
+// FP16 constant yields "constant + code" with no conversion instruction.
+//  * A code in bits 0..3 of a 16-bit half, OR-ed into 1024.0 (0x6400,
+//    mantissa unit 1), gives 1024 + q.
+//  * A code in bits 4..7, OR-ed into 64.0 (0x5400, mantissa unit 1/16),
+//    gives 64 + 16q/16 = 64 + q: no shift is needed for it.
+// Bits 8..15 of a half reach the exponent, so the upper two codes of each
+// half are first shifted down by 8.  One mask-and-or per pair of codes, plus
+// one shift per word, builds the four FP16 pairs (code k+0 and k+1 in the two
+// halves of a register, as the matrix instruction wants them) -- this is why
+// the permuted layout stores code i of a fragment at nibble {0,4,1,5,2,6,3,7}
+// [i].  Subtracting 1032 (or 72) in FP16 is exact (the result is an integer
+// in -8..7), and the FP16 multiply by the scale rounds the exact product
+// once, round-to-nearest-even.  So every weight equals fp16_rne((q - 8) * s)
 // exactly.  (Folding the subtraction into one fused multiply-add with
 // 1032 * s would round 1032 * s first and cancel catastrophically; it is not
 // used.)
 //
-// This is the one routine both the GEMM and the dequantisation check use.
+// Cost: 5 bit operations, 4 packed subtractions and 4 packed multiplies per
+// eight weights.  This is the one routine both the GEMM and the
+// dequantisation check use.
 #pragma once
 
 #include <stdint.h>
@@ -35,17 +44,30 @@ union Half8 {
   uint32_t u[4];
 };
 
+// (x & mask) | magic as one instruction.  Left to itself the compiler emits
+// an AND and an OR with literal operands (two issue slots); the three-operand
+// form needs both constants in registers, which it then keeps across the loop.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
+  return r;
+}
+
 __device__ __forceinline__ half8_t unpack_scale(uint32_t word, half2_t scale2) {
 #pragma clang fp contract(off)
-  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
+  const half2_t bias_hi = {(_Float16)72.0f, (_Float16)72.0f};      //   64 + 8
+  const uint32_t w8 = word >> 8;
+  Half8 raw;
+  raw.u[0] = and_or(word, 0x000F000Fu, 0x64006400u);  // codes 0, 1: 1024 + q
+  raw.u[1] = and_or(word, 0x00F000F0u, 0x54005400u);  // codes 2, 3:   64 + q
+  raw.u[2] = and_or(w8, 0x000F000Fu, 0x64006400u);    // codes 4, 5
+  raw.u[3] = and_or(w8, 0x00F000F0u, 0x54005400u);    // codes 6, 7
   Half8 out;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t bits = ((word >> (4 * r)) & 0x000F000Fu) | 0x64006400u;
-    half2_t h = __builtin_bit_cast(half2_t, bits);   // (1024 + q_2r, 1024 + q_2r+1)
-    h = h - bias;                                    // exact: q - 8
-    out.h2[r] = h * scale2;                          // one rounding
-  }
+  out.h2[0] = (raw.h2[0] - bias_lo) * scale2;  // exact subtraction, one rounding
+  out.h2[1] = (raw.h2[1] - bias_hi) * scale2;
+  out.h2[2] = (raw.h2[2] - bias_lo) * scale2;
+  out.h2[3] = (raw.h2[3] - bias_hi) * scale2;
   return out.v;
 }
 
