@@ -140,15 +140,25 @@ def test_gemm_matches_oracle(M, K, N, group):
     assert_gemm_close(C, C64, f"M={M} K={K} N={N} g={group}")
 
 
-@pytest.mark.parametrize("plan", ["1,4,4,1", "1,4,4,2", "1,4,4,7", "2,4,4,3", "4,4,4,5",
-                                  "8,4,4,2", "8,4,4,1"])
+STREAM_PLANS = ["1,1,4,1,2", "1,1,8,3,4", "1,2,4,2,2", "1,2,8,1,4", "1,4,4,7,2", "1,4,8,2,2",
+                "2,2,4,3,2", "2,4,4,1,2", "4,2,4,5,1", "4,4,4,1,1", "8,2,4,2,1", "8,4,4,1,1"]
+TILE_PLANS = ["4,4,2,1,0,1", "4,4,2,3,0,1", "4,4,4,2,0,1", "8,2,2,1,0,1", "8,2,2,4,0,1",
+              "8,4,2,1,0,1", "8,4,2,5,0,1", "8,4,4,1,0,1", "8,4,4,2,0,1"]
+
+
+@pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS)
 def test_gemm_forced_plans_agree(monkeypatch, plan):
-    """Every compiled variant and split count gives the same answer."""
+    """Every compiled variant and split count gives the oracle's answer
+    (M = 45 exercises ragged rows; N = 208 a ragged column tile)."""
     M, K, N = 45, 3584, 208
     A, Bq, S = make_inputs(M, K, N, 128, seed=5)
     _, C64 = oracle.gemm(A, Bq, S, 128)
     monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
-    say("forced plan", plan, "workspace", w4.w4a16_workspace_bytes(M, K, N, 128))
+    desc = w4.w4a16_describe(M, K, N, 128)
+    fields = [int(x) for x in plan.split(",")]
+    kernel = "gemm_tile_kernel" if len(fields) > 5 and fields[5] == 1 else "gemm_kernel"
+    assert desc.startswith(kernel + "<"), desc   # the forced variant is the one that runs
+    say("forced plan", plan, desc)
     C = run_gemm(A, Bq, S, 128)
     assert_gemm_close(C, C64, f"plan {plan}")
 

@@ -62,83 +62,109 @@ int check_group(int K, int group) {
   return W4A16_OK;
 }
 
-// Test and tuning override: W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth]"
+bool variant_is_compiled(const Plan& q) {
+  return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk)
+                : plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
+}
+
+// Test and tuning override: W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile]]"
 // replaces the heuristic's choice when it names a compiled variant (a field
-// <= 0 keeps the heuristic's value).  It feeds the same kernels;
-// w4a16_workspace_bytes sees it too, so sizes stay consistent within a
-// process.
+// <= 0 keeps the heuristic's value; tile is 0, the default, for the
+// streaming kernel or 1 for the tile kernel).  It feeds the same
+// kernels; w4a16_workspace_bytes sees it too, so sizes stay consistent
+// within a process.
 void apply_forced_plan(Plan* p, int KB) {
   const char* env = std::getenv("W4A16_FORCE_PLAN");
   if (!env || !*env) return;
-  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0;
-  if (std::sscanf(env, "%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth) < 4) return;
+  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0;
+  if (std::sscanf(env, "%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile) < 4) return;
+  if (tile != 0 && tile != 1) return;
   Plan q = *p;
+  q.tile = tile;  // absent: the streaming kernel
   if (mb > 0) q.mb = mb;
   if (nb > 0) q.nb = nb;
   if (wk > 0) q.wk = wk;
   if (splits > 0) q.splits = splits > KB ? KB : splits;
   if (depth > 0) q.depth = depth;
-  if (!plan_is_compiled(q.mb, q.nb, q.wk, q.depth)) {
+  if (!q.tile && !variant_is_compiled(q)) {
     // keep the forced tile but take the first compiled depth for it
     for (int d : {4, 2, 1}) {
-      if (plan_is_compiled(q.mb, q.nb, q.wk, d)) {
-        q.depth = d;
-        break;
-      }
+      q.depth = d;
+      if (variant_is_compiled(q)) break;
     }
-    if (!plan_is_compiled(q.mb, q.nb, q.wk, q.depth)) return;
   }
+  if (!variant_is_compiled(q)) return;
   *p = q;
 }
 
 }  // namespace
 
-// The heuristic.  Small batches (M <= 32) stream the weights: one or two
-// 16-row blocks per wave, narrow column tiles so that there are enough
-// workgroups, eight waves per workgroup splitting K, and up to four K blocks
-// in flight per wave.  Larger batches take 64 or 128 rows per wave, so each
-// weight is unpacked once for many rows.  K is split across workgroups only
-// as far as needed to give every compute unit about two workgroups, keeping
-// at least two K blocks per wave.
+// The heuristic (measured on MI355X at the Llama-2-7B layer shapes).
+// Small batches (M <= 16) stream the weights: one 16-row block per wave.
+// With one activation row the activation fragments cost little, so narrow
+// column tiles (16 or 32 columns) give the most workgroups; with 16 rows
+// every wave re-reads its activation fragments, so wide tiles (64 columns)
+// amortise them when N leaves enough tiles.  K is split across workgroups
+// only as far as needed to give every compute unit work, keeping at least
+// two K blocks per wave.  Larger batches take 64 or 128 rows per wave, so
+// each weight is unpacked once for many rows.
 Plan make_plan(int M, int K, int N, int group, int cus) {
   (void)group;
   Plan p{};
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
+  if (cus <= 0) cus = 256;
   if (M <= 16) {
     p.mb = 1;
-    p.nb = M <= 4 ? 1 : 2;
-    p.wk = 8;
-    p.depth = 4;
+    if (M <= 4) {
+      p.nb = n16 >= 2 * cus ? 2 : 1;
+    } else {
+      p.nb = n16 >= 2 * cus ? 4 : (KB >= 64 ? 2 : 1);
+    }
+    p.wk = KB >= 64 ? 8 : 4;
+    p.depth = 2;
   } else if (M <= 32) {
     p.mb = 2;
     p.nb = 2;
     p.wk = 4;
     p.depth = 2;
   } else {
+    // tile kernel: 64 or 128 rows by 64 (M > 64) or 128 columns
+    p.tile = 1;
     p.mb = M <= 64 ? 4 : 8;
-    p.nb = 4;
-    p.wk = 4;
-    p.depth = 1;
+    p.nb = M <= 64 ? 4 : 2;
+    p.wk = 2;
+    p.depth = 0;
   }
-  p.tiles_n = (n16 + p.nb - 1) / p.nb;
-  p.tiles_m = (M + 16 * p.mb - 1) / (16 * p.mb);
+  auto shape = [&](Plan& q) {
+    q.tm = 16 * q.mb;
+    q.tn = 16 * q.nb * (q.tile ? q.wk : 1);
+    q.tiles_n = (N + q.tn - 1) / q.tn;
+    q.tiles_m = (M + q.tm - 1) / q.tm;
+  };
+  shape(p);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-  const int64_t target = 2 * (int64_t)(cus > 0 ? cus : 256);
-  int64_t want = (target + tiles - 1) / tiles;
-  int64_t cap = KB / (2 * p.wk);
+  // Split K only when the tiles leave many compute units idle: the
+  // streaming kernel up to one workgroup per compute unit, the tile kernel
+  // (two waves per workgroup) up to about one and a half.
+  int64_t want;
+  if (p.tile) {
+    want = 10 * tiles >= 13 * (int64_t)cus ? 1 : (3 * (int64_t)cus / 2 + tiles - 1) / tiles;
+  } else {
+    want = 10 * tiles >= 6 * (int64_t)cus ? 1 : (cus + tiles - 1) / tiles;
+  }
+  int64_t cap = p.tile ? KB / 2 : KB / (2 * p.wk);
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want > 64) want = 64;
   p.splits = (int)(want < 1 ? 1 : want);
   apply_forced_plan(&p, KB);
-  p.tiles_n = (n16 + p.nb - 1) / p.nb;
-  p.tiles_m = (M + 16 * p.mb - 1) / (16 * p.mb);
+  shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
   p.workspace_bytes = 0;
   if (p.splits > 1) {
     p.workspace_bytes = counters_bytes((int)ftiles) +
-                        (size_t)ftiles * p.splits * (16 * p.mb) * (16 * p.nb) * sizeof(float);
+                        (size_t)ftiles * p.splits * p.tm * p.tn * sizeof(float);
   }
   return p;
 }
@@ -189,10 +215,16 @@ int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan p = make_plan(M, K, N, group, cus);
-  std::snprintf(buf, len,
-                "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
-                p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
-                p.splits, p.workspace_bytes);
+  if (p.tile)
+    std::snprintf(buf, len,
+                  "gemm_tile_kernel<%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                  p.mb, p.nb, p.wk, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk, p.splits,
+                  p.workspace_bytes);
+  else
+    std::snprintf(buf, len,
+                  "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                  p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
+                  p.splits, p.workspace_bytes);
   return W4A16_OK;
 }
 

@@ -14,13 +14,9 @@
 //    the FP16 tile and sets the counter back to zero.  The order of every
 //    addition is fixed, so results are bit-identical from run to run.
 //
-// The hand-off between workgroups uses device-scope relaxed atomic stores
-// and loads for the partials (they write through to, and read from, the
-// device coherence point, whichever XCD's L2 a workgroup runs behind), a
-// wait for those stores to complete before the arrival count, and no
-// device-wide fence: a device-scope fence writes back and invalidates the
-// whole L2 of the XCD, which, done by hundreds of workgroups in flight,
-// throws away the weights and activations other workgroups are streaming.
+// The hand-off between workgroups uses device-coherent 16-byte stores and
+// loads for the partials (coherent.hpp), a wait for those stores to complete
+// before the arrival count, and no device-wide fence.
 //
 // Per 128-deep K block a wave issues, for each of its NB column blocks, one
 // 16-byte load per lane of permuted codes (the lane's own operand fragments
@@ -30,13 +26,13 @@
 // per 16-row block and 32-deep step).  Loads run one step ahead of the
 // matrix instructions: the codes of the next K block and the activations of
 // the next 32-deep step are in flight while the current ones are consumed.
+#include "coherent.hpp"
 #include "internal.hpp"
 #include "layout.hpp"
 #include "unpack.hpp"
 
 namespace w4a16 {
 
-typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 template <int MB, int NB>
@@ -50,7 +46,7 @@ template <int MB, int NB, int WK, int D>
 __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
-    int group_blocks, uint32_t group_magic, int splits, unsigned* __restrict__ counters,
+    uint64_t group_magic, int splits, unsigned* __restrict__ counters,
     float* __restrict__ partials) {
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
@@ -97,8 +93,10 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   }
 
   // Scale row of K block kb: kb / group_blocks (group_magic = 0: a shift).
+  // Scale row of K block kb: kb / (group / 128), as a multiply-high by
+  // group_magic = ceil(2^32 / (group / 128)); no branch in the K loop.
   auto scale_row = [&](int kb) -> int {
-    return group_magic ? (int)__umulhi((uint32_t)kb, group_magic) : kb >> group_blocks;
+    return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
   };
   auto load = [&](Slot<MB, NB>& sl, int kb) {
     const int srow = scale_row(kb) * N;
@@ -199,15 +197,19 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     return;
   }
 
-  // Split-K: publish this workgroup's partial tile (only rows < M), wait for
-  // the stores to complete, then count the arrival.
+  // Split-K: publish this workgroup's partial tile (rows < M, row-major,
+  // 16 bytes per access, device-coherent), wait for the stores to complete,
+  // then count the arrival.
   const int tile = tile_m * gridDim.x + tile_n;
   constexpr int TE = TM * TN;
   const int rows = M - row0 < TM ? M - row0 : TM;
-  float* mine = partials + ((int64_t)tile * splits + split) * TE;
-  for (int v = threadIdx.x; v < rows * TN; v += blockDim.x) {
-    const int r = v / TN, c = v % TN;
-    __hip_atomic_store(mine + v, red[r * LDT + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float* tile_base = partials + (int64_t)tile * splits * TE;
+  {
+    const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
+    for (int v = threadIdx.x; v < rows * VPR; v += blockDim.x) {
+      const int r = v / VPR, c = (v % VPR) * VEC;
+      store_coherent(mine, v, *reinterpret_cast<const float4_t*>(&red[r * LDT + c]));
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -219,21 +221,25 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   __syncthreads();
   if (!s_last) return;
 
-  const float* base = partials + (int64_t)tile * splits * TE;
+  // Add the partials in split order; up to eight splits' loads are in
+  // flight at once.
   for (int v = threadIdx.x; v < rows * VPR; v += blockDim.x) {
     const int r = v / VPR, c = (v % VPR) * VEC;
+    float4_t x = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      float4_t part[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u < splits ? s0 + u : splits - 1;
+        part[u] = load_coherent(coherent_rsrc(tile_base + (int64_t)s * TE), v);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < splits) x = (s0 + u == 0) ? part[u] : x + part[u];
+      }
+    }
     const int gc = col0 + c;
     if (gc < N) {
-      float x[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        x[e] = __hip_atomic_load(base + r * TN + c + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int s = 1; s < splits; ++s) {
-        const float* p = base + (int64_t)s * TE + r * TN + c;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          x[e] += __hip_atomic_load(p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
       const half4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
       *reinterpret_cast<half4_t*>(C + (int64_t)(row0 + r) * N + gc) = h;
     }
@@ -245,7 +251,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
 template <int MB, int NB, int WK, int D>
 static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                              const uint16_t* S, uint16_t* C, int M, int K, int N,
-                             int group, void* workspace, hipStream_t stream) {
+                             uint64_t gmagic, void* workspace,
+                             hipStream_t stream) {
   unsigned* counters = nullptr;
   float* partials = nullptr;
   if (p.splits > 1) {
@@ -253,21 +260,10 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  // Scale row of K block kb is kb / gb, gb = group / 128: a shift when gb is
-  // a power of two, else a multiply-high by ceil(2^32 / gb), exact for
-  // kb, gb < 2^16.
-  const uint32_t gb = (uint32_t)(group / kBlockK);
-  int gshift = 0;
-  uint32_t gmagic = 0;
-  if ((gb & (gb - 1)) == 0) {
-    while ((1u << gshift) < gb) ++gshift;
-  } else {
-    gmagic = (uint32_t)((((uint64_t)1 << 32) + gb - 1) / gb);
-  }
   hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D>), dim3(p.tiles_n, p.tiles_m, p.splits),
                      dim3(64 * WK), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
                      reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
-                     M, K, N, gshift, gmagic, p.splits, counters, partials);
+                     M, K, N, gmagic, p.splits, counters, partials);
   return hipGetLastError();
 }
 
@@ -289,9 +285,16 @@ bool plan_is_compiled(int mb, int nb, int wk, int depth) {
 hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N, int group,
                        void* workspace, hipStream_t stream) {
+  // Scale row of K block kb is kb / gb, gb = group / 128, computed in the
+  // kernels as (kb * ceil(2^32 / gb)) >> 32: exact when gb is a power of two,
+  // and for any gb as long as kb, gb < 2^16 (K < 2^23 is checked).
+  const uint64_t gb = (uint64_t)(group / kBlockK);
+  const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
+  if (p.tile) return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, workspace, stream);
 #define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \
-    return launch_one<MB_, NB_, WK_, D_>(p, A, Bp, S, C, M, K, N, group, workspace, stream);
+    return launch_one<MB_, NB_, WK_, D_>(p, A, Bp, S, C, M, K, N, gmagic,           \
+                                         workspace, stream);
   W4A16_VARIANTS(W4A16_CASE)
 #undef W4A16_CASE
   return hipErrorInvalidValue;

@@ -1,0 +1,307 @@
+// The W4A16 GEMM for batches of more than 32 rows: C = A . dequant(Bpacked).
+//
+// Once a batch has dozens of rows the matrix instructions, not the weight
+// stream, set the pace ("Quant Marlin kernel" explainer, "Why architecture
+// matters here": with batching the same weights are reused and the kernel
+// becomes compute-bound; "Low-Precision Quantization Kernels in Production",
+// section 5, "Decoding Roofline Dynamics").  Two costs then matter:
+// unpacking each weight as few times as possible, and feeding the matrix
+// instructions their activation operands without saturating the caches.
+//
+// Work decomposition:
+//  * a workgroup of WN waves owns an output tile of 16*MB rows by
+//    16*NB*WN columns and one K range (grid.z splits K as in the streaming
+//    kernel, with the same deterministic last-arriver reduction);
+//  * each wave owns 16*NB columns and all 16*MB rows of the tile, so every
+//    weight is loaded and unpacked exactly once per workgroup; its codes
+//    come straight from global memory into registers (the permuted layout
+//    hands each lane its own fragments), two K blocks ahead;
+//  * the tile's activations for a 128-deep K block sit in LDS and are read
+//    by every wave.  They are copied global -> LDS by the direct 16-byte
+//    load of gfx950 (no staging registers), into one of two stages while
+//    the other is being read ("Quant Marlin kernel" explainer, "End-to-end
+//    flow": the next tile's loads go into the other half of a double buffer
+//    before the first one is consumed).  Each 256-byte row of a stage holds
+//    its sixteen 16-byte pieces in a row-dependent order (piece c of row r
+//    at slot c ^ (r & 15)), so the sixteen rows a wave reads in one fragment
+//    load fall in distinct banks.
+#include "coherent.hpp"
+#include "internal.hpp"
+#include "layout.hpp"
+#include "unpack.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* global_ptr_t;
+
+template <int NB>
+struct BSlot {
+  uint4 b[NB];
+  half2_t s[NB];
+};
+
+// s_waitcnt that waits until at most n vector-memory operations of this
+// wave are outstanding (and leaves the other counters alone).
+template <int n>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+}  // namespace
+
+template <int MB, int NB, int WN>
+__global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
+    const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
+    const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
+    uint64_t group_magic, int splits, unsigned* __restrict__ counters,
+    float* __restrict__ partials) {
+  constexpr int TM = 16 * MB;
+  constexpr int TN = 16 * NB * WN;
+  constexpr int PIECES = TM * 16;          // 16-byte pieces of one activation stage
+  constexpr int LOADS = PIECES / 64 / WN;  // direct loads per wave per stage
+  static_assert(PIECES % (64 * WN) == 0, "stage must split evenly over the waves");
+  constexpr int BLOADS = 2 * NB;           // code + scale loads per wave per K block
+  // Two separate LDS objects (rather than one array of two) let the
+  // compiler see that a direct load into one stage does not touch the other.
+  __shared__ uint4 As0[PIECES];
+  __shared__ uint4 As1[PIECES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile_n = blockIdx.x;
+  const int tile_m = blockIdx.y;
+  const int split = blockIdx.z;
+  const int KB = K / kBlockK;
+  const int kb0 = (int)((int64_t)KB * split / splits);
+  const int kb1 = (int)((int64_t)KB * (split + 1) / splits);
+  const int l16 = lane & 15;
+  const int row0 = tile_m * TM;
+  const int n16_last = N / kBlockN - 1;
+  const int n16_0 = tile_n * NB * WN + wave * NB;
+
+  // Direct load i of this wave fills stage pieces 64 * (wave + WN * i) + lane:
+  // row r = 4 * (wave + WN * i) + lane / 16, slot lane % 16, which holds
+  // piece (lane % 16) ^ (r & 15) of that row.  Rows past M read row M - 1
+  // (their sums are never stored).
+  auto load_a = [&](uint4* stage, int kb) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = 4 * (wave + WN * i) + (lane >> 4);
+      const int piece = l16 ^ (r & 15);
+      const int gr = row0 + r < M ? row0 + r : M - 1;
+      const _Float16* src = A + (int64_t)gr * K + kb * kBlockK + piece * 8;
+      __builtin_amdgcn_global_load_lds((global_ptr_t)src,
+                                       (lds_ptr_t)&stage[64 * (wave + WN * i)], 16, 0, 0);
+    }
+  };
+  const uint32_t* bcol[NB];
+  const _Float16* scol[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    // blocks past N recompute the last valid one and are dropped at the store
+    const int n16 = n16_0 + nb <= n16_last ? n16_0 + nb : n16_last;
+    bcol[nb] = Bp + block_word_offset(n16, 0, K) + lane * kWordsPerLane;
+    scol[nb] = S + n16 * kBlockN + l16;
+  }
+  // Scale row of K block kb: kb / (group / 128), as a multiply-high by
+  // group_magic = ceil(2^32 / (group / 128)); no branch in the K loop.
+  auto scale_row = [&](int kb) -> int {
+    return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
+  };
+  auto load_b = [&](BSlot<NB>& sl, int kb) {
+    const int srow = scale_row(kb) * N;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + kb * kWordsPerBlock);
+      const _Float16 sc = scol[nb][srow];
+      sl.s[nb] = half2_t{sc, sc};
+    }
+  };
+
+  float4_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // One K block: per 32-deep step, unpack the wave's NB code words, read the
+  // MB activation fragments (all issued before the first is used), then
+  // MB x NB matrix instructions.
+  auto compute = [&](const uint4* stage, const BSlot<NB>& sl) {
+    const int lg = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half8_t a[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 16 + l16;
+        a[mb] = __builtin_bit_cast(half8_t, stage[r * 16 + ((4 * j + lg) ^ (r & 15))]);
+      }
+      half8_t bf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
+                         : j == 2 ? sl.b[nb].z : sl.b[nb].w;
+        bf[nb] = unpack_scale(w, sl.s[nb]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+    }
+  };
+
+  // Issue order, which the waits below count on: A(0) B(0) A(1) B(1), then
+  // per K block t: A(t+2) B(t+2).  Loads past the range are clamped to the
+  // last block (harmless re-reads), so every iteration issues the same loads.
+  const int nblk = kb1 - kb0;  // >= 1: splits never exceed the K blocks
+  const int last = kb1 - 1;
+  BSlot<NB> b0, b1;
+  load_a(As0, kb0);
+  load_b(b0, kb0);
+  load_a(As1, kb0 + 1 <= last ? kb0 + 1 : last);
+  load_b(b1, kb0 + 1 <= last ? kb0 + 1 : last);
+
+  int t = 0;
+  for (; t + 2 <= nblk; t += 2) {
+    const int kb = kb0 + t;
+    // stage 0 holds block kb: everything but A(kb+1), B(kb+1) has landed
+    wait_vmem_at_most<LOADS + BLOADS>();
+    __syncthreads();
+    compute(As0, b0);
+    __syncthreads();  // all waves are done with stage 0
+    load_a(As0, kb + 2 <= last ? kb + 2 : last);
+    load_b(b0, kb + 2 <= last ? kb + 2 : last);
+    wait_vmem_at_most<LOADS + BLOADS>();
+    __syncthreads();
+    compute(As1, b1);
+    __syncthreads();
+    load_a(As1, kb + 3 <= last ? kb + 3 : last);
+    load_b(b1, kb + 3 <= last ? kb + 3 : last);
+  }
+  if (t < nblk) {
+    wait_vmem_at_most<LOADS + BLOADS>();
+    __syncthreads();
+    compute(As0, b0);
+  }
+
+  // Output: lane l holds rows 4*(l/16) .. +3 of column l % 16 of each block.
+  const int col_base = tile_n * TN + wave * 16 * NB + l16;
+  if (splits == 1) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int gc = col_base + nb * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
+          if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][i];
+        }
+      }
+    return;
+  }
+
+  // Split-K: publish the partial tile with device-coherent stores, wait for
+  // them, count the arrival; the last workgroup adds the partials in split
+  // order and writes C.  A partial is kept in fragment order -- wave,
+  // 16-row block, 16-column block, lane, four values -- so that each lane
+  // moves its four accumulators in one 16-byte access and the workgroup
+  // that sums finds its own fragments at the same places.  (The flag that
+  // says which workgroup is last lives in the now idle activation stages.)
+  int* s_last = reinterpret_cast<int*>(&As0[0]);
+  const int tile = tile_m * gridDim.x + tile_n;
+  constexpr int TE = TM * TN;
+  const float* tile_base = partials + (int64_t)tile * splits * TE;
+  const int frag0 = wave * MB * NB * 64 + lane;
+  {
+    const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) store_coherent(mine, frag0 + (mb * NB + nb) * 64, acc[mb][nb]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = prev == (unsigned)(splits - 1);
+  }
+  __syncthreads();
+  if (!*s_last) return;
+
+  // Sum in split order 0, 1, ... into the (now free) accumulators.
+  for (int s = 0; s < splits; ++s) {
+    const __amdgpu_buffer_rsrc_t ps = coherent_rsrc(tile_base + (int64_t)s * TE);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float4_t x = load_coherent(ps, frag0 + (mb * NB + nb) * 64);
+        acc[mb][nb] = s == 0 ? x : acc[mb][nb] + x;
+      }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int gc = col_base + nb * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
+        if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][i];
+      }
+    }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MB, int NB, int WN>
+static hipError_t launch_tile_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
+                                  const uint16_t* S, uint16_t* C, int M, int K, int N,
+                                  uint64_t gmagic, void* workspace,
+                                  hipStream_t stream) {
+  unsigned* counters = nullptr;
+  float* partials = nullptr;
+  if (p.splits > 1) {
+    counters = static_cast<unsigned*>(workspace);
+    partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        counters_bytes(p.tiles_n * p.tiles_m));
+  }
+  hipLaunchKernelGGL((gemm_tile_kernel<MB, NB, WN>), dim3(p.tiles_n, p.tiles_m, p.splits),
+                     dim3(64 * WN), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
+                     reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
+                     M, K, N, gmagic, p.splits, counters, partials);
+  return hipGetLastError();
+}
+
+// Compiled tile variants (MB, NB, WN).
+#define W4A16_TILE_VARIANTS(X) X(4, 4, 2) X(4, 4, 4) X(8, 2, 2) X(8, 4, 2) X(8, 4, 4)
+
+bool tile_is_compiled(int mb, int nb, int wn) {
+#define W4A16_TMATCH(MB_, NB_, WN_) \
+  if (mb == MB_ && nb == NB_ && wn == WN_) return true;
+  W4A16_TILE_VARIANTS(W4A16_TMATCH)
+#undef W4A16_TMATCH
+  return false;
+}
+
+hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
+                       const uint16_t* S, uint16_t* C, int M, int K, int N,
+                       uint64_t gmagic, void* workspace, hipStream_t stream) {
+#define W4A16_TCASE(MB_, NB_, WN_)                                                        \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_)                                          \
+    return launch_tile_one<MB_, NB_, WN_>(p, A, Bp, S, C, M, K, N, gmagic,                \
+                                          workspace, stream);
+  W4A16_TILE_VARIANTS(W4A16_TCASE)
+#undef W4A16_TCASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4a16
