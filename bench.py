@@ -14,13 +14,25 @@ read is served by the 256 MB Infinity Cache from an earlier launch.
 Prints one JSON line: whole-step TFLOP/s (the metric), achieved HBM TB/s,
 the roofline object of the dominant kernel (measured with HIP events on the
 launch stream over the timed region), and the CPU oracle timed on the host.
+
+Counter-based HBM traffic (``roofline.traffic``) comes from two rocprofv3
+counter runs of this script, summarised into profiles/ by
+``--pmc-summary``; it is reported only while the kernel sources still hash
+to the value recorded with the counters:
+
+    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe
+    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe
+    python3 bench.py --pmc-summary OUT/fetch OUT/write profiles/pmc_traffic_llama7b_step.json
 """
 
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import sqlite3
 import sys
 import time
 
@@ -33,6 +45,9 @@ LAYERS = [("qkv", 4096, 12288), ("o", 4096, 4096), ("gate_up", 4096, 22016),
 BATCHES = [1, 16, 128]
 GROUP = 128
 WEIGHT_COPIES = 8   # 8 x 101 MB of packed weights: far beyond the 256 MB MALL
+COPY_PROBE_BYTES = 512 * 2**20   # one-dispatch device copy of known size, counter calibration
+COPY_PROBE_RUNS = 4
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama7b_step.json")
 
 
 def parse():
@@ -43,7 +58,134 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-cols", type=int, default=0,
                     help="columns per GEMM for the CPU oracle (0 = whole GEMMs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run a one-dispatch elementwise copy (negation) "
+                         "of 512 MiB a few times: calibrates the HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                         "of this script into a traffic file and exit")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter figures are valid for this code only."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_int4_gemm_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) +
+                       glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short_kernel_name(name: str) -> str:
+    """Kernel name as w4a16_describe() prints it, e.g. 'gemm_tile_kernel<8,2,2>',
+    from a demangled ('void w4a16::gemm_tile_kernel<8, 2, 2>(...)') or mangled
+    ('_ZN5w4a1616gemm_tile_kernelILi8ELi2ELi2EEEv...') profiler name."""
+    import re
+    if name.startswith("_ZN"):
+        # length-prefixed name segments, then I <template args> E
+        i, seg = 3, ""
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            seg, i = name[j:j + n], j + n
+        if name[i:i + 1] == "I":
+            end = name.find("EE", i)
+            args = re.findall(r"Li(-?\d+)E", name[i:end + 2])
+            return f"{seg}<{','.join(args)}>"
+        return seg
+    base = name.split("(")[0].replace("void ", "").strip()
+    head, lt, rest = base.partition("<")
+    return head.split("::")[-1] + lt + rest.replace(" ", "")
+
+
+def _pmc_values(run_dir: str, counter: str):
+    """{kernel name: [value per dispatch]} from a rocprofv3 database."""
+    dbs = glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 results database under {run_dir}")
+    out = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for kname, cname, value in con.execute(
+                "select kernel_name, counter_name, value from counters_collection"):
+            if cname == counter:
+                out.setdefault(kname, []).append(float(value))
+        con.close()
+    return out
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
+    fetch = _pmc_values(fetch_dir, "FETCH_SIZE")
+    write = _pmc_values(write_dir, "WRITE_SIZE")
+
+    def median(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    # the calibration copy: the elementwise negation kernel of the probe
+    copies = [(median(v), k) for k, v in fetch.items()
+              if "neg" in k.lower() and len(v) >= COPY_PROBE_RUNS]
+    if not copies:
+        raise SystemExit("no copy-kernel dispatches found (run with --copy-probe)")
+    copy_fetch_kib, copy_name = max(copies)
+    copy_write_kib = median([x for x in write.get(copy_name, [0.0])])
+    expect_kib = COPY_PROBE_BYTES / 1024
+    fetch_scale = expect_kib / copy_fetch_kib if copy_fetch_kib else None
+    write_scale = expect_kib / copy_write_kib if copy_write_kib else None
+    kernels = {}
+    for k, v in fetch.items():
+        if "gemm" not in k:
+            continue
+        short = _short_kernel_name(k)
+        f = sum(v) / len(v)
+        w_list = write.get(k, [])
+        w = sum(w_list) / len(w_list) if w_list else 0.0
+        kernels[short] = {
+            "dispatches": len(v),
+            "fetch_kib_per_dispatch": f,
+            "write_kib_per_dispatch": w,
+            "hbm_bytes_per_dispatch": (f * (fetch_scale or 1) + w * (write_scale or 1)) * 1024,
+        }
+    summary = {
+        "what": "HBM bytes per dispatch of each GEMM kernel over the Llama-2-7B W4A16 step "
+                "(bench.py workload), from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled "
+                "by what the counter reads for a device copy of known size",
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 "
+            "--warmup 1 --no-cpu-baseline --copy-probe",
+            "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 "
+            "--warmup 1 --no-cpu-baseline --copy-probe",
+            "python3 bench.py --pmc-summary OUT/fetch OUT/write " + os.path.relpath(out_path, ROOT),
+        ],
+        "kernel_source_hash": kernel_source_hash(),
+        "copy_probe": {"kernel": copy_name, "bytes": COPY_PROBE_BYTES,
+                       "fetch_kib": copy_fetch_kib, "write_kib": copy_write_kib,
+                       "fetch_scale": fetch_scale, "write_scale": write_scale},
+        "kernels": kernels,
+    }
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    print(json.dumps(summary, indent=1))
+
+
+def measured_traffic(kernel: str):
+    """Counter-measured HBM bytes per launch of `kernel`, or None when there
+    is no summary or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            summ = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if summ.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = summ.get("kernels", {}).get(kernel)
+    return None if entry is None else entry["hbm_bytes_per_dispatch"]
 
 
 def cpu_baseline(sample_cols: int):
@@ -82,6 +224,9 @@ def cpu_baseline(sample_cols: int):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the W4A16 GEMM runs on a single device and "
@@ -203,7 +348,9 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved,
                 "peak": roofline.MFMA_F16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom_name)
+    roof["traffic_unit"] = "bytes per launch"
+    roof["algorithmic_bytes"] = dom["bytes"] / dom["launches"]
     roof["kernel"] = dom_name
     roof["avg_launch_us"] = avg_s * 1e6
     roof["launches_per_step"] = dom["launches"] // args.steps
@@ -219,6 +366,18 @@ def main():
             "roofline_frac": round(roofline.roofline_seconds(M, K, N, GROUP) / t, 3),
             "bound": roofline.bound(M, K, N, GROUP), "plan": plans[g],
         })
+
+    if args.copy_probe:
+        # torch's elementwise negation: one dispatch that reads and writes
+        # COPY_PROBE_BYTES each (a device-to-device memcpy is split into
+        # many blit dispatches and cannot serve as the reference)
+        n = COPY_PROBE_BYTES // 2
+        src = torch.empty(n, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_PROBE_RUNS):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,0 +1,52 @@
+"""Host-side pieces of bench.py (no GPU): kernel-name parsing for profiler
+output, the source hash that guards counter figures, and the one-GPU rule."""
+
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_kernel_names_from_profiler_output():
+    cases = {
+        "void w4a16::gemm_tile_kernel<8, 2, 2>(_Float16 const*, unsigned int const*)":
+            "gemm_tile_kernel<8,2,2>",
+        "_ZN5w4a1616gemm_tile_kernelILi8ELi2ELi2EEEvPKDF16_PKjS2_PDF16_iiiyiPjPf":
+            "gemm_tile_kernel<8,2,2>",
+        "_ZN5w4a1611gemm_kernelILi1ELi4ELi4ELi2EEEvPKDF16_": "gemm_kernel<1,4,4,2>",
+        "_ZN5w4a1613repack_kernelEPKjPjii": "repack_kernel",
+    }
+    for raw, short in cases.items():
+        assert bench._short_kernel_name(raw) == short
+
+
+def test_source_hash_is_stable():
+    assert bench.kernel_source_hash() == bench.kernel_source_hash()
+    assert len(bench.kernel_source_hash()) == 16
+
+
+def test_traffic_is_null_for_other_sources(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"kernel_source_hash": "0" * 16,
+                             "kernels": {"k<1>": {"hbm_bytes_per_dispatch": 5.0}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(f))
+    assert bench.measured_traffic("k<1>") is None
+    f.write_text(json.dumps({"kernel_source_hash": bench.kernel_source_hash(),
+                             "kernels": {"k<1>": {"hbm_bytes_per_dispatch": 5.0}}}))
+    assert bench.measured_traffic("k<1>") == 5.0
+    assert bench.measured_traffic("k<2>") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                          timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr
+    assert proc.stdout == ""
