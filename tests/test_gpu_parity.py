@@ -142,8 +142,10 @@ def test_gemm_matches_oracle(M, K, N, group):
 
 STREAM_PLANS = ["1,1,4,1,2", "1,1,8,3,4", "1,2,4,2,2", "1,2,8,1,4", "1,4,4,7,2", "1,4,8,2,2",
                 "2,2,4,3,2", "2,4,4,1,2", "4,2,4,5,1", "4,4,4,1,1", "8,2,4,2,1", "8,4,4,1,1"]
-TILE_PLANS = ["4,4,2,1,0,1", "4,4,2,3,0,1", "4,4,4,2,0,1", "8,2,2,1,0,1", "8,2,2,4,0,1",
-              "8,4,2,1,0,1", "8,4,2,5,0,1", "8,4,4,1,0,1", "8,4,4,2,0,1"]
+TILE_PLANS = ["4,2,2,1,4,1", "4,2,4,3,2,1", "4,2,4,1,4,1", "4,2,4,6,4,1", "4,4,2,2,4,1",
+              "4,4,4,1,4,1", "8,1,4,2,2,1", "8,2,2,1,2,1", "8,2,4,5,2,1", "8,4,2,1,2,1",
+              "8,4,4,2,2,1", "8,4,4,1,2,1", "8,4,4,3,4,1", "4,2,4,2,2,1,8", "8,1,4,3,2,1,8",
+              "4,2,4,1,4,1,8"]
 
 
 @pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS)
@@ -178,6 +180,24 @@ def test_gemm_deterministic_and_workspace_reuse():
     for i in range(20):
         if i == 10:
             run_gemm(A2, Bq2, S2, 128, workspace=ws)
+        again = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)
+        assert np.array_equal(first.view(np.uint16), again.view(np.uint16)), f"run {i}"
+    _, C64 = oracle.gemm(A, Bq, S, 128)
+    assert_gemm_close(first, C64)
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 4096, 4096), (64, 11008, 1024), (300, 2048, 512)])
+def test_tile_kernel_split_k_deterministic(M, K, N):
+    """The tile kernel's split-K path: bit-identical repeats on one workspace."""
+    import torch
+    A, Bq, S = make_inputs(M, K, N, 128, seed=M + K)
+    desc = w4.w4a16_describe(M, K, N, 128)
+    assert desc.startswith("gemm_tile_kernel<"), desc
+    ws = w4.alloc_workspace(M, K, N, 128)
+    Bp = repack_on_device(dev(Bq), K, N)
+    say("tile determinism", M, K, N, desc)
+    first = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)
+    for i in range(10):
         again = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)
         assert np.array_equal(first.view(np.uint16), again.view(np.uint16)), f"run {i}"
     _, C64 = oracle.gemm(A, Bq, S, 128)

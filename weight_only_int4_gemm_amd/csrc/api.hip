@@ -63,21 +63,24 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q) {
-  return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk)
+  return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk, q.depth, q.bdepth)
                 : plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
 }
 
-// Test and tuning override: W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile]]"
-// replaces the heuristic's choice when it names a compiled variant (a field
-// <= 0 keeps the heuristic's value; tile is 0, the default, for the
-// streaming kernel or 1 for the tile kernel).  It feeds the same
-// kernels; w4a16_workspace_bytes sees it too, so sizes stay consistent
-// within a process.
+// Test and tuning override:
+// W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile[,bdepth]]]" replaces the
+// heuristic's choice when it names a compiled variant (a field <= 0 keeps
+// the heuristic's value; tile is 0, the default, for the streaming kernel
+// or 1 for the tile kernel).  It feeds the same kernels;
+// w4a16_workspace_bytes sees it too, so sizes stay consistent within a
+// process.
 void apply_forced_plan(Plan* p, int KB) {
   const char* env = std::getenv("W4A16_FORCE_PLAN");
   if (!env || !*env) return;
-  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0;
-  if (std::sscanf(env, "%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile) < 4) return;
+  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0, bdepth = 0;
+  if (std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
+                  &bdepth) < 4)
+    return;
   if (tile != 0 && tile != 1) return;
   Plan q = *p;
   q.tile = tile;  // absent: the streaming kernel
@@ -86,7 +89,8 @@ void apply_forced_plan(Plan* p, int KB) {
   if (wk > 0) q.wk = wk;
   if (splits > 0) q.splits = splits > KB ? KB : splits;
   if (depth > 0) q.depth = depth;
-  if (!q.tile && !variant_is_compiled(q)) {
+  q.bdepth = bdepth > 0 ? bdepth : (q.tile ? 4 : 0);
+  if (!variant_is_compiled(q)) {
     // keep the forced tile but take the first compiled depth for it
     for (int d : {4, 2, 1}) {
       q.depth = d;
@@ -117,24 +121,37 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   if (M <= 16) {
     p.mb = 1;
     if (M <= 4) {
-      p.nb = n16 >= 2 * cus ? 2 : 1;
+      p.nb = n16 >= 4 * cus ? 2 : 1;
+      p.wk = 8;
+      p.depth = 2;
     } else {
-      p.nb = n16 >= 2 * cus ? 4 : (KB >= 64 ? 2 : 1);
+      p.nb = n16 >= 2 * cus || KB >= 64 ? 4 : 1;
+      p.wk = 4;
+      p.depth = KB >= 64 ? 4 : 2;
     }
-    p.wk = KB >= 64 ? 8 : 4;
-    p.depth = 2;
   } else if (M <= 32) {
     p.mb = 2;
     p.nb = 2;
     p.wk = 4;
     p.depth = 2;
-  } else {
-    // tile kernel: 64 or 128 rows by 64 (M > 64) or 128 columns
+  } else if (M <= 128) {
+    // tile kernel, 64 x 128 tiles (four waves of 64 x 32): small tiles keep
+    // enough waves in flight; each weight is unpacked once per 64 rows
     p.tile = 1;
-    p.mb = M <= 64 ? 4 : 8;
-    p.nb = M <= 64 ? 4 : 2;
-    p.wk = 2;
-    p.depth = 0;
+    p.mb = 4;
+    p.nb = 2;
+    p.wk = 4;
+    p.depth = 2;
+    p.bdepth = 4;
+  } else {
+    // prefill: 128 x 256 tiles (four waves of 128 x 64), each weight
+    // unpacked once per 128 rows and each activation fragment used 4 times
+    p.tile = 1;
+    p.mb = 8;
+    p.nb = 4;
+    p.wk = 4;
+    p.depth = 2;
+    p.bdepth = 4;
   }
   auto shape = [&](Plan& q) {
     q.tm = 16 * q.mb;
@@ -148,12 +165,18 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   // streaming kernel up to one workgroup per compute unit, the tile kernel
   // (two waves per workgroup) up to about one and a half.
   int64_t want;
+  int64_t cap;
   if (p.tile) {
-    want = 10 * tiles >= 13 * (int64_t)cus ? 1 : (3 * (int64_t)cus / 2 + tiles - 1) / tiles;
+    // about 1.6 workgroups per compute unit (2 for deep K), at most 8 splits
+    const int64_t target = (KB >= 64 ? 2 : 1) * (int64_t)cus * 8 / 5;
+    want = (target + tiles / 2) / tiles;
+    cap = KB / 4 < 8 ? KB / 4 : 8;
   } else {
-    want = 10 * tiles >= 6 * (int64_t)cus ? 1 : (cus + tiles - 1) / tiles;
+    // one workgroup per compute unit, two for deep K (K >= 8192)
+    const int64_t target = (KB >= 64 ? 2 : 1) * (int64_t)cus;
+    want = 10 * tiles >= 6 * (int64_t)cus ? 1 : (target + tiles - 1) / tiles;
+    cap = KB / (2 * p.wk);
   }
-  int64_t cap = p.tile ? KB / 2 : KB / (2 * p.wk);
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want > 64) want = 64;
@@ -217,9 +240,10 @@ int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   const Plan p = make_plan(M, K, N, group, cus);
   if (p.tile)
     std::snprintf(buf, len,
-                  "gemm_tile_kernel<%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
-                  p.mb, p.nb, p.wk, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk, p.splits,
-                  p.workspace_bytes);
+                  "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
+                  "workspace=%zu",
+                  p.mb, p.nb, p.wk, p.depth, p.bdepth, p.tiles_n, p.tiles_m, p.splits,
+                  64 * p.wk, p.splits, p.workspace_bytes);
   else
     std::snprintf(buf, len,
                   "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",

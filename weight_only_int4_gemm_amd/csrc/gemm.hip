@@ -269,10 +269,11 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
 
 // Compiled variants (MB, NB, WK, D).
 #define W4A16_VARIANTS(X)                                                        \
-  X(1, 1, 4, 2) X(1, 1, 4, 4) X(1, 1, 8, 2) X(1, 1, 8, 4)                        \
-  X(1, 2, 4, 2) X(1, 2, 4, 4) X(1, 2, 8, 2) X(1, 2, 8, 4)                        \
-  X(1, 4, 4, 2) X(1, 4, 8, 2)                                                    \
-  X(2, 2, 4, 2) X(2, 4, 4, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) X(8, 2, 4, 1) X(8, 4, 4, 1)
+  X(1, 1, 4, 2) X(1, 1, 4, 4) X(1, 1, 8, 2) X(1, 1, 8, 4) X(1, 1, 16, 2)         \
+  X(1, 1, 16, 4) X(1, 2, 4, 2) X(1, 2, 4, 4) X(1, 2, 8, 2) X(1, 2, 8, 4)         \
+  X(1, 2, 16, 2) X(1, 4, 4, 2) X(1, 4, 4, 4) X(1, 4, 8, 2) X(1, 4, 16, 2)        \
+  X(2, 2, 4, 2) X(2, 2, 8, 2) X(2, 4, 4, 2) X(2, 4, 8, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) \
+  X(8, 2, 4, 1) X(8, 4, 4, 1)
 
 bool plan_is_compiled(int mb, int nb, int wk, int depth) {
 #define W4A16_MATCH(MB_, NB_, WK_, D_) \

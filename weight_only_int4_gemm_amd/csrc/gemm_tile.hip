@@ -15,7 +15,7 @@
 //  * each wave owns 16*NB columns and all 16*MB rows of the tile, so every
 //    weight is loaded and unpacked exactly once per workgroup; its codes
 //    come straight from global memory into registers (the permuted layout
-//    hands each lane its own fragments), two K blocks ahead;
+//    hands each lane its own fragments), four K blocks ahead;
 //  * the tile's activations for a 128-deep K block sit in LDS and are read
 //    by every wave.  They are copied global -> LDS by the direct 16-byte
 //    load of gfx950 (no staging registers), into one of two stages while
@@ -53,7 +53,7 @@ __device__ __forceinline__ void wait_vmem_at_most() {
 
 }  // namespace
 
-template <int MB, int NB, int WN>
+template <int MB, int NB, int WN, int NS, int DB>
 __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
@@ -65,10 +65,13 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
   constexpr int LOADS = PIECES / 64 / WN;  // direct loads per wave per stage
   static_assert(PIECES % (64 * WN) == 0, "stage must split evenly over the waves");
   constexpr int BLOADS = 2 * NB;           // code + scale loads per wave per K block
-  // Two separate LDS objects (rather than one array of two) let the
-  // compiler see that a direct load into one stage does not touch the other.
+  static_assert(NS == 2 || NS == 4, "two or four activation stages");
+  // Separate LDS objects (rather than one array) let the compiler see that
+  // a direct load into one stage does not touch the others.
   __shared__ uint4 As0[PIECES];
   __shared__ uint4 As1[PIECES];
+  __shared__ uint4 As2[NS > 2 ? PIECES : 1];
+  __shared__ uint4 As3[NS > 2 ? PIECES : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,19 +131,26 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // One K block: per 32-deep step, unpack the wave's NB code words, read the
-  // MB activation fragments (all issued before the first is used), then
-  // MB x NB matrix instructions.
-  auto compute = [&](const uint4* stage, const BSlot<NB>& sl) {
+  // One K block, four 32-deep steps.  The activation fragments of step j+1
+  // are read from LDS before the matrix instructions of step j are issued,
+  // so LDS latency hides behind them; the codes of step j are unpacked
+  // just before they are used.
+  auto read_a = [&](const uint4* stage, int j, half8_t* a) {
     const int lg = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half8_t a[MB];
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = mb * 16 + l16;
+      a[mb] = __builtin_bit_cast(half8_t, stage[r * 16 + ((4 * j + lg) ^ (r & 15))]);
+    }
+  };
+  auto compute = [&](const uint4* stage, const BSlot<NB>& sl) {
+    half8_t a0[MB], a1[MB];
+    read_a(stage, 0, a0);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = mb * 16 + l16;
-        a[mb] = __builtin_bit_cast(half8_t, stage[r * 16 + ((4 * j + lg) ^ (r & 15))]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      half8_t* cur = (j & 1) ? a1 : a0;
+      half8_t* nxt = (j & 1) ? a0 : a1;
+      if (j < 3) read_a(stage, j + 1, nxt);
       half8_t bf[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -152,43 +162,55 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mb], bf[nb], acc[mb][nb], 0, 0, 0);
     }
   };
 
-  // Issue order, which the waits below count on: A(0) B(0) A(1) B(1), then
-  // per K block t: A(t+2) B(t+2).  Loads past the range are clamped to the
-  // last block (harmless re-reads), so every iteration issues the same loads.
+  // The pipeline.  Step t consumes K block kb0 + t from activation stage
+  // t % NS and code slot t % DB.  Step s issues, in this order, the
+  // activations of block s + NS - 1 (into the stage that block s - 1 used,
+  // which every wave has finished with once it passed this step's barrier)
+  // and the codes of block s + DB (into the slot step s has just consumed);
+  // the prologue issues what steps -DB .. -1 would have.  So when step t
+  // waits, the loads allowed to be still in flight are exactly the
+  // activations of blocks t+1 .. t+NS-2 and the NS - 1 code loads issued
+  // after A(t): the codes come from HBM DB blocks ahead, the activations
+  // from L2 NS - 1 blocks ahead, and one barrier per step does.  Loads past
+  // the range are clamped to the last block (harmless re-reads into stages
+  // or slots that are never consumed again).
+  static_assert(DB == 4 || DB == 8, "four or eight code slots");
   const int nblk = kb1 - kb0;  // >= 1: splits never exceed the K blocks
   const int last = kb1 - 1;
-  BSlot<NB> b0, b1;
-  load_a(As0, kb0);
-  load_b(b0, kb0);
-  load_a(As1, kb0 + 1 <= last ? kb0 + 1 : last);
-  load_b(b1, kb0 + 1 <= last ? kb0 + 1 : last);
+  auto clamp = [&](int kb) { return kb <= last ? kb : last; };
+  uint4* const stages[4] = {As0, As1, NS > 2 ? As2 : As0, NS > 2 ? As3 : As1};
+  BSlot<NB> slots[DB];
+#pragma unroll
+  for (int s = -DB; s < 0; ++s) {
+    if (s + NS - 1 >= 0) load_a(stages[(s + NS - 1) % NS], clamp(kb0 + s + NS - 1));
+    load_b(slots[s + DB], clamp(kb0 + s + DB));
+  }
+  constexpr int IN_FLIGHT = (NS - 2) * LOADS + (NS - 1) * BLOADS;
 
+  auto step = [&](int u, int kb) {  // u = t % DB
+    wait_vmem_at_most<IN_FLIGHT>();
+    __syncthreads();  // this block's stage has landed; block kb - 1's is free
+    load_a(stages[(u + NS - 1) % NS], clamp(kb + NS - 1));
+    compute(stages[u % NS], slots[u]);
+    load_b(slots[u], clamp(kb + DB));
+  };
   int t = 0;
-  for (; t + 2 <= nblk; t += 2) {
-    const int kb = kb0 + t;
-    // stage 0 holds block kb: everything but A(kb+1), B(kb+1) has landed
-    wait_vmem_at_most<LOADS + BLOADS>();
-    __syncthreads();
-    compute(As0, b0);
-    __syncthreads();  // all waves are done with stage 0
-    load_a(As0, kb + 2 <= last ? kb + 2 : last);
-    load_b(b0, kb + 2 <= last ? kb + 2 : last);
-    wait_vmem_at_most<LOADS + BLOADS>();
-    __syncthreads();
-    compute(As1, b1);
-    __syncthreads();
-    load_a(As1, kb + 3 <= last ? kb + 3 : last);
-    load_b(b1, kb + 3 <= last ? kb + 3 : last);
+  for (; t + DB <= nblk; t += DB) {
+#pragma unroll
+    for (int u = 0; u < DB; ++u) step(u, kb0 + t + u);
   }
-  if (t < nblk) {
-    wait_vmem_at_most<LOADS + BLOADS>();
-    __syncthreads();
-    compute(As0, b0);
+  // The last, partial round (fewer than DB blocks left).
+#pragma unroll
+  for (int u = 0; u < DB - 1; ++u) {
+    if (t + u < nblk) step(u, kb0 + t + u);
   }
+  // No direct load may still be landing in LDS when the stages are reused
+  // below or the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Output: lane l holds rows 4*(l/16) .. +3 of column l % 16 of each block.
   const int col_base = tile_n * TN + wave * 16 * NB + l16;
@@ -262,7 +284,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
     __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WN>
+template <int MB, int NB, int WN, int NS, int DB>
 static hipError_t launch_tile_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                   const uint16_t* S, uint16_t* C, int M, int K, int N,
                                   uint64_t gmagic, void* workspace,
@@ -274,19 +296,22 @@ static hipError_t launch_tile_one(const Plan& p, const uint16_t* A, const uint32
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  hipLaunchKernelGGL((gemm_tile_kernel<MB, NB, WN>), dim3(p.tiles_n, p.tiles_m, p.splits),
+  hipLaunchKernelGGL((gemm_tile_kernel<MB, NB, WN, NS, DB>), dim3(p.tiles_n, p.tiles_m, p.splits),
                      dim3(64 * WN), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
                      reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
                      M, K, N, gmagic, p.splits, counters, partials);
   return hipGetLastError();
 }
 
-// Compiled tile variants (MB, NB, WN).
-#define W4A16_TILE_VARIANTS(X) X(4, 4, 2) X(4, 4, 4) X(8, 2, 2) X(8, 4, 2) X(8, 4, 4)
+// Compiled tile variants (MB, NB, WN, NS, DB).
+#define W4A16_TILE_VARIANTS(X)                                                      \
+  X(4, 2, 2, 4, 4) X(4, 2, 4, 2, 4) X(4, 2, 4, 2, 8) X(4, 2, 4, 4, 4) X(4, 2, 4, 4, 8) \
+  X(4, 4, 2, 4, 4) X(4, 4, 4, 4, 4) X(8, 1, 4, 2, 4) X(8, 1, 4, 2, 8) X(8, 2, 2, 2, 4) \
+  X(8, 2, 4, 2, 4) X(8, 4, 2, 2, 4) X(8, 4, 4, 2, 4) X(8, 4, 4, 4, 4)
 
-bool tile_is_compiled(int mb, int nb, int wn) {
-#define W4A16_TMATCH(MB_, NB_, WN_) \
-  if (mb == MB_ && nb == NB_ && wn == WN_) return true;
+bool tile_is_compiled(int mb, int nb, int wn, int ns, int db) {
+#define W4A16_TMATCH(MB_, NB_, WN_, NS_, DB_) \
+  if (mb == MB_ && nb == NB_ && wn == WN_ && ns == NS_ && db == DB_) return true;
   W4A16_TILE_VARIANTS(W4A16_TMATCH)
 #undef W4A16_TMATCH
   return false;
@@ -295,10 +320,10 @@ bool tile_is_compiled(int mb, int nb, int wn) {
 hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
                        uint64_t gmagic, void* workspace, hipStream_t stream) {
-#define W4A16_TCASE(MB_, NB_, WN_)                                                        \
-  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_)                                          \
-    return launch_tile_one<MB_, NB_, WN_>(p, A, Bp, S, C, M, K, N, gmagic,                \
-                                          workspace, stream);
+#define W4A16_TCASE(MB_, NB_, WN_, NS_, DB_)                                            \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_ && p.bdepth == DB_)   \
+    return launch_tile_one<MB_, NB_, WN_, NS_, DB_>(p, A, Bp, S, C, M, K, N, gmagic,    \
+                                                    workspace, stream);
   W4A16_TILE_VARIANTS(W4A16_TCASE)
 #undef W4A16_TCASE
   return hipErrorInvalidValue;

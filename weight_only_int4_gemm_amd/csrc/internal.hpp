@@ -17,9 +17,12 @@ namespace w4a16 {
 //         Tile kernel: they split the N tile, which is 16 * nb * wk.
 //  splits K ranges per output tile, one workgroup each; their FP32
 //         partials go through the workspace and are added in split order
-//  depth  K blocks each wave keeps in flight (streaming kernel)
+//  depth  streaming kernel: K blocks each wave keeps in flight; tile
+//         kernel: activation stages in LDS (K blocks of activations in
+//         flight + 1)
+//  bdepth tile kernel: K blocks of codes in flight (register slots)
 struct Plan {
-  int tile, mb, nb, wk, splits, depth;
+  int tile, mb, nb, wk, splits, depth, bdepth;
   int tm, tn;              // output tile of one workgroup
   int tiles_n, tiles_m;
   size_t workspace_bytes;  // 0 when splits == 1
@@ -27,7 +30,7 @@ struct Plan {
 
 Plan make_plan(int M, int K, int N, int group, int cus);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
-bool tile_is_compiled(int mb, int nb, int wn);
+bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);
