@@ -146,23 +146,36 @@ TILE_PLANS = ["4,2,2,1,4,1", "4,2,4,3,2,1", "4,2,4,1,4,1", "4,2,4,6,4,1", "4,4,2
               "4,4,4,1,4,1", "8,1,4,2,2,1", "8,2,2,1,2,1", "8,2,4,5,2,1", "8,4,2,1,2,1",
               "8,4,4,2,2,1", "8,4,4,1,2,1", "8,4,4,3,4,1", "4,2,4,2,2,1,8", "8,1,4,3,2,1,8",
               "4,2,4,1,4,1,8"]
+LDS_PLANS = ["4,2,2,1,3,2", "4,2,4,3,3,2", "4,2,4,1,4,2", "4,2,4,6,4,2", "4,4,4,2,3,2",
+             "8,1,4,3,3,2", "8,2,4,1,2,2", "8,2,4,5,3,2", "8,4,4,2,2,2", "8,4,4,1,3,2"]
+KERNEL_OF_TILE = {0: "gemm_kernel", 1: "gemm_tile_kernel", 2: "gemm_lds_kernel"}
 
 
-@pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS)
-def test_gemm_forced_plans_agree(monkeypatch, plan):
-    """Every compiled variant and split count gives the oracle's answer
-    (M = 45 exercises ragged rows; N = 208 a ragged column tile)."""
+def _forced_plan_case(monkeypatch, plan, group):
+    """M = 45 exercises ragged rows; N = 208 a ragged column tile."""
     M, K, N = 45, 3584, 208
-    A, Bq, S = make_inputs(M, K, N, 128, seed=5)
-    _, C64 = oracle.gemm(A, Bq, S, 128)
+    A, Bq, S = make_inputs(M, K, N, group, seed=5)
+    _, C64 = oracle.gemm(A, Bq, S, group)
     monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
-    desc = w4.w4a16_describe(M, K, N, 128)
+    desc = w4.w4a16_describe(M, K, N, group)
     fields = [int(x) for x in plan.split(",")]
-    kernel = "gemm_tile_kernel" if len(fields) > 5 and fields[5] == 1 else "gemm_kernel"
+    kernel = KERNEL_OF_TILE[fields[5] if len(fields) > 5 else 0]
     assert desc.startswith(kernel + "<"), desc   # the forced variant is the one that runs
-    say("forced plan", plan, desc)
-    C = run_gemm(A, Bq, S, 128)
-    assert_gemm_close(C, C64, f"plan {plan}")
+    say("forced plan", plan, "group", group, desc)
+    C = run_gemm(A, Bq, S, group)
+    assert_gemm_close(C, C64, f"plan {plan} group {group}")
+
+
+@pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS + LDS_PLANS)
+def test_gemm_forced_plans_agree(monkeypatch, plan):
+    """Every compiled variant and split count gives the oracle's answer."""
+    _forced_plan_case(monkeypatch, plan, 128)
+
+
+@pytest.mark.parametrize("plan", ["1,2,4,3,2", "4,2,4,3,2,1", "4,2,4,3,3,2", "8,4,4,2,2,2"])
+def test_gemm_forced_plans_coarse_groups(monkeypatch, plan):
+    """A scale group of four K blocks (512): each K block finds its group row."""
+    _forced_plan_case(monkeypatch, plan, 512)
 
 
 def test_gemm_deterministic_and_workspace_reuse():
@@ -187,15 +200,16 @@ def test_gemm_deterministic_and_workspace_reuse():
 
 
 @pytest.mark.parametrize("M,K,N", [(128, 4096, 4096), (64, 11008, 1024), (300, 2048, 512)])
-def test_tile_kernel_split_k_deterministic(M, K, N):
-    """The tile kernel's split-K path: bit-identical repeats on one workspace."""
+def test_lds_kernel_split_k_deterministic(M, K, N):
+    """The LDS kernel's split-K path, as the heuristic picks it: bit-identical
+    repeats on one workspace."""
     import torch
     A, Bq, S = make_inputs(M, K, N, 128, seed=M + K)
     desc = w4.w4a16_describe(M, K, N, 128)
-    assert desc.startswith("gemm_tile_kernel<"), desc
+    assert desc.startswith("gemm_lds_kernel<") and "splits=1 " not in desc, desc
     ws = w4.alloc_workspace(M, K, N, 128)
     Bp = repack_on_device(dev(Bq), K, N)
-    say("tile determinism", M, K, N, desc)
+    say("lds determinism", M, K, N, desc)
     first = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)
     for i in range(10):
         again = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm_tile.hip", "repack.hip", "dequant.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm_tile.hip", "gemm_lds.hip", "repack.hip", "dequant.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -63,6 +63,7 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q) {
+  if (q.tile == 2) return lds_is_compiled(q.mb, q.nb, q.wk, q.depth);
   return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk, q.depth, q.bdepth)
                 : plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
 }
@@ -70,8 +71,8 @@ bool variant_is_compiled(const Plan& q) {
 // Test and tuning override:
 // W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile[,bdepth]]]" replaces the
 // heuristic's choice when it names a compiled variant (a field <= 0 keeps
-// the heuristic's value; tile is 0, the default, for the streaming kernel
-// or 1 for the tile kernel).  It feeds the same kernels;
+// the heuristic's value; tile is 0, the default, for the streaming kernel,
+// 1 for the tile kernel or 2 for the LDS kernel).  It feeds the same kernels;
 // w4a16_workspace_bytes sees it too, so sizes stay consistent within a
 // process.
 void apply_forced_plan(Plan* p, int KB) {
@@ -81,7 +82,7 @@ void apply_forced_plan(Plan* p, int KB) {
   if (std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
                   &bdepth) < 4)
     return;
-  if (tile != 0 && tile != 1) return;
+  if (tile < 0 || tile > 2) return;
   Plan q = *p;
   q.tile = tile;  // absent: the streaming kernel
   if (mb > 0) q.mb = mb;
@@ -89,10 +90,10 @@ void apply_forced_plan(Plan* p, int KB) {
   if (wk > 0) q.wk = wk;
   if (splits > 0) q.splits = splits > KB ? KB : splits;
   if (depth > 0) q.depth = depth;
-  q.bdepth = bdepth > 0 ? bdepth : (q.tile ? 4 : 0);
+  q.bdepth = bdepth > 0 ? bdepth : (q.tile == 1 ? 4 : 0);
   if (!variant_is_compiled(q)) {
     // keep the forced tile but take the first compiled depth for it
-    for (int d : {4, 2, 1}) {
+    for (int d : {4, 3, 2, 1}) {
       q.depth = d;
       if (variant_is_compiled(q)) break;
     }
@@ -103,15 +104,16 @@ void apply_forced_plan(Plan* p, int KB) {
 
 }  // namespace
 
-// The heuristic (measured on MI355X at the Llama-2-7B layer shapes).
+// The heuristic (measured on MI355X at the Llama-2-7B layer shapes and an
+// 8192 x 28672 prefill layer).
 // Small batches (M <= 16) stream the weights: one 16-row block per wave.
 // With one activation row the activation fragments cost little, so narrow
 // column tiles (16 or 32 columns) give the most workgroups; with 16 rows
 // every wave re-reads its activation fragments, so wide tiles (64 columns)
 // amortise them when N leaves enough tiles.  K is split across workgroups
 // only as far as needed to give every compute unit work, keeping at least
-// two K blocks per wave.  Larger batches take 64 or 128 rows per wave, so
-// each weight is unpacked once for many rows.
+// two K blocks per wave.  Larger batches go to the LDS kernel with 64 or 128
+// rows per wave, so each weight is unpacked once for many rows.
 Plan make_plan(int M, int K, int N, int group, int cus) {
   (void)group;
   Plan p{};
@@ -135,41 +137,39 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
     p.wk = 4;
     p.depth = 2;
   } else if (M <= 128) {
-    // tile kernel, 64 x 128 tiles (four waves of 64 x 32): small tiles keep
-    // enough waves in flight; each weight is unpacked once per 64 rows
-    p.tile = 1;
+    // LDS kernel, 64 x 128 tiles (four waves of 64 x 32): small tiles keep
+    // enough workgroups; each weight is unpacked once per 64 rows
+    p.tile = 2;
     p.mb = 4;
     p.nb = 2;
     p.wk = 4;
-    p.depth = 2;
-    p.bdepth = 4;
+    p.depth = 3;
   } else {
     // prefill: 128 x 256 tiles (four waves of 128 x 64), each weight
     // unpacked once per 128 rows and each activation fragment used 4 times
-    p.tile = 1;
+    p.tile = 2;
     p.mb = 8;
     p.nb = 4;
     p.wk = 4;
-    p.depth = 2;
-    p.bdepth = 4;
+    p.depth = 3;
   }
   auto shape = [&](Plan& q) {
     q.tm = 16 * q.mb;
-    q.tn = 16 * q.nb * (q.tile ? q.wk : 1);
+    q.tn = 16 * q.nb * (q.tile ? q.wk : 1);  // tile and LDS kernels split N over waves
     q.tiles_n = (N + q.tn - 1) / q.tn;
     q.tiles_m = (M + q.tm - 1) / q.tm;
   };
   shape(p);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
   // Split K only when the tiles leave many compute units idle: the
-  // streaming kernel up to one workgroup per compute unit, the tile kernel
-  // (two waves per workgroup) up to about one and a half.
+  // streaming kernel up to one workgroup per compute unit (two for deep K),
+  // the tile and LDS kernels up to about one workgroup per compute unit.
   int64_t want;
   int64_t cap;
   if (p.tile) {
-    // about 1.6 workgroups per compute unit (2 for deep K), at most 8 splits
-    const int64_t target = (KB >= 64 ? 2 : 1) * (int64_t)cus * 8 / 5;
-    want = (target + tiles / 2) / tiles;
+    // whole splits only: an extra, partly filled wave of workgroups costs
+    // more than idle compute units
+    want = cus / tiles;
     cap = KB / 4 < 8 ? KB / 4 : 8;
   } else {
     // one workgroup per compute unit, two for deep K (K >= 8192)
@@ -238,7 +238,12 @@ int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan p = make_plan(M, K, N, group, cus);
-  if (p.tile)
+  if (p.tile == 2)
+    std::snprintf(buf, len,
+                  "gemm_lds_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                  p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
+                  p.splits, p.workspace_bytes);
+  else if (p.tile)
     std::snprintf(buf, len,
                   "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
                   "workspace=%zu",

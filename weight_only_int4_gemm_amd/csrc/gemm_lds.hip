@@ -1,0 +1,257 @@
+// The W4A16 GEMM for batches of more than 32 rows, with every operand
+// staged through LDS: C = A . dequant(Bpacked).
+//
+// Same work decomposition as the tile kernel (gemm_tile.hip): a workgroup of
+// WN waves owns a 16*MB x 16*NB*WN output tile and one K range; each wave
+// owns 16*NB columns and all rows, so every weight is unpacked once per
+// workgroup.  The difference is the load pipeline.  Vector-memory loads of a
+// wave complete in issue order, so in the tile kernel the wait for an
+// activation stage also waits for every code load issued before it, and the
+// codes (which come from HBM) never get more than a couple of K blocks of
+// latency allowance however early they are issued.  Here one K block's
+// activations, codes and scales form one LDS stage and are all brought in by
+// the direct 16-byte global -> LDS load ("Quant Marlin kernel" explainer,
+// "The architecture", top row: async copies of the next tile into shared
+// memory while the current one is multiplied; "End-to-end flow": loads for
+// the tile after next already in flight).  With NS stages, the loads of a
+// stage are issued NS - 1 K blocks before the stage is consumed, and the
+// single count-based wait before a step covers exactly the loads of that
+// step's stage.
+//
+// Stage layout (per K block):
+//  * activations: 16*MB rows x 16 pieces of 16 bytes, piece c of row r at
+//    slot c ^ (r & 15) (conflict-free fragment reads, as in the tile kernel);
+//  * codes: the NB*WN fragment blocks of the tile, 1 KiB each, in the
+//    permuted layout's own order (lane l's four words at 16*l), so a wave
+//    reads its fragments with one conflict-free 16-byte read per block;
+//  * scales: the tile's 16*NB*WN FP16 scales of this K block's group.
+#include <type_traits>
+
+#include "layout.hpp"
+#include "tile_common.hpp"
+#include "unpack.hpp"
+
+namespace w4a16 {
+
+template <int MB, int NB, int WN, int NS>
+__global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
+    const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
+    const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
+    uint64_t group_magic, int splits, unsigned* __restrict__ counters,
+    float* __restrict__ partials) {
+  constexpr int TM = 16 * MB;
+  constexpr int TN = 16 * NB * WN;
+  constexpr int APIECES = TM * 16;             // 16-byte pieces of activations
+  constexpr int ALOADS = APIECES / 64 / WN;    // direct loads per wave
+  static_assert(APIECES % (64 * WN) == 0, "activations must split evenly over the waves");
+  constexpr int BPIECES = NB * WN * 64;        // 16-byte pieces of codes
+  constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
+  constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
+  constexpr int LOADS = ALOADS + NB + SLOADS;  // direct loads per wave per stage
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  struct Stage {
+    uint4 a[APIECES];
+    uint4 b[BPIECES];
+    uint32_t s[64 * SLOADS];
+  };
+  // one LDS object per stage: the compiler sees that a load into one stage
+  // does not touch the others
+  __shared__ Stage st0;
+  __shared__ Stage st1;
+  // stages 2 and 3 only where NS asks for them (a byte otherwise)
+  __shared__ typename std::conditional<(NS > 2), Stage, char>::type st2;
+  __shared__ typename std::conditional<(NS > 3), Stage, char>::type st3;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile_n = blockIdx.x;
+  const int tile_m = blockIdx.y;
+  const int split = blockIdx.z;
+  const int KB = K / kBlockK;
+  const int kb0 = (int)((int64_t)KB * split / splits);
+  const int kb1 = (int)((int64_t)KB * (split + 1) / splits);
+  const int l16 = lane & 15;
+  const int row0 = tile_m * TM;
+  const int col0 = tile_n * TN;
+  const int n16_last = N / kBlockN - 1;
+
+  // Code source of this wave's column blocks (blocks past N re-read the last
+  // valid one; their columns are dropped at the store).
+  const uint32_t* bsrc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n16 = tile_n * NB * WN + wave * NB + nb;
+    bsrc[nb] = Bp + block_word_offset(n16 <= n16_last ? n16 : n16_last, 0, K) +
+               lane * kWordsPerLane;
+  }
+  // Scale source: word i*64 + lane of the stage holds columns 2w, 2w+1.
+  const _Float16* ssrc[SLOADS];
+#pragma unroll
+  for (int i = 0; i < SLOADS; ++i) {
+    const int c = col0 + 2 * (64 * i + lane);
+    ssrc[i] = S + (c <= N - 2 ? c : N - 2);
+  }
+  auto scale_row = [&](int kb) -> int {
+    return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
+  };
+
+  auto load_stage = [&](Stage& sg, int kb) {
+#pragma unroll
+    for (int i = 0; i < ALOADS; ++i) {
+      // activation load i of this wave: stage pieces 64 * (wave + WN * i) + lane
+      const int r = 4 * (wave + WN * i) + (lane >> 4);
+      const int piece = l16 ^ (r & 15);
+      const int gr = row0 + r < M ? row0 + r : M - 1;  // rows past M: never stored
+      const _Float16* src = A + (int64_t)gr * K + kb * kBlockK + piece * 8;
+      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)&sg.a[64 * (wave + WN * i)],
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[nb] + kb * kWordsPerBlock),
+                                       (lds_ptr_t)&sg.b[64 * (wave * NB + nb)], 16, 0, 0);
+    }
+    const int srow = scale_row(kb) * N;
+#pragma unroll
+    for (int i = 0; i < SLOADS; ++i) {
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(ssrc[i] + srow), (lds_ptr_t)&sg.s[64 * i],
+                                       4, 0, 0);
+    }
+  };
+
+  float4_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto read_a = [&](const Stage& sg, int j, half8_t* a) {
+    const int lg = lane >> 4;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = mb * 16 + l16;
+      a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + ((4 * j + lg) ^ (r & 15))]);
+    }
+  };
+  // One K block in four 32-deep slices.  Software-pipelined by one slice:
+  // while the matrix instructions of slice j run, the activation fragments
+  // of slice j+1 are read and its codes unpacked, so the vector ALU work has
+  // independent matrix work to overlap with.
+  auto compute = [&](const Stage& sg) {
+    uint4 w[NB];
+    half2_t s2[NB];
+    const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      w[nb] = sg.b[64 * (wave * NB + nb) + lane];
+      const _Float16 sc = sh[wave * 16 * NB + nb * 16 + l16];
+      s2[nb] = half2_t{sc, sc};
+    }
+    auto unpack_slice = [&](int j, half8_t* bf) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t word = j == 0 ? w[nb].x : j == 1 ? w[nb].y : j == 2 ? w[nb].z : w[nb].w;
+        bf[nb] = unpack_scale(word, s2[nb]);
+      }
+    };
+    half8_t a0[MB], a1[MB];
+    half8_t b0[NB], b1[NB];
+    read_a(sg, 0, a0);
+    unpack_slice(0, b0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half8_t* cur = (j & 1) ? a1 : a0;
+      half8_t* nxt = (j & 1) ? a0 : a1;
+      half8_t* bcur = (j & 1) ? b1 : b0;
+      half8_t* bnxt = (j & 1) ? b0 : b1;
+      if (j < 3) {
+        read_a(sg, j + 1, nxt);
+        unpack_slice(j + 1, bnxt);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+    }
+  };
+
+  // The pipeline: step t consumes stage t % NS; before it, once every wave
+  // has passed the step's barrier (so the stage of block t - 1 is free), the
+  // loads of block t + NS - 1 go into that stage.  The prologue fills stages
+  // 0 .. NS-2.  Loads past the range are clamped to the last block
+  // (harmless re-reads into a stage that is never consumed again).
+  const int nblk = kb1 - kb0;  // >= 1: splits never exceed the K blocks
+  const int last = kb1 - 1;
+  auto clamp = [&](int kb) { return kb <= last ? kb : last; };
+  Stage* const stages[4] = {&st0, &st1, NS > 2 ? reinterpret_cast<Stage*>(&st2) : &st0,
+                            NS > 3 ? reinterpret_cast<Stage*>(&st3) : &st1};
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) load_stage(*stages[s], clamp(kb0 + s));
+  auto step = [&](int u, int kb) {  // u = t % NS
+    stage_barrier<(NS - 2) * LOADS>();
+    load_stage(*stages[(u + NS - 1) % NS], clamp(kb + NS - 1));
+    keep_load_order();  // issue the loads before this step's work, not after
+    compute(*stages[u]);
+  };
+  int t = 0;
+  for (; t + NS <= nblk; t += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(u, kb0 + t + u);
+  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) {
+    if (t + u < nblk) step(u, kb0 + t + u);
+  }
+  // No direct load may still be landing in LDS when the stages are reused
+  // below or the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  store_output_tile<MB, NB, WN>(acc, C, M, N, row0, col0, split, splits, counters, partials,
+                                reinterpret_cast<int*>(&st0.s[0]));
+}
+
+template <int MB, int NB, int WN, int NS>
+static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
+                                 const uint16_t* S, uint16_t* C, int M, int K, int N,
+                                 uint64_t gmagic, void* workspace, hipStream_t stream) {
+  unsigned* counters = nullptr;
+  float* partials = nullptr;
+  if (p.splits > 1) {
+    counters = static_cast<unsigned*>(workspace);
+    partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        counters_bytes(p.tiles_n * p.tiles_m));
+  }
+  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS>), dim3(p.tiles_n, p.tiles_m, p.splits),
+                     dim3(64 * WN), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
+                     reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
+                     M, K, N, gmagic, p.splits, counters, partials);
+  return hipGetLastError();
+}
+
+// Compiled variants (MB, NB, WN, NS).
+#define W4A16_LDS_VARIANTS(X)                                                   \
+  X(4, 2, 2, 3) X(4, 2, 4, 3) X(4, 2, 4, 4) X(4, 4, 4, 3) X(8, 1, 4, 3)          \
+  X(8, 2, 4, 2) X(8, 2, 4, 3) X(8, 4, 4, 2) X(8, 4, 4, 3)
+
+bool lds_is_compiled(int mb, int nb, int wn, int ns) {
+#define W4A16_LMATCH(MB_, NB_, WN_, NS_) \
+  if (mb == MB_ && nb == NB_ && wn == WN_ && ns == NS_) return true;
+  W4A16_LDS_VARIANTS(W4A16_LMATCH)
+#undef W4A16_LMATCH
+  return false;
+}
+
+hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
+                      const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
+                      void* workspace, hipStream_t stream) {
+#define W4A16_LCASE(MB_, NB_, WN_, NS_)                                            \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_)                 \
+    return launch_lds_one<MB_, NB_, WN_, NS_>(p, A, Bp, S, C, M, K, N, gmagic,     \
+                                              workspace, stream);
+  W4A16_LDS_VARIANTS(W4A16_LCASE)
+#undef W4A16_LCASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4a16

@@ -25,31 +25,23 @@
 //    its sixteen 16-byte pieces in a row-dependent order (piece c of row r
 //    at slot c ^ (r & 15)), so the sixteen rows a wave reads in one fragment
 //    load fall in distinct banks.
-#include "coherent.hpp"
-#include "internal.hpp"
 #include "layout.hpp"
+#include "tile_common.hpp"
 #include "unpack.hpp"
 
 namespace w4a16 {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* global_ptr_t;
-
 template <int NB>
 struct BSlot {
   uint4 b[NB];
-  half2_t s[NB];
+  // The scale's bits as loaded, one per register; they are broadcast to
+  // both halves only where they are used, so no instruction right after the
+  // load has to wait for it (that wait would drain every load in flight,
+  // loads completing in order).
+  uint32_t s[NB];
 };
-
-// s_waitcnt that waits until at most n vector-memory operations of this
-// wave are outstanding (and leaves the other counters alone).
-template <int n>
-__device__ __forceinline__ void wait_vmem_at_most() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
 
 }  // namespace
 
@@ -120,8 +112,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + kb * kWordsPerBlock);
-      const _Float16 sc = scol[nb][srow];
-      sl.s[nb] = half2_t{sc, sc};
+      sl.s[nb] = reinterpret_cast<const uint16_t*>(scol[nb])[srow];
     }
   };
 
@@ -156,7 +147,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
       for (int nb = 0; nb < NB; ++nb) {
         const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
                          : j == 2 ? sl.b[nb].z : sl.b[nb].w;
-        bf[nb] = unpack_scale(w, sl.s[nb]);
+        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)sl.s[nb]);
+        bf[nb] = unpack_scale(w, half2_t{sc, sc});
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -187,14 +179,16 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
 #pragma unroll
   for (int s = -DB; s < 0; ++s) {
     if (s + NS - 1 >= 0) load_a(stages[(s + NS - 1) % NS], clamp(kb0 + s + NS - 1));
+    keep_load_order();
     load_b(slots[s + DB], clamp(kb0 + s + DB));
+    keep_load_order();
   }
   constexpr int IN_FLIGHT = (NS - 2) * LOADS + (NS - 1) * BLOADS;
 
   auto step = [&](int u, int kb) {  // u = t % DB
-    wait_vmem_at_most<IN_FLIGHT>();
-    __syncthreads();  // this block's stage has landed; block kb - 1's is free
+    stage_barrier<IN_FLIGHT>();  // this block's stage has landed; block kb - 1's is free
     load_a(stages[(u + NS - 1) % NS], clamp(kb + NS - 1));
+    keep_load_order();
     compute(stages[u % NS], slots[u]);
     load_b(slots[u], clamp(kb + DB));
   };
@@ -212,76 +206,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Output: lane l holds rows 4*(l/16) .. +3 of column l % 16 of each block.
-  const int col_base = tile_n * TN + wave * 16 * NB + l16;
-  if (splits == 1) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int gc = col_base + nb * 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
-          if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][i];
-        }
-      }
-    return;
-  }
-
-  // Split-K: publish the partial tile with device-coherent stores, wait for
-  // them, count the arrival; the last workgroup adds the partials in split
-  // order and writes C.  A partial is kept in fragment order -- wave,
-  // 16-row block, 16-column block, lane, four values -- so that each lane
-  // moves its four accumulators in one 16-byte access and the workgroup
-  // that sums finds its own fragments at the same places.  (The flag that
-  // says which workgroup is last lives in the now idle activation stages.)
-  int* s_last = reinterpret_cast<int*>(&As0[0]);
-  const int tile = tile_m * gridDim.x + tile_n;
-  constexpr int TE = TM * TN;
-  const float* tile_base = partials + (int64_t)tile * splits * TE;
-  const int frag0 = wave * MB * NB * 64 + lane;
-  {
-    const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) store_coherent(mine, frag0 + (mb * NB + nb) * 64, acc[mb][nb]);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = prev == (unsigned)(splits - 1);
-  }
-  __syncthreads();
-  if (!*s_last) return;
-
-  // Sum in split order 0, 1, ... into the (now free) accumulators.
-  for (int s = 0; s < splits; ++s) {
-    const __amdgpu_buffer_rsrc_t ps = coherent_rsrc(tile_base + (int64_t)s * TE);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float4_t x = load_coherent(ps, frag0 + (mb * NB + nb) * 64);
-        acc[mb][nb] = s == 0 ? x : acc[mb][nb] + x;
-      }
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int gc = col_base + nb * 16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
-        if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][i];
-      }
-    }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  store_output_tile<MB, NB, WN>(acc, C, M, N, row0, tile_n * TN, split, splits, counters,
+                                partials, reinterpret_cast<int*>(&As0[0]));
 }
 
 template <int MB, int NB, int WN, int NS, int DB>

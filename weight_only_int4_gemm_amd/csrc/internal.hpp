@@ -9,17 +9,20 @@ namespace w4a16 {
 
 // How one w4a16_gemm call is cut into work.
 //  tile   0: the streaming kernel (small batches), 1: the tile kernel
+//         (codes through registers), 2: the LDS kernel (every operand
+//         through LDS stages)
 //  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
 //  nb     16-column blocks per wave
 //  wk     waves per workgroup.  Streaming kernel: they split the
 //         workgroup's K range (every wk-th 128-deep K block each) and their
 //         sums are added in wave order through LDS; the N tile is 16 * nb.
-//         Tile kernel: they split the N tile, which is 16 * nb * wk.
+//         Tile and LDS kernels: they split the N tile, which is
+//         16 * nb * wk.
 //  splits K ranges per output tile, one workgroup each; their FP32
 //         partials go through the workspace and are added in split order
 //  depth  streaming kernel: K blocks each wave keeps in flight; tile
 //         kernel: activation stages in LDS (K blocks of activations in
-//         flight + 1)
+//         flight + 1); LDS kernel: stages of activations, codes and scales
 //  bdepth tile kernel: K blocks of codes in flight (register slots)
 struct Plan {
   int tile, mb, nb, wk, splits, depth, bdepth;
@@ -31,6 +34,7 @@ struct Plan {
 Plan make_plan(int M, int K, int N, int group, int cus);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
+bool lds_is_compiled(int mb, int nb, int wn, int ns);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);
@@ -39,6 +43,9 @@ hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
 hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
                        uint64_t gmagic, void* workspace, hipStream_t stream);
+hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
+                      const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
+                      void* workspace, hipStream_t stream);
 hipError_t launch_gemm(const Plan& plan, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
                        int group, void* workspace, hipStream_t stream);

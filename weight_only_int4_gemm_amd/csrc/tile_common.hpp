@@ -1,0 +1,125 @@
+// Pieces shared by the two LDS-staged GEMM kernels (gemm_tile.hip,
+// gemm_lds.hip): address-space casts for the direct global -> LDS load, a
+// count-based wait, and the output stage with its split-K hand-off.
+#pragma once
+
+#include "coherent.hpp"
+#include "internal.hpp"
+
+namespace w4a16 {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* global_ptr_t;
+
+// s_waitcnt that waits until at most n vector-memory operations of this
+// wave are outstanding (and leaves the other counters alone).  Loads return
+// in issue order, so this is "everything but the n most recent".
+template <int n>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Keeps the compiler from moving memory operations across this point.  The
+// count-based waits assume the loads leave in program order (direct loads
+// into LDS and plain loads into registers touch different memory, so
+// without it the scheduler may interleave them).
+__device__ __forceinline__ void keep_load_order() { asm volatile("" ::: "memory"); }
+
+// The barrier between two K blocks of a pipeline whose stages are filled by
+// direct global -> LDS loads: wait until at most n of this wave's loads are
+// outstanding and its LDS reads have returned, then meet the other waves.
+// __syncthreads() would add a workgroup-scope release fence, and for the
+// compiler a release fence has to wait for every direct load still writing
+// LDS -- including the stages loaded for later K blocks, which would shrink
+// the pipeline to a single K block.  The stages in flight are not ones any
+// wave reads before a later barrier, so the count-based wait is all the
+// ordering needed.  The empty asm keeps the compiler from moving LDS reads
+// or writes across the barrier.
+template <int n>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  keep_load_order();
+}
+
+// Write a workgroup's output tile.  acc[mb][nb] holds, in lane l, rows
+// 4*(l/16) .. +3 of column l % 16 of the 16x16 block (mb, nb) of this wave,
+// whose columns start at tile column wave * 16 * NB.
+//
+// With splits > 1: publish the partial tile with device-coherent stores,
+// wait for them, count the arrival; the last workgroup of the tile adds the
+// partials in split order and writes C.  A partial is kept in fragment
+// order -- wave, 16-row block, 16-column block, lane, four values -- so each
+// lane moves its four accumulators in one 16-byte access and the workgroup
+// that sums finds its own fragments at the same places.  `flag` is an int in
+// LDS no wave touches any more.
+template <int MB, int NB, int WN>
+__device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
+                                                  _Float16* __restrict__ C, int M, int N,
+                                                  int row0, int col0, int split, int splits,
+                                                  unsigned* __restrict__ counters,
+                                                  float* __restrict__ partials, int* flag) {
+  constexpr int TM = 16 * MB;
+  constexpr int TN = 16 * NB * WN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int col_base = col0 + wave * 16 * NB + l16;
+  auto write_c = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int gc = col_base + nb * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
+          if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][i];
+        }
+      }
+  };
+  if (splits == 1) {
+    write_c();
+    return;
+  }
+
+  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+  constexpr int TE = TM * TN;
+  const float* tile_base = partials + (int64_t)tile * splits * TE;
+  const int frag0 = wave * MB * NB * 64 + lane;
+  {
+    const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) store_coherent(mine, frag0 + (mb * NB + nb) * 64, acc[mb][nb]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev == (unsigned)(splits - 1);
+  }
+  __syncthreads();
+  if (!*flag) return;
+
+  // Sum in split order 0, 1, ... into the (now free) accumulators.
+  for (int s = 0; s < splits; ++s) {
+    const __amdgpu_buffer_rsrc_t ps = coherent_rsrc(tile_base + (int64_t)s * TE);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float4_t x = load_coherent(ps, frag0 + (mb * NB + nb) * 64);
+        acc[mb][nb] = s == 0 ? x : acc[mb][nb] + x;
+      }
+  }
+  write_c();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace w4a16
