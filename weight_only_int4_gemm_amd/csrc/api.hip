@@ -137,20 +137,21 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
     p.wk = 4;
     p.depth = 2;
   } else if (M <= 128) {
-    // LDS kernel, 64 x 128 tiles (four waves of 64 x 32): small tiles keep
-    // enough workgroups; each weight is unpacked once per 64 rows
+    // LDS kernel, 64 x 128 tiles (eight waves of 64 x 16, two per SIMD):
+    // small tiles keep enough workgroups; each weight is unpacked once per
+    // 64 rows
     p.tile = 2;
     p.mb = 4;
-    p.nb = 2;
-    p.wk = 4;
+    p.nb = 1;
+    p.wk = 8;
     p.depth = 3;
   } else {
-    // prefill: 128 x 256 tiles (four waves of 128 x 64), each weight
-    // unpacked once per 128 rows and each activation fragment used 4 times
+    // prefill: 128 x 256 tiles (eight waves of 128 x 32), each weight
+    // unpacked once per 128 rows
     p.tile = 2;
     p.mb = 8;
-    p.nb = 4;
-    p.wk = 4;
+    p.nb = 2;
+    p.wk = 8;
     p.depth = 3;
   }
   auto shape = [&](Plan& q) {

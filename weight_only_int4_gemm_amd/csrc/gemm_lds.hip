@@ -188,11 +188,22 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
                             NS > 3 ? reinterpret_cast<Stage*>(&st3) : &st1};
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) load_stage(*stages[s], clamp(kb0 + s));
+  // A wave issues in order, and a direct load waits at issue while the
+  // address unit is busy with earlier ones (a burst of a dozen 1 KiB loads
+  // from four waves stalls each wave for hundreds of cycles).  So the
+  // step's loads are spread between its matrix instructions: one load
+  // after every MFMA_PER_LOAD of them.
+  constexpr int NMFMA = 4 * MB * NB;
+  constexpr int MFMA_PER_LOAD = NMFMA / (LOADS + 1) > 0 ? NMFMA / (LOADS + 1) : 1;
   auto step = [&](int u, int kb) {  // u = t % NS
     stage_barrier<(NS - 2) * LOADS>();
     load_stage(*stages[(u + NS - 1) % NS], clamp(kb + NS - 1));
-    keep_load_order();  // issue the loads before this step's work, not after
     compute(*stages[u]);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, MFMA_PER_LOAD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0010, 1, 0);
+    }
   };
   int t = 0;
   for (; t + NS <= nblk; t += NS) {
@@ -232,7 +243,8 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
 // Compiled variants (MB, NB, WN, NS).
 #define W4A16_LDS_VARIANTS(X)                                                   \
   X(4, 2, 2, 3) X(4, 2, 4, 3) X(4, 2, 4, 4) X(4, 4, 4, 3) X(8, 1, 4, 3)          \
-  X(8, 2, 4, 2) X(8, 2, 4, 3) X(8, 4, 4, 2) X(8, 4, 4, 3)
+  X(8, 2, 4, 2) X(8, 2, 4, 3) X(8, 4, 4, 2) X(8, 4, 4, 3) X(4, 1, 8, 3) X(4, 2, 8, 3)     \
+  X(8, 1, 8, 3) X(8, 2, 8, 3)
 
 bool lds_is_compiled(int mb, int nb, int wn, int ns) {
 #define W4A16_LMATCH(MB_, NB_, WN_, NS_) \
