@@ -23,6 +23,12 @@ to the value recorded with the counters:
     rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe
     rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe
     python3 bench.py --pmc-summary OUT/fetch OUT/write profiles/pmc_traffic_llama7b_step.json
+
+``--configs-report OUT.md`` instead times every workload shape one GEMM at a
+time (the single 4096 x 4096 layer, the Llama-2-7B layers, the 18432 x 73728
+batch sweep, the 8192 x 28672 prefill layer and the deep-K layers with group
+128 and group K) and writes a table of time, TFLOP/s, HBM TB/s and roofline
+fraction per call.
 """
 
 from __future__ import annotations
@@ -49,6 +55,22 @@ COPY_PROBE_BYTES = 512 * 2**20   # one-dispatch device copy of known size, count
 COPY_PROBE_RUNS = 4
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama7b_step.json")
 
+# Every workload shape, for --configs-report: (label, K, N, group, batch sizes).
+REPORT_SHAPES = [
+    ("single layer 4096x4096", 4096, 4096, 128, [16]),
+    ("Llama-2-7B qkv", 4096, 12288, 128, [1, 16, 128]),
+    ("Llama-2-7B o", 4096, 4096, 128, [1, 16, 128]),
+    ("Llama-2-7B gate/up", 4096, 22016, 128, [1, 16, 128]),
+    ("Llama-2-7B down", 11008, 4096, 128, [1, 16, 128]),
+    ("large layer 18432x73728", 18432, 73728, 128, [1, 2, 4, 8, 16, 32, 64, 128]),
+    ("prefill 8192x28672", 8192, 28672, 128, [512, 1024, 4096]),
+    ("deep K 28672x8192, group 128", 28672, 8192, 128, [1, 8, 32]),
+    ("deep K 28672x8192, group K", 28672, 8192, 28672, [1, 8, 32]),
+    ("deep K 13824x5120, group 128", 13824, 5120, 128, [1, 8, 32]),
+    ("deep K 13824x5120, group K", 13824, 5120, 13824, [1, 8, 32]),
+]
+ROTATE_BYTES = 512 * 10**6   # weight copies cycled per shape: beyond the 256 MB MALL
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -61,6 +83,9 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a one-dispatch elementwise copy (negation) "
                          "of 512 MiB a few times: calibrates the HBM byte counters")
+    ap.add_argument("--configs-report", metavar="OUT",
+                    help="time every workload shape, one GEMM at a time, write a "
+                         "markdown table to OUT and exit")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script into a traffic file and exit")
@@ -222,10 +247,96 @@ def cpu_baseline(sample_cols: int):
     }
 
 
+def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
+    """Time each workload shape one GEMM at a time: hipEvents around
+    ``launches`` back-to-back calls that cycle over enough copies of the
+    packed weights to exceed the Infinity Cache, median of ``repeats``."""
+    import numpy as np
+    import torch
+
+    import weight_only_int4_gemm_amd as w4
+    from weight_only_int4_gemm_amd import roofline
+    from synth import make_activations, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = w4.load()
+    sh = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for label, K, N, group, batches in REPORT_SHAPES:
+        _, Bq, S = make_inputs(1, K, N, group, seed=0)
+        Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
+        first = w4.alloc_packed(K, N)
+        w4.w4a16_repack(Bq_d, first, K, N)
+        del Bq_d, Bq
+        ncopy = max(1, -(-ROTATE_BYTES // (K * N // 2)))
+        copies = [first] + [first.clone() for _ in range(ncopy - 1)]
+        S_d = torch.from_numpy(S).to(dev)
+        for M in batches:
+            A_d = torch.from_numpy(make_activations(M, K, seed=M)).to(dev)
+            C_d = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, group), 256),
+                             dtype=torch.uint8, device=dev)
+            calls = [(A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K, N,
+                      group, ws.data_ptr(), sh) for c in copies]
+            for i in range(max(5, ncopy)):
+                rc = lib.w4a16_gemm(*calls[i % ncopy])
+                if rc != 0:
+                    raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(repeats):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(launches):
+                    lib.w4a16_gemm(*calls[i % ncopy])
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e-3 / launches)
+            t = float(np.median(times))
+            flops = roofline.flops(M, K, N)
+            nbytes = roofline.algorithmic_bytes(M, K, N, group)
+            rows.append(dict(shape=label, M=M, K=K, N=N, group=group, us=t * 1e6,
+                             tflops=flops / t / 1e12, tbps=nbytes / t / 1e12,
+                             bound=roofline.bound(M, K, N, group),
+                             frac=roofline.roofline_seconds(M, K, N, group) / t,
+                             plan=w4.w4a16_describe(M, K, N, group).split(" workspace")[0]))
+            print(json.dumps(rows[-1]), flush=True)
+            del A_d, C_d, ws
+        del copies, first, S_d
+        torch.cuda.empty_cache()
+
+    lines = [
+        "# W4A16 GEMM on one MI355X: every workload shape",
+        "",
+        "Command (repository root, GPU box): `python3 bench.py --configs-report " +
+        os.path.relpath(out_path, ROOT) + "`",
+        "",
+        f"Kernel source hash: `{kernel_source_hash()}`. Per call: hipEvents around "
+        f"{launches} back-to-back launches cycling over enough copies of the packed weights "
+        f"to exceed 512 MB (so weights come from HBM, not the Infinity Cache), median of "
+        f"{repeats} repeats; the time includes launch gaps. Inputs: seeded synthetic data "
+        "(weights seed 0, activations seed M). Roofline: HBM 8 TB/s, dense FP16 MFMA "
+        "2.5 PFLOP/s; `frac` is the bound's time over the measured time.",
+        "",
+        "| shape | M | us | TFLOP/s | HBM TB/s | bound | frac | plan |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| {r['shape']} | {r['M']} | {r['us']:.1f} | {r['tflops']:.1f} | "
+                     f"{r['tbps']:.2f} | {r['bound']} | {r['frac']:.3f} | `{r['plan']}` |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.configs_report:
+        configs_report(args.configs_report)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

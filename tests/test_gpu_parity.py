@@ -148,7 +148,9 @@ TILE_PLANS = ["4,2,2,1,4,1", "4,2,4,3,2,1", "4,2,4,1,4,1", "4,2,4,6,4,1", "4,4,2
               "4,2,4,1,4,1,8"]
 LDS_PLANS = ["4,2,2,1,3,2", "4,2,4,3,3,2", "4,2,4,1,4,2", "4,2,4,6,4,2", "4,4,4,2,3,2",
              "8,1,4,3,3,2", "8,2,4,1,2,2", "8,2,4,5,3,2", "8,4,4,2,2,2", "8,4,4,1,3,2",
-             "4,1,8,2,3,2", "4,2,8,1,3,2", "8,1,8,3,3,2", "8,2,8,1,3,2"]
+             "4,1,8,2,3,2", "4,2,8,1,3,2", "8,1,8,3,3,2", "8,2,8,1,3,2",
+             "1,4,4,2,4,2", "1,8,4,1,4,2", "1,2,8,4,4,2", "1,4,8,1,4,2", "2,4,4,3,4,2",
+             "2,2,8,8,4,2", "2,4,8,1,3,2"]
 KERNEL_OF_TILE = {0: "gemm_kernel", 1: "gemm_tile_kernel", 2: "gemm_lds_kernel"}
 
 

@@ -106,7 +106,8 @@ void apply_forced_plan(Plan* p, int KB) {
 
 // The heuristic (measured on MI355X at the Llama-2-7B layer shapes and an
 // 8192 x 28672 prefill layer).
-// Small batches (M <= 16) stream the weights: one 16-row block per wave.
+// Small batches (M <= 4, or M <= 16 with N < 8192) stream the weights:
+// one 16-row block per wave.
 // With one activation row the activation fragments cost little, so narrow
 // column tiles (16 or 32 columns) give the most workgroups; with 16 rows
 // every wave re-reads its activation fragments, so wide tiles (64 columns)
@@ -120,7 +121,8 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
   if (cus <= 0) cus = 256;
-  if (M <= 16) {
+  if (M <= 4 || (M <= 16 && N < 8192)) {
+    // streaming kernel: activations straight from global memory
     p.mb = 1;
     if (M <= 4) {
       p.nb = n16 >= 4 * cus ? 2 : 1;
@@ -132,10 +134,14 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
       p.depth = KB >= 64 ? 4 : 2;
     }
   } else if (M <= 32) {
-    p.mb = 2;
+    // LDS kernel with 16- or 32-row tiles and 256 columns (eight waves of
+    // 16 or 32 x 32): one activation tile in LDS serves every wave, where
+    // the streaming kernel would have each wave load its own copy
+    p.tile = 2;
+    p.mb = M <= 16 ? 1 : 2;
     p.nb = 2;
-    p.wk = 4;
-    p.depth = 2;
+    p.wk = 8;
+    p.depth = 4;
   } else if (M <= 128) {
     // LDS kernel, 64 x 128 tiles (eight waves of 64 x 16, two per SIMD):
     // small tiles keep enough workgroups; each weight is unpacked once per
@@ -167,11 +173,28 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   // the tile and LDS kernels up to about one workgroup per compute unit.
   int64_t want;
   int64_t cap;
-  if (p.tile) {
-    // whole splits only: an extra, partly filled wave of workgroups costs
-    // more than idle compute units
+  if (p.tile && tiles < cus) {
+    // fewer tiles than compute units: split K as far as whole splits fill
+    // the compute units (a partly filled extra wave of workgroups costs
+    // more than idle compute units), a power of two
     want = cus / tiles;
+    while (want & (want - 1)) want &= want - 1;
     cap = KB / 4 < 8 ? KB / 4 : 8;
+  } else if (p.tile) {
+    // more tiles than compute units: the last wave of workgroups may run
+    // nearly empty (288 tiles on 256 CUs keep 56% of them busy on average).
+    // Take the smallest power-of-two split, with at least 16 K blocks per
+    // split, that keeps 85% of the compute units busy.
+    want = 1;
+    for (int64_t sp = 1; sp <= 8 && sp * 16 <= KB; sp *= 2) {
+      const int64_t wgs = tiles * sp;
+      const int64_t waves_of_wgs = (wgs + cus - 1) / cus;
+      if (wgs * 100 >= 85 * waves_of_wgs * cus) {
+        want = sp;
+        break;
+      }
+    }
+    cap = 8;
   } else {
     // one workgroup per compute unit, two for deep K (K >= 8192)
     const int64_t target = (KB >= 64 ? 2 : 1) * (int64_t)cus;

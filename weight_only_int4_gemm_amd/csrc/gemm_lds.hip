@@ -42,8 +42,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB * WN;
   constexpr int APIECES = TM * 16;             // 16-byte pieces of activations
-  constexpr int ALOADS = APIECES / 64 / WN;    // direct loads per wave
-  static_assert(APIECES % (64 * WN) == 0, "activations must split evenly over the waves");
+  constexpr int ACHUNKS = APIECES / 64;        // 1 KiB wave-loads of activations
+  // direct activation loads per wave; with fewer chunks than waves some
+  // chunks are loaded twice (same bytes to the same place)
+  constexpr int ALOADS = (ACHUNKS + WN - 1) / WN;
   constexpr int BPIECES = NB * WN * 64;        // 16-byte pieces of codes
   constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
   constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
@@ -98,13 +100,14 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   auto load_stage = [&](Stage& sg, int kb) {
 #pragma unroll
     for (int i = 0; i < ALOADS; ++i) {
-      // activation load i of this wave: stage pieces 64 * (wave + WN * i) + lane
-      const int r = 4 * (wave + WN * i) + (lane >> 4);
+      // activation load i of this wave: stage pieces 64 * chunk + lane
+      const int chunk = (wave + WN * i) % ACHUNKS;
+      const int r = 4 * chunk + (lane >> 4);
       const int piece = l16 ^ (r & 15);
       const int gr = row0 + r < M ? row0 + r : M - 1;  // rows past M: never stored
       const _Float16* src = A + (int64_t)gr * K + kb * kBlockK + piece * 8;
-      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)&sg.a[64 * (wave + WN * i)],
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)&sg.a[64 * chunk], 16, 0,
+                                       0);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -244,7 +247,8 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
 #define W4A16_LDS_VARIANTS(X)                                                   \
   X(4, 2, 2, 3) X(4, 2, 4, 3) X(4, 2, 4, 4) X(4, 4, 4, 3) X(8, 1, 4, 3)          \
   X(8, 2, 4, 2) X(8, 2, 4, 3) X(8, 4, 4, 2) X(8, 4, 4, 3) X(4, 1, 8, 3) X(4, 2, 8, 3)     \
-  X(8, 1, 8, 3) X(8, 2, 8, 3)
+  X(8, 1, 8, 3) X(8, 2, 8, 3) X(1, 4, 4, 4) X(1, 8, 4, 4) X(1, 2, 8, 4) X(1, 4, 8, 4)     \
+  X(2, 4, 4, 4) X(2, 2, 8, 4) X(2, 4, 8, 3)
 
 bool lds_is_compiled(int mb, int nb, int wn, int ns) {
 #define W4A16_LMATCH(MB_, NB_, WN_, NS_) \
