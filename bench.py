@@ -247,10 +247,45 @@ def cpu_baseline(sample_cols: int):
     }
 
 
+def _time_calls(calls, launches: int, repeats: int) -> float:
+    """Median over ``repeats`` of the mean time of ``launches`` back-to-back
+    calls (cycling over ``calls``), from HIP events on the current stream."""
+    import numpy as np
+    import torch
+    for i in range(max(5, len(calls))):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(launches):
+            calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3 / launches)
+    return float(np.median(times))
+
+
+def _gpu_clocks() -> str:
+    """The current clocks as rocm-smi reports them (empty if unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE,
+                             stderr=subprocess.STDOUT, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return ""
+    keep = [l.strip() for l in out.splitlines() if "sclk" in l or "mclk" in l or "fclk" in l]
+    return "; ".join(keep)
+
+
 def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
     """Time each workload shape one GEMM at a time: hipEvents around
     ``launches`` back-to-back calls that cycle over enough copies of the
-    packed weights to exceed the Infinity Cache, median of ``repeats``."""
+    packed weights to exceed the Infinity Cache, median of ``repeats``.
+    Next to it, an FP16 GEMM (torch.matmul, i.e. hipBLASLt) on the same
+    weights dequantised to FP16, the comparison the pages make."""
     import numpy as np
     import torch
 
@@ -262,6 +297,7 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
     torch.cuda.set_device(dev)
     lib = w4.load()
     sh = torch.cuda.current_stream().cuda_stream
+    clocks_before = _gpu_clocks()
     rows = []
     for label, K, N, group, batches in REPORT_SHAPES:
         _, Bq, S = make_inputs(1, K, N, group, seed=0)
@@ -272,40 +308,44 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         ncopy = max(1, -(-ROTATE_BYTES // (K * N // 2)))
         copies = [first] + [first.clone() for _ in range(ncopy - 1)]
         S_d = torch.from_numpy(S).to(dev)
+        # the same weights as FP16 for the comparison, with their own rotation
+        W = torch.empty((K, N), dtype=torch.float16, device=dev)
+        w4.w4a16_dequant_debug(first, S_d, W, K, N, group)
+        nw = max(1, -(-ROTATE_BYTES // (K * N * 2)))
+        wcopies = [W] + [W.clone() for _ in range(nw - 1)]
         for M in batches:
             A_d = torch.from_numpy(make_activations(M, K, seed=M)).to(dev)
             C_d = torch.empty((M, N), dtype=torch.float16, device=dev)
             ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, group), 256),
                              dtype=torch.uint8, device=dev)
-            calls = [(A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K, N,
-                      group, ws.data_ptr(), sh) for c in copies]
-            for i in range(max(5, ncopy)):
-                rc = lib.w4a16_gemm(*calls[i % ncopy])
-                if rc != 0:
-                    raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
-            torch.cuda.synchronize()
-            times = []
-            for _ in range(repeats):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for i in range(launches):
-                    lib.w4a16_gemm(*calls[i % ncopy])
-                e1.record()
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1) * 1e-3 / launches)
-            t = float(np.median(times))
+
+            def gemm_call(c):
+                args = (A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K, N,
+                        group, ws.data_ptr(), sh)
+
+                def run():
+                    rc = lib.w4a16_gemm(*args)
+                    if rc != 0:
+                        raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+                return run
+
+            t = _time_calls([gemm_call(c) for c in copies], launches, repeats)
+            C16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+            t16 = _time_calls([(lambda w=w: torch.matmul(A_d, w, out=C16)) for w in wcopies],
+                              launches, repeats)
             flops = roofline.flops(M, K, N)
             nbytes = roofline.algorithmic_bytes(M, K, N, group)
             rows.append(dict(shape=label, M=M, K=K, N=N, group=group, us=t * 1e6,
                              tflops=flops / t / 1e12, tbps=nbytes / t / 1e12,
                              bound=roofline.bound(M, K, N, group),
                              frac=roofline.roofline_seconds(M, K, N, group) / t,
+                             fp16_us=t16 * 1e6, speedup=t16 / t,
                              plan=w4.w4a16_describe(M, K, N, group).split(" workspace")[0]))
             print(json.dumps(rows[-1]), flush=True)
-            del A_d, C_d, ws
-        del copies, first, S_d
+            del A_d, C_d, ws, C16
+        del copies, first, S_d, W, wcopies
         torch.cuda.empty_cache()
+    clocks_after = _gpu_clocks()
 
     lines = [
         "# W4A16 GEMM on one MI355X: every workload shape",
@@ -318,14 +358,21 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         f"to exceed 512 MB (so weights come from HBM, not the Infinity Cache), median of "
         f"{repeats} repeats; the time includes launch gaps. Inputs: seeded synthetic data "
         "(weights seed 0, activations seed M). Roofline: HBM 8 TB/s, dense FP16 MFMA "
-        "2.5 PFLOP/s; `frac` is the bound's time over the measured time.",
+        "2.5 PFLOP/s; `frac` is the bound's time over the measured time. `FP16 us` is "
+        "torch.matmul (hipBLASLt) on the same weights dequantised to FP16, timed the same "
+        "way with its own rotation of weight copies; `x FP16` is its time over ours.",
         "",
-        "| shape | M | us | TFLOP/s | HBM TB/s | bound | frac | plan |",
-        "|---|---|---|---|---|---|---|---|",
+        f"Clocks before (rocm-smi): {clocks_before or 'n/a'}",
+        "",
+        f"Clocks after: {clocks_after or 'n/a'}",
+        "",
+        "| shape | M | us | TFLOP/s | HBM TB/s | bound | frac | FP16 us | x FP16 | plan |",
+        "|---|---|---|---|---|---|---|---|---|---|",
     ]
     for r in rows:
         lines.append(f"| {r['shape']} | {r['M']} | {r['us']:.1f} | {r['tflops']:.1f} | "
-                     f"{r['tbps']:.2f} | {r['bound']} | {r['frac']:.3f} | `{r['plan']}` |")
+                     f"{r['tbps']:.2f} | {r['bound']} | {r['frac']:.3f} | {r['fp16_us']:.1f} | "
+                     f"{r['speedup']:.2f} | `{r['plan']}` |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 

@@ -151,7 +151,10 @@ LDS_PLANS = ["4,2,2,1,3,2", "4,2,4,3,3,2", "4,2,4,1,4,2", "4,2,4,6,4,2", "4,4,4,
              "4,1,8,2,3,2", "4,2,8,1,3,2", "8,1,8,3,3,2", "8,2,8,1,3,2",
              "1,4,4,2,4,2", "1,8,4,1,4,2", "1,2,8,4,4,2", "1,4,8,1,4,2", "2,4,4,3,4,2",
              "2,2,8,8,4,2", "2,4,8,1,3,2"]
-KERNEL_OF_TILE = {0: "gemm_kernel", 1: "gemm_tile_kernel", 2: "gemm_lds_kernel"}
+# LDS kernel with 32 x 32 matrix blocks (mb, nb count 32-row / 32-column blocks)
+LDS32_PLANS = ["4,1,8,1,3,3", "4,1,8,3,3,3", "2,1,8,3,3,3", "4,1,4,1,3,3", "2,2,4,5,3,3"]
+KERNEL_OF_TILE = {0: "gemm_kernel", 1: "gemm_tile_kernel", 2: "gemm_lds_kernel",
+                  3: "gemm_lds_kernel"}
 
 
 def _forced_plan_case(monkeypatch, plan, group):
@@ -169,13 +172,14 @@ def _forced_plan_case(monkeypatch, plan, group):
     assert_gemm_close(C, C64, f"plan {plan} group {group}")
 
 
-@pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS + LDS_PLANS)
+@pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS + LDS_PLANS + LDS32_PLANS)
 def test_gemm_forced_plans_agree(monkeypatch, plan):
     """Every compiled variant and split count gives the oracle's answer."""
     _forced_plan_case(monkeypatch, plan, 128)
 
 
-@pytest.mark.parametrize("plan", ["1,2,4,3,2", "4,2,4,3,2,1", "4,2,4,3,3,2", "8,4,4,2,2,2"])
+@pytest.mark.parametrize("plan", ["1,2,4,3,2", "4,2,4,3,2,1", "4,2,4,3,3,2", "8,4,4,2,2,2",
+                                  "4,1,8,2,3,3"])
 def test_gemm_forced_plans_coarse_groups(monkeypatch, plan):
     """A scale group of four K blocks (512): each K block finds its group row."""
     _forced_plan_case(monkeypatch, plan, 512)

@@ -63,7 +63,7 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q) {
-  if (q.tile == 2) return lds_is_compiled(q.mb, q.nb, q.wk, q.depth);
+  if (q.tile >= 2) return lds_is_compiled(q.mb, q.nb, q.wk, q.depth, q.tile == 3 ? 32 : 16);
   return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk, q.depth, q.bdepth)
                 : plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
 }
@@ -72,7 +72,8 @@ bool variant_is_compiled(const Plan& q) {
 // W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile[,bdepth]]]" replaces the
 // heuristic's choice when it names a compiled variant (a field <= 0 keeps
 // the heuristic's value; tile is 0, the default, for the streaming kernel,
-// 1 for the tile kernel or 2 for the LDS kernel).  It feeds the same kernels;
+// 1 for the tile kernel, 2 for the LDS kernel with 16 x 16 blocks or 3 for
+// the LDS kernel with 32 x 32 blocks).  It feeds the same kernels;
 // w4a16_workspace_bytes sees it too, so sizes stay consistent within a
 // process.
 void apply_forced_plan(Plan* p, int KB) {
@@ -82,7 +83,7 @@ void apply_forced_plan(Plan* p, int KB) {
   if (std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
                   &bdepth) < 4)
     return;
-  if (tile < 0 || tile > 2) return;
+  if (tile < 0 || tile > 3) return;
   Plan q = *p;
   q.tile = tile;  // absent: the streaming kernel
   if (mb > 0) q.mb = mb;
@@ -161,8 +162,9 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
     p.depth = 3;
   }
   auto shape = [&](Plan& q) {
-    q.tm = 16 * q.mb;
-    q.tn = 16 * q.nb * (q.tile ? q.wk : 1);  // tile and LDS kernels split N over waves
+    const int f = q.tile == 3 ? 32 : 16;
+    q.tm = f * q.mb;
+    q.tn = f * q.nb * (q.tile ? q.wk : 1);  // tile and LDS kernels split N over waves
     q.tiles_n = (N + q.tn - 1) / q.tn;
     q.tiles_m = (M + q.tm - 1) / q.tm;
   };
@@ -262,11 +264,12 @@ int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan p = make_plan(M, K, N, group, cus);
-  if (p.tile == 2)
+  if (p.tile >= 2)
     std::snprintf(buf, len,
-                  "gemm_lds_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
-                  p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
-                  p.splits, p.workspace_bytes);
+                  "gemm_lds_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
+                  "workspace=%zu",
+                  p.mb, p.nb, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
+                  p.splits, 64 * p.wk, p.splits, p.workspace_bytes);
   else if (p.tile)
     std::snprintf(buf, len,
                   "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "

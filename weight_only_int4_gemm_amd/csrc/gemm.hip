@@ -291,7 +291,7 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
   // and for any gb as long as kb, gb < 2^16 (K < 2^23 is checked).
   const uint64_t gb = (uint64_t)(group / kBlockK);
   const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
-  if (p.tile == 2) return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, workspace, stream);
+  if (p.tile >= 2) return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, workspace, stream);
   if (p.tile) return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, workspace, stream);
 #define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \

@@ -33,23 +33,31 @@
 
 namespace w4a16 {
 
-template <int MB, int NB, int WN, int NS>
+// F is the edge of the matrix instruction's output block: 16 for
+// v_mfma_f32_16x16x32_f16, 32 for v_mfma_f32_32x32x16_f16 (MB and NB count
+// F-row and F-column blocks).  The 32 x 32 form does twice the work per
+// instruction at the same operand size and issues at the full rate, where
+// the 16 x 16 form sustains about 80% of it; it reads the same packed layout
+// (the lane-to-word map below).
+template <int MB, int NB, int WN, int NS, int F>
 __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
     float* __restrict__ partials) {
-  constexpr int TM = 16 * MB;
-  constexpr int TN = 16 * NB * WN;
+  static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
+  constexpr int TM = F * MB;
+  constexpr int TN = F * NB * WN;
+  constexpr int NB16 = NB * F / 16;            // 16-column code blocks per wave
   constexpr int APIECES = TM * 16;             // 16-byte pieces of activations
   constexpr int ACHUNKS = APIECES / 64;        // 1 KiB wave-loads of activations
   // direct activation loads per wave; with fewer chunks than waves some
   // chunks are loaded twice (same bytes to the same place)
   constexpr int ALOADS = (ACHUNKS + WN - 1) / WN;
-  constexpr int BPIECES = NB * WN * 64;        // 16-byte pieces of codes
+  constexpr int BPIECES = NB16 * WN * 64;      // 16-byte pieces of codes
   constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
   constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
-  constexpr int LOADS = ALOADS + NB + SLOADS;  // direct loads per wave per stage
+  constexpr int LOADS = ALOADS + NB16 + SLOADS;  // direct loads per wave per stage
   static_assert(NS >= 2 && NS <= 4, "two to four stages");
   struct Stage {
     uint4 a[APIECES];
@@ -79,10 +87,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
 
   // Code source of this wave's column blocks (blocks past N re-read the last
   // valid one; their columns are dropped at the store).
-  const uint32_t* bsrc[NB];
+  const uint32_t* bsrc[NB16];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n16 = tile_n * NB * WN + wave * NB + nb;
+  for (int nb = 0; nb < NB16; ++nb) {
+    const int n16 = tile_n * NB16 * WN + wave * NB16 + nb;
     bsrc[nb] = Bp + block_word_offset(n16 <= n16_last ? n16 : n16_last, 0, K) +
                lane * kWordsPerLane;
   }
@@ -110,9 +118,9 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
                                        0);
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NB16; ++nb) {
       __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[nb] + kb * kWordsPerBlock),
-                                       (lds_ptr_t)&sg.b[64 * (wave * NB + nb)], 16, 0, 0);
+                                       (lds_ptr_t)&sg.b[64 * (wave * NB16 + nb)], 16, 0, 0);
     }
     const int srow = scale_row(kb) * N;
 #pragma unroll
@@ -122,12 +130,18 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     }
   };
 
-  float4_t acc[MB][NB];
+  typedef typename std::conditional<F == 16, float4_t, float16_t>::type acc_t;
+  acc_t acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < F * F / 64; ++i) acc[mb][nb][i] = 0.f;  // F*F/64 values per lane
 
+  // ---- 16 x 16 blocks: four 32-deep slices per K block -------------------
+  // Lane l takes activation row l % 16, in-features 8(l/16) .. +7 of the
+  // slice, and the code word j of its own 16-byte piece of the block.
   auto read_a = [&](const Stage& sg, int j, half8_t* a) {
     const int lg = lane >> 4;
 #pragma unroll
@@ -136,11 +150,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
       a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + ((4 * j + lg) ^ (r & 15))]);
     }
   };
-  // One K block in four 32-deep slices.  Software-pipelined by one slice:
-  // while the matrix instructions of slice j run, the activation fragments
-  // of slice j+1 are read and its codes unpacked, so the vector ALU work has
-  // independent matrix work to overlap with.
-  auto compute = [&](const Stage& sg) {
+  // Software-pipelined by one slice: while the matrix instructions of slice
+  // j run, the activation fragments of slice j+1 are read and its codes
+  // unpacked, so the vector ALU work has independent matrix work to overlap.
+  auto compute16 = [&](const Stage& sg) {
     uint4 w[NB];
     half2_t s2[NB];
     const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
@@ -174,9 +187,82 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (F == 16)
+            acc[mb][nb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+        }
     }
+  };
+
+  // ---- 32 x 32 blocks: eight 16-deep slices per K block ------------------
+  // Lane l takes activation row l % 32, in-features 8(l/32) .. +7 of the
+  // slice, and for column c = l % 32 the eight codes of those in-features.
+  // In the packed layout (16-column blocks, lane l' holding column l' % 16
+  // and in-features 32j + 8(l'/16) .. +7 in its word j) these are word s/2
+  // of lane (l % 16) + 16 (2 (s % 2) + l / 32) of block c / 16: even slices
+  // take the four words of one lane, odd slices of another.
+  auto read_a32 = [&](const Stage& sg, int s, half8_t* a) {
+    const int r32 = lane & 31;
+    const int piece = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = mb * 32 + r32;
+      a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + (piece ^ (r & 15))]);
+    }
+  };
+  auto compute32 = [&](const Stage& sg) {
+    uint4 we[NB], wo[NB];  // words of the even and of the odd slices
+    half2_t s2[NB];
+    const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
+    const int c32 = lane & 31;
+    const int le = l16 + 16 * (lane >> 5);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int blk = 64 * (wave * NB16 + 2 * nb + (c32 >> 4));
+      we[nb] = sg.b[blk + le];
+      wo[nb] = sg.b[blk + le + 32];
+      const _Float16 sc = sh[wave * 32 * NB + nb * 32 + c32];
+      s2[nb] = half2_t{sc, sc};
+    }
+    auto unpack_slice = [&](int s, half8_t* bf) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4& w = (s & 1) ? wo[nb] : we[nb];
+        const int j = s >> 1;
+        const uint32_t word = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+        bf[nb] = unpack_scale(word, s2[nb]);
+      }
+    };
+    half8_t a0[MB], a1[MB];
+    half8_t b0[NB], b1[NB];
+    read_a32(sg, 0, a0);
+    unpack_slice(0, b0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      half8_t* cur = (s & 1) ? a1 : a0;
+      half8_t* nxt = (s & 1) ? a0 : a1;
+      half8_t* bcur = (s & 1) ? b1 : b0;
+      half8_t* bnxt = (s & 1) ? b0 : b1;
+      if (s < 7) {
+        read_a32(sg, s + 1, nxt);
+        unpack_slice(s + 1, bnxt);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (F == 32)
+            acc[mb][nb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+        }
+    }
+  };
+  auto compute = [&](const Stage& sg) {
+    if constexpr (F == 16)
+      compute16(sg);
+    else
+      compute32(sg);
   };
 
   // The pipeline: step t consumes stage t % NS; before it, once every wave
@@ -196,7 +282,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   // from four waves stalls each wave for hundreds of cycles).  So the
   // step's loads are spread between its matrix instructions: one load
   // after every MFMA_PER_LOAD of them.
-  constexpr int NMFMA = 4 * MB * NB;
+  constexpr int NMFMA = (F == 16 ? 4 : 8) * MB * NB;
   constexpr int MFMA_PER_LOAD = NMFMA / (LOADS + 1) > 0 ? NMFMA / (LOADS + 1) : 1;
   auto step = [&](int u, int kb) {  // u = t % NS
     stage_barrier<(NS - 2) * LOADS>();
@@ -221,11 +307,15 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  store_output_tile<MB, NB, WN>(acc, C, M, N, row0, col0, split, splits, counters, partials,
-                                reinterpret_cast<int*>(&st0.s[0]));
+  if constexpr (F == 16)
+    store_output_tile<MB, NB, WN>(acc, C, M, N, row0, col0, split, splits, counters, partials,
+                                  reinterpret_cast<int*>(&st0.s[0]));
+  else
+    store_output_tile32<MB, NB, WN>(acc, C, M, N, row0, col0, split, splits, counters,
+                                    partials, reinterpret_cast<int*>(&st0.s[0]));
 }
 
-template <int MB, int NB, int WN, int NS>
+template <int MB, int NB, int WN, int NS, int F>
 static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                  const uint16_t* S, uint16_t* C, int M, int K, int N,
                                  uint64_t gmagic, void* workspace, hipStream_t stream) {
@@ -236,23 +326,24 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS>), dim3(p.tiles_n, p.tiles_m, p.splits),
+  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS, F>), dim3(p.tiles_n, p.tiles_m, p.splits),
                      dim3(64 * WN), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
                      reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
                      M, K, N, gmagic, p.splits, counters, partials);
   return hipGetLastError();
 }
 
-// Compiled variants (MB, NB, WN, NS).
-#define W4A16_LDS_VARIANTS(X)                                                   \
-  X(4, 2, 2, 3) X(4, 2, 4, 3) X(4, 2, 4, 4) X(4, 4, 4, 3) X(8, 1, 4, 3)          \
-  X(8, 2, 4, 2) X(8, 2, 4, 3) X(8, 4, 4, 2) X(8, 4, 4, 3) X(4, 1, 8, 3) X(4, 2, 8, 3)     \
-  X(8, 1, 8, 3) X(8, 2, 8, 3) X(1, 4, 4, 4) X(1, 8, 4, 4) X(1, 2, 8, 4) X(1, 4, 8, 4)     \
-  X(2, 4, 4, 4) X(2, 2, 8, 4) X(2, 4, 8, 3)
+// Compiled variants (MB, NB, WN, NS, F).
+#define W4A16_LDS_VARIANTS(X)                                                               \
+  X(4, 2, 2, 3, 16) X(4, 2, 4, 3, 16) X(4, 2, 4, 4, 16) X(4, 4, 4, 3, 16) X(8, 1, 4, 3, 16)  \
+  X(8, 2, 4, 2, 16) X(8, 2, 4, 3, 16) X(8, 4, 4, 2, 16) X(8, 4, 4, 3, 16) X(4, 1, 8, 3, 16)  \
+  X(4, 2, 8, 3, 16) X(8, 1, 8, 3, 16) X(8, 2, 8, 3, 16) X(1, 4, 4, 4, 16) X(1, 8, 4, 4, 16)  \
+  X(1, 2, 8, 4, 16) X(1, 4, 8, 4, 16) X(2, 4, 4, 4, 16) X(2, 2, 8, 4, 16) X(2, 4, 8, 3, 16)  \
+  X(4, 1, 8, 3, 32) X(2, 1, 8, 3, 32) X(4, 1, 4, 3, 32) X(2, 2, 4, 3, 32)
 
-bool lds_is_compiled(int mb, int nb, int wn, int ns) {
-#define W4A16_LMATCH(MB_, NB_, WN_, NS_) \
-  if (mb == MB_ && nb == NB_ && wn == WN_ && ns == NS_) return true;
+bool lds_is_compiled(int mb, int nb, int wn, int ns, int f) {
+#define W4A16_LMATCH(MB_, NB_, WN_, NS_, F_) \
+  if (mb == MB_ && nb == NB_ && wn == WN_ && ns == NS_ && f == F_) return true;
   W4A16_LDS_VARIANTS(W4A16_LMATCH)
 #undef W4A16_LMATCH
   return false;
@@ -261,10 +352,11 @@ bool lds_is_compiled(int mb, int nb, int wn, int ns) {
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
                       void* workspace, hipStream_t stream) {
-#define W4A16_LCASE(MB_, NB_, WN_, NS_)                                            \
-  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_)                 \
-    return launch_lds_one<MB_, NB_, WN_, NS_>(p, A, Bp, S, C, M, K, N, gmagic,     \
-                                              workspace, stream);
+  const int f = p.tile == 3 ? 32 : 16;
+#define W4A16_LCASE(MB_, NB_, WN_, NS_, F_)                                                \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_ && f == F_)              \
+    return launch_lds_one<MB_, NB_, WN_, NS_, F_>(p, A, Bp, S, C, M, K, N, gmagic,         \
+                                                  workspace, stream);
   W4A16_LDS_VARIANTS(W4A16_LCASE)
 #undef W4A16_LCASE
   return hipErrorInvalidValue;

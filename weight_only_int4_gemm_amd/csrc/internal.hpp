@@ -10,7 +10,9 @@ namespace w4a16 {
 // How one w4a16_gemm call is cut into work.
 //  tile   0: the streaming kernel (small batches), 1: the tile kernel
 //         (codes through registers), 2: the LDS kernel (every operand
-//         through LDS stages)
+//         through LDS stages) with 16 x 16 matrix blocks, 3: the LDS kernel
+//         with 32 x 32 blocks (mb and nb then count 32-row / 32-column
+//         blocks)
 //  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
 //  nb     16-column blocks per wave
 //  wk     waves per workgroup.  Streaming kernel: they split the
@@ -34,7 +36,7 @@ struct Plan {
 Plan make_plan(int M, int K, int N, int group, int cus);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
-bool lds_is_compiled(int mb, int nb, int wn, int ns);
+bool lds_is_compiled(int mb, int nb, int wn, int ns, int f);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);
