@@ -20,8 +20,8 @@ counter runs of this script, summarised into profiles/ by
 ``--pmc-summary``; it is reported only while the kernel sources still hash
 to the value recorded with the counters:
 
-    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe
-    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe
+    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-graph --copy-probe
+    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-graph --copy-probe
     python3 bench.py --pmc-summary OUT/fetch OUT/write profiles/pmc_traffic_llama7b_step.json
 
 ``--configs-report OUT.md`` instead times every workload shape one GEMM at a
@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (profiler runs)")
     ap.add_argument("--cpu-sample-cols", type=int, default=0,
                     help="columns per GEMM for the CPU oracle (0 = whole GEMMs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -86,6 +88,10 @@ def parse():
     ap.add_argument("--configs-report", metavar="OUT",
                     help="time every workload shape, one GEMM at a time, write a "
                          "markdown table to OUT and exit")
+    ap.add_argument("--epilogue-report", metavar="OUT",
+                    help="time the fused output stage (bias + SiLU inside the GEMM) "
+                         "against the plain GEMM and against the plain GEMM followed by "
+                         "torch's bias add and SiLU, write a markdown table to OUT and exit")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script into a traffic file and exit")
@@ -182,9 +188,9 @@ def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
                 "by what the counter reads for a device copy of known size",
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 "
-            "--warmup 1 --no-cpu-baseline --copy-probe",
+            "--warmup 1 --no-cpu-baseline --no-graph --copy-probe",
             "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 "
-            "--warmup 1 --no-cpu-baseline --copy-probe",
+            "--warmup 1 --no-cpu-baseline --no-graph --copy-probe",
             "python3 bench.py --pmc-summary OUT/fetch OUT/write " + os.path.relpath(out_path, ROOT),
         ],
         "kernel_source_hash": kernel_source_hash(),
@@ -377,6 +383,111 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+# Shapes for --epilogue-report: (label, K, N, batch sizes).
+EPILOGUE_SHAPES = [
+    ("Llama-2-7B gate/up", 4096, 22016, [1, 16, 128]),
+    ("Llama-2-7B qkv", 4096, 12288, [1, 128]),
+    ("prefill 8192x28672", 8192, 28672, [1024]),
+]
+
+
+def epilogue_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
+    """Per call, timed like --configs-report: the plain GEMM; the fused
+    entry point with a bias and SiLU; and the plain GEMM followed by the same
+    operation as two torch kernels (in-place bias add, in-place SiLU) -- the
+    extra pass over C that fusing removes."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import weight_only_int4_gemm_amd as w4
+    from synth import make_activations, make_bias, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = w4.load()
+    sh = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for label, K, N, batches in EPILOGUE_SHAPES:
+        _, Bq, S = make_inputs(1, K, N, GROUP, seed=0)
+        Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
+        first = w4.alloc_packed(K, N)
+        w4.w4a16_repack(Bq_d, first, K, N)
+        del Bq_d, Bq
+        ncopy = max(1, -(-ROTATE_BYTES // (K * N // 2)))
+        copies = [first] + [first.clone() for _ in range(ncopy - 1)]
+        S_d = torch.from_numpy(S).to(dev)
+        bias = torch.from_numpy(make_bias(N, seed=1)).to(dev)
+        for M in batches:
+            A_d = torch.from_numpy(make_activations(M, K, seed=M)).to(dev)
+            C_d = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, GROUP), 256),
+                             dtype=torch.uint8, device=dev)
+
+            def call(c, fused):
+                if fused:
+                    args = (A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), bias.data_ptr(),
+                            w4.W4A16_ACT_SILU, C_d.data_ptr(), M, K, N, GROUP, ws.data_ptr(), sh)
+                    fn = lib.w4a16_gemm_fused
+                else:
+                    args = (A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K,
+                            N, GROUP, ws.data_ptr(), sh)
+                    fn = lib.w4a16_gemm
+
+                def run():
+                    rc = fn(*args)
+                    if rc != 0:
+                        raise RuntimeError(f"gemm failed: {w4.w4a16_status_string(rc)}")
+                return run
+
+            plain = [call(c, False) for c in copies]
+
+            def unfused(i):
+                def run():
+                    plain[i]()
+                    C_d.add_(bias)
+                    F.silu(C_d, inplace=True)
+                return run
+
+            # the three forms interleaved, repeat by repeat: the clock drifts
+            # over a run by more than the differences measured here
+            forms = [plain, [call(c, True) for c in copies],
+                     [unfused(i) for i in range(len(copies))]]
+            times = [[], [], []]
+            for _ in range(repeats):
+                for f, form in enumerate(forms):
+                    times[f].append(_time_calls(form, launches, 1))
+            t_plain, t_fused, t_unf = (float(np.median(t)) for t in times)
+            rows.append(dict(shape=label, M=M, K=K, N=N, plain_us=t_plain * 1e6,
+                             fused_us=t_fused * 1e6, unfused_us=t_unf * 1e6,
+                             plan=w4.w4a16_describe(M, K, N, GROUP).split(" workspace")[0]))
+            print(json.dumps(rows[-1]), flush=True)
+            del A_d, C_d, ws
+        del copies, first, S_d, bias
+        torch.cuda.empty_cache()
+    lines = [
+        "# Fused output stage (bias + SiLU) on one MI355X",
+        "",
+        "Command (repository root, GPU box): `python3 bench.py --epilogue-report " +
+        os.path.relpath(out_path, ROOT) + "`",
+        "",
+        f"Kernel source hash: `{kernel_source_hash()}`. Per form: hipEvents around "
+        f"{launches} back-to-back calls cycling over weight copies beyond 512 MB; the three "
+        f"forms are timed in turn, {repeats} rounds, median per form. `plain`: w4a16_gemm. `fused`: w4a16_gemm_fused with "
+        "an FP16 bias and SiLU. `unfused`: w4a16_gemm, then torch's in-place bias add and "
+        "in-place SiLU on C (two more kernels, two more passes over C).",
+        "",
+        "| shape | M | plain us | fused us | unfused us | fused - plain | unfused - fused | plan |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| {r['shape']} | {r['M']} | {r['plain_us']:.1f} | {r['fused_us']:.1f} | "
+                     f"{r['unfused_us']:.1f} | {r['fused_us'] - r['plain_us']:+.1f} | "
+                     f"{r['unfused_us'] - r['fused_us']:+.1f} | `{r['plan']}` |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -384,6 +495,9 @@ def main():
         return
     if args.configs_report:
         configs_report(args.configs_report)
+        return
+    if args.epilogue_report:
+        epilogue_report(args.epilogue_report)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -477,6 +591,36 @@ def main():
         run_step(s, step_events[s])
     end_event.record(stream)
     torch.cuda.synchronize()
+
+    # The same steps replayed from HIP graphs: one graph per weight-copy
+    # rotation, each holding the step's twelve launches, captured once on a
+    # side stream.  A replay submits the step in one call, which removes the
+    # host's per-launch cost and the gaps it leaves between small kernels.
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graphs = []
+    with torch.cuda.stream(cap):
+        for s in range(0 if args.no_graph else WEIGHT_COPIES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for a in calls_per_step[s]:
+                    rc = lib.w4a16_gemm(*a[:-1], cap.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+            graphs.append(g)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    graph_wall = None
+    if graphs:
+        for s in range(args.warmup):
+            graphs[s % WEIGHT_COPIES].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[s % WEIGHT_COPIES].replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+    del graphs
 
     # per-launch durations from the events
     per_gemm_ms = {g: [] for g in gemms}
@@ -573,6 +717,10 @@ def main():
         "hbm_tbps": step_bytes / (wall / args.steps) / 1e12,
         "step_roofline_frac": step_roof_s / (wall / args.steps),
         "events_pass_ms_per_step": gpu_ms_total / args.steps,
+        "graph": None if graph_wall is None else {
+            "launch": f"one HIP graph per step ({n_launch} kernel nodes), replayed",
+            "ms_per_step": graph_wall * 1e3 / args.steps,
+            "value": step_flops / (graph_wall / args.steps) / 1e12, "unit": "TFLOP/s"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_gemm": per_gemm,

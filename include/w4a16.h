@@ -53,7 +53,15 @@ enum w4a16_status {
     W4A16_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned            */
     W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed       */
     W4A16_ERR_LAUNCH = -6,    /* the kernel launch failed                    */
-    W4A16_ERR_DEVICE = -7     /* no usable current HIP device                */
+    W4A16_ERR_DEVICE = -7,    /* no usable current HIP device                */
+    W4A16_ERR_EPILOGUE = -8   /* unknown activation for w4a16_gemm_fused     */
+};
+
+/* Activations the fused epilogue applies (w4a16_gemm_fused). */
+enum w4a16_activation {
+    W4A16_ACT_NONE = 0,       /* y = x                                       */
+    W4A16_ACT_RELU = 1,       /* y = max(x, 0)                               */
+    W4A16_ACT_SILU = 2        /* y = x / (1 + exp(-x))                       */
 };
 
 /* Version of the permuted layout written by w4a16_repack.  Callers that
@@ -148,6 +156,28 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group);
 int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked,
                const uint16_t* scales, uint16_t* C, int M, int K, int N,
                int group, void* workspace, void* stream);
+
+/*
+ * w4a16_gemm_fused -- C = act(A . dequant(Bpacked, scales) + bias).
+ *
+ * The pages hand the GEMM's output straight to the next operation -- a bias
+ * add, an activation -- with no visible dequantisation step ("Quant Marlin
+ * kernel" explainer, section "End-to-end flow").  Here that operation runs
+ * in the GEMM's output stage, on the FP32 sum before the one rounding to
+ * FP16, so C makes a single trip to memory.
+ *
+ * bias       (device, read) FP16 [N], or NULL for no bias.
+ * activation one of enum w4a16_activation.
+ * The other arguments, alignment rules and errors are those of w4a16_gemm,
+ * plus W4A16_ERR_EPILOGUE for an unknown activation.  bias must not overlap
+ * C.  Numerics: y = act(sum + float(bias[n])) in FP32 (SiLU with the
+ * device's single-precision exp), then rounded once to FP16.
+ * w4a16_gemm is w4a16_gemm_fused with bias NULL and W4A16_ACT_NONE.
+ */
+int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked,
+                     const uint16_t* scales, const uint16_t* bias, int activation,
+                     uint16_t* C, int M, int K, int N, int group, void* workspace,
+                     void* stream);
 
 /*
  * w4a16_dequant_debug -- W = dequant(Bpacked, scales), written out.

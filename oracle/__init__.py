@@ -17,9 +17,13 @@ plain numpy, with no blocking, fusion or reordering beyond that description:
 * Same page, "End-to-end flow": FP16 activations (tokens x in-features) times
   INT4 weights (in-features x out-features), per-128 group scales.
 
+* Same page, "End-to-end flow": the product goes straight on to a bias add
+  or an activation (``gemm_fused``).
+
 Readings where the pages leave a step open (zero point 8, LSB-first nibble
 order along K, scale layout ``[K/group][N]``, single RNE rounding of the
-dequantised weight) are stated in ``w4a16_ref``'s docstrings.
+dequantised weight, the bias and activation of the fused output) are stated
+in ``w4a16_ref``'s docstrings.
 """
 
 from .w4a16_ref import (  # noqa: F401
@@ -33,4 +37,10 @@ from .w4a16_ref import (  # noqa: F401
     gemm_columns,
     repack,
     unrepack,
+    ACT_NONE,
+    ACT_RELU,
+    ACT_SILU,
+    activation,
+    epilogue,
+    gemm_fused,
 )

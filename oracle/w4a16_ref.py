@@ -214,3 +214,55 @@ def unrepack(Bp: np.ndarray, K: int, N: int) -> np.ndarray:
         frag[..., i] = (Bp >> np.uint32(4 * _NIBBLE_OF_CODE[i])) & np.uint32(0xF)
     q6 = frag.transpose(1, 4, 2, 5, 0, 3)            # kb, j, lg, i, n16, nl
     return pack_codes(q6.reshape(K, N))
+
+
+# ---------------------------------------------------------------------------
+# The fused output operation.  "Quant Marlin kernel" explainer, section
+# "End-to-end flow": the product goes straight on to the next operation -- a
+# bias add, an activation -- as if it came from a plain matmul.
+#
+# Readings (the pages fix none of these):
+#  7. The bias is one FP16 value per output column (``bias[N]``), added to
+#     the sum; the activation comes after the bias.
+#  8. Fusing means one rounding: ``C = fp16_rne(act(sum + bias))``, with no
+#     FP16 rounding of the sum in between.
+#  9. The pages name no particular activation.  Offered: none, ReLU
+#     (``max(x, 0)``) and SiLU (``x * sigmoid(x)``, the activation of the
+#     Llama-family feed-forward layers whose shapes the workload uses).
+# ---------------------------------------------------------------------------
+
+ACT_NONE, ACT_RELU, ACT_SILU = 0, 1, 2
+
+
+def activation(x, act: int) -> np.ndarray:
+    """``act`` applied elementwise in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    if act == ACT_NONE:
+        return x.copy()
+    if act == ACT_RELU:
+        return np.where(x > 0.0, x, 0.0)
+    if act == ACT_SILU:
+        # sigmoid(x) = 1 / (1 + e^-x), taken on the side where the
+        # exponential cannot overflow: e^-|x| <= 1 always.
+        e = np.exp(-np.abs(x))
+        sig = np.where(x >= 0.0, 1.0 / (1.0 + e), e / (1.0 + e))
+        return x * sig
+    raise ValueError(f"unknown activation {act}")
+
+
+def epilogue(C64: np.ndarray, bias, act: int) -> np.ndarray:
+    """Float64 ``act(C64 + bias)`` (readings 7-9); ``bias`` None is no bias."""
+    Z = np.asarray(C64, dtype=np.float64)
+    if bias is not None:
+        Z = Z + np.asarray(bias, dtype=np.float16).astype(np.float64)[None, :]
+    return activation(Z, act)
+
+
+def gemm_fused(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int, bias=None,
+               act: int = ACT_NONE):
+    """``(C16, Y64, Z64)``: the pre-activation ``Z64 = C64 + bias``, the
+    float64 output ``Y64 = act(Z64)`` and its single FP16 rounding ``C16``."""
+    _, C64 = gemm(A, Bq, S, group)
+    Z64 = epilogue(C64, bias, ACT_NONE)
+    Y64 = activation(Z64, act)
+    return Y64.astype(np.float16), Y64, Z64

@@ -16,6 +16,8 @@ Recipe (the same for every shape):
   independent codes uniform on 0..15.
 * Scales ``S``: ``uniform(0.005, 0.02)`` in float64, rounded to float16,
   shape ``[K/group][N]`` row-major.
+* Bias (fused output stage only, its own generator): ``standard_normal``
+  float32 scaled by ``bias_std``, rounded to float16, shape ``[N]``.
 
 The value distributions are the ones the workload description gives: a
 Gaussian activation, uniform codes, and small positive scales, one per group
@@ -51,3 +53,13 @@ def make_words(K: int, N: int, seed: int = 0):
     """Uniform ``uint32`` weight words alone, shape ``[K/8][N]``."""
     rng = np.random.default_rng(seed)
     return rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+
+
+def make_bias(N: int, seed: int = 0, bias_std: float = 2.0):
+    """Per-column bias, ``bias_std * standard_normal`` rounded to float16.
+
+    The default spread is of the order of the products' own (a sum of K
+    terms of unit-variance activations and weights of magnitude ~0.05), so
+    the activation sees both signs."""
+    rng = np.random.default_rng(seed)
+    return (bias_std * rng.standard_normal(N, dtype=np.float32)).astype(np.float16)

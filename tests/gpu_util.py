@@ -51,3 +51,21 @@ def run_gemm(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int,
     w4.w4a16_gemm(A_d, Bp, S_d, C_d, M, K, N, group, ws)
     torch.cuda.synchronize()
     return host_f16(C_d)
+
+
+def run_gemm_fused(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int, bias, act: int,
+                   workspace=None, Bp=None):
+    """C (numpy float16) = act(A . dequant(B) + bias) from the library's fused
+    entry point; ``bias`` None passes a NULL bias."""
+    import torch
+    M, K = A.shape
+    N = Bq.shape[1]
+    if Bp is None:
+        Bp = repack_on_device(dev(Bq), K, N)
+    A_d, S_d = dev(A), dev(S)
+    b_d = None if bias is None else dev(bias)
+    C_d = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    ws = workspace if workspace is not None else w4.alloc_workspace(M, K, N, group)
+    w4.w4a16_gemm_fused(A_d, Bp, S_d, b_d, act, C_d, M, K, N, group, ws)
+    torch.cuda.synchronize()
+    return host_f16(C_d)

@@ -20,10 +20,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN = 0, -1, -2, -3, -4
+ERR_EPILOGUE = -8
 
 # Fake, 16-byte aligned addresses: the checks below return before any of
 # them is dereferenced or handed to the runtime.
 P_A, P_B, P_S, P_C, P_W = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+P_BIAS = 0x60000000
 
 
 def _declared_functions():
@@ -98,6 +100,28 @@ def test_gemm_empty_output_is_a_no_op(lib):
     # M == 0 or N == 0: nothing to compute, nothing launched, NULLs allowed
     assert lib.w4a16_gemm(None, None, None, None, 0, 256, 64, 128, None, None) == OK
     assert lib.w4a16_gemm(None, None, None, None, 5, 256, 0, 128, None, None) == OK
+
+
+def test_gemm_fused_rejects_bad_arguments(lib):
+    f = lib.w4a16_gemm_fused
+    assert w4.w4a16_status_string(ERR_EPILOGUE) == "W4A16_ERR_EPILOGUE"
+    for act in (-1, 3, 100):
+        assert f(P_A, P_B, P_S, P_BIAS, act, P_C, 4, 256, 64, 128, None, None) == ERR_EPILOGUE
+    # the plain checks still apply, in the same order as w4a16_gemm's
+    assert f(P_A, P_B, P_S, P_BIAS, 2, P_C, 4, 100, 64, 128, None, None) == ERR_SHAPE
+    assert f(P_A, P_B, P_S, P_BIAS, 2, P_C, 4, 256, 64, 64, None, None) == ERR_GROUP
+    assert f(None, P_B, P_S, P_BIAS, 1, P_C, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert f(P_A, P_B, P_S, P_BIAS + 2, 1, P_C, 4, 256, 64, 128, None, None) == ERR_ALIGN
+    # C overlapping the bias
+    assert f(P_A, P_B, P_S, P_C + 64, 0, P_C, 4, 256, 64, 128, None, None) == ERR_SHAPE
+    # empty output: nothing to do, the bias may be NULL or not
+    assert f(None, None, None, None, 2, None, 0, 256, 64, 128, None, None) == OK
+    assert f(None, None, None, P_BIAS, 1, None, 4, 256, 0, 128, None, None) == OK
+    # constants of the binding and the header agree
+    text = open(HEADER).read()
+    for name in ("W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU"):
+        value = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
+        assert getattr(w4, name) == value, name
 
 
 def test_repack_and_dequant_reject_bad_arguments(lib):

@@ -363,3 +363,101 @@ def test_ideal_speedup_matches_byte_accounting():
     assert math.floor(ratio * 100) / 100 == vals["ideal_speedup"]
     # decode-sized activations barely move the ratio
     assert abs(roofline.algorithmic_bytes(1, K, N, g) / w4 - 1) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# The fused output operation (bias + activation)
+# ---------------------------------------------------------------------------
+
+def test_activation_closed_forms():
+    """ReLU and SiLU at points whose values are known in closed form.
+
+    sigmoid(ln 3) = 1 / (1 + 1/3) = 3/4, so SiLU(ln 3) = (3/4) ln 3 and
+    SiLU(-ln 3) = -(1/4) ln 3; SiLU(0) = 0; SiLU(x) -> x for large x and
+    -> 0 (from below) for very negative x.  A sign slip in the sigmoid
+    (x * sigmoid(-x)) would swap 3/4 and 1/4."""
+    ln3 = math.log(3.0)
+    x = np.array([ln3, -ln3, 0.0, 40.0, -40.0, -800.0, 800.0])
+    silu = oracle.activation(x, oracle.ACT_SILU)
+    assert silu[0] == pytest.approx(0.75 * ln3, rel=1e-15)
+    assert silu[1] == pytest.approx(-0.25 * ln3, rel=1e-15)
+    assert silu[2] == 0.0
+    assert silu[3] == pytest.approx(40.0, rel=1e-16)
+    assert silu[4] == pytest.approx(-40.0 * math.exp(-40.0), rel=1e-14)
+    assert silu[5] == 0.0 and math.copysign(1.0, silu[5]) == -1.0   # no overflow, -0
+    assert silu[6] == 800.0
+    relu = oracle.activation(x, oracle.ACT_RELU)
+    assert list(relu) == [ln3, 0.0, 0.0, 40.0, 0.0, 0.0, 800.0]
+    assert np.array_equal(oracle.activation(x, oracle.ACT_NONE), x)
+    with pytest.raises(ValueError):
+        oracle.activation(x, 3)
+
+
+def test_activation_odd_part_identities():
+    """act(x) - act(-x) = x for both ReLU and SiLU (sigmoid(x) + sigmoid(-x)
+    = 1), on a dense grid that crosses zero."""
+    x = np.linspace(-30.0, 30.0, 6001)
+    for act in (oracle.ACT_RELU, oracle.ACT_SILU):
+        d = oracle.activation(x, act) - oracle.activation(-x, act)
+        assert np.max(np.abs(d - x)) <= 1e-14 * np.max(np.abs(x))
+    # SiLU's minimum: about -0.278465 at x about -1.278465
+    s = oracle.activation(x, oracle.ACT_SILU)
+    assert s.min() == pytest.approx(-0.2784645427610738, abs=1e-6)
+
+
+def test_fused_without_bias_or_activation_is_the_plain_product():
+    A, Bq, S = make_inputs(5, 512, 48, 128, seed=21)
+    C16, C64 = oracle.gemm(A, Bq, S, 128)
+    F16, Y64, Z64 = oracle.gemm_fused(A, Bq, S, 128)
+    assert np.array_equal(Y64, C64) and np.array_equal(Z64, C64)
+    assert np.array_equal(F16.view(np.uint16), C16.view(np.uint16))
+
+
+def test_fused_zero_activations_give_act_of_bias():
+    """A = 0: every row of the output is act(bias), exactly."""
+    from synth import make_bias
+    _, Bq, S = make_inputs(1, 256, 64, 128, seed=22)
+    A = np.zeros((3, 256), dtype=np.float16)
+    bias = make_bias(64, seed=5)
+    b64 = bias.astype(np.float64)
+    for act, f in ((oracle.ACT_NONE, lambda v: v), (oracle.ACT_RELU, lambda v: max(v, 0.0)),
+                   (oracle.ACT_SILU, lambda v: v / (1.0 + math.exp(-v)))):
+        C16, Y64, _ = oracle.gemm_fused(A, Bq, S, 128, bias, act)
+        for n in range(64):
+            want = f(float(b64[n]))
+            assert np.all(Y64[:, n] == pytest.approx(want, rel=1e-15, abs=1e-300))
+            assert np.all(C16[:, n].astype(np.float64) == _fp16_struct(float(Y64[0, n])))
+
+
+def test_fused_one_hot_rows_add_bias_to_weight_rows():
+    """Row m of A = e_k: Z[m][n] = W[k][n] + bias[n] (column index of the
+    bias, not row index: a transposed bias fails on a non-square case)."""
+    from synth import make_bias
+    K, N = 384, 40
+    _, Bq, S = make_inputs(1, K, N, 128, seed=23)
+    W = oracle.dequant(Bq, S, 128).astype(np.float64)
+    ks = [0, 5, 200, 383]
+    A = np.zeros((len(ks), K), dtype=np.float16)
+    A[np.arange(len(ks)), ks] = 1.0
+    bias = make_bias(N, seed=6)
+    _, _, Z64 = oracle.gemm_fused(A, Bq, S, 128, bias, oracle.ACT_RELU)
+    for m, k in enumerate(ks):
+        assert np.array_equal(Z64[m], W[k] + bias.astype(np.float64))
+
+
+@pytest.mark.parametrize("act", [1, 2])
+def test_fused_brute_force(act):
+    """Exact sums (Fractions) plus bias, activation in Python floats, one
+    rounding to FP16 by Python's own half packer."""
+    from synth import make_bias
+    M, K, N = 2, 256, 24
+    A, Bq, S = make_inputs(M, K, N, 128, seed=30 + act)
+    bias = make_bias(N, seed=7)
+    exact = _brute_force(A, Bq, S, 128)
+    C16, Y64, _ = oracle.gemm_fused(A, Bq, S, 128, bias, act)
+    for m in range(M):
+        for n in range(N):
+            z = float(exact[m][n] + Fraction(float(bias[n])))
+            y = max(z, 0.0) if act == 1 else z / (1.0 + math.exp(-z))
+            assert Y64[m, n] == pytest.approx(y, rel=1e-12, abs=1e-12)
+            assert float(C16[m, n]) == _fp16_struct(y)

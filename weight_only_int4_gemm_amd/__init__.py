@@ -6,6 +6,8 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
 
     w4a16_repack(Bq, Bpacked, K, N, stream=None)
     w4a16_gemm(A, Bpacked, scales, C, M, K, N, group, workspace, stream=None)
+    w4a16_gemm_fused(A, Bpacked, scales, bias, activation, C, M, K, N, group,
+                     workspace, stream=None)
     w4a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
     w4a16_workspace_bytes(M, K, N, group)
     w4a16_packed_bytes(K, N)
@@ -22,7 +24,8 @@ import os
 
 __all__ = [
     "W4A16Error", "LibraryNotBuilt", "library_path", "load",
-    "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
+    "w4a16_repack", "w4a16_gemm", "w4a16_gemm_fused", "w4a16_dequant_debug",
+    "W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
     "w4a16_status_string", "w4a16_describe", "EXPORTED_SYMBOLS",
 ]
@@ -30,13 +33,16 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libw4a16.so"
 
-# Status codes of include/w4a16.h.
+# Status codes and activations of include/w4a16.h.
 W4A16_OK = 0
+W4A16_ACT_NONE = 0
+W4A16_ACT_RELU = 1
+W4A16_ACT_SILU = 2
 
 EXPORTED_SYMBOLS = (
     "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_workspace_bytes", "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
-    "w4a16_describe",
+    "w4a16_describe", "w4a16_gemm_fused",
 )
 
 
@@ -81,6 +87,8 @@ def load():
     lib.w4a16_repack.restype = i
     lib.w4a16_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp]
     lib.w4a16_gemm.restype = i
+    lib.w4a16_gemm_fused.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, vp, vp]
+    lib.w4a16_gemm_fused.restype = i
     lib.w4a16_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.w4a16_dequant_debug.restype = i
     lib.w4a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
@@ -171,6 +179,20 @@ def w4a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
     _check("w4a16_gemm", load().w4a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
                                            int(M), int(K), int(N), int(group),
                                            _ptr(workspace), _stream(stream)))
+
+
+def w4a16_gemm_fused(A, Bpacked, scales, bias, activation: int, C, M: int, K: int, N: int,
+                     group: int, workspace=None, stream=None) -> None:
+    import torch
+    _expect(A, torch.float16, "A")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(bias, torch.float16, "bias")
+    _expect(C, torch.float16, "C")
+    _check("w4a16_gemm_fused",
+           load().w4a16_gemm_fused(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(bias),
+                                   int(activation), _ptr(C), int(M), int(K), int(N),
+                                   int(group), _ptr(workspace), _stream(stream)))
 
 
 def w4a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,

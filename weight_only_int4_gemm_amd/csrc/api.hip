@@ -236,6 +236,7 @@ const char* w4a16_status_string(int status) {
     case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE";
     case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH";
     case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE";
+    case W4A16_ERR_EPILOGUE: return "W4A16_ERR_EPILOGUE";
     default: return "W4A16_ERR_UNKNOWN";
   }
 }
@@ -312,9 +313,12 @@ int w4a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_
   return W4A16_OK;
 }
 
-int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
-               uint16_t* C, int M, int K, int N, int group, void* workspace,
-               void* stream) {
+int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                     const uint16_t* bias, int activation, uint16_t* C, int M, int K, int N,
+                     int group, void* workspace, void* stream) {
+  if (activation != W4A16_ACT_NONE && activation != W4A16_ACT_RELU &&
+      activation != W4A16_ACT_SILU)
+    return W4A16_ERR_EPILOGUE;
   if (M < 0) return W4A16_ERR_SHAPE;
   int rc = check_kn(K, N, true);
   if (rc != W4A16_OK) return rc;
@@ -322,12 +326,14 @@ int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scale
   if (rc != W4A16_OK) return rc;
   if (M == 0 || N == 0) return W4A16_OK;  // empty output: nothing to do
   if (!A || !Bpacked || !scales || !C) return W4A16_ERR_NULL;
-  if (!aligned16(A) || !aligned16(Bpacked) || !aligned16(scales) || !aligned16(C))
+  if (!aligned16(A) || !aligned16(Bpacked) || !aligned16(scales) || !aligned16(C) ||
+      (bias && !aligned16(bias)))
     return W4A16_ERR_ALIGN;
   const size_t cbytes = (size_t)M * N * 2;
   if (overlap(C, cbytes, A, (size_t)M * K * 2) ||
       overlap(C, cbytes, Bpacked, w4a16_packed_bytes(K, N)) ||
-      overlap(C, cbytes, scales, (size_t)(K / group) * N * 2))
+      overlap(C, cbytes, scales, (size_t)(K / group) * N * 2) ||
+      (bias && overlap(C, cbytes, bias, (size_t)N * 2)))
     return W4A16_ERR_SHAPE;
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
@@ -337,10 +343,18 @@ int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scale
     if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
     if (overlap(C, cbytes, workspace, plan.workspace_bytes)) return W4A16_ERR_SHAPE;
   }
-  if (launch_gemm(plan, A, Bpacked, scales, C, M, K, N, group, workspace,
+  const Epilogue ep{reinterpret_cast<const _Float16*>(bias), activation};
+  if (launch_gemm(plan, A, Bpacked, scales, C, M, K, N, group, ep, workspace,
                   static_cast<hipStream_t>(stream)) != hipSuccess)
     return W4A16_ERR_LAUNCH;
   return W4A16_OK;
+}
+
+int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+               uint16_t* C, int M, int K, int N, int group, void* workspace,
+               void* stream) {
+  return w4a16_gemm_fused(A, Bpacked, scales, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
+                          workspace, stream);
 }
 
 }  // extern "C"

@@ -27,6 +27,7 @@
 // matrix instructions: the codes of the next K block and the activations of
 // the next 32-deep step are in flight while the current ones are consumed.
 #include "coherent.hpp"
+#include "epilogue.hpp"
 #include "internal.hpp"
 #include "layout.hpp"
 #include "unpack.hpp"
@@ -42,12 +43,12 @@ struct Slot {
   half8_t a[MB][4];    // activation fragments, four 32-deep steps
 };
 
-template <int MB, int NB, int WK, int D>
+template <int MB, int NB, int WK, int D, bool EPI>
 __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, Epilogue ep) {
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
@@ -67,6 +68,17 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   const int n16_0 = tile_n * NB;
   // column blocks of this tile inside N (ragged N: the rest are skipped)
   const int nvalid = N / kBlockN - n16_0 < NB ? N / kBlockN - n16_0 : NB;
+
+  // Fused epilogue: the bias of the four columns this thread stores, read
+  // now so that the load's latency hides behind the main loop.  Every
+  // vector a thread stores (output stage below) starts at tile column
+  // (threadIdx.x % (TN / 4)) * 4, since the block size is a multiple of TN / 4.
+  static_assert((64 * WK) % (4 * NB) == 0, "a thread's output columns stay fixed");
+  half4_t bias4 = {};
+  if constexpr (EPI) {
+    const int gc = tile_n * 16 * NB + (int)(threadIdx.x % (4 * NB)) * 4;
+    if (ep.bias && gc < N) bias4 = *reinterpret_cast<const half4_t*>(ep.bias + gc);
+  }
 
   float4_t acc[MB][NB];
 #pragma unroll
@@ -183,6 +195,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   constexpr int VPR = TN / VEC;  // float4 vectors per tile row
   const int row0 = tile_m * TM;
   const int col0 = tile_n * TN;
+  // Four consecutive columns of C (through the epilogue), rounded to FP16.
+  auto finish = [&](const float4_t& x) {
+    half4_t h;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      h[j] = (_Float16)(EPI ? epilogue_apply(ep, x[j], (float)bias4[j]) : x[j]);
+    return h;
+  };
 
   if (splits == 1) {
     for (int v = threadIdx.x; v < TM * VPR; v += blockDim.x) {
@@ -190,8 +210,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
       const int gr = row0 + r, gc = col0 + c;
       if (gr < M && gc < N) {
         const float4_t x = *reinterpret_cast<const float4_t*>(&red[r * LDT + c]);
-        const half4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-        *reinterpret_cast<half4_t*>(C + (int64_t)gr * N + gc) = h;
+        *reinterpret_cast<half4_t*>(C + (int64_t)gr * N + gc) = finish(x);
       }
     }
     return;
@@ -239,10 +258,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
       }
     }
     const int gc = col0 + c;
-    if (gc < N) {
-      const half4_t h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-      *reinterpret_cast<half4_t*>(C + (int64_t)(row0 + r) * N + gc) = h;
-    }
+    if (gc < N) *reinterpret_cast<half4_t*>(C + (int64_t)(row0 + r) * N + gc) = finish(x);
   }
   if (threadIdx.x == 0)  // ready for the next call
     __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -251,7 +267,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
 template <int MB, int NB, int WK, int D>
 static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                              const uint16_t* S, uint16_t* C, int M, int K, int N,
-                             uint64_t gmagic, void* workspace,
+                             uint64_t gmagic, Epilogue ep, void* workspace,
                              hipStream_t stream) {
   unsigned* counters = nullptr;
   float* partials = nullptr;
@@ -260,10 +276,16 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D>), dim3(p.tiles_n, p.tiles_m, p.splits),
-                     dim3(64 * WK), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
-                     reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
-                     M, K, N, gmagic, p.splits, counters, partials);
+  const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WK);
+  auto a = reinterpret_cast<const _Float16*>(A);
+  auto s = reinterpret_cast<const _Float16*>(S);
+  auto c = reinterpret_cast<_Float16*>(C);
+  if (epilogue_needed(ep))
+    hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, true>), grid, block, 0, stream, a, Bp, s, c,
+                       M, K, N, gmagic, p.splits, counters, partials, ep);
+  else
+    hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, false>), grid, block, 0, stream, a, Bp, s, c,
+                       M, K, N, gmagic, p.splits, counters, partials, ep);
   return hipGetLastError();
 }
 
@@ -285,17 +307,17 @@ bool plan_is_compiled(int mb, int nb, int wk, int depth) {
 
 hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N, int group,
-                       void* workspace, hipStream_t stream) {
+                       Epilogue ep, void* workspace, hipStream_t stream) {
   // Scale row of K block kb is kb / gb, gb = group / 128, computed in the
   // kernels as (kb * ceil(2^32 / gb)) >> 32: exact when gb is a power of two,
   // and for any gb as long as kb, gb < 2^16 (K < 2^23 is checked).
   const uint64_t gb = (uint64_t)(group / kBlockK);
   const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
-  if (p.tile >= 2) return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, workspace, stream);
-  if (p.tile) return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, workspace, stream);
+  if (p.tile >= 2) return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, ep, workspace, stream);
+  if (p.tile) return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, ep, workspace, stream);
 #define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \
-    return launch_one<MB_, NB_, WK_, D_>(p, A, Bp, S, C, M, K, N, gmagic,           \
+    return launch_one<MB_, NB_, WK_, D_>(p, A, Bp, S, C, M, K, N, gmagic, ep,       \
                                          workspace, stream);
   W4A16_VARIANTS(W4A16_CASE)
 #undef W4A16_CASE

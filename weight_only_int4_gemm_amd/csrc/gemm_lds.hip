@@ -39,12 +39,12 @@ namespace w4a16 {
 // instruction at the same operand size and issues at the full rate, where
 // the 16 x 16 form sustains about 80% of it; it reads the same packed layout
 // (the lane-to-word map below).
-template <int MB, int NB, int WN, int NS, int F>
+template <int MB, int NB, int WN, int NS, int F, bool EPI>
 __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, Epilogue ep) {
   static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
   constexpr int TM = F * MB;
   constexpr int TN = F * NB * WN;
@@ -84,6 +84,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   const int row0 = tile_m * TM;
   const int col0 = tile_n * TN;
   const int n16_last = N / kBlockN - 1;
+  LaneBias<NB, F, EPI> bias;
+  bias.load(ep, col0, N);
 
   // Code source of this wave's column blocks (blocks past N re-read the last
   // valid one; their columns are dropped at the store).
@@ -308,17 +310,18 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   if constexpr (F == 16)
-    store_output_tile<MB, NB, WN>(acc, C, M, N, row0, col0, split, splits, counters, partials,
-                                  reinterpret_cast<int*>(&st0.s[0]));
+    store_output_tile<MB, NB, WN, EPI>(acc, C, M, N, row0, col0, split, splits, counters, partials,
+                                  reinterpret_cast<int*>(&st0.s[0]), ep, bias);
   else
-    store_output_tile32<MB, NB, WN>(acc, C, M, N, row0, col0, split, splits, counters,
-                                    partials, reinterpret_cast<int*>(&st0.s[0]));
+    store_output_tile32<MB, NB, WN, EPI>(acc, C, M, N, row0, col0, split, splits, counters,
+                                    partials, reinterpret_cast<int*>(&st0.s[0]), ep, bias);
 }
 
 template <int MB, int NB, int WN, int NS, int F>
 static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                  const uint16_t* S, uint16_t* C, int M, int K, int N,
-                                 uint64_t gmagic, void* workspace, hipStream_t stream) {
+                                 uint64_t gmagic, Epilogue ep, void* workspace,
+                                 hipStream_t stream) {
   unsigned* counters = nullptr;
   float* partials = nullptr;
   if (p.splits > 1) {
@@ -326,10 +329,16 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS, F>), dim3(p.tiles_n, p.tiles_m, p.splits),
-                     dim3(64 * WN), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
-                     reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
-                     M, K, N, gmagic, p.splits, counters, partials);
+  const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WN);
+  auto a = reinterpret_cast<const _Float16*>(A);
+  auto s = reinterpret_cast<const _Float16*>(S);
+  auto c = reinterpret_cast<_Float16*>(C);
+  if (epilogue_needed(ep))
+    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS, F, true>), grid, block, 0, stream, a,
+                       Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
+  else
+    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS, F, false>), grid, block, 0, stream, a,
+                       Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
   return hipGetLastError();
 }
 
@@ -351,11 +360,11 @@ bool lds_is_compiled(int mb, int nb, int wn, int ns, int f) {
 
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
-                      void* workspace, hipStream_t stream) {
+                      Epilogue ep, void* workspace, hipStream_t stream) {
   const int f = p.tile == 3 ? 32 : 16;
 #define W4A16_LCASE(MB_, NB_, WN_, NS_, F_)                                                \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_ && f == F_)              \
-    return launch_lds_one<MB_, NB_, WN_, NS_, F_>(p, A, Bp, S, C, M, K, N, gmagic,         \
+    return launch_lds_one<MB_, NB_, WN_, NS_, F_>(p, A, Bp, S, C, M, K, N, gmagic, ep,     \
                                                   workspace, stream);
   W4A16_LDS_VARIANTS(W4A16_LCASE)
 #undef W4A16_LCASE

@@ -45,12 +45,12 @@ struct BSlot {
 
 }  // namespace
 
-template <int MB, int NB, int WN, int NS, int DB>
+template <int MB, int NB, int WN, int NS, int DB, bool EPI>
 __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, Epilogue ep) {
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB * WN;
   constexpr int PIECES = TM * 16;          // 16-byte pieces of one activation stage
@@ -77,6 +77,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
   const int row0 = tile_m * TM;
   const int n16_last = N / kBlockN - 1;
   const int n16_0 = tile_n * NB * WN + wave * NB;
+  LaneBias<NB, 16, EPI> bias;
+  bias.load(ep, tile_n * TN, N);
 
   // Direct load i of this wave fills stage pieces 64 * (wave + WN * i) + lane:
   // row r = 4 * (wave + WN * i) + lane / 16, slot lane % 16, which holds
@@ -206,14 +208,14 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  store_output_tile<MB, NB, WN>(acc, C, M, N, row0, tile_n * TN, split, splits, counters,
-                                partials, reinterpret_cast<int*>(&As0[0]));
+  store_output_tile<MB, NB, WN, EPI>(acc, C, M, N, row0, tile_n * TN, split, splits, counters,
+                                partials, reinterpret_cast<int*>(&As0[0]), ep, bias);
 }
 
 template <int MB, int NB, int WN, int NS, int DB>
 static hipError_t launch_tile_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                   const uint16_t* S, uint16_t* C, int M, int K, int N,
-                                  uint64_t gmagic, void* workspace,
+                                  uint64_t gmagic, Epilogue ep, void* workspace,
                                   hipStream_t stream) {
   unsigned* counters = nullptr;
   float* partials = nullptr;
@@ -222,10 +224,16 @@ static hipError_t launch_tile_one(const Plan& p, const uint16_t* A, const uint32
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  hipLaunchKernelGGL((gemm_tile_kernel<MB, NB, WN, NS, DB>), dim3(p.tiles_n, p.tiles_m, p.splits),
-                     dim3(64 * WN), 0, stream, reinterpret_cast<const _Float16*>(A), Bp,
-                     reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(C),
-                     M, K, N, gmagic, p.splits, counters, partials);
+  const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WN);
+  auto a = reinterpret_cast<const _Float16*>(A);
+  auto s = reinterpret_cast<const _Float16*>(S);
+  auto c = reinterpret_cast<_Float16*>(C);
+  if (epilogue_needed(ep))
+    hipLaunchKernelGGL((gemm_tile_kernel<MB, NB, WN, NS, DB, true>), grid, block, 0, stream, a,
+                       Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<MB, NB, WN, NS, DB, false>), grid, block, 0, stream, a,
+                       Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
   return hipGetLastError();
 }
 
@@ -245,11 +253,11 @@ bool tile_is_compiled(int mb, int nb, int wn, int ns, int db) {
 
 hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
-                       uint64_t gmagic, void* workspace, hipStream_t stream) {
+                       uint64_t gmagic, Epilogue ep, void* workspace, hipStream_t stream) {
 #define W4A16_TCASE(MB_, NB_, WN_, NS_, DB_)                                            \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_ && p.bdepth == DB_)   \
     return launch_tile_one<MB_, NB_, WN_, NS_, DB_>(p, A, Bp, S, C, M, K, N, gmagic,    \
-                                                    workspace, stream);
+                                                    ep, workspace, stream);
   W4A16_TILE_VARIANTS(W4A16_TCASE)
 #undef W4A16_TCASE
   return hipErrorInvalidValue;

@@ -33,6 +33,14 @@ struct Plan {
   size_t workspace_bytes;  // 0 when splits == 1
 };
 
+// The operation the output stage applies to each FP32 sum before its one
+// rounding to FP16: y = act(x + bias[col]).  bias null: no bias; act is a
+// value of enum w4a16_activation.  Plain w4a16_gemm passes {nullptr, 0}.
+struct Epilogue {
+  const _Float16* bias;
+  int act;
+};
+
 Plan make_plan(int M, int K, int N, int group, int cus);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
@@ -44,13 +52,13 @@ hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
                           int K, int N, int group, hipStream_t stream);
 hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
-                       uint64_t gmagic, void* workspace, hipStream_t stream);
+                       uint64_t gmagic, Epilogue ep, void* workspace, hipStream_t stream);
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
-                      void* workspace, hipStream_t stream);
+                      Epilogue ep, void* workspace, hipStream_t stream);
 hipError_t launch_gemm(const Plan& plan, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
-                       int group, void* workspace, hipStream_t stream);
+                       int group, Epilogue ep, void* workspace, hipStream_t stream);
 
 // Workspace layout for a plan with splits > 1: one 32-bit arrival counter
 // per output tile (padded to 256 bytes), then FP32 partial tiles

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "coherent.hpp"
+#include "epilogue.hpp"
 #include "internal.hpp"
 
 namespace w4a16 {
@@ -45,6 +46,36 @@ __device__ __forceinline__ void stage_barrier() {
   keep_load_order();
 }
 
+// First output column of this lane in a workgroup tile starting at column
+// col0: each wave owns NB column blocks of F columns, lane l stores column
+// l % F of each (col + F * nb for block nb).
+template <int NB, int F>
+__device__ __forceinline__ int lane_out_col(int col0) {
+  return col0 + (int)(threadIdx.x >> 6) * F * NB + (int)(threadIdx.x & (F - 1));
+}
+
+// The bias of the columns this lane stores, loaded as raw FP16 at kernel
+// start (fused epilogue only) so that the load's latency hides behind the
+// main loop; it is converted where the output stage uses it.  The count-
+// based waits of the pipelines stay correct: this load is older than every
+// stage load, and loads complete in order.
+template <int NB, int F, bool EPI>
+struct LaneBias {
+  _Float16 v[NB];
+  __device__ __forceinline__ void load(const Epilogue& ep, int col0, int N) {
+    if constexpr (EPI) {
+      const int c = lane_out_col<NB, F>(col0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        v[nb] = (ep.bias && c + F * nb < N) ? ep.bias[c + F * nb] : (_Float16)0.f;
+    }
+  }
+  __device__ __forceinline__ float operator[](int nb) const {
+    if constexpr (EPI) return (float)v[nb];
+    return 0.f;
+  }
+};
+
 // Write a workgroup's output tile.  acc[mb][nb] holds, in lane l, rows
 // 4*(l/16) .. +3 of column l % 16 of the 16x16 block (mb, nb) of this wave,
 // whose columns start at tile column wave * 16 * NB.
@@ -55,29 +86,34 @@ __device__ __forceinline__ void stage_barrier() {
 // order -- wave, 16-row block, 16-column block, lane, four values -- so each
 // lane moves its four accumulators in one 16-byte access and the workgroup
 // that sums finds its own fragments at the same places.  `flag` is an int in
-// LDS no wave touches any more.
-template <int MB, int NB, int WN>
+// LDS no wave touches any more.  The epilogue is applied to the final sums
+// only.
+template <int MB, int NB, int WN, bool EPI>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
                                                   int row0, int col0, int split, int splits,
                                                   unsigned* __restrict__ counters,
-                                                  float* __restrict__ partials, int* flag) {
+                                                  float* __restrict__ partials, int* flag,
+                                                  const Epilogue& ep,
+                                                  const LaneBias<NB, 16, EPI>& bias) {
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB * WN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int l16 = lane & 15;
-  const int col_base = col0 + wave * 16 * NB + l16;
+  const int col_base = lane_out_col<NB, 16>(col0);
   auto write_c = [&]() {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int gc = col_base + nb * 16;
+        if (gc >= N) continue;
+        const float b = bias[nb];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
-          if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][i];
+          const float x = acc[mb][nb][i];
+          if (gr < M) C[(int64_t)gr * N + gc] = (_Float16)(EPI ? epilogue_apply(ep, x, b) : x);
         }
       }
   };
@@ -128,17 +164,19 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
 // 4q + i (q, i = 0..3); the wave's columns start at tile column
 // wave * 32 * NB.  A partial is kept in fragment order (wave, row block,
 // column block, q, lane, four values).
-template <int MB, int NB, int WN>
+template <int MB, int NB, int WN, bool EPI>
 __device__ __forceinline__ void store_output_tile32(float16_t (&acc)[MB][NB],
                                                     _Float16* __restrict__ C, int M, int N,
                                                     int row0, int col0, int split, int splits,
                                                     unsigned* __restrict__ counters,
-                                                    float* __restrict__ partials, int* flag) {
+                                                    float* __restrict__ partials, int* flag,
+                                                    const Epilogue& ep,
+                                                    const LaneBias<NB, 32, EPI>& bias) {
   constexpr int TM = 32 * MB;
   constexpr int TN = 32 * NB * WN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col_base = col0 + wave * 32 * NB + (lane & 31);
+  const int col_base = lane_out_col<NB, 32>(col0);
   const int row_lane = 4 * (lane >> 5);
   auto write_c = [&]() {
 #pragma unroll
@@ -146,12 +184,15 @@ __device__ __forceinline__ void store_output_tile32(float16_t (&acc)[MB][NB],
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int gc = col_base + nb * 32;
+        if (gc >= N) continue;
+        const float b = bias[nb];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int gr = row0 + mb * 32 + 8 * q + row_lane + i;
-            if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (_Float16)acc[mb][nb][4 * q + i];
+            const float x = acc[mb][nb][4 * q + i];
+            if (gr < M) C[(int64_t)gr * N + gc] = (_Float16)(EPI ? epilogue_apply(ep, x, b) : x);
           }
       }
   };
