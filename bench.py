@@ -11,9 +11,16 @@ before timing starts.  Each of the twelve GEMMs of a step reads its own copy
 of the layer's weights, and the copies rotate over steps, so that no weight
 read is served by the 256 MB Infinity Cache from an earlier launch.
 
+Warmup runs the W steps asked for and continues until at least half a
+second of steps has run (the GPU's clocks ramp up from idle); the JSON line
+gives both W and the number of warmup steps run.  The timed region is
+exactly K steps.  The same K steps are then replayed from HIP graphs (one
+graph per weight-copy rotation) and reported under ``graph``.
+
 Prints one JSON line: whole-step TFLOP/s (the metric), achieved HBM TB/s,
-the roofline object of the dominant kernel (measured with HIP events on the
-launch stream over the timed region), and the CPU oracle timed on the host.
+the roofline object of the dominant kernel (per-launch durations from HIP
+events around back-to-back batches of each GEMM on the launch stream), and
+the CPU oracle timed on the host.
 
 Counter-based HBM traffic (``roofline.traffic``) comes from two rocprofv3
 counter runs of this script, summarised into profiles/ by
@@ -53,6 +60,7 @@ GROUP = 128
 WEIGHT_COPIES = 8   # 8 x 101 MB of packed weights: far beyond the 256 MB MALL
 COPY_PROBE_BYTES = 512 * 2**20   # one-dispatch device copy of known size, counter calibration
 COPY_PROBE_RUNS = 4
+WARMUP_MIN_S = 0.5   # untimed steps run at least this long before timing
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama7b_step.json")
 
 # Every workload shape, for --configs-report: (label, K, N, group, batch sizes).
@@ -558,39 +566,58 @@ def main():
     calls_per_step = [[args_for(g, (len(BATCHES) * s + BATCHES.index(g[3])) % WEIGHT_COPIES)
                        for g in gemms] for s in range(WEIGHT_COPIES)]
 
-    def run_step(s, events=None):
-        calls = calls_per_step[s % WEIGHT_COPIES]
-        for i, a in enumerate(calls):
-            if events is not None:
-                events[i].record(stream)
+    def run_step(s):
+        for a in calls_per_step[s % WEIGHT_COPIES]:
             rc = lib.w4a16_gemm(*a)
             if rc != 0:
                 raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
 
-    for s in range(args.warmup):
-        run_step(s)
+    # Warmup: the W steps asked for, continued (untimed) until at least
+    # WARMUP_MIN_S of back-to-back steps have run: from idle the GPU takes a
+    # fraction of a second to reach its working clocks, and a few steps
+    # alone would time the ramp, not the kernels.
+    t_w = time.perf_counter()
+    warmup_run = 0
+    while warmup_run < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+        run_step(warmup_run)
+        warmup_run += 1
+        if warmup_run % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # ---- timed region ------------------------------------------------------
     # The step as a user runs it: launches only.  (Recording an event per
     # launch costs host time comparable to the small kernels themselves.)
     torch.cuda.synchronize()
+    # (the weight-copy rotation continues from the warmup)
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(s)
+        run_step(warmup_run + s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # The same steps again with a HIP event between launches, on the launch
-    # stream: the per-kernel durations behind the roofline object.
-    step_events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
-                   for _ in range(args.steps)]
-    end_event = torch.cuda.Event(enable_timing=True)
+    # Per-GEMM durations behind the roofline object: each of the step's GEMMs
+    # launched K times back to back (its weight copies rotating) between two
+    # HIP events on the launch stream; duration per launch = span / K.  An
+    # event pair around every single launch would add the event packets'
+    # own time (a few microseconds) to each kernel.
+    n_rep = max(args.steps, 20)
+    per_gemm_ms = {}
     torch.cuda.synchronize()
-    for s in range(args.steps):
-        run_step(s, step_events[s])
-    end_event.record(stream)
+    for gi, g in enumerate(gemms):
+        calls = [calls_per_step[s][gi] for s in range(WEIGHT_COPIES)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(n_rep):
+            rc = lib.w4a16_gemm(*calls[r % WEIGHT_COPIES])
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+        e1.record(stream)
+        per_gemm_ms[g] = (e0, e1)
     torch.cuda.synchronize()
+    per_gemm_ms = {g: [e0.elapsed_time(e1) / n_rep] * n_rep for g, (e0, e1) in per_gemm_ms.items()}
+    gpu_ms_total = sum(v[0] for v in per_gemm_ms.values()) * n_rep
 
     # The same steps replayed from HIP graphs: one graph per weight-copy
     # rotation, each holding the step's twelve launches, captured once on a
@@ -612,23 +639,17 @@ def main():
     torch.cuda.synchronize()
     graph_wall = None
     if graphs:
-        for s in range(args.warmup):
+        n_warm = max(args.warmup, 2 * WEIGHT_COPIES)
+        for s in range(n_warm):
             graphs[s % WEIGHT_COPIES].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(args.steps):
-            graphs[s % WEIGHT_COPIES].replay()
+            graphs[(n_warm + s) % WEIGHT_COPIES].replay()
         torch.cuda.synchronize()
         graph_wall = time.perf_counter() - t0
     del graphs
 
-    # per-launch durations from the events
-    per_gemm_ms = {g: [] for g in gemms}
-    for s in range(args.steps):
-        evs = step_events[s] + ([step_events[s + 1][0]] if s + 1 < args.steps else [end_event])
-        for i, g in enumerate(gemms):
-            per_gemm_ms[g].append(evs[i].elapsed_time(evs[i + 1]))
-    gpu_ms_total = step_events[0][0].elapsed_time(end_event)
 
     step_flops = sum(roofline.flops(M, K, N) for (_, K, N, M) in gemms)
     step_bytes = sum(roofline.algorithmic_bytes(M, K, N, GROUP) for (_, K, N, M) in gemms)
@@ -664,7 +685,7 @@ def main():
     roof["algorithmic_bytes"] = dom["bytes"] / dom["launches"]
     roof["kernel"] = dom_name
     roof["avg_launch_us"] = avg_s * 1e6
-    roof["launches_per_step"] = dom["launches"] // args.steps
+    roof["launches_per_step"] = dom["launches"] // n_rep
 
     per_gemm = []
     for g in gemms:
@@ -701,6 +722,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmup_run,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -716,7 +738,7 @@ def main():
         },
         "hbm_tbps": step_bytes / (wall / args.steps) / 1e12,
         "step_roofline_frac": step_roof_s / (wall / args.steps),
-        "events_pass_ms_per_step": gpu_ms_total / args.steps,
+        "events_pass_ms_per_step": gpu_ms_total / n_rep,
         "graph": None if graph_wall is None else {
             "launch": f"one HIP graph per step ({n_launch} kernel nodes), replayed",
             "ms_per_step": graph_wall * 1e3 / args.steps,

@@ -108,7 +108,9 @@ void apply_forced_plan(Plan* p, int KB) {
 // The heuristic (measured on MI355X at the Llama-2-7B layer shapes and an
 // 8192 x 28672 prefill layer).
 // Small batches (M <= 4, or M <= 16 with N < 8192) stream the weights:
-// one 16-row block per wave.
+// one 16-row block per wave.  Plans were chosen by sweeping every compiled
+// variant and split count at the workload shapes (Llama-2-7B layers,
+// 18432 x 73728, 28672 x 8192, 13824 x 5120, 8192 x 28672).
 // With one activation row the activation fragments cost little, so narrow
 // column tiles (16 or 32 columns) give the most workgroups; with 16 rows
 // every wave re-reads its activation fragments, so wide tiles (64 columns)
@@ -126,13 +128,15 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
     // streaming kernel: activations straight from global memory
     p.mb = 1;
     if (M <= 4) {
-      p.nb = n16 >= 4 * cus ? 2 : 1;
+      // 16-column tiles; 32 for wide N or deep K (there split three ways
+      // below), 64 for very wide N
+      p.nb = n16 >= 8 * cus ? 4 : (n16 >= 4 * cus || KB >= 96) ? 2 : 1;
       p.wk = 8;
       p.depth = 2;
     } else {
       p.nb = n16 >= 2 * cus || KB >= 64 ? 4 : 1;
       p.wk = 4;
-      p.depth = KB >= 64 ? 4 : 2;
+      p.depth = KB >= 64 && KB < 96 ? 4 : 2;
     }
   } else if (M <= 32) {
     // LDS kernel with 16- or 32-row tiles and 256 columns (eight waves of
@@ -197,6 +201,17 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
       }
     }
     cap = 8;
+  } else if (M <= 4 && KB >= 96 && n16 < 4 * cus) {
+    // streaming, one to four rows, deep K (K >= 12288) and moderate N: three
+    // K ranges per 32-column tile (measured best for 28672 x 8192 and
+    // 13824 x 5120: 1.2-1.25x over unsplit 16-column tiles)
+    want = 3;
+    cap = KB / (2 * p.wk);
+  } else if (M > 4 && KB >= 96) {
+    // streaming, five to sixteen rows, deep K: eight K ranges per 64-column
+    // tile (13824 x 5120: 1.3x over the default below)
+    want = 8;
+    cap = KB / (2 * p.wk);
   } else {
     // one workgroup per compute unit, two for deep K (K >= 8192)
     const int64_t target = (KB >= 64 ? 2 : 1) * (int64_t)cus;
