@@ -282,6 +282,18 @@ def _time_calls(calls, launches: int, repeats: int) -> float:
     return float(np.median(times))
 
 
+def _warm_clocks(seconds: float = 1.0) -> None:
+    """Keep the GPU busy for ``seconds`` so its clocks leave the idle state
+    before anything is timed."""
+    import torch
+    x = torch.randn(4096, 4096, device="cuda", dtype=torch.float16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            torch.matmul(x, x)
+        torch.cuda.synchronize()
+
+
 def _gpu_clocks() -> str:
     """The current clocks as rocm-smi reports them (empty if unavailable)."""
     import subprocess
@@ -311,6 +323,7 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
     torch.cuda.set_device(dev)
     lib = w4.load()
     sh = torch.cuda.current_stream().cuda_stream
+    _warm_clocks()
     clocks_before = _gpu_clocks()
     rows = []
     for label, K, N, group, batches in REPORT_SHAPES:
@@ -376,7 +389,8 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         "torch.matmul (hipBLASLt) on the same weights dequantised to FP16, timed the same "
         "way with its own rotation of weight copies; `x FP16` is its time over ours.",
         "",
-        f"Clocks before (rocm-smi): {clocks_before or 'n/a'}",
+        f"Clocks after a one-second warm-up, before the first shape (rocm-smi): "
+        f"{clocks_before or 'n/a'}",
         "",
         f"Clocks after: {clocks_after or 'n/a'}",
         "",
@@ -415,6 +429,7 @@ def epilogue_report(out_path: str, repeats: int = 7, launches: int = 50) -> None
     torch.cuda.set_device(dev)
     lib = w4.load()
     sh = torch.cuda.current_stream().cuda_stream
+    _warm_clocks()
     rows = []
     for label, K, N, batches in EPILOGUE_SHAPES:
         _, Bq, S = make_inputs(1, K, N, GROUP, seed=0)
