@@ -139,7 +139,10 @@ def _short_kernel_name(name: str) -> str:
         return seg
     base = name.split("(")[0].replace("void ", "").strip()
     head, lt, rest = base.partition("<")
-    return head.split("::")[-1] + lt + rest.replace(" ", "")
+    # bool template arguments (the fused-epilogue switch) are not part of
+    # the plan's name
+    rest = rest.replace(" ", "").replace(",false>", ">").replace(",true>", ">")
+    return head.split("::")[-1] + lt + rest
 
 
 def _pmc_values(run_dir: str, counter: str):

@@ -21,6 +21,11 @@ def test_kernel_names_from_profiler_output():
             "gemm_tile_kernel<8,2,2>",
         "_ZN5w4a1611gemm_kernelILi1ELi4ELi4ELi2EEEvPKDF16_": "gemm_kernel<1,4,4,2>",
         "_ZN5w4a1613repack_kernelEPKjPjii": "repack_kernel",
+        # the fused-epilogue switch (a bool template argument) is dropped
+        "_ZN5w4a1615gemm_lds_kernelILi4ELi2ELi2ELi4ELi3ELi16ELb1EEEvPKDF16_PKjS2_PDF16_iiimiPjPf"
+        "NS_8EpilogueE": "gemm_lds_kernel<4,2,2,4,3,16>",
+        "void w4a16::gemm_lds_kernel<4, 1, 1, 8, 3, 16, false>(_Float16 const*)":
+            "gemm_lds_kernel<4,1,1,8,3,16>",
     }
     for raw, short in cases.items():
         assert bench._short_kernel_name(raw) == short

@@ -63,13 +63,15 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q) {
-  if (q.tile >= 2) return lds_is_compiled(q.mb, q.nb, q.wk, q.depth, q.tile == 3 ? 32 : 16);
+  if (q.tile >= 2)
+    return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth, q.tile == 3 ? 32 : 16);
+  if (q.wm != 1) return false;
   return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk, q.depth, q.bdepth)
                 : plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
 }
 
 // Test and tuning override:
-// W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile[,bdepth]]]" replaces the
+// W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile[,bdepth[,wm]]]]" replaces the
 // heuristic's choice when it names a compiled variant (a field <= 0 keeps
 // the heuristic's value; tile is 0, the default, for the streaming kernel,
 // 1 for the tile kernel, 2 for the LDS kernel with 16 x 16 blocks or 3 for
@@ -79,9 +81,9 @@ bool variant_is_compiled(const Plan& q) {
 void apply_forced_plan(Plan* p, int KB) {
   const char* env = std::getenv("W4A16_FORCE_PLAN");
   if (!env || !*env) return;
-  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0, bdepth = 0;
-  if (std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
-                  &bdepth) < 4)
+  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0, bdepth = 0, wm = 0;
+  if (std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
+                  &bdepth, &wm) < 4)
     return;
   if (tile < 0 || tile > 3) return;
   Plan q = *p;
@@ -92,6 +94,7 @@ void apply_forced_plan(Plan* p, int KB) {
   if (splits > 0) q.splits = splits > KB ? KB : splits;
   if (depth > 0) q.depth = depth;
   q.bdepth = bdepth > 0 ? bdepth : (q.tile == 1 ? 4 : 0);
+  q.wm = wm > 0 ? wm : 1;
   if (!variant_is_compiled(q)) {
     // keep the forced tile but take the first compiled depth for it
     for (int d : {4, 3, 2, 1}) {
@@ -121,6 +124,7 @@ void apply_forced_plan(Plan* p, int KB) {
 Plan make_plan(int M, int K, int N, int group, int cus) {
   (void)group;
   Plan p{};
+  p.wm = 1;
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
   if (cus <= 0) cus = 256;
@@ -150,12 +154,25 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   } else if (M <= 128) {
     // LDS kernel, 64 x 128 tiles (eight waves of 64 x 16, two per SIMD):
     // small tiles keep enough workgroups; each weight is unpacked once per
-    // 64 rows
+    // 64 rows.  Above 64 rows, where N gives at least half a tile per
+    // compute unit at 128 columns, 128-row tiles read each weight once:
+    // 128 x 128 as a 2 x 4 grid of 64 x 32 wave tiles, or, with two tiles
+    // per compute unit, 128 x 256 (eight waves of 128 x 32).  Measured
+    // 1.2x at 4096 x 22016 and 18432 x 73728 for M = 128.
+    const int n128 = (N + 127) / 128;
     p.tile = 2;
     p.mb = 4;
     p.nb = 1;
     p.wk = 8;
     p.depth = 3;
+    if (M > 64 && n128 >= 2 * cus) {
+      p.mb = 8;
+      p.nb = 2;
+    } else if (M > 64 && 2 * n128 >= cus) {
+      p.nb = 2;
+      p.wm = 2;
+      p.wk = 4;
+    }
   } else {
     // prefill: 128 x 256 tiles (eight waves of 128 x 32), each weight
     // unpacked once per 128 rows
@@ -167,7 +184,7 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   }
   auto shape = [&](Plan& q) {
     const int f = q.tile == 3 ? 32 : 16;
-    q.tm = f * q.mb;
+    q.tm = f * q.mb * q.wm;
     q.tn = f * q.nb * (q.tile ? q.wk : 1);  // tile and LDS kernels split N over waves
     q.tiles_n = (N + q.tn - 1) / q.tn;
     q.tiles_m = (M + q.tm - 1) / q.tm;
@@ -282,10 +299,10 @@ int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   const Plan p = make_plan(M, K, N, group, cus);
   if (p.tile >= 2)
     std::snprintf(buf, len,
-                  "gemm_lds_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
+                  "gemm_lds_kernel<%d,%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
                   "workspace=%zu",
-                  p.mb, p.nb, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
-                  p.splits, 64 * p.wk, p.splits, p.workspace_bytes);
+                  p.mb, p.nb, p.wm, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
+                  p.splits, 64 * p.wm * p.wk, p.splits, p.workspace_bytes);
   else if (p.tile)
     std::snprintf(buf, len,
                   "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "

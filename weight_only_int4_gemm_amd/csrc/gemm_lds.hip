@@ -1,10 +1,14 @@
 // The W4A16 GEMM for batches of more than 32 rows, with every operand
 // staged through LDS: C = A . dequant(Bpacked).
 //
-// Same work decomposition as the tile kernel (gemm_tile.hip): a workgroup of
-// WN waves owns a 16*MB x 16*NB*WN output tile and one K range; each wave
-// owns 16*NB columns and all rows, so every weight is unpacked once per
-// workgroup.  The difference is the load pipeline.  Vector-memory loads of a
+// A workgroup of WM x WN waves owns an F*MB*WM x F*NB*WN output tile and one
+// K range; wave (wm, wn) owns the F*MB x F*NB block at row block wm, column
+// block wn.  With WM = 1 every wave spans all rows and each weight is
+// unpacked once per workgroup (the tile kernel's decomposition); with
+// WM > 1 each weight is unpacked by WM waves, but a wave reads only its own
+// rows of the activation stage, which divides the LDS bytes read per matrix
+// instruction (each wave re-reads its activation rows for every K block).
+// The difference from the tile kernel (gemm_tile.hip) is the load pipeline.  Vector-memory loads of a
 // wave complete in issue order, so in the tile kernel the wait for an
 // activation stage also waits for every code load issued before it, and the
 // codes (which come from HBM) never get more than a couple of K blocks of
@@ -21,9 +25,9 @@
 // Stage layout (per K block):
 //  * activations: 16*MB rows x 16 pieces of 16 bytes, piece c of row r at
 //    slot c ^ (r & 15) (conflict-free fragment reads, as in the tile kernel);
-//  * codes: the NB*WN fragment blocks of the tile, 1 KiB each, in the
-//    permuted layout's own order (lane l's four words at 16*l), so a wave
-//    reads its fragments with one conflict-free 16-byte read per block;
+//  * codes: the NB*WN (16-column) fragment blocks of the tile, 1 KiB each,
+//    in the permuted layout's own order (lane l's four words at 16*l), so a
+//    wave reads its fragments with one conflict-free 16-byte read per block;
 //  * scales: the tile's 16*NB*WN FP16 scales of this K block's group.
 #include <type_traits>
 
@@ -39,25 +43,29 @@ namespace w4a16 {
 // instruction at the same operand size and issues at the full rate, where
 // the 16 x 16 form sustains about 80% of it; it reads the same packed layout
 // (the lane-to-word map below).
-template <int MB, int NB, int WN, int NS, int F, bool EPI>
-__global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
+template <int MB, int NB, int WM, int WN, int NS, int F, bool EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
     float* __restrict__ partials, Epilogue ep) {
   static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
-  constexpr int TM = F * MB;
+  constexpr int WAVES = WM * WN;
+  constexpr int TM = F * MB * WM;
   constexpr int TN = F * NB * WN;
   constexpr int NB16 = NB * F / 16;            // 16-column code blocks per wave
+  constexpr int BLOCKS = NB16 * WN;            // 16-column code blocks of the tile
   constexpr int APIECES = TM * 16;             // 16-byte pieces of activations
   constexpr int ACHUNKS = APIECES / 64;        // 1 KiB wave-loads of activations
-  // direct activation loads per wave; with fewer chunks than waves some
-  // chunks are loaded twice (same bytes to the same place)
-  constexpr int ALOADS = (ACHUNKS + WN - 1) / WN;
-  constexpr int BPIECES = NB16 * WN * 64;      // 16-byte pieces of codes
+  // direct loads per wave of activation chunks and of code blocks; with
+  // fewer chunks (blocks) than waves some are loaded twice (same bytes to
+  // the same place), so every wave issues the same number of loads
+  constexpr int ALOADS = (ACHUNKS + WAVES - 1) / WAVES;
+  constexpr int BLOADS = (BLOCKS + WAVES - 1) / WAVES;
+  constexpr int BPIECES = BLOCKS * 64;         // 16-byte pieces of codes
   constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
   constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
-  constexpr int LOADS = ALOADS + NB16 + SLOADS;  // direct loads per wave per stage
+  constexpr int LOADS = ALOADS + BLOADS + SLOADS;  // direct loads per wave per stage
   static_assert(NS >= 2 && NS <= 4, "two to four stages");
   struct Stage {
     uint4 a[APIECES];
@@ -74,6 +82,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN;  // this wave's row block and column block
+  const int wn = wave % WN;
   const int tile_n = blockIdx.x;
   const int tile_m = blockIdx.y;
   const int split = blockIdx.z;
@@ -84,17 +94,22 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   const int row0 = tile_m * TM;
   const int col0 = tile_n * TN;
   const int n16_last = N / kBlockN - 1;
+  const int wrow0 = row0 + wm * F * MB;  // this wave's tile
+  const int wcol0 = col0 + wn * F * NB;
   LaneBias<NB, F, EPI> bias;
-  bias.load(ep, col0, N);
+  bias.load(ep, wcol0, N);
 
-  // Code source of this wave's column blocks (blocks past N re-read the last
-  // valid one; their columns are dropped at the store).
-  const uint32_t* bsrc[NB16];
+  // Code blocks this wave loads: tile block (wave + WAVES * i) % BLOCKS for
+  // load i (blocks past N re-read the last valid one; their columns are
+  // dropped at the store).
+  const uint32_t* bsrc[BLOADS];
+  int bblk[BLOADS];
 #pragma unroll
-  for (int nb = 0; nb < NB16; ++nb) {
-    const int n16 = tile_n * NB16 * WN + wave * NB16 + nb;
-    bsrc[nb] = Bp + block_word_offset(n16 <= n16_last ? n16 : n16_last, 0, K) +
-               lane * kWordsPerLane;
+  for (int i = 0; i < BLOADS; ++i) {
+    bblk[i] = (wave + WAVES * i) % BLOCKS;
+    const int n16 = tile_n * BLOCKS + bblk[i];
+    bsrc[i] = Bp + block_word_offset(n16 <= n16_last ? n16 : n16_last, 0, K) +
+              lane * kWordsPerLane;
   }
   // Scale source: word i*64 + lane of the stage holds columns 2w, 2w+1.
   const _Float16* ssrc[SLOADS];
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
 #pragma unroll
     for (int i = 0; i < ALOADS; ++i) {
       // activation load i of this wave: stage pieces 64 * chunk + lane
-      const int chunk = (wave + WN * i) % ACHUNKS;
+      const int chunk = (wave + WAVES * i) % ACHUNKS;
       const int r = 4 * chunk + (lane >> 4);
       const int piece = l16 ^ (r & 15);
       const int gr = row0 + r < M ? row0 + r : M - 1;  // rows past M: never stored
@@ -120,9 +135,9 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
                                        0);
     }
 #pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) {
-      __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[nb] + kb * kWordsPerBlock),
-                                       (lds_ptr_t)&sg.b[64 * (wave * NB16 + nb)], 16, 0, 0);
+    for (int i = 0; i < BLOADS; ++i) {
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[i] + kb * kWordsPerBlock),
+                                       (lds_ptr_t)&sg.b[64 * bblk[i]], 16, 0, 0);
     }
     const int srow = scale_row(kb) * N;
 #pragma unroll
@@ -148,7 +163,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     const int lg = lane >> 4;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int r = mb * 16 + l16;
+      const int r = (wm * MB + mb) * 16 + l16;
       a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + ((4 * j + lg) ^ (r & 15))]);
     }
   };
@@ -161,8 +176,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      w[nb] = sg.b[64 * (wave * NB + nb) + lane];
-      const _Float16 sc = sh[wave * 16 * NB + nb * 16 + l16];
+      w[nb] = sg.b[64 * (wn * NB + nb) + lane];
+      const _Float16 sc = sh[wn * 16 * NB + nb * 16 + l16];
       s2[nb] = half2_t{sc, sc};
     }
     auto unpack_slice = [&](int j, half8_t* bf) {
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     const int piece = 2 * s + (lane >> 5);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int r = mb * 32 + r32;
+      const int r = (wm * MB + mb) * 32 + r32;
       a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + (piece ^ (r & 15))]);
     }
   };
@@ -221,10 +236,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
     const int le = l16 + 16 * (lane >> 5);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int blk = 64 * (wave * NB16 + 2 * nb + (c32 >> 4));
+      const int blk = 64 * (wn * NB16 + 2 * nb + (c32 >> 4));
       we[nb] = sg.b[blk + le];
       wo[nb] = sg.b[blk + le + 32];
-      const _Float16 sc = sh[wave * 32 * NB + nb * 32 + c32];
+      const _Float16 sc = sh[wn * 32 * NB + nb * 32 + c32];
       s2[nb] = half2_t{sc, sc};
     }
     auto unpack_slice = [&](int s, half8_t* bf) {
@@ -310,14 +325,15 @@ __global__ __launch_bounds__(64 * WN) void gemm_lds_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   if constexpr (F == 16)
-    store_output_tile<MB, NB, WN, EPI>(acc, C, M, N, row0, col0, split, splits, counters, partials,
-                                  reinterpret_cast<int*>(&st0.s[0]), ep, bias);
+    store_output_tile<MB, NB, WAVES, EPI>(acc, C, M, N, wrow0, wcol0, split, splits, counters,
+                                          partials, reinterpret_cast<int*>(&st0.s[0]), ep, bias);
   else
-    store_output_tile32<MB, NB, WN, EPI>(acc, C, M, N, row0, col0, split, splits, counters,
-                                    partials, reinterpret_cast<int*>(&st0.s[0]), ep, bias);
+    store_output_tile32<MB, NB, WAVES, EPI>(acc, C, M, N, wrow0, wcol0, split, splits,
+                                            counters, partials, reinterpret_cast<int*>(&st0.s[0]),
+                                            ep, bias);
 }
 
-template <int MB, int NB, int WN, int NS, int F>
+template <int MB, int NB, int WM, int WN, int NS, int F>
 static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                  const uint16_t* S, uint16_t* C, int M, int K, int N,
                                  uint64_t gmagic, Epilogue ep, void* workspace,
@@ -329,30 +345,35 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         counters_bytes(p.tiles_n * p.tiles_m));
   }
-  const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WN);
+  const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WM * WN);
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
   if (epilogue_needed(ep))
-    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS, F, true>), grid, block, 0, stream, a,
-                       Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
+    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, true>), grid, block, 0, stream,
+                       a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
   else
-    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WN, NS, F, false>), grid, block, 0, stream, a,
-                       Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
+    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, false>), grid, block, 0, stream,
+                       a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
   return hipGetLastError();
 }
 
-// Compiled variants (MB, NB, WN, NS, F).
-#define W4A16_LDS_VARIANTS(X)                                                               \
-  X(4, 2, 2, 3, 16) X(4, 2, 4, 3, 16) X(4, 2, 4, 4, 16) X(4, 4, 4, 3, 16) X(8, 1, 4, 3, 16)  \
-  X(8, 2, 4, 2, 16) X(8, 2, 4, 3, 16) X(8, 4, 4, 2, 16) X(8, 4, 4, 3, 16) X(4, 1, 8, 3, 16)  \
-  X(4, 2, 8, 3, 16) X(8, 1, 8, 3, 16) X(8, 2, 8, 3, 16) X(1, 4, 4, 4, 16) X(1, 8, 4, 4, 16)  \
-  X(1, 2, 8, 4, 16) X(1, 4, 8, 4, 16) X(2, 4, 4, 4, 16) X(2, 2, 8, 4, 16) X(2, 4, 8, 3, 16)  \
-  X(4, 1, 8, 3, 32) X(2, 1, 8, 3, 32) X(4, 1, 4, 3, 32) X(2, 2, 4, 3, 32)
+// Compiled variants (MB, NB, WM, WN, NS, F).  WM = 1: every wave spans the
+// tile's rows; WM > 1: a grid of WM x WN wave tiles.
+#define W4A16_LDS_VARIANTS(X)                                                              \
+  X(4, 2, 1, 2, 3, 16) X(4, 2, 1, 4, 3, 16) X(4, 2, 1, 4, 4, 16) X(4, 4, 1, 4, 3, 16)       \
+  X(8, 1, 1, 4, 3, 16) X(8, 2, 1, 4, 2, 16) X(8, 2, 1, 4, 3, 16) X(8, 4, 1, 4, 2, 16)       \
+  X(8, 4, 1, 4, 3, 16) X(4, 1, 1, 8, 3, 16) X(4, 2, 1, 8, 3, 16) X(8, 1, 1, 8, 3, 16)       \
+  X(8, 2, 1, 8, 3, 16) X(1, 4, 1, 4, 4, 16) X(1, 8, 1, 4, 4, 16) X(1, 2, 1, 8, 4, 16)       \
+  X(1, 4, 1, 8, 4, 16) X(2, 4, 1, 4, 4, 16) X(2, 2, 1, 8, 4, 16) X(2, 4, 1, 8, 3, 16)       \
+  X(4, 1, 1, 8, 3, 32) X(2, 1, 1, 8, 3, 32) X(4, 1, 1, 4, 3, 32) X(2, 2, 1, 4, 3, 32)       \
+  X(4, 4, 2, 4, 3, 16) X(2, 4, 4, 2, 3, 16) X(4, 2, 2, 4, 3, 16) X(2, 2, 4, 2, 3, 16)       \
+  X(2, 2, 2, 4, 3, 16) X(2, 4, 2, 4, 3, 16) X(4, 4, 2, 2, 3, 16) X(2, 4, 2, 2, 3, 16)       \
+  X(1, 2, 4, 2, 3, 32) X(1, 4, 4, 2, 3, 32) X(2, 2, 2, 4, 3, 32)
 
-bool lds_is_compiled(int mb, int nb, int wn, int ns, int f) {
-#define W4A16_LMATCH(MB_, NB_, WN_, NS_, F_) \
-  if (mb == MB_ && nb == NB_ && wn == WN_ && ns == NS_ && f == F_) return true;
+bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f) {
+#define W4A16_LMATCH(MB_, NB_, WM_, WN_, NS_, F_) \
+  if (mb == MB_ && nb == NB_ && wm == WM_ && wn == WN_ && ns == NS_ && f == F_) return true;
   W4A16_LDS_VARIANTS(W4A16_LMATCH)
 #undef W4A16_LMATCH
   return false;
@@ -362,10 +383,10 @@ hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
                       Epilogue ep, void* workspace, hipStream_t stream) {
   const int f = p.tile == 3 ? 32 : 16;
-#define W4A16_LCASE(MB_, NB_, WN_, NS_, F_)                                                \
-  if (p.mb == MB_ && p.nb == NB_ && p.wk == WN_ && p.depth == NS_ && f == F_)              \
-    return launch_lds_one<MB_, NB_, WN_, NS_, F_>(p, A, Bp, S, C, M, K, N, gmagic, ep,     \
-                                                  workspace, stream);
+#define W4A16_LCASE(MB_, NB_, WM_, WN_, NS_, F_)                                             \
+  if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_ && f == F_) \
+    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, F_>(p, A, Bp, S, C, M, K, N, gmagic, ep,  \
+                                                       workspace, stream);
   W4A16_LDS_VARIANTS(W4A16_LCASE)
 #undef W4A16_LCASE
   return hipErrorInvalidValue;

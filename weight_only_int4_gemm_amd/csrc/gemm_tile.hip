@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
   const int n16_last = N / kBlockN - 1;
   const int n16_0 = tile_n * NB * WN + wave * NB;
   LaneBias<NB, 16, EPI> bias;
-  bias.load(ep, tile_n * TN, N);
+  bias.load(ep, tile_n * TN + wave * 16 * NB, N);
 
   // Direct load i of this wave fills stage pieces 64 * (wave + WN * i) + lane:
   // row r = 4 * (wave + WN * i) + lane / 16, slot lane % 16, which holds
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_tile_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  store_output_tile<MB, NB, WN, EPI>(acc, C, M, N, row0, tile_n * TN, split, splits, counters,
+  store_output_tile<MB, NB, WN, EPI>(acc, C, M, N, row0, tile_n * TN + wave * 16 * NB, split,
+                                     splits, counters,
                                 partials, reinterpret_cast<int*>(&As0[0]), ep, bias);
 }
 

@@ -15,11 +15,14 @@ namespace w4a16 {
 //         blocks)
 //  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
 //  nb     16-column blocks per wave
-//  wk     waves per workgroup.  Streaming kernel: they split the
-//         workgroup's K range (every wk-th 128-deep K block each) and their
-//         sums are added in wave order through LDS; the N tile is 16 * nb.
-//         Tile and LDS kernels: they split the N tile, which is
-//         16 * nb * wk.
+//  wk     waves per workgroup (LDS kernel: waves along N).  Streaming
+//         kernel: they split the workgroup's K range (every wk-th 128-deep
+//         K block each) and their sums are added in wave order through LDS;
+//         the N tile is 16 * nb.  Tile and LDS kernels: they split the N
+//         tile, which is 16 * nb * wk.
+//  wm     LDS kernel: waves along M (1 elsewhere); the M tile is
+//         16 * mb * wm (32 * ... with 32 x 32 blocks), the workgroup
+//         wm * wk waves
 //  splits K ranges per output tile, one workgroup each; their FP32
 //         partials go through the workspace and are added in split order
 //  depth  streaming kernel: K blocks each wave keeps in flight; tile
@@ -27,7 +30,7 @@ namespace w4a16 {
 //         flight + 1); LDS kernel: stages of activations, codes and scales
 //  bdepth tile kernel: K blocks of codes in flight (register slots)
 struct Plan {
-  int tile, mb, nb, wk, splits, depth, bdepth;
+  int tile, mb, nb, wk, splits, depth, bdepth, wm;
   int tm, tn;              // output tile of one workgroup
   int tiles_n, tiles_m;
   size_t workspace_bytes;  // 0 when splits == 1
@@ -44,7 +47,7 @@ struct Epilogue {
 Plan make_plan(int M, int K, int N, int group, int cus);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
-bool lds_is_compiled(int mb, int nb, int wn, int ns, int f);
+bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);

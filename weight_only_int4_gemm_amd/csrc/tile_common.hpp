@@ -46,25 +46,19 @@ __device__ __forceinline__ void stage_barrier() {
   keep_load_order();
 }
 
-// First output column of this lane in a workgroup tile starting at column
-// col0: each wave owns NB column blocks of F columns, lane l stores column
-// l % F of each (col + F * nb for block nb).
-template <int NB, int F>
-__device__ __forceinline__ int lane_out_col(int col0) {
-  return col0 + (int)(threadIdx.x >> 6) * F * NB + (int)(threadIdx.x & (F - 1));
-}
-
 // The bias of the columns this lane stores, loaded as raw FP16 at kernel
 // start (fused epilogue only) so that the load's latency hides behind the
 // main loop; it is converted where the output stage uses it.  The count-
 // based waits of the pipelines stay correct: this load is older than every
 // stage load, and loads complete in order.
+// `wcol0` is the first column of the wave's own tile; lane l stores column
+// l % F of each of its NB column blocks (wcol0 + F * nb + l % F).
 template <int NB, int F, bool EPI>
 struct LaneBias {
   _Float16 v[NB];
-  __device__ __forceinline__ void load(const Epilogue& ep, int col0, int N) {
+  __device__ __forceinline__ void load(const Epilogue& ep, int wcol0, int N) {
     if constexpr (EPI) {
-      const int c = lane_out_col<NB, F>(col0);
+      const int c = wcol0 + (int)(threadIdx.x & (F - 1));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         v[nb] = (ep.bias && c + F * nb < N) ? ep.bias[c + F * nb] : (_Float16)0.f;
@@ -76,9 +70,10 @@ struct LaneBias {
   }
 };
 
-// Write a workgroup's output tile.  acc[mb][nb] holds, in lane l, rows
-// 4*(l/16) .. +3 of column l % 16 of the 16x16 block (mb, nb) of this wave,
-// whose columns start at tile column wave * 16 * NB.
+// Write a workgroup's output tile.  Each of its WAVES waves owns a
+// 16*MB x 16*NB block of it starting at row wrow0, column wcol0; acc[mb][nb]
+// holds, in lane l, rows 4*(l/16) .. +3 of column l % 16 of the 16x16 block
+// (mb, nb) of that wave tile.
 //
 // With splits > 1: publish the partial tile with device-coherent stores,
 // wait for them, count the arrival; the last workgroup of the tile adds the
@@ -88,19 +83,17 @@ struct LaneBias {
 // that sums finds its own fragments at the same places.  `flag` is an int in
 // LDS no wave touches any more.  The epilogue is applied to the final sums
 // only.
-template <int MB, int NB, int WN, bool EPI>
+template <int MB, int NB, int WAVES, bool EPI>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
-                                                  int row0, int col0, int split, int splits,
+                                                  int wrow0, int wcol0, int split, int splits,
                                                   unsigned* __restrict__ counters,
                                                   float* __restrict__ partials, int* flag,
                                                   const Epilogue& ep,
                                                   const LaneBias<NB, 16, EPI>& bias) {
-  constexpr int TM = 16 * MB;
-  constexpr int TN = 16 * NB * WN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col_base = lane_out_col<NB, 16>(col0);
+  const int col_base = wcol0 + (lane & 15);
   auto write_c = [&]() {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -111,7 +104,7 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
         const float b = bias[nb];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int gr = row0 + mb * 16 + (lane >> 4) * 4 + i;
+          const int gr = wrow0 + mb * 16 + (lane >> 4) * 4 + i;
           const float x = acc[mb][nb][i];
           if (gr < M) C[(int64_t)gr * N + gc] = (_Float16)(EPI ? epilogue_apply(ep, x, b) : x);
         }
@@ -123,7 +116,7 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
   }
 
   const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-  constexpr int TE = TM * TN;
+  constexpr int TE = WAVES * MB * NB * 256;  // elements of the tile
   const float* tile_base = partials + (int64_t)tile * splits * TE;
   const int frag0 = wave * MB * NB * 64 + lane;
   {
@@ -161,22 +154,20 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
 
 // The same for 32 x 32 blocks (v_mfma_f32_32x32x16_f16): acc[mb][nb] holds,
 // in lane l, column l % 32 of the block and rows 8q + 4(l/32) + i in element
-// 4q + i (q, i = 0..3); the wave's columns start at tile column
-// wave * 32 * NB.  A partial is kept in fragment order (wave, row block,
-// column block, q, lane, four values).
-template <int MB, int NB, int WN, bool EPI>
+// 4q + i (q, i = 0..3) of the wave tile starting at (wrow0, wcol0).  A
+// partial is kept in fragment order (wave, row block, column block, q, lane,
+// four values).
+template <int MB, int NB, int WAVES, bool EPI>
 __device__ __forceinline__ void store_output_tile32(float16_t (&acc)[MB][NB],
                                                     _Float16* __restrict__ C, int M, int N,
-                                                    int row0, int col0, int split, int splits,
+                                                    int wrow0, int wcol0, int split, int splits,
                                                     unsigned* __restrict__ counters,
                                                     float* __restrict__ partials, int* flag,
                                                     const Epilogue& ep,
                                                     const LaneBias<NB, 32, EPI>& bias) {
-  constexpr int TM = 32 * MB;
-  constexpr int TN = 32 * NB * WN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col_base = lane_out_col<NB, 32>(col0);
+  const int col_base = wcol0 + (lane & 31);
   const int row_lane = 4 * (lane >> 5);
   auto write_c = [&]() {
 #pragma unroll
@@ -190,7 +181,7 @@ __device__ __forceinline__ void store_output_tile32(float16_t (&acc)[MB][NB],
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int gr = row0 + mb * 32 + 8 * q + row_lane + i;
+            const int gr = wrow0 + mb * 32 + 8 * q + row_lane + i;
             const float x = acc[mb][nb][4 * q + i];
             if (gr < M) C[(int64_t)gr * N + gc] = (_Float16)(EPI ? epilogue_apply(ep, x, b) : x);
           }
@@ -202,7 +193,7 @@ __device__ __forceinline__ void store_output_tile32(float16_t (&acc)[MB][NB],
   }
 
   const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-  constexpr int TE = TM * TN;
+  constexpr int TE = WAVES * MB * NB * 1024;  // elements of the tile
   const float* tile_base = partials + (int64_t)tile * splits * TE;
   const int frag0 = wave * MB * NB * 4 * 64 + lane;
   auto quad = [&](const float16_t& v, int q) {
