@@ -19,6 +19,9 @@ plain numpy, with no blocking, fusion or reordering beyond that description:
 
 * Same page, "End-to-end flow": the product goes straight on to a bias add
   or an activation (``gemm_fused``).
+* "Low-Precision Quantization Kernels in Production" (llms.blog), section 1
+  and the table of section 5 (AWQ checkpoints), introduction and section 4
+  (BF16): zero points and BF16 (``dequant_awq``, ``gemm_awq``).
 
 Readings where the pages leave a step open (zero point 8, LSB-first nibble
 order along K, scale layout ``[K/group][N]``, single RNE rounding of the
@@ -43,4 +46,10 @@ from .w4a16_ref import (  # noqa: F401
     activation,
     epilogue,
     gemm_fused,
+    DTYPE_F16,
+    DTYPE_BF16,
+    bf16_to_f64,
+    f64_to_bf16,
+    dequant_awq,
+    gemm_awq,
 )

@@ -266,3 +266,111 @@ def gemm_fused(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int, bias=No
     Z64 = epilogue(C64, bias, ACT_NONE)
     Y64 = activation(Z64, act)
     return Y64.astype(np.float16), Y64, Z64
+
+
+# ---------------------------------------------------------------------------
+# AWQ-style zero points and BF16.  "Low-Precision Quantization Kernels in
+# Production" (llms.blog), section 1 on production engines and the table of
+# section 5: the same kernel serves GPTQ and AWQ checkpoints; its
+# introduction and section 4: FP16 and BF16 activations.
+#
+# Readings (the pages define neither format):
+# 10. An AWQ-style code carries a zero point per group and output column,
+#     w = (q - z) * s, with z an unsigned byte (AWQ's are 0..15) stored
+#     uint8 [K/group][N] like the scales.  Without zero points z = 8.
+# 11. In the BF16 variant A, the scales and C are BF16; the weight is the
+#     exact (q - z) * s rounded once to BF16 (round to nearest, ties to
+#     even), the sum is exact (float64 here) and rounded once to BF16.
+# BF16 values are carried as their raw 16-bit patterns (uint16): numpy has
+# no BF16 type.
+# ---------------------------------------------------------------------------
+
+DTYPE_F16, DTYPE_BF16 = 0, 1
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """BF16 bit patterns (uint16) -> their values as float64 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round float64 values to BF16, to nearest with ties to even; returns the
+    bit patterns (uint16).  Finite inputs only; overflow gives infinity.
+
+    Rounding is done on the exact value, not through float32: BF16 keeps 8
+    significant bits, so x = m * 2^e with the integer m scaled to 2^7..2^8,
+    and the rest of the significand decides the rounding."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.uint16)
+    sign = np.signbit(x)
+    a = np.abs(x)
+    nz = a > 0
+    # exponent of the leading bit; BF16 normals start at 2^-126, below that
+    # the quantum stays 2^-133 (subnormals)
+    e = np.floor(np.log2(np.where(nz, a, 1.0))).astype(np.int64)
+    # guard against log2 rounding at exact powers of two
+    e = np.where(np.ldexp(1.0, e) > a, e - 1, e)
+    e = np.where(np.ldexp(1.0, e + 1) <= a, e + 1, e)
+    e = np.maximum(e, -126)
+    q = np.ldexp(a, 7 - e)                    # significand in units of the quantum
+    fl = np.floor(q)
+    rem = q - fl                              # exact: q has at most 53 bits
+    up = (rem > 0.5) | ((rem == 0.5) & (np.fmod(fl, 2) == 1))
+    m = (fl + up).astype(np.int64)            # 0 .. 256
+    # m == 256 carries into the next binade
+    carry = m == 256
+    m = np.where(carry, 128, m)
+    e = np.where(carry, e + 1, e)
+    normal = m >= 128
+    exp_field = np.where(normal, e + 127, 0)
+    mant = np.where(normal, m - 128, m)       # subnormal: m < 128 at e = -126
+    inf = exp_field >= 255
+    bits = np.where(inf, 0x7F80, (exp_field << 7) | mant)
+    bits = np.where(nz, bits, 0)
+    out[...] = bits.astype(np.uint16)
+    out |= (sign.astype(np.uint16) << np.uint16(15))
+    return out
+
+
+def dequant_awq(Bq: np.ndarray, S: np.ndarray, Z, group: int, dtype: int) -> np.ndarray:
+    """Weights of the AWQ-style formats (readings 10, 11).
+
+    ``S`` is float16 [K/group][N] for DTYPE_F16 and BF16 bits (uint16) for
+    DTYPE_BF16; ``Z`` uint8 [K/group][N] or None (z = 8).  Returns float16
+    W[K][N] (DTYPE_F16) or BF16 bits uint16 W[K][N] (DTYPE_BF16), each the
+    exact (q - z) * s rounded once."""
+    q = unpack_codes(Bq).astype(np.float64)
+    K = q.shape[0]
+    if Z is None:
+        z = np.full(q.shape, float(ZERO_POINT))
+    else:
+        z = np.repeat(np.asarray(Z, dtype=np.uint8).astype(np.float64), group, axis=0)[:K]
+    if dtype == DTYPE_F16:
+        s = np.repeat(np.asarray(S, dtype=np.float16).astype(np.float64), group, axis=0)[:K]
+        # (q - z) has at most 9 bits and s 11: the float64 product is exact
+        return ((q - z) * s).astype(np.float16)
+    if dtype == DTYPE_BF16:
+        s = np.repeat(bf16_to_f64(S), group, axis=0)[:K]
+        return f64_to_bf16((q - z) * s)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def gemm_awq(A, Bq: np.ndarray, S, Z, group: int, dtype: int, cols=None):
+    """``(C, C64)`` of the AWQ-style formats: C64 = the float64 sum of
+    A . W (W from ``dequant_awq``), C its single rounding to ``dtype``
+    (float16, or BF16 bits).  ``A`` is float16 [M][K] or BF16 bits.  With
+    ``cols``, only those output columns (sampled checks of large shapes)."""
+    if cols is not None:
+        cols = np.asarray(cols, dtype=np.int64)
+        Bq = np.ascontiguousarray(Bq[:, cols])
+        S = np.ascontiguousarray(np.asarray(S)[:, cols])
+        Z = None if Z is None else np.ascontiguousarray(np.asarray(Z)[:, cols])
+    W = dequant_awq(Bq, S, Z, group, dtype)
+    if dtype == DTYPE_F16:
+        A64 = np.asarray(A, dtype=np.float16).astype(np.float64)
+        C64 = A64 @ W.astype(np.float64)
+        return C64.astype(np.float16), C64
+    A64 = bf16_to_f64(A)
+    C64 = A64 @ bf16_to_f64(W)
+    return f64_to_bf16(C64), C64

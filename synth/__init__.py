@@ -18,6 +18,12 @@ Recipe (the same for every shape):
   shape ``[K/group][N]`` row-major.
 * Bias (fused output stage only, its own generator): ``standard_normal``
   float32 scaled by ``bias_std``, rounded to float16, shape ``[N]``.
+* Zero-point and BF16 formats (``make_inputs_awq``): the same draws in the
+  same order, then zero points ``integers(0, 16)`` as uint8
+  ``[K/group][N]``.  For BF16 the float32 draws are cut to their upper 16
+  bits (truncation, not rounding: a choice of the generator, so that no
+  rounding rule is shared with the code under test); values are carried as
+  uint16 bit patterns.
 
 The value distributions are the ones the workload description gives: a
 Gaussian activation, uniform codes, and small positive scales, one per group
@@ -63,3 +69,24 @@ def make_bias(N: int, seed: int = 0, bias_std: float = 2.0):
     the activation sees both signs."""
     rng = np.random.default_rng(seed)
     return (bias_std * rng.standard_normal(N, dtype=np.float32)).astype(np.float16)
+
+
+def make_inputs_awq(M: int, K: int, N: int, group: int = 128, seed: int = 0,
+                    bf16: bool = False):
+    """Return ``(A, Bq, S, Z)``: as ``make_inputs`` plus uint8 zero points
+    ``Z[K/group][N]`` uniform on 0..15.  With ``bf16`` A and S are BF16 bit
+    patterns (uint16): the float32 draws with their low 16 bits dropped."""
+    if K % 8 or group <= 0 or K % group:
+        raise ValueError(f"bad shape K={K} group={group}")
+    rng = np.random.default_rng(seed)
+    A32 = rng.standard_normal((M, K), dtype=np.float32)
+    Bq = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+    S64 = rng.uniform(SCALE_LO, SCALE_HI, size=(K // group, N))
+    Z = rng.integers(0, 16, size=(K // group, N), dtype=np.uint8)
+    if bf16:
+        A = (A32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        S = (S64.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    else:
+        A = A32.astype(np.float16)
+        S = S64.astype(np.float16)
+    return A, Bq, S, Z

@@ -461,3 +461,188 @@ def test_fused_brute_force(act):
             y = max(z, 0.0) if act == 1 else z / (1.0 + math.exp(-z))
             assert Y64[m, n] == pytest.approx(y, rel=1e-12, abs=1e-12)
             assert float(C16[m, n]) == _fp16_struct(y)
+
+
+# ---------------------------------------------------------------------------
+# Zero points and BF16
+# ---------------------------------------------------------------------------
+
+def _bf16_exact(fr: Fraction) -> float:
+    """Round an exact rational to BF16 (8 significant bits, exponent from
+    -126, subnormal quantum 2^-133), ties to even, by integer arithmetic."""
+    if fr == 0:
+        return 0.0
+    sign = -1.0 if fr < 0 else 1.0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 7)
+    units = a / quantum
+    fl = units.numerator // units.denominator
+    rem = units - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    value = fl * quantum
+    if value >= Fraction(2) ** 128:          # past the largest finite BF16
+        return sign * math.inf
+    return sign * float(value)
+
+
+def _bits_value(bits):
+    return oracle.bf16_to_f64(np.array([bits], dtype=np.uint16))[0]
+
+
+def test_bf16_rounding_matches_torch():
+    """float32 -> BF16 against torch's conversion (round to nearest even), on
+    random values and on values built to sit exactly on, just above and just
+    below a rounding midpoint, both signs, normals and subnormals."""
+    import torch
+    rng = np.random.default_rng(3)
+    hi = rng.integers(0, 2**16, size=20000, dtype=np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]                 # finite only
+    lows = np.array([0x0000, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    bits = ((hi[:, None] << np.uint32(16)) | lows[None, :]).ravel()
+    rnd = rng.integers(0, 2**32, size=20000, dtype=np.uint32)
+    rnd = rnd[((rnd >> 23) & 0xFF) != 0xFF]
+    x32 = np.concatenate([bits, rnd]).view(np.float32)
+    x32 = x32[np.isfinite(x32) & (np.abs(x32) < 3.3e38)]   # no overflow to inf
+    ours = oracle.f64_to_bf16(x32.astype(np.float64))
+    ref = torch.from_numpy(x32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_rounding_exact_rationals():
+    """Worked values: ties go to the even neighbour, just-above ties round up,
+    subnormals keep the 2^-133 quantum, and float64-only values (between
+    float32 neighbours) still round on their exact value."""
+    cases = [Fraction(1) + Fraction(1, 2**8), Fraction(1) + Fraction(3, 2**8),
+             Fraction(1) + Fraction(1, 2**8) + Fraction(1, 2**40),
+             Fraction(-255, 2**7) - Fraction(1, 2**9), Fraction(3, 2**134), Fraction(1, 2**134),
+             Fraction(129, 2**133), Fraction(2**8 - 1, 2**8) + Fraction(1, 2**9),
+             Fraction(12345, 1000), Fraction(-7, 3)]
+    for fr in cases:
+        got = _bits_value(oracle.f64_to_bf16(np.array([float(fr)]))[0])
+        if float(fr) != fr:      # not exact in float64: compare to the float64 value's rounding
+            fr = Fraction(float(fr))
+        assert got == _bf16_exact(fr), fr
+
+
+def _scale_sets():
+    """A few hundred FP16 and BF16 scales of both signs across the range."""
+    rng = np.random.default_rng(11)
+    f16 = rng.integers(0, 2**16, size=400, dtype=np.uint16).view(np.float16)
+    f16 = f16[np.isfinite(f16) & (f16 != 0)]
+    f16 = np.concatenate([f16, np.array([1.0, -1.0, 2.0**-24, 65504.0, 0.0123], np.float16)])
+    b16 = rng.integers(0, 2**16, size=400, dtype=np.uint16)
+    b16 = b16[((b16 >> 7) & 0xFF) != 0xFF]
+    b16 = b16[(b16 & 0x7FFF) != 0]
+    b16 = np.concatenate([b16, np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F], np.uint16)])
+    return f16, b16
+
+
+def _codes_zeros_grid(ns):
+    """Bq, Z for K = 128, N = ns * 256: column block c holds all 16 codes of
+    each of the 16 zero points (q varies along K, z along N)."""
+    q = np.tile(np.arange(16), 8)[:, None] * np.ones((1, 256 * ns), dtype=np.int64)
+    z = np.tile(np.repeat(np.arange(16), 16), ns)[None, :].astype(np.uint8)
+    return oracle.pack_codes(q), z
+
+
+def test_dequant_awq_fp16_exhaustive_codes_and_zeros():
+    f16, _ = _scale_sets()
+    Bq, Z = _codes_zeros_grid(1)
+    for s in f16:
+        S = np.full((1, 256), s, dtype=np.float16)
+        W = oracle.dequant_awq(Bq, S, Z, 128, oracle.DTYPE_F16)
+        for k in range(16):
+            for zz in range(16):
+                n = zz * 16 + (k % 16)
+                q = k % 16
+                want = _fp16_exact((q - zz) * Fraction(float(s)))
+                got = float(W[k, n])
+                assert got == want or (got == 0 and want == 0), (s, q, zz)
+
+
+def test_dequant_awq_bf16_exhaustive_codes_and_zeros():
+    _, b16 = _scale_sets()
+    Bq, Z = _codes_zeros_grid(1)
+    for sb in b16:
+        S = np.full((1, 256), sb, dtype=np.uint16)
+        W = oracle.dequant_awq(Bq, S, Z, 128, oracle.DTYPE_BF16)
+        sv = Fraction(float(_bits_value(sb)))
+        vals = oracle.bf16_to_f64(W)
+        for q in range(16):
+            for zz in range(16):
+                n = zz * 16 + q
+                assert vals[q, n] == _bf16_exact((q - zz) * sv), (hex(sb), q, zz)
+
+
+def test_dequant_awq_zero_point_eight_is_the_symmetric_format():
+    from synth import make_inputs_awq
+    A, Bq, S, Z = make_inputs_awq(1, 512, 48, 128, seed=4)
+    Z8 = np.full_like(Z, 8)
+    W0 = oracle.dequant(Bq, S, 128)
+    assert np.array_equal(oracle.dequant_awq(Bq, S, None, 128, 0).view(np.uint16), W0.view(np.uint16))
+    assert np.array_equal(oracle.dequant_awq(Bq, S, Z8, 128, 0).view(np.uint16), W0.view(np.uint16))
+    _, _, Sb, _ = make_inputs_awq(1, 512, 48, 128, seed=4, bf16=True)
+    assert np.array_equal(oracle.dequant_awq(Bq, Sb, None, 128, 1),
+                          oracle.dequant_awq(Bq, Sb, Z8, 128, 1))
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("M,K,N,group,seed", [(2, 256, 16, 128, 1), (3, 256, 24, 256, 2)])
+def test_gemm_awq_brute_force(dtype, M, K, N, group, seed):
+    """Exact rational sums from first principles (codes read bit by bit,
+    zero points and scales by index), rounded once by integer arithmetic."""
+    from synth import make_inputs_awq
+    A, Bq, S, Z = make_inputs_awq(M, K, N, group, seed=seed, bf16=dtype == 1)
+    C, C64 = oracle.gemm_awq(A, Bq, S, Z, group, dtype)
+    val = (lambda b: Fraction(float(_bits_value(b)))) if dtype else (lambda h: Fraction(float(h)))
+    rnd = _bf16_exact if dtype else _fp16_exact
+    for m in range(M):
+        for n in range(N):
+            total = Fraction(0)
+            for k in range(K):
+                q = (int(Bq[k // 8, n]) >> (4 * (k % 8))) & 0xF
+                w = rnd((q - int(Z[k // group, n])) * val(S[k // group, n]))
+                total += val(A[m, k]) * Fraction(w)
+            got = float(oracle.bf16_to_f64(np.array([C[m, n]]))[0]) if dtype else float(C[m, n])
+            assert got == rnd(total), (m, n)
+            assert abs(C64[m, n] - float(total)) <= 1e-12 * max(1.0, abs(float(total)))
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_gemm_awq_codes_at_their_zero_points_give_zero(dtype):
+    from synth import make_inputs_awq
+    A, _, S, Z = make_inputs_awq(5, 256, 32, 128, seed=9, bf16=dtype == 1)
+    q = np.repeat(Z, 128, axis=0)          # every code equals its zero point
+    Bq = oracle.pack_codes(q)
+    C, C64 = oracle.gemm_awq(A, Bq, S, Z, 128, dtype)
+    assert not np.any(C64) and not np.any(oracle.bf16_to_f64(C) if dtype else C.astype(float))
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_gemm_awq_one_hot_rows_select_weight_rows(dtype):
+    from synth import make_inputs_awq
+    _, Bq, S, Z = make_inputs_awq(1, 384, 40, 128, seed=12, bf16=dtype == 1)
+    W = oracle.dequant_awq(Bq, S, Z, 128, dtype)
+    ks = [0, 7, 200, 383]
+    one = 0x3F80 if dtype else np.float16(1.0).view(np.uint16)
+    A = np.zeros((len(ks), 384), dtype=np.uint16)
+    A[np.arange(len(ks)), ks] = one
+    if not dtype:
+        A = A.view(np.float16)
+    C, _ = oracle.gemm_awq(A, Bq, S, Z, 128, dtype)
+    for m, k in enumerate(ks):
+        assert np.array_equal(C[m].view(np.uint16), W[k].view(np.uint16))
+
+
+def test_gemm_awq_sampled_columns_match_full():
+    from synth import make_inputs_awq
+    A, Bq, S, Z = make_inputs_awq(4, 512, 64, 128, seed=13, bf16=True)
+    C, C64 = oracle.gemm_awq(A, Bq, S, Z, 128, 1)
+    cols = [0, 5, 33, 63]
+    Cs, C64s = oracle.gemm_awq(A, Bq, S, Z, 128, 1, cols=cols)
+    assert np.array_equal(Cs, C[:, cols]) and np.array_equal(C64s, C64[:, cols])
