@@ -100,6 +100,10 @@ def parse():
                     help="time the fused output stage (bias + SiLU inside the GEMM) "
                          "against the plain GEMM and against the plain GEMM followed by "
                          "torch's bias add and SiLU, write a markdown table to OUT and exit")
+    ap.add_argument("--formats-report", metavar="OUT",
+                    help="time the weight formats (FP16, FP16 with zero points, BF16, BF16 "
+                         "with zero points) side by side, write a markdown table to OUT "
+                         "and exit")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script into a traffic file and exit")
@@ -514,6 +518,103 @@ def epilogue_report(out_path: str, repeats: int = 7, launches: int = 50) -> None
         f.write("\n".join(lines) + "\n")
 
 
+# Shapes for --formats-report: (label, K, N, batch sizes).
+FORMAT_SHAPES = [
+    ("Llama-2-7B qkv", 4096, 12288, [1, 16, 128]),
+    ("Llama-2-7B gate/up", 4096, 22016, [1, 16, 128]),
+    ("Llama-2-7B down", 11008, 4096, [1, 16, 128]),
+    ("prefill 8192x28672", 8192, 28672, [1024]),
+]
+FORMATS = [("FP16", 0, False), ("FP16 + zero points", 0, True), ("BF16", 1, False),
+           ("BF16 + zero points", 1, True)]
+
+
+def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
+    """Per shape, the four weight formats through w4a16_gemm_awq, timed in
+    turn (interleaved rounds, median), weight copies rotating beyond 512 MB."""
+    import numpy as np
+    import torch
+
+    import weight_only_int4_gemm_amd as w4
+    from weight_only_int4_gemm_amd import roofline
+    from synth import make_inputs_awq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = w4.load()
+    sh = torch.cuda.current_stream().cuda_stream
+    _warm_clocks()
+    rows = []
+    for label, K, N, batches in FORMAT_SHAPES:
+        _, Bq, S16, Z = make_inputs_awq(1, K, N, GROUP, seed=0)
+        _, _, Sb, _ = make_inputs_awq(1, K, N, GROUP, seed=0, bf16=True)
+        Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
+        first = w4.alloc_packed(K, N)
+        w4.w4a16_repack(Bq_d, first, K, N)
+        del Bq_d, Bq
+        ncopy = max(1, -(-ROTATE_BYTES // (K * N // 2)))
+        copies = [first] + [first.clone() for _ in range(ncopy - 1)]
+        scales = {0: torch.from_numpy(S16.view(np.int16)).to(dev),
+                  1: torch.from_numpy(Sb.view(np.int16)).to(dev)}
+        zeros = torch.from_numpy(Z).to(dev)
+        for M in batches:
+            A16, _, _, _ = make_inputs_awq(M, K, 8, GROUP, seed=M)
+            Ab, _, _, _ = make_inputs_awq(M, K, 8, GROUP, seed=M, bf16=True)
+            acts = {0: torch.from_numpy(A16.view(np.int16)).to(dev),
+                    1: torch.from_numpy(Ab.view(np.int16)).to(dev)}
+            C_d = torch.empty((M, N), dtype=torch.int16, device=dev)
+            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, GROUP), 256),
+                             dtype=torch.uint8, device=dev)
+
+            def form(dtype, zp):
+                def call(c):
+                    args = (acts[dtype].data_ptr(), c.data_ptr(), scales[dtype].data_ptr(),
+                            zeros.data_ptr() if zp else None, C_d.data_ptr(), M, K, N, GROUP,
+                            dtype, ws.data_ptr(), sh)
+
+                    def run():
+                        rc = lib.w4a16_gemm_awq(*args)
+                        if rc != 0:
+                            raise RuntimeError(f"w4a16_gemm_awq: {w4.w4a16_status_string(rc)}")
+                    return run
+                return [call(c) for c in copies]
+
+            forms = [form(dt, zp) for _, dt, zp in FORMATS]
+            times = [[] for _ in forms]
+            for _ in range(repeats):
+                for f, calls in enumerate(forms):
+                    times[f].append(_time_calls(calls, launches, 1))
+            med = [float(np.median(t)) for t in times]
+            flops = roofline.flops(M, K, N)
+            rows.append(dict(shape=label, M=M, us=[t * 1e6 for t in med],
+                             tflops=[flops / t / 1e12 for t in med],
+                             plan=w4.w4a16_describe(M, K, N, GROUP).split(" workspace")[0]))
+            print(json.dumps(rows[-1]), flush=True)
+            del acts, C_d, ws
+        del copies, first, scales, zeros
+        torch.cuda.empty_cache()
+    lines = [
+        "# Weight formats on one MI355X: FP16, zero points, BF16",
+        "",
+        "Command (repository root, GPU box): `python3 bench.py --formats-report " +
+        os.path.relpath(out_path, ROOT) + "`",
+        "",
+        f"Kernel source hash: `{kernel_source_hash()}`. Each format through `w4a16_gemm_awq` "
+        f"(FP16 without zero points is the plain kernel), hipEvents around {launches} "
+        f"back-to-back calls cycling over weight copies beyond 512 MB; the four formats are "
+        f"timed in turn, {repeats} rounds, median per format. Zero points: uint8 per group "
+        "and column (one more byte per 64 code bytes at group 128).",
+        "",
+        "| shape | M | " + " | ".join(f"{n} us" for n, _, _ in FORMATS) + " | plan |",
+        "|---|---|" + "---|" * len(FORMATS) + "---|",
+    ]
+    for r in rows:
+        lines.append(f"| {r['shape']} | {r['M']} | " +
+                     " | ".join(f"{u:.1f}" for u in r["us"]) + f" | `{r['plan']}` |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -524,6 +625,9 @@ def main():
         return
     if args.epilogue_report:
         epilogue_report(args.epilogue_report)
+        return
+    if args.formats_report:
+        formats_report(args.formats_report)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -54,7 +54,14 @@ enum w4a16_status {
     W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed       */
     W4A16_ERR_LAUNCH = -6,    /* the kernel launch failed                    */
     W4A16_ERR_DEVICE = -7,    /* no usable current HIP device                */
-    W4A16_ERR_EPILOGUE = -8   /* unknown activation for w4a16_gemm_fused     */
+    W4A16_ERR_EPILOGUE = -8,  /* unknown activation for w4a16_gemm_fused     */
+    W4A16_ERR_DTYPE = -9      /* unknown dtype for the *_awq entry points    */
+};
+
+/* 16-bit types of activations, scales and output (the *_awq entry points). */
+enum w4a16_dtype {
+    W4A16_DTYPE_F16 = 0,      /* IEEE binary16                               */
+    W4A16_DTYPE_BF16 = 1      /* bfloat16: 8 exponent bits, 7 mantissa bits  */
 };
 
 /* Activations the fused epilogue applies (w4a16_gemm_fused). */
@@ -178,6 +185,44 @@ int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked,
                      const uint16_t* scales, const uint16_t* bias, int activation,
                      uint16_t* C, int M, int K, int N, int group, void* workspace,
                      void* stream);
+
+/*
+ * w4a16_gemm_awq -- C = A . W with AWQ-style zero points and/or BF16.
+ *
+ * The serving stacks the pages describe run AWQ checkpoints through the same
+ * kernel ("Low-Precision Quantization Kernels in Production", section 1 on
+ * production engines and the comparison table of section 5), and models
+ * kept in BF16 (same page, introduction; section 4's activation formats).
+ * Here:
+ *   w[k][n] = rnd((q[k][n] - z[k/group][n]) * s[k/group][n])
+ * with rnd the rounding (to nearest even) to the 16-bit type `dtype`, and
+ * z = 8 when `zeros` is NULL.  A, scales and C hold `dtype` values; the sum
+ * is FP32 and rounded once to `dtype`.
+ *
+ * zeros   (device, read) uint8 [K/group][N] row-major, the zero point of
+ *         each group and column (AWQ uses 0..15; any byte value gives the
+ *         formula above exactly), or NULL.  16-byte aligned.
+ * dtype   W4A16_DTYPE_F16 or W4A16_DTYPE_BF16; anything else returns
+ *         W4A16_ERR_DTYPE.
+ * The other arguments, layouts, alignment, workspace and errors are those
+ * of w4a16_gemm (same plan and workspace size).  With dtype F16 and zeros
+ * NULL this is w4a16_gemm.  The BF16 and zero-point kernels are compiled
+ * for the variants the library's plans choose; a plan forced outside them
+ * (a tuning override) returns W4A16_ERR_LAUNCH.  No fused epilogue here.
+ */
+int w4a16_gemm_awq(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                   const uint8_t* zeros, uint16_t* C, int M, int K, int N, int group,
+                   int dtype, void* workspace, void* stream);
+
+/*
+ * w4a16_dequant_awq_debug -- the weights of w4a16_gemm_awq, written out:
+ * W [K][N] row-major `dtype` values, produced by the GEMM's own unpack
+ * routine for that format.  Arguments as in w4a16_dequant_debug plus
+ * `zeros` (NULL: z = 8) and `dtype`.
+ */
+int w4a16_dequant_awq_debug(const uint32_t* Bpacked, const uint16_t* scales,
+                            const uint8_t* zeros, uint16_t* W, int K, int N, int group,
+                            int dtype, void* stream);
 
 /*
  * w4a16_dequant_debug -- W = dequant(Bpacked, scales), written out.

@@ -348,8 +348,10 @@ def dequant_awq(Bq: np.ndarray, S: np.ndarray, Z, group: int, dtype: int) -> np.
         z = np.repeat(np.asarray(Z, dtype=np.uint8).astype(np.float64), group, axis=0)[:K]
     if dtype == DTYPE_F16:
         s = np.repeat(np.asarray(S, dtype=np.float16).astype(np.float64), group, axis=0)[:K]
-        # (q - z) has at most 9 bits and s 11: the float64 product is exact
-        return ((q - z) * s).astype(np.float16)
+        # (q - z) has at most 9 bits and s 11: the float64 product is exact;
+        # values past the FP16 range round to infinity
+        with np.errstate(over="ignore"):
+            return ((q - z) * s).astype(np.float16)
     if dtype == DTYPE_BF16:
         s = np.repeat(bf16_to_f64(S), group, axis=0)[:K]
         return f64_to_bf16((q - z) * s)

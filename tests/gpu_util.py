@@ -20,6 +20,8 @@ def dev(x: np.ndarray):
     import torch
     if x.dtype == np.uint32:
         x = x.view(np.int32)
+    if x.dtype == np.uint16:          # BF16 bit patterns travel as int16
+        x = x.view(np.int16)
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
@@ -69,3 +71,25 @@ def run_gemm_fused(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, group: int, bia
     w4.w4a16_gemm_fused(A_d, Bp, S_d, b_d, act, C_d, M, K, N, group, ws)
     torch.cuda.synchronize()
     return host_f16(C_d)
+
+
+def host_u16(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_gemm_awq(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, Z, group: int, dtype: int,
+                 workspace=None, Bp=None):
+    """C as uint16 bits (BF16) or float16 (FP16) from w4a16_gemm_awq."""
+    import torch
+    M, K = A.shape
+    N = Bq.shape[1]
+    if Bp is None:
+        Bp = repack_on_device(dev(Bq), K, N)
+    A_d, S_d = dev(A), dev(S)
+    Z_d = None if Z is None else torch.from_numpy(np.ascontiguousarray(Z)).cuda()
+    C_d = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    ws = workspace if workspace is not None else w4.alloc_workspace(M, K, N, group)
+    w4.w4a16_gemm_awq(A_d, Bp, S_d, Z_d, C_d, M, K, N, group, dtype, ws)
+    torch.cuda.synchronize()
+    C = host_u16(C_d)
+    return C if dtype else C.view(np.float16)

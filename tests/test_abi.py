@@ -21,6 +21,7 @@ HEADER = os.path.join(ROOT, "include", "w4a16.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN = 0, -1, -2, -3, -4
 ERR_EPILOGUE = -8
+ERR_DTYPE = -9
 
 # Fake, 16-byte aligned addresses: the checks below return before any of
 # them is dereferenced or handed to the runtime.
@@ -120,6 +121,30 @@ def test_gemm_fused_rejects_bad_arguments(lib):
     # constants of the binding and the header agree
     text = open(HEADER).read()
     for name in ("W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU"):
+        value = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
+        assert getattr(w4, name) == value, name
+
+
+def test_awq_entry_points_reject_bad_arguments(lib):
+    g, d = lib.w4a16_gemm_awq, lib.w4a16_dequant_awq_debug
+    P_Z = 0x70000000
+    assert w4.w4a16_status_string(ERR_DTYPE) == "W4A16_ERR_DTYPE"
+    for dt in (-1, 2, 7):
+        assert g(P_A, P_B, P_S, P_Z, P_C, 4, 256, 64, 128, dt, None, None) == ERR_DTYPE
+        assert d(P_B, P_S, P_Z, P_W, 256, 64, 128, dt, None) == ERR_DTYPE
+    for dt in (0, 1):
+        assert g(P_A, P_B, P_S, P_Z, P_C, 4, 100, 64, 128, dt, None, None) == ERR_SHAPE
+        assert g(P_A, P_B, P_S, P_Z, P_C, 4, 256, 64, 96, dt, None, None) == ERR_GROUP
+        assert g(None, P_B, P_S, P_Z, P_C, 4, 256, 64, 128, dt, None, None) == ERR_NULL
+        assert g(P_A, P_B, P_S, P_Z + 4, P_C, 4, 256, 64, 128, dt, None, None) == ERR_ALIGN
+        # C overlapping the zero points
+        assert g(P_A, P_B, P_S, P_C + 256, P_C, 4, 256, 64, 128, dt, None, None) == ERR_SHAPE
+        assert g(None, None, None, None, None, 0, 256, 64, 128, dt, None, None) == OK
+        assert d(None, P_S, P_Z, P_W, 256, 64, 128, dt, None) == ERR_NULL
+        assert d(P_B, P_S, P_Z + 8, P_W, 256, 64, 128, dt, None) == ERR_ALIGN
+        assert d(P_B, P_S, P_Z, P_W, 256, 64, 96, dt, None) == ERR_GROUP
+    text = open(HEADER).read()
+    for name in ("W4A16_DTYPE_F16", "W4A16_DTYPE_BF16"):
         value = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
         assert getattr(w4, name) == value, name
 

@@ -63,3 +63,18 @@ def assert_epilogue_close(C, Z_ref, Y_ref, what=""):
     bound = epilogue_bound(Z_ref, Y_ref)
     assert err <= bound, f"{what}: max|C - act(Z_ref)| = {err:.4g} > bound {bound:.4g}"
     return err, bound
+
+
+def ulp_bf16(x: float) -> float:
+    """Spacing of BF16 values at magnitude ``x`` (normal range)."""
+    x = abs(float(x))
+    if x == 0:
+        return 2.0 ** -133
+    e = int(np.floor(np.log2(x)))
+    return 2.0 ** (max(e, -126) - 7)
+
+
+def bf16_bound(C_ref) -> float:
+    """The GEMM bound with a BF16 output: 5e-3 max|C_ref| + one BF16 ulp."""
+    m = float(np.max(np.abs(np.asarray(C_ref, dtype=np.float64)))) if np.size(C_ref) else 0.0
+    return REL_TOL * m + ulp_bf16(m)

@@ -9,6 +9,10 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
     w4a16_gemm_fused(A, Bpacked, scales, bias, activation, C, M, K, N, group,
                      workspace, stream=None)
     w4a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
+    w4a16_gemm_awq(A, Bpacked, scales, zeros, C, M, K, N, group, dtype,
+                   workspace, stream=None)
+    w4a16_dequant_awq_debug(Bpacked, scales, zeros, W, K, N, group, dtype,
+                            stream=None)
     w4a16_workspace_bytes(M, K, N, group)
     w4a16_packed_bytes(K, N)
     w4a16_layout_version()
@@ -26,6 +30,7 @@ __all__ = [
     "W4A16Error", "LibraryNotBuilt", "library_path", "load",
     "w4a16_repack", "w4a16_gemm", "w4a16_gemm_fused", "w4a16_dequant_debug",
     "W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU",
+    "w4a16_gemm_awq", "w4a16_dequant_awq_debug", "W4A16_DTYPE_F16", "W4A16_DTYPE_BF16",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
     "w4a16_status_string", "w4a16_describe", "EXPORTED_SYMBOLS",
 ]
@@ -38,11 +43,13 @@ W4A16_OK = 0
 W4A16_ACT_NONE = 0
 W4A16_ACT_RELU = 1
 W4A16_ACT_SILU = 2
+W4A16_DTYPE_F16 = 0
+W4A16_DTYPE_BF16 = 1
 
 EXPORTED_SYMBOLS = (
     "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_workspace_bytes", "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
-    "w4a16_describe", "w4a16_gemm_fused",
+    "w4a16_describe", "w4a16_gemm_fused", "w4a16_gemm_awq", "w4a16_dequant_awq_debug",
 )
 
 
@@ -89,6 +96,10 @@ def load():
     lib.w4a16_gemm.restype = i
     lib.w4a16_gemm_fused.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, vp, vp]
     lib.w4a16_gemm_fused.restype = i
+    lib.w4a16_gemm_awq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp]
+    lib.w4a16_gemm_awq.restype = i
+    lib.w4a16_dequant_awq_debug.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    lib.w4a16_dequant_awq_debug.restype = i
     lib.w4a16_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.w4a16_dequant_debug.restype = i
     lib.w4a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
@@ -193,6 +204,43 @@ def w4a16_gemm_fused(A, Bpacked, scales, bias, activation: int, C, M: int, K: in
            load().w4a16_gemm_fused(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(bias),
                                    int(activation), _ptr(C), int(M), int(K), int(N),
                                    int(group), _ptr(workspace), _stream(stream)))
+
+
+def _expect16(t, what):
+    """A 16-bit tensor: float16, or BF16 passed as bfloat16 / int16 bits."""
+    import torch
+    if t is None or isinstance(t, int):
+        return
+    if t.dtype not in (torch.float16, torch.bfloat16, torch.int16):
+        raise TypeError(f"{what}: expected a 16-bit tensor, got {t.dtype}")
+    _expect(t, t.dtype, what)
+
+
+def w4a16_gemm_awq(A, Bpacked, scales, zeros, C, M: int, K: int, N: int, group: int,
+                   dtype: int, workspace=None, stream=None) -> None:
+    import torch
+    _expect16(A, "A")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect16(scales, "scales")
+    _expect(zeros, torch.uint8, "zeros")
+    _expect16(C, "C")
+    _check("w4a16_gemm_awq",
+           load().w4a16_gemm_awq(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(zeros), _ptr(C),
+                                 int(M), int(K), int(N), int(group), int(dtype),
+                                 _ptr(workspace), _stream(stream)))
+
+
+def w4a16_dequant_awq_debug(Bpacked, scales, zeros, W, K: int, N: int, group: int, dtype: int,
+                            stream=None) -> None:
+    import torch
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect16(scales, "scales")
+    _expect(zeros, torch.uint8, "zeros")
+    _expect16(W, "W")
+    _check("w4a16_dequant_awq_debug",
+           load().w4a16_dequant_awq_debug(_ptr(Bpacked), _ptr(scales), _ptr(zeros), _ptr(W),
+                                          int(K), int(N), int(group), int(dtype),
+                                          _stream(stream)))
 
 
 def w4a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,

@@ -269,6 +269,7 @@ const char* w4a16_status_string(int status) {
     case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH";
     case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE";
     case W4A16_ERR_EPILOGUE: return "W4A16_ERR_EPILOGUE";
+    case W4A16_ERR_DTYPE: return "W4A16_ERR_DTYPE";
     default: return "W4A16_ERR_UNKNOWN";
   }
 }
@@ -345,12 +346,36 @@ int w4a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_
   return W4A16_OK;
 }
 
-int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
-                     const uint16_t* bias, int activation, uint16_t* C, int M, int K, int N,
-                     int group, void* workspace, void* stream) {
-  if (activation != W4A16_ACT_NONE && activation != W4A16_ACT_RELU &&
-      activation != W4A16_ACT_SILU)
-    return W4A16_ERR_EPILOGUE;
+int w4a16_dequant_awq_debug(const uint32_t* Bpacked, const uint16_t* scales,
+                            const uint8_t* zeros, uint16_t* W, int K, int N, int group,
+                            int dtype, void* stream) {
+  if (dtype != W4A16_DTYPE_F16 && dtype != W4A16_DTYPE_BF16) return W4A16_ERR_DTYPE;
+  if (!Bpacked || !scales || !W) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bpacked) || !aligned16(scales) || !aligned16(W) ||
+      (zeros && !aligned16(zeros)))
+    return W4A16_ERR_ALIGN;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  const int fmt = (dtype == W4A16_DTYPE_BF16 ? 2 : 0) + (zeros ? 1 : 0);
+  if (launch_dequant_fmt(Bpacked, scales, zeros, W, K, N, group, fmt,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The GEMM behind every entry point: argument checks, then the plan and the
+// launch.  fmt is a weight format of format.hpp (0: FP16, 1: FP16 with zero
+// points, 2: BF16, 3: BF16 with zero points).
+int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                 const uint8_t* zeros, const uint16_t* bias, int activation, uint16_t* C,
+                 int M, int K, int N, int group, int fmt, void* workspace, void* stream) {
   if (M < 0) return W4A16_ERR_SHAPE;
   int rc = check_kn(K, N, true);
   if (rc != W4A16_OK) return rc;
@@ -359,13 +384,14 @@ int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked, const uint16_t*
   if (M == 0 || N == 0) return W4A16_OK;  // empty output: nothing to do
   if (!A || !Bpacked || !scales || !C) return W4A16_ERR_NULL;
   if (!aligned16(A) || !aligned16(Bpacked) || !aligned16(scales) || !aligned16(C) ||
-      (bias && !aligned16(bias)))
+      (bias && !aligned16(bias)) || (zeros && !aligned16(zeros)))
     return W4A16_ERR_ALIGN;
   const size_t cbytes = (size_t)M * N * 2;
   if (overlap(C, cbytes, A, (size_t)M * K * 2) ||
       overlap(C, cbytes, Bpacked, w4a16_packed_bytes(K, N)) ||
       overlap(C, cbytes, scales, (size_t)(K / group) * N * 2) ||
-      (bias && overlap(C, cbytes, bias, (size_t)N * 2)))
+      (bias && overlap(C, cbytes, bias, (size_t)N * 2)) ||
+      (zeros && overlap(C, cbytes, zeros, (size_t)(K / group) * N)))
     return W4A16_ERR_SHAPE;
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
@@ -376,17 +402,41 @@ int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked, const uint16_t*
     if (overlap(C, cbytes, workspace, plan.workspace_bytes)) return W4A16_ERR_SHAPE;
   }
   const Epilogue ep{reinterpret_cast<const _Float16*>(bias), activation};
-  if (launch_gemm(plan, A, Bpacked, scales, C, M, K, N, group, ep, workspace,
+  const WeightFormat wf{fmt, zeros};
+  if (launch_gemm(plan, A, Bpacked, scales, C, M, K, N, group, ep, wf, workspace,
                   static_cast<hipStream_t>(stream)) != hipSuccess)
     return W4A16_ERR_LAUNCH;
   return W4A16_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                     const uint16_t* bias, int activation, uint16_t* C, int M, int K, int N,
+                     int group, void* workspace, void* stream) {
+  if (activation != W4A16_ACT_NONE && activation != W4A16_ACT_RELU &&
+      activation != W4A16_ACT_SILU)
+    return W4A16_ERR_EPILOGUE;
+  return gemm_checked(A, Bpacked, scales, nullptr, bias, activation, C, M, K, N, group, 0,
+                      workspace, stream);
+}
+
 int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
                uint16_t* C, int M, int K, int N, int group, void* workspace,
                void* stream) {
-  return w4a16_gemm_fused(A, Bpacked, scales, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
-                          workspace, stream);
+  return gemm_checked(A, Bpacked, scales, nullptr, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
+                      0, workspace, stream);
+}
+
+int w4a16_gemm_awq(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                   const uint8_t* zeros, uint16_t* C, int M, int K, int N, int group, int dtype,
+                   void* workspace, void* stream) {
+  if (dtype != W4A16_DTYPE_F16 && dtype != W4A16_DTYPE_BF16) return W4A16_ERR_DTYPE;
+  const int fmt = (dtype == W4A16_DTYPE_BF16 ? 2 : 0) + (zeros ? 1 : 0);
+  return gemm_checked(A, Bpacked, scales, zeros, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
+                      fmt, workspace, stream);
 }
 
 }  // extern "C"

@@ -1,18 +1,23 @@
-// w4a16_dequant_debug's kernel: permuted words -> FP16 W[K][N].
+// w4a16_dequant_debug's kernel: permuted words -> W[K][N] (FP16, or BF16
+// for the BF16 formats of w4a16_dequant_awq_debug).
 //
-// It runs the GEMM's own unpack-and-scale routine on every word, so W shows
-// bit for bit the weights the GEMM feeds to the matrix instruction.  One
+// It runs the GEMM's own unpack-and-scale routine of the format on every
+// word, so W shows bit for bit the weights the GEMM feeds to the matrix
+// instruction.  One
 // wave handles one fragment block (16 columns x 128 in-features): lane l
 // reads its four words (16 bytes) and the scale of its column, exactly as
 // the GEMM does, and writes its 32 weights.
+#include "format.hpp"
 #include "internal.hpp"
 #include "layout.hpp"
 #include "unpack.hpp"
 
 namespace w4a16 {
 
+template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ Bp,
                                                       const _Float16* __restrict__ S,
+                                                      const uint8_t* __restrict__ Z,
                                                       _Float16* __restrict__ W,
                                                       int K, int N, int group) {
   const int KB = K / kBlockK;
@@ -26,13 +31,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     const int n = n16 * kBlockN + (lane & 15);
     const uint4 words =
         *reinterpret_cast<const uint4*>(Bp + block_word_offset(n16, kb, K) + lane * 4);
-    const _Float16 s = S[(int64_t)(kb * kBlockK / group) * N + n];
-    const half2_t s2 = {s, s};
+    const int64_t g = (int64_t)(kb * kBlockK / group) * N + n;
+    const _Float16 s = S[g];
+    const ColParams cp = make_col<FMT>(half2_t{s, s}, Format<FMT>::kZp ? (uint32_t)Z[g] : 8u);
     const uint32_t w4[4] = {words.x, words.y, words.z, words.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       Half8 h;
-      h.v = unpack_scale(w4[j], s2);
+      h.v = unpack_col<FMT>(w4[j], cp);
       const int k0 = kb * kBlockK + 32 * j + 8 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < 8; ++i) W[(int64_t)(k0 + i) * N + n] = h.v[i];
@@ -40,15 +46,40 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   }
 }
 
-hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
-                          int K, int N, int group, hipStream_t stream) {
+hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8_t* Z,
+                              uint16_t* W, int K, int N, int group, int fmt,
+                              hipStream_t stream) {
   const int64_t blocks = (int64_t)(N / kBlockN) * (K / kBlockK);
   int64_t wgs = (blocks + 3) / 4;   // four waves per workgroup
   if (wgs > 65536) wgs = 65536;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, Bp,
-                     reinterpret_cast<const _Float16*>(S), reinterpret_cast<_Float16*>(W),
-                     K, N, group);
+  auto s = reinterpret_cast<const _Float16*>(S);
+  auto w = reinterpret_cast<_Float16*>(W);
+  const dim3 grid((unsigned)wgs), block(256);
+  switch (fmt) {
+    case kFmtF16:
+      hipLaunchKernelGGL(dequant_kernel<kFmtF16>, grid, block, 0, stream, Bp, s, Z, w, K, N, group);
+      break;
+    case kFmtF16Zp:
+      hipLaunchKernelGGL(dequant_kernel<kFmtF16Zp>, grid, block, 0, stream, Bp, s, Z, w, K, N,
+                         group);
+      break;
+    case kFmtBf16:
+      hipLaunchKernelGGL(dequant_kernel<kFmtBf16>, grid, block, 0, stream, Bp, s, Z, w, K, N,
+                         group);
+      break;
+    case kFmtBf16Zp:
+      hipLaunchKernelGGL(dequant_kernel<kFmtBf16Zp>, grid, block, 0, stream, Bp, s, Z, w, K, N,
+                         group);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
+                          int K, int N, int group, hipStream_t stream) {
+  return launch_dequant_fmt(Bp, S, nullptr, W, K, N, group, kFmtF16, stream);
 }
 
 }  // namespace w4a16

@@ -1,0 +1,154 @@
+// Weight and activation formats of the GEMM kernels.
+//
+// Format 0 is the path the pages describe: FP16 activations, scales and
+// output, codes centred on 8, w = fp16_rne((q - 8) * s) ("Quant Marlin
+// kernel" explainer, "The architecture: every piece explained").  Serving
+// stacks also run AWQ checkpoints through the same kernel ("Low-Precision
+// Quantization Kernels in Production", section 1 on production engines, and
+// the comparison table of section 5: GPTQ and AWQ formats), whose codes
+// carry a zero point per group and column, and models kept in BF16 (same
+// page: the introduction's 16-bit FP16/BF16 weights, section 4's FP16 and
+// BF16 activation formats).  The other formats add those:
+//
+//   1  FP16, zero point z per (group, column):   w = fp16_rne((q - z) * s)
+//   2  BF16 activations, scales and output:      w = bf16_rne((q - 8) * s)
+//   3  BF16 with zero points:                    w = bf16_rne((q - z) * s)
+//
+// In every format (q - z) is an integer in -15..15 and the product with the
+// scale is exact before its one rounding to the 16-bit type.
+//
+// FP16 with a zero point uses the FP16 trick of unpack.hpp with the
+// subtrahends 1024 + z and 64 + z instead of 1032 and 72: both are exact in
+// FP16, so the difference is the exact integer q - z.  The BF16 formats take
+// that same exact q - z in FP16, widen each half to FP32, multiply by the
+// scale in FP32 (exact: at most 9 by 8 significant bits) and convert the
+// pair to BF16, which rounds once, to nearest even.  The FP32 product is
+// exact for every BF16 scale (BF16 and FP32 share their exponent range), and
+// a code equal to its zero point gives 0 * s, signed as the scale.  That is
+// 29 vector instructions per eight weights against 13 for FP16: BF16 pays in
+// unpacking, not in bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "unpack.hpp"
+
+namespace w4a16 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_fmt_t __attribute__((ext_vector_type(4)));
+
+enum : int { kFmtF16 = 0, kFmtF16Zp = 1, kFmtBf16 = 2, kFmtBf16Zp = 3 };
+
+template <int FMT>
+struct Format {
+  static_assert(FMT >= 0 && FMT <= 3, "four formats");
+  static constexpr bool kBf16 = FMT >= 2;
+  static constexpr bool kZp = (FMT & 1) != 0;
+};
+
+// What the unpack of one (group, column) needs, made once per K block and
+// column from the raw 16-bit scale (FP16 or BF16 bits, in both halves of s2)
+// and the zero point z (8 for the formats without one).
+struct ColParams {
+  half2_t s2;        // FP16 formats: the scale in both halves
+  half2_t zlo, zhi;  // formats 1-3: 1024 + z and 64 + z in both halves
+  float s;           // BF16 formats: the scale as FP32
+};
+
+template <int FMT>
+__device__ __forceinline__ ColParams make_col(half2_t s2, uint32_t z) {
+  ColParams p;
+  p.s2 = s2;
+  if constexpr (FMT != kFmtF16) {
+    const _Float16 lo = (_Float16)(float)(1024u + z);  // exact: integers to 2048
+    const _Float16 hi = (_Float16)(float)(64u + z);    // exact: quarter units above 256
+    p.zlo = half2_t{lo, lo};
+    p.zhi = half2_t{hi, hi};
+  }
+  if constexpr (Format<FMT>::kBf16) {
+    // BF16 bits in the low half of the register; as FP32 they sit in the
+    // upper half
+    const uint32_t bits = __builtin_bit_cast(uint32_t, s2) << 16;
+    p.s = __builtin_bit_cast(float, bits);
+  }
+  return p;
+}
+
+// The exact integers q - z of one word, as four FP16 pairs in B-operand
+// order: unpack_scale's steps with the subtrahends 1024 + z (codes at bits
+// 0..3) and 64 + z (codes at bits 4..7).
+__device__ __forceinline__ Half8 codes_minus_zero(uint32_t word, half2_t zlo, half2_t zhi) {
+#pragma clang fp contract(off)
+  const uint32_t w8 = word >> 8;
+  Half8 raw;
+  raw.u[0] = and_or(word, 0x000F000Fu, 0x64006400u);
+  raw.u[1] = and_or(word, 0x00F000F0u, 0x54005400u);
+  raw.u[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
+  raw.u[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
+  Half8 d;
+  d.h2[0] = raw.h2[0] - zlo;  // exact
+  d.h2[1] = raw.h2[1] - zhi;
+  d.h2[2] = raw.h2[2] - zlo;
+  d.h2[3] = raw.h2[3] - zhi;
+  return d;
+}
+
+// FP16 with a zero point: (q - z) * s, one rounding.
+__device__ __forceinline__ half8_t unpack_scale_zp(uint32_t word, half2_t scale2, half2_t zlo,
+                                                   half2_t zhi) {
+#pragma clang fp contract(off)
+  Half8 out = codes_minus_zero(word, zlo, zhi);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out.h2[i] = out.h2[i] * scale2;
+  return out.v;
+}
+
+// BF16: eight weights bf16_rne((q - z) * s) in the B-operand order of the
+// 16x16x32 BF16 matrix instruction (the same order as FP16), as raw bits.
+__device__ __forceinline__ half8_t unpack_scale_bf16(uint32_t word, float s, half2_t zlo,
+                                                     half2_t zhi) {
+#pragma clang fp contract(off)
+  const Half8 d = codes_minus_zero(word, zlo, zhi);
+  Half8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t pair = {(__bf16)((float)d.h2[i][0] * s), (__bf16)((float)d.h2[i][1] * s)};
+    out.u[i] = __builtin_bit_cast(uint32_t, pair);
+  }
+  return out.v;
+}
+
+template <int FMT>
+__device__ __forceinline__ half8_t unpack_col(uint32_t word, const ColParams& p) {
+  if constexpr (FMT == kFmtF16)
+    return unpack_scale(word, p.s2);
+  else if constexpr (FMT == kFmtF16Zp)
+    return unpack_scale_zp(word, p.s2, p.zlo, p.zhi);
+  else
+    return unpack_scale_bf16(word, p.s, p.zlo, p.zhi);
+}
+
+// One 16x16x32 matrix instruction on raw 16-bit fragments.
+template <int FMT>
+__device__ __forceinline__ float4_fmt_t mma16(half8_t a, half8_t b, float4_fmt_t acc) {
+  if constexpr (Format<FMT>::kBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+
+// An FP32 result rounded to the output type (to nearest even), as the raw
+// 16 bits in a _Float16 container.
+template <int FMT>
+__device__ __forceinline__ _Float16 out16(float x) {
+  if constexpr (Format<FMT>::kBf16)
+    return __builtin_bit_cast(_Float16, (__bf16)x);
+  else
+    return (_Float16)x;
+}
+
+}  // namespace w4a16

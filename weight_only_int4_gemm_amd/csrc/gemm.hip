@@ -28,6 +28,7 @@
 // the next 32-deep step are in flight while the current ones are consumed.
 #include "coherent.hpp"
 #include "epilogue.hpp"
+#include "format.hpp"
 #include "internal.hpp"
 #include "layout.hpp"
 #include "unpack.hpp"
@@ -36,19 +37,32 @@ namespace w4a16 {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-template <int MB, int NB>
+template <int MB, int NB, bool ZP>
 struct Slot {
   uint4 b[NB];         // permuted codes: one 128-deep K block per column block
   half2_t s[NB];       // the group scale of this lane's column, in both halves
   half8_t a[MB][4];    // activation fragments, four 32-deep steps
 };
+// With zero points: the group zero point of this lane's column as well.
+template <int MB, int NB>
+struct Slot<MB, NB, true> {
+  uint4 b[NB];
+  half2_t s[NB];
+  half8_t a[MB][4];
+  uint32_t z[NB];
+};
 
-template <int MB, int NB, int WK, int D, bool EPI>
+// FMT: the weight format (format.hpp); formats other than 0 are compiled
+// without the fused epilogue.  A, S and C hold raw 16-bit values (FP16, or
+// BF16 for formats 2 and 3); Z the zero points of formats 1 and 3.
+template <int MB, int NB, int WK, int D, bool EPI, int FMT>
 __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
-    float* __restrict__ partials, Epilogue ep) {
+    float* __restrict__ partials, Epilogue ep, const uint8_t* __restrict__ Z) {
+  static_assert(!EPI || FMT == kFmtF16, "the fused epilogue is FP16 only");
+  constexpr bool ZP = Format<FMT>::kZp;
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
@@ -97,11 +111,13 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   }
   const uint32_t* bcol[NB];
   const _Float16* scol[NB];
+  const uint8_t* zcol[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n16 = n16_0 + (nb < nvalid ? nb : nvalid - 1);
     bcol[nb] = Bp + block_word_offset(n16, 0, K) + lane * kWordsPerLane;
     scol[nb] = S + n16 * kBlockN + l16;
+    if constexpr (ZP) zcol[nb] = Z + n16 * kBlockN + l16;
   }
 
   // Scale row of K block kb: kb / group_blocks (group_magic = 0: a shift).
@@ -110,13 +126,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   auto scale_row = [&](int kb) -> int {
     return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
   };
-  auto load = [&](Slot<MB, NB>& sl, int kb) {
+  auto load = [&](Slot<MB, NB, ZP>& sl, int kb) {
     const int srow = scale_row(kb) * N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + kb * kWordsPerBlock);
       const _Float16 sc = scol[nb][srow];
       sl.s[nb] = half2_t{sc, sc};
+      if constexpr (ZP) sl.z[nb] = zcol[nb][srow];
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -124,7 +141,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
       for (int j = 0; j < 4; ++j)
         sl.a[mb][j] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
   };
-  auto compute = [&](const Slot<MB, NB>& sl) {
+  auto compute = [&](const Slot<MB, NB, ZP>& sl) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -133,10 +150,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
         // drops them -- a branch here would stall the load pipeline)
         const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
                          : j == 2 ? sl.b[nb].z : sl.b[nb].w;
-        const half8_t b = unpack_scale(w, sl.s[nb]);
+        uint32_t z = 8;
+        if constexpr (ZP) z = sl.z[nb];
+        const half8_t b = unpack_col<FMT>(w, make_col<FMT>(sl.s[nb], z));
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sl.a[mb][j], b, acc[mb][nb], 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mma16<FMT>(sl.a[mb][j], b, acc[mb][nb]);
       }
     }
   };
@@ -149,7 +167,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   const int nblk = first < kb1 ? (kb1 - first + WK - 1) / WK : 0;
   if (nblk > 0) {
     const int last = first + (nblk - 1) * WK;
-    Slot<MB, NB> slot[D];
+    Slot<MB, NB, ZP> slot[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int kb = first + u * WK;
@@ -195,12 +213,13 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   constexpr int VPR = TN / VEC;  // float4 vectors per tile row
   const int row0 = tile_m * TM;
   const int col0 = tile_n * TN;
-  // Four consecutive columns of C (through the epilogue), rounded to FP16.
+  // Four consecutive columns of C (through the epilogue), rounded to the
+  // output type.
   auto finish = [&](const float4_t& x) {
     half4_t h;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
-      h[j] = (_Float16)(EPI ? epilogue_apply(ep, x[j], (float)bias4[j]) : x[j]);
+      h[j] = out16<FMT>(EPI ? epilogue_apply(ep, x[j], (float)bias4[j]) : x[j]);
     return h;
   };
 
@@ -264,10 +283,10 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK, int D>
+template <int MB, int NB, int WK, int D, int FMT>
 static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                              const uint16_t* S, uint16_t* C, int M, int K, int N,
-                             uint64_t gmagic, Epilogue ep, void* workspace,
+                             uint64_t gmagic, Epilogue ep, const uint8_t* Z, void* workspace,
                              hipStream_t stream) {
   unsigned* counters = nullptr;
   float* partials = nullptr;
@@ -280,12 +299,17 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
-  if (epilogue_needed(ep))
-    hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, true>), grid, block, 0, stream, a, Bp, s, c,
-                       M, K, N, gmagic, p.splits, counters, partials, ep);
-  else
-    hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, false>), grid, block, 0, stream, a, Bp, s, c,
-                       M, K, N, gmagic, p.splits, counters, partials, ep);
+  if constexpr (FMT == kFmtF16) {
+    if (epilogue_needed(ep)) {
+      hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, true, FMT>), grid, block, 0, stream, a, Bp,
+                         s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
+      return hipGetLastError();
+    }
+  } else {
+    if (epilogue_needed(ep)) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, false, FMT>), grid, block, 0, stream, a, Bp, s,
+                     c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
   return hipGetLastError();
 }
 
@@ -297,6 +321,10 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
   X(2, 2, 4, 2) X(2, 2, 8, 2) X(2, 4, 4, 2) X(2, 4, 8, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) \
   X(8, 2, 4, 1) X(8, 4, 4, 1)
 
+// Variants compiled for the other formats too: the ones the plans pick.
+#define W4A16_FMT_VARIANTS(X) \
+  X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 8, 2) X(1, 1, 4, 2) X(1, 4, 4, 4) X(1, 4, 4, 2)
+
 bool plan_is_compiled(int mb, int nb, int wk, int depth) {
 #define W4A16_MATCH(MB_, NB_, WK_, D_) \
   if (mb == MB_ && nb == NB_ && wk == WK_ && depth == D_) return true;
@@ -307,20 +335,41 @@ bool plan_is_compiled(int mb, int nb, int wk, int depth) {
 
 hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N, int group,
-                       Epilogue ep, void* workspace, hipStream_t stream) {
+                       Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream) {
   // Scale row of K block kb is kb / gb, gb = group / 128, computed in the
   // kernels as (kb * ceil(2^32 / gb)) >> 32: exact when gb is a power of two,
   // and for any gb as long as kb, gb < 2^16 (K < 2^23 is checked).
   const uint64_t gb = (uint64_t)(group / kBlockK);
   const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
-  if (p.tile >= 2) return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, ep, workspace, stream);
-  if (p.tile) return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, ep, workspace, stream);
+  if (p.tile >= 2)
+    return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, ep, wf, workspace, stream);
+  if (p.tile) {
+    if (wf.fmt != kFmtF16) return hipErrorInvalidValue;  // the tile kernel is FP16 only
+    return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, ep, workspace, stream);
+  }
+  if (wf.fmt == kFmtF16) {
 #define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \
-    return launch_one<MB_, NB_, WK_, D_>(p, A, Bp, S, C, M, K, N, gmagic, ep,       \
-                                         workspace, stream);
-  W4A16_VARIANTS(W4A16_CASE)
+    return launch_one<MB_, NB_, WK_, D_, kFmtF16>(p, A, Bp, S, C, M, K, N, gmagic, ep, \
+                                                  nullptr, workspace, stream);
+    W4A16_VARIANTS(W4A16_CASE)
 #undef W4A16_CASE
+    return hipErrorInvalidValue;
+  }
+#define W4A16_FCASE(MB_, NB_, WK_, D_)                                                    \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_) {                       \
+    if (wf.fmt == kFmtF16Zp)                                                              \
+      return launch_one<MB_, NB_, WK_, D_, kFmtF16Zp>(p, A, Bp, S, C, M, K, N, gmagic, ep, \
+                                                      wf.zeros, workspace, stream);       \
+    if (wf.fmt == kFmtBf16)                                                               \
+      return launch_one<MB_, NB_, WK_, D_, kFmtBf16>(p, A, Bp, S, C, M, K, N, gmagic, ep,  \
+                                                     nullptr, workspace, stream);         \
+    if (wf.fmt == kFmtBf16Zp)                                                             \
+      return launch_one<MB_, NB_, WK_, D_, kFmtBf16Zp>(p, A, Bp, S, C, M, K, N, gmagic,   \
+                                                       ep, wf.zeros, workspace, stream);  \
+  }
+  W4A16_FMT_VARIANTS(W4A16_FCASE)
+#undef W4A16_FCASE
   return hipErrorInvalidValue;
 }
 

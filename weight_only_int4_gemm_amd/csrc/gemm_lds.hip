@@ -43,13 +43,19 @@ namespace w4a16 {
 // instruction at the same operand size and issues at the full rate, where
 // the 16 x 16 form sustains about 80% of it; it reads the same packed layout
 // (the lane-to-word map below).
-template <int MB, int NB, int WM, int WN, int NS, int F, bool EPI>
+//
+// FMT is the weight format (format.hpp): formats other than 0 (zero points,
+// BF16) use the 16 x 16 blocks and no fused epilogue; their zero points are
+// one more part of each stage, loaded like the scales.
+template <int MB, int NB, int WM, int WN, int NS, int F, bool EPI, int FMT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
-    float* __restrict__ partials, Epilogue ep) {
+    float* __restrict__ partials, Epilogue ep, const uint8_t* __restrict__ Z) {
   static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
+  static_assert(FMT == kFmtF16 || (F == 16 && !EPI), "formats 1-3: 16 x 16 blocks, no epilogue");
+  constexpr bool ZP = Format<FMT>::kZp;
   constexpr int WAVES = WM * WN;
   constexpr int TM = F * MB * WM;
   constexpr int TN = F * NB * WN;
@@ -65,13 +71,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   constexpr int BPIECES = BLOCKS * 64;         // 16-byte pieces of codes
   constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
   constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
-  constexpr int LOADS = ALOADS + BLOADS + SLOADS;  // direct loads per wave per stage
+  constexpr int ZLOADS = ZP ? (TN / 4 + 63) / 64 : 0;  // zero points: 4-byte loads, all waves
+  constexpr int LOADS = ALOADS + BLOADS + SLOADS + ZLOADS;  // direct loads per wave per stage
   static_assert(NS >= 2 && NS <= 4, "two to four stages");
-  struct Stage {
+  struct StagePlain {
     uint4 a[APIECES];
     uint4 b[BPIECES];
     uint32_t s[64 * SLOADS];
   };
+  struct StageZp {
+    uint4 a[APIECES];
+    uint4 b[BPIECES];
+    uint32_t s[64 * SLOADS];
+    uint32_t z[64 * (ZLOADS > 0 ? ZLOADS : 1)];  // the tile's zero points, one byte each
+  };
+  typedef typename std::conditional<ZP, StageZp, StagePlain>::type Stage;
   // one LDS object per stage: the compiler sees that a load into one stage
   // does not touch the others
   __shared__ Stage st0;
@@ -118,6 +132,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     const int c = col0 + 2 * (64 * i + lane);
     ssrc[i] = S + (c <= N - 2 ? c : N - 2);
   }
+  // Zero-point source: word i*64 + lane of the stage holds columns 4w .. 4w+3.
+  const uint8_t* zsrc[ZLOADS > 0 ? ZLOADS : 1];
+#pragma unroll
+  for (int i = 0; i < ZLOADS; ++i) {
+    const int c = col0 + 4 * (64 * i + lane);
+    zsrc[i] = Z + (c <= N - 4 ? c : N - 4);
+  }
   auto scale_row = [&](int kb) -> int {
     return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
   };
@@ -144,6 +165,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     for (int i = 0; i < SLOADS; ++i) {
       __builtin_amdgcn_global_load_lds((global_ptr_t)(ssrc[i] + srow), (lds_ptr_t)&sg.s[64 * i],
                                        4, 0, 0);
+    }
+    if constexpr (ZP) {
+#pragma unroll
+      for (int i = 0; i < ZLOADS; ++i)
+        __builtin_amdgcn_global_load_lds((global_ptr_t)(zsrc[i] + srow),
+                                         (lds_ptr_t)&sg.z[64 * i], 4, 0, 0);
     }
   };
 
@@ -172,19 +199,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // unpacked, so the vector ALU work has independent matrix work to overlap.
   auto compute16 = [&](const Stage& sg) {
     uint4 w[NB];
-    half2_t s2[NB];
+    ColParams cp[NB];
     const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       w[nb] = sg.b[64 * (wn * NB + nb) + lane];
-      const _Float16 sc = sh[wn * 16 * NB + nb * 16 + l16];
-      s2[nb] = half2_t{sc, sc};
+      const int c = wn * 16 * NB + nb * 16 + l16;
+      const _Float16 sc = sh[c];
+      uint32_t z = 8;
+      if constexpr (ZP) z = reinterpret_cast<const uint8_t*>(sg.z)[c];
+      cp[nb] = make_col<FMT>(half2_t{sc, sc}, z);
     }
     auto unpack_slice = [&](int j, half8_t* bf) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint32_t word = j == 0 ? w[nb].x : j == 1 ? w[nb].y : j == 2 ? w[nb].z : w[nb].w;
-        bf[nb] = unpack_scale(word, s2[nb]);
+        bf[nb] = unpack_col<FMT>(word, cp[nb]);
       }
     };
     half8_t a0[MB], a1[MB];
@@ -205,9 +235,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          if constexpr (F == 16)
-            acc[mb][nb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+          if constexpr (F == 16) acc[mb][nb] = mma16<FMT>(cur[mb], bcur[nb], acc[mb][nb]);
         }
     }
   };
@@ -325,18 +353,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   if constexpr (F == 16)
-    store_output_tile<MB, NB, WAVES, EPI>(acc, C, M, N, wrow0, wcol0, split, splits, counters,
-                                          partials, reinterpret_cast<int*>(&st0.s[0]), ep, bias);
+    store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, splits,
+                                               counters, partials,
+                                               reinterpret_cast<int*>(&st0.s[0]), ep, bias);
   else
     store_output_tile32<MB, NB, WAVES, EPI>(acc, C, M, N, wrow0, wcol0, split, splits,
                                             counters, partials, reinterpret_cast<int*>(&st0.s[0]),
                                             ep, bias);
 }
 
-template <int MB, int NB, int WM, int WN, int NS, int F>
+template <int MB, int NB, int WM, int WN, int NS, int F, int FMT>
 static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                  const uint16_t* S, uint16_t* C, int M, int K, int N,
-                                 uint64_t gmagic, Epilogue ep, void* workspace,
+                                 uint64_t gmagic, Epilogue ep, const uint8_t* Z, void* workspace,
                                  hipStream_t stream) {
   unsigned* counters = nullptr;
   float* partials = nullptr;
@@ -349,12 +378,18 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
-  if (epilogue_needed(ep))
-    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, true>), grid, block, 0, stream,
-                       a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
-  else
-    hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, false>), grid, block, 0, stream,
-                       a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep);
+  if constexpr (FMT == kFmtF16) {
+    if (epilogue_needed(ep)) {
+      hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, true, FMT>), grid, block, 0,
+                         stream, a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep,
+                         Z);
+      return hipGetLastError();
+    }
+  } else {
+    if (epilogue_needed(ep)) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, false, FMT>), grid, block, 0,
+                     stream, a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
   return hipGetLastError();
 }
 
@@ -371,6 +406,11 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
   X(2, 2, 2, 4, 3, 16) X(2, 4, 2, 4, 3, 16) X(4, 4, 2, 2, 3, 16) X(2, 4, 2, 2, 3, 16)       \
   X(1, 2, 4, 2, 3, 32) X(1, 4, 4, 2, 3, 32) X(2, 2, 2, 4, 3, 32)
 
+// Variants compiled for the other formats too (16 x 16 blocks): the ones
+// the plans pick.
+#define W4A16_LDS_FMT_VARIANTS(X)                                                     \
+  X(1, 2, 1, 8, 4) X(2, 2, 1, 8, 4) X(4, 1, 1, 8, 3) X(8, 2, 1, 8, 3) X(4, 2, 2, 4, 3)
+
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f) {
 #define W4A16_LMATCH(MB_, NB_, WM_, WN_, NS_, F_) \
   if (mb == MB_ && nb == NB_ && wm == WM_ && wn == WN_ && ns == NS_ && f == F_) return true;
@@ -381,14 +421,33 @@ bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f) {
 
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
-                      Epilogue ep, void* workspace, hipStream_t stream) {
+                      Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream) {
   const int f = p.tile == 3 ? 32 : 16;
+  if (wf.fmt == kFmtF16) {
 #define W4A16_LCASE(MB_, NB_, WM_, WN_, NS_, F_)                                             \
   if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_ && f == F_) \
-    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, F_>(p, A, Bp, S, C, M, K, N, gmagic, ep,  \
-                                                       workspace, stream);
-  W4A16_LDS_VARIANTS(W4A16_LCASE)
+    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, F_, kFmtF16>(p, A, Bp, S, C, M, K, N,      \
+                                                                gmagic, ep, nullptr,         \
+                                                                workspace, stream);
+    W4A16_LDS_VARIANTS(W4A16_LCASE)
 #undef W4A16_LCASE
+    return hipErrorInvalidValue;
+  }
+  if (f != 16) return hipErrorInvalidValue;
+#define W4A16_LFCASE(MB_, NB_, WM_, WN_, NS_)                                                 \
+  if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_) {           \
+    if (wf.fmt == kFmtF16Zp)                                                                  \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtF16Zp>(                          \
+          p, A, Bp, S, C, M, K, N, gmagic, ep, wf.zeros, workspace, stream);                  \
+    if (wf.fmt == kFmtBf16)                                                                   \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtBf16>(                           \
+          p, A, Bp, S, C, M, K, N, gmagic, ep, nullptr, workspace, stream);                   \
+    if (wf.fmt == kFmtBf16Zp)                                                                 \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtBf16Zp>(                         \
+          p, A, Bp, S, C, M, K, N, gmagic, ep, wf.zeros, workspace, stream);                  \
+  }
+  W4A16_LDS_FMT_VARIANTS(W4A16_LFCASE)
+#undef W4A16_LFCASE
   return hipErrorInvalidValue;
 }
 

@@ -44,6 +44,14 @@ struct Epilogue {
   int act;
 };
 
+// The weight format of a call (format.hpp): 0 FP16, 1 FP16 with zero
+// points, 2 BF16, 3 BF16 with zero points; `zeros` are the zero points
+// uint8[K/group][N] of formats 1 and 3 (null otherwise).
+struct WeightFormat {
+  int fmt;
+  const uint8_t* zeros;
+};
+
 Plan make_plan(int M, int K, int N, int group, int cus);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
@@ -58,10 +66,14 @@ hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                        uint64_t gmagic, Epilogue ep, void* workspace, hipStream_t stream);
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
-                      Epilogue ep, void* workspace, hipStream_t stream);
+                      Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream);
 hipError_t launch_gemm(const Plan& plan, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
-                       int group, Epilogue ep, void* workspace, hipStream_t stream);
+                       int group, Epilogue ep, WeightFormat wf, void* workspace,
+                       hipStream_t stream);
+hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8_t* Z,
+                              uint16_t* W, int K, int N, int group, int fmt,
+                              hipStream_t stream);
 
 // Workspace layout for a plan with splits > 1: one 32-bit arrival counter
 // per output tile (padded to 256 bytes), then FP32 partial tiles

@@ -5,6 +5,7 @@
 
 #include "coherent.hpp"
 #include "epilogue.hpp"
+#include "format.hpp"
 #include "internal.hpp"
 
 namespace w4a16 {
@@ -82,8 +83,8 @@ struct LaneBias {
 // lane moves its four accumulators in one 16-byte access and the workgroup
 // that sums finds its own fragments at the same places.  `flag` is an int in
 // LDS no wave touches any more.  The epilogue is applied to the final sums
-// only.
-template <int MB, int NB, int WAVES, bool EPI>
+// only; FMT sets the output type (FP16, or BF16 for formats 2 and 3).
+template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
                                                   int wrow0, int wcol0, int split, int splits,
@@ -106,7 +107,7 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
         for (int i = 0; i < 4; ++i) {
           const int gr = wrow0 + mb * 16 + (lane >> 4) * 4 + i;
           const float x = acc[mb][nb][i];
-          if (gr < M) C[(int64_t)gr * N + gc] = (_Float16)(EPI ? epilogue_apply(ep, x, b) : x);
+          if (gr < M) C[(int64_t)gr * N + gc] = out16<FMT>(EPI ? epilogue_apply(ep, x, b) : x);
         }
       }
   };
