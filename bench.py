@@ -138,14 +138,23 @@ def _short_kernel_name(name: str) -> str:
             seg, i = name[j:j + n], j + n
         if name[i:i + 1] == "I":
             end = name.find("EE", i)
-            args = re.findall(r"Li(-?\d+)E", name[i:end + 2])
+            targs = name[i:end + 2]
+            # the plan's integer arguments come before the first bool (the
+            # fused-epilogue switch); the weight format after it is not part
+            # of the plan's name
+            if "Lb" in targs:
+                targs = targs[:targs.index("Lb")]
+            args = re.findall(r"Li(-?\d+)E", targs)
             return f"{seg}<{','.join(args)}>"
         return seg
     base = name.split("(")[0].replace("void ", "").strip()
     head, lt, rest = base.partition("<")
-    # bool template arguments (the fused-epilogue switch) are not part of
-    # the plan's name
-    rest = rest.replace(" ", "").replace(",false>", ">").replace(",true>", ">")
+    # the fused-epilogue switch (a bool) and the weight format after it are
+    # not part of the plan's name
+    rest = rest.replace(" ", "")
+    for flag in (",false", ",true"):
+        if flag in rest:
+            rest = rest[:rest.index(flag)] + ">"
     return head.split("::")[-1] + lt + rest
 
 

@@ -26,6 +26,10 @@ def test_kernel_names_from_profiler_output():
         "NS_8EpilogueE": "gemm_lds_kernel<4,2,2,4,3,16>",
         "void w4a16::gemm_lds_kernel<4, 1, 1, 8, 3, 16, false>(_Float16 const*)":
             "gemm_lds_kernel<4,1,1,8,3,16>",
+        # and so is the weight format after it
+        "_ZN5w4a1615gemm_lds_kernelILi4ELi1ELi1ELi8ELi3ELi16ELb0ELi2EEEvPKDF16_PKjS2_PDF16_"
+        "iiimiPjPfNS_8EpilogueEPKh": "gemm_lds_kernel<4,1,1,8,3,16>",
+        "void w4a16::gemm_kernel<1, 1, 8, 2, false, 3>(_Float16 const*)": "gemm_kernel<1,1,8,2>",
     }
     for raw, short in cases.items():
         assert bench._short_kernel_name(raw) == short
