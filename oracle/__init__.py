@@ -21,7 +21,9 @@ plain numpy, with no blocking, fusion or reordering beyond that description:
   or an activation (``gemm_fused``).
 * "Low-Precision Quantization Kernels in Production" (llms.blog), section 1
   and the table of section 5 (AWQ checkpoints), introduction and section 4
-  (BF16): zero points and BF16 (``dequant_awq``, ``gemm_awq``).
+  (BF16): zero points and BF16 (``dequant_awq``, ``gemm_awq``); section 1
+  and the same table (4-bit and 8-bit checkpoints): 8-bit weights
+  (``dequant8``, ``gemm8``, ``repack8``).
 
 Readings where the pages leave a step open (zero point 8, LSB-first nibble
 order along K, scale layout ``[K/group][N]``, single RNE rounding of the
@@ -52,4 +54,11 @@ from .w4a16_ref import (  # noqa: F401
     f64_to_bf16,
     dequant_awq,
     gemm_awq,
+    ZERO_POINT8,
+    unpack_codes8,
+    pack_codes8,
+    dequant8,
+    gemm8,
+    repack8,
+    unrepack8,
 )

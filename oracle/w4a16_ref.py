@@ -376,3 +376,114 @@ def gemm_awq(A, Bq: np.ndarray, S, Z, group: int, dtype: int, cols=None):
     A64 = bf16_to_f64(A)
     C64 = A64 @ bf16_to_f64(W)
     return f64_to_bf16(C64), C64
+
+
+# ---------------------------------------------------------------------------
+# 8-bit weights.  "Low-Precision Quantization Kernels in Production"
+# (llms.blog), section 1 on production engines: the same kernel serves 4-bit
+# and 8-bit checkpoints; the table of section 5: INT4 and INT8.
+#
+# Readings (the pages define no 8-bit format):
+# 12. Codes q in 0..255 centred on 128: w = fp16_rne((q - 128) * s), one FP16
+#     scale per group of in-features and column, as for 4 bits.
+# 13. Canonical packing: four codes per 32-bit word along K, least
+#     significant byte first: code k = 4j + i is bits 8i .. 8i+7 of word
+#     Bq8[j][n], Bq8 uint32 [K/4][N].
+# 14. The permuted layout (this library's own, version 1 for 8 bits): blocks
+#     of 16 columns x 64 in-features (1 KiB), column-block-major then along
+#     K; in a block, lane l = (n % 16) + 16 * ((k % 32) // 8) owns words
+#     4l .. 4l+3, word j = 2 * ((k % 64) // 32) + (k % 8) // 4, and code k
+#     sits at byte (0, 2, 1, 3)[k % 4] of its word.  One 16-byte lane piece
+#     then holds the lane's operands of two 32-deep steps of the 16x16x32
+#     matrix instruction, and a byte mask pairs codes k, k+1 in the two
+#     halves of a register.
+# ---------------------------------------------------------------------------
+
+ZERO_POINT8 = 128
+_BYTE_OF_CODE8 = (0, 2, 1, 3)
+
+
+def _check_words8(Bq8: np.ndarray) -> None:
+    if Bq8.dtype != np.uint32 or Bq8.ndim != 2:
+        raise ValueError("Bq8 must be uint32 [K/4][N]")
+
+
+def unpack_codes8(Bq8: np.ndarray) -> np.ndarray:
+    """Codes ``q[K][N]`` (uint8) from canonical words ``Bq8[K/4][N]``."""
+    _check_words8(Bq8)
+    K4, N = Bq8.shape
+    q = np.empty((K4, 4, N), dtype=np.uint8)
+    for i in range(4):
+        q[:, i, :] = (Bq8 >> np.uint32(8 * i)) & np.uint32(0xFF)
+    return q.reshape(K4 * 4, N)
+
+
+def pack_codes8(q: np.ndarray) -> np.ndarray:
+    """Canonical words ``Bq8[K/4][N]`` from codes ``q[K][N]`` (0..255)."""
+    q = np.asarray(q)
+    if q.ndim != 2 or q.shape[0] % 4:
+        raise ValueError("q must be [K][N] with K a multiple of 4")
+    if q.min() < 0 or q.max() > 255:
+        raise ValueError("codes must be in 0..255")
+    K, N = q.shape
+    q4 = q.reshape(K // 4, 4, N).astype(np.uint32)
+    out = np.zeros((K // 4, N), dtype=np.uint32)
+    for i in range(4):
+        out |= q4[:, i, :] << np.uint32(8 * i)
+    return out
+
+
+def dequant8(Bq8: np.ndarray, S: np.ndarray, group: int) -> np.ndarray:
+    """FP16 weights ``W[K][N] = fp16_rne((q - 128) * s)`` (reading 12)."""
+    q = unpack_codes8(Bq8).astype(np.float64)
+    K = q.shape[0]
+    s = np.repeat(np.asarray(S, dtype=np.float16).astype(np.float64), group, axis=0)[:K]
+    # (q - 128) has 8 bits and s 11: the float64 product is exact
+    with np.errstate(over="ignore"):
+        return ((q - ZERO_POINT8) * s).astype(np.float16)
+
+
+def gemm8(A: np.ndarray, Bq8: np.ndarray, S: np.ndarray, group: int, cols=None):
+    """``(C16, C64)`` for 8-bit weights: the float64 sum of A . W and its
+    single FP16 rounding; with ``cols``, only those output columns."""
+    if cols is not None:
+        cols = np.asarray(cols, dtype=np.int64)
+        Bq8 = np.ascontiguousarray(Bq8[:, cols])
+        S = np.ascontiguousarray(np.asarray(S)[:, cols])
+    W = dequant8(Bq8, S, group)
+    C64 = np.asarray(A, dtype=np.float16).astype(np.float64) @ W.astype(np.float64)
+    return C64.astype(np.float16), C64
+
+
+def repack8(Bq8: np.ndarray) -> np.ndarray:
+    """Permuted words (flat uint32, K*N/4 of them) from canonical ``Bq8``
+    (reading 14)."""
+    _check_words8(Bq8)
+    K, N = Bq8.shape[0] * 4, Bq8.shape[1]
+    if K % 64 or N % 16:
+        raise ValueError("K must be a multiple of 64 and N of 16")
+    q = unpack_codes8(Bq8).astype(np.uint32)
+    out = np.zeros(K * N // 4, dtype=np.uint32)
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    lane = (n % 16) + 16 * ((k % 32) // 8)
+    j = 2 * ((k % 64) // 32) + (k % 8) // 4
+    word = (((n // 16) * (K // 64) + k // 64) * 64 + lane) * 4 + j
+    byte = np.array(_BYTE_OF_CODE8, dtype=np.uint32)[k % 4]
+    np.bitwise_or.at(out, word.ravel(), (q << (np.uint32(8) * byte)).ravel())
+    return out
+
+
+def unrepack8(Bp: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Canonical ``Bq8[K/4][N]`` from permuted words (inverse of ``repack8``)."""
+    Bp = np.asarray(Bp, dtype=np.uint32).ravel()
+    if Bp.size != K * N // 4:
+        raise ValueError("size mismatch")
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    lane = (n % 16) + 16 * ((k % 32) // 8)
+    j = 2 * ((k % 64) // 32) + (k % 8) // 4
+    word = (((n // 16) * (K // 64) + k // 64) * 64 + lane) * 4 + j
+    byte = np.array(_BYTE_OF_CODE8, dtype=np.uint32)[k % 4]
+    q = (Bp[word] >> (np.uint32(8) * byte)) & np.uint32(0xFF)
+    return pack_codes8(q)

@@ -646,3 +646,140 @@ def test_gemm_awq_sampled_columns_match_full():
     cols = [0, 5, 33, 63]
     Cs, C64s = oracle.gemm_awq(A, Bq, S, Z, 128, 1, cols=cols)
     assert np.array_equal(Cs, C[:, cols]) and np.array_equal(C64s, C64[:, cols])
+
+
+# ---------------------------------------------------------------------------
+# 8-bit weights
+# ---------------------------------------------------------------------------
+
+def _golden8():
+    canon, perm = [], []
+    with open(os.path.join(GOLDEN, "byte_order8.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            p = line.split()
+            if p[0] == "canonical":
+                canon.append((int(p[1], 16), [int(x) for x in p[2:6]]))
+            else:
+                perm.append(([int(x) for x in p[1:5]], int(p[5], 16)))
+    return canon, perm
+
+
+def test_byte_order8_golden():
+    canon, perm = _golden8()
+    for word, codes in canon:
+        Bq8 = np.array([[word]], dtype=np.uint32)
+        assert list(oracle.unpack_codes8(Bq8)[:, 0]) == codes
+        assert oracle.pack_codes8(np.array(codes)[:, None])[0, 0] == word
+    for codes, word in perm:
+        # one column, K = 64: codes k = 0..3 of column 0 are word 0 of lane 0
+        q = np.zeros((64, 16), dtype=np.int64)
+        q[0:4, 0] = codes
+        Bp = oracle.repack8(oracle.pack_codes8(q))
+        assert Bp[0] == word, (codes, hex(Bp[0]))
+
+
+def test_pack_unpack8_roundtrips_and_positions():
+    for i in range(4):
+        for v in (0, 1, 127, 128, 255):
+            q = np.zeros((4, 3), dtype=np.int64)
+            q[i, 1] = v
+            w = oracle.pack_codes8(q)
+            assert w[0, 1] == v << (8 * i) and w[0, 0] == 0
+            assert np.array_equal(oracle.unpack_codes8(w), q.astype(np.uint8))
+    rng = np.random.default_rng(5)
+    B = rng.integers(0, 2**32, size=(64, 48), dtype=np.uint32)
+    assert np.array_equal(oracle.pack_codes8(oracle.unpack_codes8(B)), B)
+
+
+def test_repack8_is_a_bijection():
+    rng = np.random.default_rng(6)
+    K, N = 192, 48
+    B = rng.integers(0, 2**32, size=(K // 4, N), dtype=np.uint32)
+    Bp = oracle.repack8(B)
+    assert Bp.size == K * N // 4
+    assert np.array_equal(oracle.unrepack8(Bp, K, N), B)
+    # every code lands in exactly one byte: permuting the codes permutes bytes
+    assert np.array_equal(np.sort(Bp.view(np.uint8)), np.sort(B.view(np.uint8).ravel()))
+
+
+def test_dequant8_codes_times_scales():
+    """All 256 codes against 4096 FP16 scales of both signs plus extremes,
+    against the exact double product rounded by Python's half packer."""
+    rng = np.random.default_rng(7)
+    sc = rng.integers(0, 2**16, size=4096, dtype=np.uint16).view(np.float16)
+    sc = sc[np.isfinite(sc) & (sc != 0)]
+    sc = np.concatenate([sc, np.array([1.0, -1.0, 2**-24, 65504.0, 0.01], np.float16)])
+    q = np.repeat(np.arange(256), 1)[:, None] * np.ones((1, sc.size), dtype=np.int64)
+    Bq8 = oracle.pack_codes8(q)
+    W = oracle.dequant8(Bq8, sc[None, :], 256)
+    for ci in range(0, 256, 1):
+        row = W[ci]
+        for j in range(0, sc.size, 7):          # every 7th scale per code
+            want = _fp16_struct((ci - 128) * float(sc[j]))
+            got = float(row[j])
+            assert got == want or (got == 0 and want == 0), (ci, sc[j])
+
+
+def test_repack8_feeds_the_matrix_instruction():
+    """Consume the permuted 8-bit words the way a wave does and recover
+    ``A . W``: per 16-column block and 64-deep block a lane reads words
+    4l .. 4l+3; step s of the block takes words 2s and 2s+1, each split by
+    a byte mask 0x00FF00FF (codes k, k+1) and the same mask after a shift by
+    8 (codes k+2, k+3)."""
+    M, K, N = 16, 128, 32
+    A, _, S = make_inputs(M, K, N, 128, seed=14)
+    Bq8 = np.random.default_rng(15).integers(0, 2**32, size=(K // 4, N), dtype=np.uint32)
+    Bp = oracle.repack8(Bq8).reshape(N // 16, K // 64, 64, 4)
+    Af = A.astype(np.float64)
+    C = np.zeros((M, N))
+    for n16 in range(N // 16):
+        for kb in range(K // 64):
+            for st in range(2):
+                k0 = 64 * kb + 32 * st
+                a_frag = [[Af[l % 16, k0 + 8 * (l // 16) + i] for i in range(8)]
+                          for l in range(64)]
+                b_frag = []
+                for l in range(64):
+                    s = float(S[k0 // 128, 16 * n16 + l % 16])
+                    vals = []
+                    for j in (2 * st, 2 * st + 1):
+                        word = int(Bp[n16, kb, l, j])
+                        for pair in (word & 0x00FF00FF, (word >> 8) & 0x00FF00FF):
+                            for code in (pair & 0xFF, pair >> 16):
+                                vals.append(_fp16_struct((code - 128) * s))
+                    b_frag.append(vals)
+                C[:, 16 * n16:16 * n16 + 16] += _mfma16x16x32_model(a_frag, b_frag)
+    _, C64 = oracle.gemm8(A, Bq8, S, 128)
+    assert np.allclose(C, C64, rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("M,K,N,group,seed", [(2, 128, 16, 128, 1), (3, 256, 24, 128, 2)])
+def test_gemm8_brute_force(M, K, N, group, seed):
+    A, _, S = make_inputs(M, K, N, group, seed)
+    Bq8 = np.random.default_rng(seed + 50).integers(0, 2**32, size=(K // 4, N), dtype=np.uint32)
+    C16, C64 = oracle.gemm8(A, Bq8, S, group)
+    for m in range(M):
+        for n in range(N):
+            total = Fraction(0)
+            for k in range(K):
+                q = (int(Bq8[k // 4, n]) >> (8 * (k % 4))) & 0xFF
+                w = _fp16_struct((q - 128) * float(S[k // group, n]))
+                total += Fraction(float(A[m, k])) * Fraction(w)
+            assert float(C16[m, n]) == _fp16_exact(total)
+            assert abs(C64[m, n] - float(total)) <= 1e-12 * max(1.0, abs(float(total)))
+
+
+def test_gemm8_all_codes_128_is_zero_and_one_hot_rows():
+    A, _, S = make_inputs(4, 256, 32, 128, seed=3)
+    Bq8 = np.full((64, 32), 0x80808080, dtype=np.uint32)
+    assert not np.any(oracle.gemm8(A, Bq8, S, 128)[1])
+    Bq8 = np.random.default_rng(4).integers(0, 2**32, size=(64, 32), dtype=np.uint32)
+    W = oracle.dequant8(Bq8, S, 128)
+    ks = [0, 3, 100, 255]
+    A1 = np.zeros((4, 256), dtype=np.float16)
+    A1[np.arange(4), ks] = 1.0
+    C, _ = oracle.gemm8(A1, Bq8, S, 128)
+    for m, k in enumerate(ks):
+        assert np.array_equal(C[m].view(np.uint16), W[k].view(np.uint16))
