@@ -102,8 +102,8 @@ def parse():
                          "torch's bias add and SiLU, write a markdown table to OUT and exit")
     ap.add_argument("--formats-report", metavar="OUT",
                     help="time the weight formats (FP16, FP16 with zero points, BF16, BF16 "
-                         "with zero points) side by side, write a markdown table to OUT "
-                         "and exit")
+                         "with zero points, 8-bit weights) side by side, write a markdown "
+                         "table to OUT and exit")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script into a traffic file and exit")
@@ -535,7 +535,7 @@ FORMAT_SHAPES = [
     ("prefill 8192x28672", 8192, 28672, [1024]),
 ]
 FORMATS = [("FP16", 0, False), ("FP16 + zero points", 0, True), ("BF16", 1, False),
-           ("BF16 + zero points", 1, True)]
+           ("BF16 + zero points", 1, True), ("8-bit weights", None, False)]
 
 
 def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
@@ -546,7 +546,7 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
 
     import weight_only_int4_gemm_amd as w4
     from weight_only_int4_gemm_amd import roofline
-    from synth import make_inputs_awq
+    from synth import make_inputs_awq, make_words
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -566,6 +566,14 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
         scales = {0: torch.from_numpy(S16.view(np.int16)).to(dev),
                   1: torch.from_numpy(Sb.view(np.int16)).to(dev)}
         zeros = torch.from_numpy(Z).to(dev)
+        # 8-bit codes: uniform words [K/4][N], repacked, with their own rotation
+        Bq8 = np.concatenate([make_words(K, N, 1), make_words(K, N, 2)])
+        Bq8_d = torch.from_numpy(Bq8.view(np.int32)).to(dev)
+        first8 = w4.alloc_packed8(K, N)
+        w4.w8a16_repack(Bq8_d, first8, K, N)
+        del Bq8_d, Bq8
+        ncopy8 = max(1, -(-ROTATE_BYTES // (K * N)))
+        copies8 = [first8] + [first8.clone() for _ in range(ncopy8 - 1)]
         for M in batches:
             A16, _, _, _ = make_inputs_awq(M, K, 8, GROUP, seed=M)
             Ab, _, _, _ = make_inputs_awq(M, K, 8, GROUP, seed=M, bf16=True)
@@ -576,6 +584,18 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
                              dtype=torch.uint8, device=dev)
 
             def form(dtype, zp):
+                if dtype is None:       # 8-bit weights, FP16 activations
+                    def call8(c):
+                        args = (acts[0].data_ptr(), c.data_ptr(), scales[0].data_ptr(),
+                                C_d.data_ptr(), M, K, N, GROUP, ws.data_ptr(), sh)
+
+                        def run():
+                            rc = lib.w8a16_gemm(*args)
+                            if rc != 0:
+                                raise RuntimeError(f"w8a16_gemm: {w4.w4a16_status_string(rc)}")
+                        return run
+                    return [call8(c) for c in copies8]
+
                 def call(c):
                     args = (acts[dtype].data_ptr(), c.data_ptr(), scales[dtype].data_ptr(),
                             zeros.data_ptr() if zp else None, C_d.data_ptr(), M, K, N, GROUP,
@@ -600,10 +620,10 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
                              plan=w4.w4a16_describe(M, K, N, GROUP).split(" workspace")[0]))
             print(json.dumps(rows[-1]), flush=True)
             del acts, C_d, ws
-        del copies, first, scales, zeros
+        del copies, first, scales, zeros, copies8, first8
         torch.cuda.empty_cache()
     lines = [
-        "# Weight formats on one MI355X: FP16, zero points, BF16",
+        "# Weight formats on one MI355X: FP16, zero points, BF16, 8-bit weights",
         "",
         "Command (repository root, GPU box): `python3 bench.py --formats-report " +
         os.path.relpath(out_path, ROOT) + "`",
@@ -612,7 +632,8 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
         f"(FP16 without zero points is the plain kernel), hipEvents around {launches} "
         f"back-to-back calls cycling over weight copies beyond 512 MB; the four formats are "
         f"timed in turn, {repeats} rounds, median per format. Zero points: uint8 per group "
-        "and column (one more byte per 64 code bytes at group 128).",
+        "and column (one more byte per 64 code bytes at group 128). 8-bit weights: "
+        "`w8a16_gemm` (twice the code bytes of 4-bit).",
         "",
         "| shape | M | " + " | ".join(f"{n} us" for n, _, _ in FORMATS) + " | plan |",
         "|---|---|" + "---|" * len(FORMATS) + "---|",

@@ -225,6 +225,39 @@ int w4a16_dequant_awq_debug(const uint32_t* Bpacked, const uint16_t* scales,
                             int dtype, void* stream);
 
 /*
+ * 8-bit weights (W8A16).  The same kernel family serves 4-bit and 8-bit
+ * checkpoints ("Low-Precision Quantization Kernels in Production", section 1
+ * on production engines; the comparison table of section 5: INT4, INT8).
+ * Codes q in 0..255 centred on 128:  w = fp16_rne((q - 128) * s), scales as
+ * for 4 bits (FP16 [K/group][N]).
+ *
+ * Canonical input Bq uint32 [K/4][N]: code k = 4j + i of column n is bits
+ * 8i..8i+7 of Bq[j][n].  Permuted layout (version 1 for 8 bits): blocks of
+ * 16 columns x 64 in-features (1 KiB), block(n16, kb64) = n16 * K/64 + kb64;
+ * in a block lane l = (n % 16) + 16 * ((k % 32) / 8) owns words 4l..4l+3,
+ * word 2 * ((k % 64) / 32) + (k % 8) / 4 holds codes k0..k0+3 (k0 % 4 == 0),
+ * code k0 + i at byte {0,2,1,3}[i].  K*N bytes.
+ */
+
+/* Bytes of the permuted 8-bit layout: K*N (0 for non-positive sizes). */
+size_t w8a16_packed_bytes(int K, int N);
+
+/* The offline permutation for 8 bits: Bq [K/4][N] -> Bpacked (K*N bytes),
+ * device to device on `stream`.  Requirements and errors as w4a16_repack. */
+int w8a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N, void* stream);
+
+/* C = A . dequant8(Bpacked, scales): arguments, layouts, workspace (the
+ * same plan and size as w4a16_workspace_bytes), alignment and errors as
+ * w4a16_gemm. */
+int w8a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales, uint16_t* C,
+               int M, int K, int N, int group, void* workspace, void* stream);
+
+/* The FP16 weights of w8a16_gemm, written out W [K][N] by the GEMM's own
+ * unpack routine.  Arguments as w4a16_dequant_debug. */
+int w8a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_t* W, int K,
+                        int N, int group, void* stream);
+
+/*
  * w4a16_dequant_debug -- W = dequant(Bpacked, scales), written out.
  *
  * Uses the same device unpack-and-scale routine as w4a16_gemm, so it shows

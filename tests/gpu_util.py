@@ -93,3 +93,25 @@ def run_gemm_awq(A: np.ndarray, Bq: np.ndarray, S: np.ndarray, Z, group: int, dt
     torch.cuda.synchronize()
     C = host_u16(C_d)
     return C if dtype else C.view(np.float16)
+
+
+def repack8_on_device(Bq8_d, K: int, N: int):
+    Bp = w4.alloc_packed8(K, N)
+    w4.w8a16_repack(Bq8_d, Bp, K, N)
+    return Bp
+
+
+def run_gemm8(A: np.ndarray, Bq8: np.ndarray, S: np.ndarray, group: int, workspace=None,
+              Bp=None):
+    """C (numpy float16) from w8a16_gemm on the given host inputs."""
+    import torch
+    M, K = A.shape
+    N = Bq8.shape[1]
+    if Bp is None:
+        Bp = repack8_on_device(dev(Bq8), K, N)
+    A_d, S_d = dev(A), dev(S)
+    C_d = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    ws = workspace if workspace is not None else w4.alloc_workspace(M, K, N, group)
+    w4.w8a16_gemm(A_d, Bp, S_d, C_d, M, K, N, group, ws)
+    torch.cuda.synchronize()
+    return host_f16(C_d)

@@ -32,7 +32,7 @@ P_BIAS = 0x60000000
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w[48]a16_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -147,6 +147,25 @@ def test_awq_entry_points_reject_bad_arguments(lib):
     for name in ("W4A16_DTYPE_F16", "W4A16_DTYPE_BF16"):
         value = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
         assert getattr(w4, name) == value, name
+
+
+def test_w8a16_entry_points(lib):
+    assert w4.w8a16_packed_bytes(4096, 4096) == 4096 * 4096
+    assert w4.w8a16_packed_bytes(0, 16) == 0
+    assert lib.w8a16_repack(None, P_B, 256, 64, None) == ERR_NULL
+    assert lib.w8a16_repack(P_A, P_B, 200, 64, None) == ERR_SHAPE
+    assert lib.w8a16_repack(P_A + 4, P_B, 256, 64, None) == ERR_ALIGN
+    assert lib.w8a16_repack(P_A, P_A + 1024, 256, 64, None) == ERR_SHAPE   # overlap (K*N bytes)
+    assert lib.w8a16_gemm(P_A, P_B, P_S, P_C, 4, 100, 64, 128, None, None) == ERR_SHAPE
+    assert lib.w8a16_gemm(P_A, P_B, P_S, P_C, 4, 256, 64, 96, None, None) == ERR_GROUP
+    assert lib.w8a16_gemm(None, P_B, P_S, P_C, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert lib.w8a16_gemm(P_A, P_B, P_S, P_C + 2, 4, 256, 64, 128, None, None) == ERR_ALIGN
+    # C overlapping the 8-bit codes (K*N bytes, twice the 4-bit size)
+    assert lib.w8a16_gemm(P_A, P_B, P_S, P_B + 256 * 64 - 64, 4, 256, 64, 128, None,
+                          None) == ERR_SHAPE
+    assert lib.w8a16_gemm(None, None, None, None, 0, 256, 64, 128, None, None) == OK
+    assert lib.w8a16_dequant_debug(None, P_S, P_W, 256, 64, 128, None) == ERR_NULL
+    assert lib.w8a16_dequant_debug(P_B, P_S, P_W, 256, 64, 96, None) == ERR_GROUP
 
 
 def test_repack_and_dequant_reject_bad_arguments(lib):

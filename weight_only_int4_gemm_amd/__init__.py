@@ -13,6 +13,10 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
                    workspace, stream=None)
     w4a16_dequant_awq_debug(Bpacked, scales, zeros, W, K, N, group, dtype,
                             stream=None)
+    w8a16_repack(Bq8, Bpacked, K, N, stream=None)
+    w8a16_gemm(A, Bpacked, scales, C, M, K, N, group, workspace, stream=None)
+    w8a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
+    w8a16_packed_bytes(K, N)
     w4a16_workspace_bytes(M, K, N, group)
     w4a16_packed_bytes(K, N)
     w4a16_layout_version()
@@ -31,6 +35,7 @@ __all__ = [
     "w4a16_repack", "w4a16_gemm", "w4a16_gemm_fused", "w4a16_dequant_debug",
     "W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU",
     "w4a16_gemm_awq", "w4a16_dequant_awq_debug", "W4A16_DTYPE_F16", "W4A16_DTYPE_BF16",
+    "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug", "w8a16_packed_bytes",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
     "w4a16_status_string", "w4a16_describe", "EXPORTED_SYMBOLS",
 ]
@@ -50,6 +55,7 @@ EXPORTED_SYMBOLS = (
     "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_workspace_bytes", "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
     "w4a16_describe", "w4a16_gemm_fused", "w4a16_gemm_awq", "w4a16_dequant_awq_debug",
+    "w8a16_packed_bytes", "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug",
 )
 
 
@@ -100,6 +106,14 @@ def load():
     lib.w4a16_gemm_awq.restype = i
     lib.w4a16_dequant_awq_debug.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.w4a16_dequant_awq_debug.restype = i
+    lib.w8a16_packed_bytes.argtypes = [i, i]
+    lib.w8a16_packed_bytes.restype = sz
+    lib.w8a16_repack.argtypes = [vp, vp, i, i, vp]
+    lib.w8a16_repack.restype = i
+    lib.w8a16_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp]
+    lib.w8a16_gemm.restype = i
+    lib.w8a16_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.w8a16_dequant_debug.restype = i
     lib.w4a16_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.w4a16_dequant_debug.restype = i
     lib.w4a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
@@ -243,6 +257,40 @@ def w4a16_dequant_awq_debug(Bpacked, scales, zeros, W, K: int, N: int, group: in
                                           _stream(stream)))
 
 
+def w8a16_packed_bytes(K: int, N: int) -> int:
+    return load().w8a16_packed_bytes(int(K), int(N))
+
+
+def w8a16_repack(Bq8, Bpacked, K: int, N: int, stream=None) -> None:
+    import torch
+    _expect(Bq8, torch.int32, "Bq8")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _check("w8a16_repack", load().w8a16_repack(_ptr(Bq8), _ptr(Bpacked), int(K), int(N),
+                                               _stream(stream)))
+
+
+def w8a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
+               workspace=None, stream=None) -> None:
+    import torch
+    _expect(A, torch.float16, "A")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(C, torch.float16, "C")
+    _check("w8a16_gemm", load().w8a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
+                                           int(M), int(K), int(N), int(group),
+                                           _ptr(workspace), _stream(stream)))
+
+
+def w8a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int, stream=None) -> None:
+    import torch
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(W, torch.float16, "W")
+    _check("w8a16_dequant_debug",
+           load().w8a16_dequant_debug(_ptr(Bpacked), _ptr(scales), _ptr(W), int(K), int(N),
+                                      int(group), _stream(stream)))
+
+
 def w4a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,
                         stream=None) -> None:
     import torch
@@ -271,3 +319,9 @@ def alloc_packed(K: int, N: int, device=None):
     """An int32 tensor of ``w4a16_packed_bytes(K, N)`` bytes for repacked codes."""
     import torch
     return torch.empty(K * N // 8, dtype=torch.int32, device=device or "cuda")
+
+
+def alloc_packed8(K: int, N: int, device=None):
+    """An int32 tensor of ``w8a16_packed_bytes(K, N)`` bytes for repacked 8-bit codes."""
+    import torch
+    return torch.empty(K * N // 4, dtype=torch.int32, device=device or "cuda")

@@ -7,6 +7,7 @@
 #include <cstdlib>
 
 #include "../../include/w4a16.h"
+#include "format.hpp"
 #include "internal.hpp"
 #include "layout.hpp"
 
@@ -387,8 +388,9 @@ int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* sca
       (bias && !aligned16(bias)) || (zeros && !aligned16(zeros)))
     return W4A16_ERR_ALIGN;
   const size_t cbytes = (size_t)M * N * 2;
+  const size_t pbytes = fmt == kFmtW8 ? (size_t)K * N : w4a16_packed_bytes(K, N);
   if (overlap(C, cbytes, A, (size_t)M * K * 2) ||
-      overlap(C, cbytes, Bpacked, w4a16_packed_bytes(K, N)) ||
+      overlap(C, cbytes, Bpacked, pbytes) ||
       overlap(C, cbytes, scales, (size_t)(K / group) * N * 2) ||
       (bias && overlap(C, cbytes, bias, (size_t)N * 2)) ||
       (zeros && overlap(C, cbytes, zeros, (size_t)(K / group) * N)))
@@ -428,6 +430,45 @@ int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scale
                void* stream) {
   return gemm_checked(A, Bpacked, scales, nullptr, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
                       0, workspace, stream);
+}
+
+size_t w8a16_packed_bytes(int K, int N) {
+  if (K <= 0 || N <= 0) return 0;
+  return (size_t)K * (size_t)N;
+}
+
+int w8a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N, void* stream) {
+  if (!Bq || !Bpacked) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bq) || !aligned16(Bpacked)) return W4A16_ERR_ALIGN;
+  const size_t bytes = w8a16_packed_bytes(K, N);
+  if (overlap(Bq, bytes, Bpacked, bytes)) return W4A16_ERR_SHAPE;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  if (launch_repack8(Bq, Bpacked, K, N, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+int w8a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_t* W, int K,
+                        int N, int group, void* stream) {
+  if (!Bpacked || !scales || !W) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bpacked) || !aligned16(scales) || !aligned16(W)) return W4A16_ERR_ALIGN;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  if (launch_dequant_fmt(Bpacked, scales, nullptr, W, K, N, group, kFmtW8,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+int w8a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales, uint16_t* C,
+               int M, int K, int N, int group, void* workspace, void* stream) {
+  return gemm_checked(A, Bpacked, scales, nullptr, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
+                      kFmtW8, workspace, stream);
 }
 
 int w4a16_gemm_awq(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,

@@ -46,10 +46,40 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   }
 }
 
+// 8-bit codes: one wave per 16-column x 64-deep block; lane l's four words
+// hold its operands of the block's two 32-deep steps (words 2s, 2s+1).
+__global__ __launch_bounds__(256) void dequant8_kernel(const uint32_t* __restrict__ Bp,
+                                                       const _Float16* __restrict__ S,
+                                                       _Float16* __restrict__ W,
+                                                       int K, int N, int group) {
+  const int KB = K / kBlockK8;
+  const int64_t blocks = (int64_t)(N / kBlockN) * KB;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t wstride = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t blk = wave0; blk < blocks; blk += wstride) {
+    const int n16 = (int)(blk / KB);
+    const int kb = (int)(blk % KB);
+    const int n = n16 * kBlockN + (lane & 15);
+    const uint4 words =
+        *reinterpret_cast<const uint4*>(Bp + block_word_offset8(n16, kb, K) + lane * 4);
+    const _Float16 s = S[(int64_t)(kb * kBlockK8 / group) * N + n];
+    const half2_t s2 = {s, s};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      Half8 h;
+      h.v = unpack8_scale(st ? words.z : words.x, st ? words.w : words.y, s2);
+      const int k0 = kb * kBlockK8 + 32 * st + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) W[(int64_t)(k0 + i) * N + n] = h.v[i];
+    }
+  }
+}
+
 hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8_t* Z,
                               uint16_t* W, int K, int N, int group, int fmt,
                               hipStream_t stream) {
-  const int64_t blocks = (int64_t)(N / kBlockN) * (K / kBlockK);
+  const int64_t blocks = (int64_t)(N / kBlockN) * (K / (fmt == kFmtW8 ? kBlockK8 : kBlockK));
   int64_t wgs = (blocks + 3) / 4;   // four waves per workgroup
   if (wgs > 65536) wgs = 65536;
   auto s = reinterpret_cast<const _Float16*>(S);
@@ -70,6 +100,9 @@ hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8
     case kFmtBf16Zp:
       hipLaunchKernelGGL(dequant_kernel<kFmtBf16Zp>, grid, block, 0, stream, Bp, s, Z, w, K, N,
                          group);
+      break;
+    case kFmtW8:
+      hipLaunchKernelGGL(dequant8_kernel, grid, block, 0, stream, Bp, s, w, K, N, group);
       break;
     default:
       return hipErrorInvalidValue;

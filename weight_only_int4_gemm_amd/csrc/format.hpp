@@ -13,6 +13,8 @@
 //   1  FP16, zero point z per (group, column):   w = fp16_rne((q - z) * s)
 //   2  BF16 activations, scales and output:      w = bf16_rne((q - 8) * s)
 //   3  BF16 with zero points:                    w = bf16_rne((q - z) * s)
+//   4  FP16, 8-bit codes centred on 128:         w = fp16_rne((q - 128) * s)
+//      (same page, section 1: the kernel serves 4-bit and 8-bit checkpoints)
 //
 // In every format (q - z) is an integer in -15..15 and the product with the
 // scale is exact before its one rounding to the 16-bit type.
@@ -40,13 +42,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_fmt_t __attribute__((ext_vector_type(4)));
 
-enum : int { kFmtF16 = 0, kFmtF16Zp = 1, kFmtBf16 = 2, kFmtBf16Zp = 3 };
+enum : int { kFmtF16 = 0, kFmtF16Zp = 1, kFmtBf16 = 2, kFmtBf16Zp = 3, kFmtW8 = 4 };
 
 template <int FMT>
 struct Format {
-  static_assert(FMT >= 0 && FMT <= 3, "four formats");
-  static constexpr bool kBf16 = FMT >= 2;
-  static constexpr bool kZp = (FMT & 1) != 0;
+  static_assert(FMT >= 0 && FMT <= 4, "five formats");
+  static constexpr bool kBf16 = FMT == kFmtBf16 || FMT == kFmtBf16Zp;
+  static constexpr bool kZp = FMT == kFmtF16Zp || FMT == kFmtBf16Zp;
+  static constexpr bool kW8 = FMT == kFmtW8;  // two code words per 32-deep step
 };
 
 // What the unpack of one (group, column) needs, made once per K block and
@@ -62,7 +65,7 @@ template <int FMT>
 __device__ __forceinline__ ColParams make_col(half2_t s2, uint32_t z) {
   ColParams p;
   p.s2 = s2;
-  if constexpr (FMT != kFmtF16) {
+  if constexpr (FMT != kFmtF16 && FMT != kFmtW8) {
     const _Float16 lo = (_Float16)(float)(1024u + z);  // exact: integers to 2048
     const _Float16 hi = (_Float16)(float)(64u + z);    // exact: quarter units above 256
     p.zlo = half2_t{lo, lo};
@@ -129,6 +132,27 @@ __device__ __forceinline__ half8_t unpack_col(uint32_t word, const ColParams& p)
     return unpack_scale_zp(word, p.s2, p.zlo, p.zhi);
   else
     return unpack_scale_bf16(word, p.s, p.zlo, p.zhi);
+}
+
+// 8-bit codes: the eight FP16 weights (q - 128) * s of one 32-deep step
+// from its two words.  A byte code OR-ed into 1024.0 (0x6400, mantissa unit
+// 1, ten mantissa bits) gives 1024 + q exactly; the mask 0x00FF00FF keeps
+// bytes 0 and 2 (codes k, k+1 in the layout), the same mask after a shift
+// by 8 bytes 1 and 3 (codes k+2, k+3); subtracting 1152 = 1024 + 128 is
+// exact and the multiply by the scale rounds once.  14 instructions per
+// eight weights.
+__device__ __forceinline__ half8_t unpack8_scale(uint32_t w0, uint32_t w1, half2_t scale2) {
+#pragma clang fp contract(off)
+  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  Half8 raw;
+  raw.u[0] = and_or(w0, 0x00FF00FFu, 0x64006400u);        // codes k, k+1
+  raw.u[1] = and_or(w0 >> 8, 0x00FF00FFu, 0x64006400u);   // codes k+2, k+3
+  raw.u[2] = and_or(w1, 0x00FF00FFu, 0x64006400u);        // codes k+4, k+5
+  raw.u[3] = and_or(w1 >> 8, 0x00FF00FFu, 0x64006400u);   // codes k+6, k+7
+  Half8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out.h2[i] = (raw.h2[i] - bias) * scale2;
+  return out.v;
 }
 
 // One 16x16x32 matrix instruction on raw 16-bit fragments.

@@ -37,7 +37,7 @@ namespace w4a16 {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-template <int MB, int NB, bool ZP>
+template <int MB, int NB, bool ZP, bool W8>
 struct Slot {
   uint4 b[NB];         // permuted codes: one 128-deep K block per column block
   half2_t s[NB];       // the group scale of this lane's column, in both halves
@@ -45,11 +45,20 @@ struct Slot {
 };
 // With zero points: the group zero point of this lane's column as well.
 template <int MB, int NB>
-struct Slot<MB, NB, true> {
+struct Slot<MB, NB, true, false> {
   uint4 b[NB];
   half2_t s[NB];
   half8_t a[MB][4];
   uint32_t z[NB];
+};
+// 8-bit codes: a 128-deep K block is two 16-byte pieces per column block
+// (b: steps 0 and 1, b2: steps 2 and 3).
+template <int MB, int NB>
+struct Slot<MB, NB, false, true> {
+  uint4 b[NB];
+  half2_t s[NB];
+  half8_t a[MB][4];
+  uint4 b2[NB];
 };
 
 // FMT: the weight format (format.hpp); formats other than 0 are compiled
@@ -63,6 +72,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
     float* __restrict__ partials, Epilogue ep, const uint8_t* __restrict__ Z) {
   static_assert(!EPI || FMT == kFmtF16, "the fused epilogue is FP16 only");
   constexpr bool ZP = Format<FMT>::kZp;
+  constexpr bool W8 = Format<FMT>::kW8;
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
@@ -115,7 +125,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n16 = n16_0 + (nb < nvalid ? nb : nvalid - 1);
-    bcol[nb] = Bp + block_word_offset(n16, 0, K) + lane * kWordsPerLane;
+    bcol[nb] = Bp + (W8 ? block_word_offset8(n16, 0, K) : block_word_offset(n16, 0, K)) +
+               lane * kWordsPerLane;
     scol[nb] = S + n16 * kBlockN + l16;
     if constexpr (ZP) zcol[nb] = Z + n16 * kBlockN + l16;
   }
@@ -126,11 +137,18 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   auto scale_row = [&](int kb) -> int {
     return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
   };
-  auto load = [&](Slot<MB, NB, ZP>& sl, int kb) {
+  auto load = [&](Slot<MB, NB, ZP, W8>& sl, int kb) {
     const int srow = scale_row(kb) * N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + kb * kWordsPerBlock);
+      if constexpr (W8) {
+        // the two 64-deep blocks of this 128-deep K block
+        sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + 2 * kb * kWordsPerBlock);
+        sl.b2[nb] =
+            *reinterpret_cast<const uint4*>(bcol[nb] + (2 * kb + 1) * kWordsPerBlock);
+      } else {
+        sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + kb * kWordsPerBlock);
+      }
       const _Float16 sc = scol[nb][srow];
       sl.s[nb] = half2_t{sc, sc};
       if constexpr (ZP) sl.z[nb] = zcol[nb][srow];
@@ -141,18 +159,24 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
       for (int j = 0; j < 4; ++j)
         sl.a[mb][j] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
   };
-  auto compute = [&](const Slot<MB, NB, ZP>& sl) {
+  auto compute = [&](const Slot<MB, NB, ZP, W8>& sl) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // (column blocks past N recompute the last valid block; the store
         // drops them -- a branch here would stall the load pipeline)
-        const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
-                         : j == 2 ? sl.b[nb].z : sl.b[nb].w;
-        uint32_t z = 8;
-        if constexpr (ZP) z = sl.z[nb];
-        const half8_t b = unpack_col<FMT>(w, make_col<FMT>(sl.s[nb], z));
+        half8_t b;
+        if constexpr (W8) {
+          const uint4& pc = j < 2 ? sl.b[nb] : sl.b2[nb];
+          b = unpack8_scale((j & 1) ? pc.z : pc.x, (j & 1) ? pc.w : pc.y, sl.s[nb]);
+        } else {
+          const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
+                           : j == 2 ? sl.b[nb].z : sl.b[nb].w;
+          uint32_t z = 8;
+          if constexpr (ZP) z = sl.z[nb];
+          b = unpack_col<FMT>(w, make_col<FMT>(sl.s[nb], z));
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mma16<FMT>(sl.a[mb][j], b, acc[mb][nb]);
       }
@@ -167,7 +191,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(
   const int nblk = first < kb1 ? (kb1 - first + WK - 1) / WK : 0;
   if (nblk > 0) {
     const int last = first + (nblk - 1) * WK;
-    Slot<MB, NB, ZP> slot[D];
+    Slot<MB, NB, ZP, W8> slot[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int kb = first + u * WK;
@@ -367,6 +391,9 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
     if (wf.fmt == kFmtBf16Zp)                                                             \
       return launch_one<MB_, NB_, WK_, D_, kFmtBf16Zp>(p, A, Bp, S, C, M, K, N, gmagic,   \
                                                        ep, wf.zeros, workspace, stream);  \
+    if (wf.fmt == kFmtW8)                                                                 \
+      return launch_one<MB_, NB_, WK_, D_, kFmtW8>(p, A, Bp, S, C, M, K, N, gmagic, ep,    \
+                                                   nullptr, workspace, stream);           \
   }
   W4A16_FMT_VARIANTS(W4A16_FCASE)
 #undef W4A16_FCASE

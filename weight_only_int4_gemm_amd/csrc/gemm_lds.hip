@@ -56,6 +56,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
   static_assert(FMT == kFmtF16 || (F == 16 && !EPI), "formats 1-3: 16 x 16 blocks, no epilogue");
   constexpr bool ZP = Format<FMT>::kZp;
+  constexpr int PPB = Format<FMT>::kW8 ? 2 : 1;  // 1 KiB pieces per code block and K block
   constexpr int WAVES = WM * WN;
   constexpr int TM = F * MB * WM;
   constexpr int TN = F * NB * WN;
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // fewer chunks (blocks) than waves some are loaded twice (same bytes to
   // the same place), so every wave issues the same number of loads
   constexpr int ALOADS = (ACHUNKS + WAVES - 1) / WAVES;
-  constexpr int BLOADS = (BLOCKS + WAVES - 1) / WAVES;
-  constexpr int BPIECES = BLOCKS * 64;         // 16-byte pieces of codes
+  constexpr int BLOADS = (BLOCKS * PPB + WAVES - 1) / WAVES;
+  constexpr int BPIECES = BLOCKS * PPB * 64;   // 16-byte pieces of codes
   constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
   constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
   constexpr int ZLOADS = ZP ? (TN / 4 + 63) / 64 : 0;  // zero points: 4-byte loads, all waves
@@ -113,16 +114,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   LaneBias<NB, F, EPI> bias;
   bias.load(ep, wcol0, N);
 
-  // Code blocks this wave loads: tile block (wave + WAVES * i) % BLOCKS for
-  // load i (blocks past N re-read the last valid one; their columns are
-  // dropped at the store).
+  // Code pieces this wave loads: piece (wave + WAVES * i) % (BLOCKS * PPB)
+  // of the stage for load i, i.e. tile block piece / PPB and, for 8-bit
+  // codes, its 64-deep half piece % PPB (blocks past N re-read the last
+  // valid one; their columns are dropped at the store).
   const uint32_t* bsrc[BLOADS];
   int bblk[BLOADS];
 #pragma unroll
   for (int i = 0; i < BLOADS; ++i) {
-    bblk[i] = (wave + WAVES * i) % BLOCKS;
-    const int n16 = tile_n * BLOCKS + bblk[i];
-    bsrc[i] = Bp + block_word_offset(n16 <= n16_last ? n16 : n16_last, 0, K) +
+    bblk[i] = (wave + WAVES * i) % (BLOCKS * PPB);
+    const int n16 = tile_n * BLOCKS + bblk[i] / PPB;
+    const int n16c = n16 <= n16_last ? n16 : n16_last;
+    bsrc[i] = Bp +
+              (PPB == 2 ? block_word_offset8(n16c, bblk[i] % 2, K) : block_word_offset(n16c, 0, K)) +
               lane * kWordsPerLane;
   }
   // Scale source: word i*64 + lane of the stage holds columns 2w, 2w+1.
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     }
 #pragma unroll
     for (int i = 0; i < BLOADS; ++i) {
-      __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[i] + kb * kWordsPerBlock),
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[i] + PPB * kb * kWordsPerBlock),
                                        (lds_ptr_t)&sg.b[64 * bblk[i]], 16, 0, 0);
     }
     const int srow = scale_row(kb) * N;
@@ -199,11 +203,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // unpacked, so the vector ALU work has independent matrix work to overlap.
   auto compute16 = [&](const Stage& sg) {
     uint4 w[NB];
+    uint4 w2[PPB == 2 ? NB : 1];  // 8-bit codes: the second 64-deep half
     ColParams cp[NB];
     const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      w[nb] = sg.b[64 * (wn * NB + nb) + lane];
+      w[nb] = sg.b[64 * PPB * (wn * NB + nb) + lane];
+      if constexpr (PPB == 2) w2[nb] = sg.b[64 * (2 * (wn * NB + nb) + 1) + lane];
       const int c = wn * 16 * NB + nb * 16 + l16;
       const _Float16 sc = sh[c];
       uint32_t z = 8;
@@ -213,8 +219,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     auto unpack_slice = [&](int j, half8_t* bf) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const uint32_t word = j == 0 ? w[nb].x : j == 1 ? w[nb].y : j == 2 ? w[nb].z : w[nb].w;
-        bf[nb] = unpack_col<FMT>(word, cp[nb]);
+        if constexpr (PPB == 2) {
+          const uint4& pc = j < 2 ? w[nb] : w2[nb];
+          bf[nb] = unpack8_scale((j & 1) ? pc.z : pc.x, (j & 1) ? pc.w : pc.y, cp[nb].s2);
+        } else {
+          const uint32_t word =
+              j == 0 ? w[nb].x : j == 1 ? w[nb].y : j == 2 ? w[nb].z : w[nb].w;
+          bf[nb] = unpack_col<FMT>(word, cp[nb]);
+        }
       }
     };
     half8_t a0[MB], a1[MB];
@@ -419,6 +431,16 @@ bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f) {
   return false;
 }
 
+// Stages for 8-bit codes, whose code pieces are twice the size: as many of
+// the plan's NS as fit in the 160 KiB of LDS (the same tiles, splits and
+// workspace; only the pipeline depth differs).
+constexpr int w8_stages(int mb, int nb, int wm, int wn, int ns) {
+  const int tm = 16 * mb * wm, tn = 16 * nb * wn;
+  const int stage = tm * 256 + nb * wn * 2 * 1024 + (tn / 2 + 63) / 64 * 256;
+  while (ns > 2 && ns * stage > 160 * 1024) --ns;
+  return ns;
+}
+
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
                       Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream) {
@@ -445,6 +467,10 @@ hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
     if (wf.fmt == kFmtBf16Zp)                                                                 \
       return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtBf16Zp>(                         \
           p, A, Bp, S, C, M, K, N, gmagic, ep, wf.zeros, workspace, stream);                  \
+    if (wf.fmt == kFmtW8)                                                                     \
+      return launch_lds_one<MB_, NB_, WM_, WN_, w8_stages(MB_, NB_, WM_, WN_, NS_), 16,       \
+                            kFmtW8>(p, A, Bp, S, C, M, K, N, gmagic, ep, nullptr, workspace,  \
+                                    stream);                                                  \
   }
   W4A16_LDS_FMT_VARIANTS(W4A16_LFCASE)
 #undef W4A16_LFCASE

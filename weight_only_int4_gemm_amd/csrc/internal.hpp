@@ -45,8 +45,9 @@ struct Epilogue {
 };
 
 // The weight format of a call (format.hpp): 0 FP16, 1 FP16 with zero
-// points, 2 BF16, 3 BF16 with zero points; `zeros` are the zero points
-// uint8[K/group][N] of formats 1 and 3 (null otherwise).
+// points, 2 BF16, 3 BF16 with zero points, 4 FP16 with 8-bit weights;
+// `zeros` are the zero points uint8[K/group][N] of formats 1 and 3 (null
+// otherwise).
 struct WeightFormat {
   int fmt;
   const uint8_t* zeros;
@@ -59,6 +60,8 @@ bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);
+hipError_t launch_repack8(const uint32_t* Bq, uint32_t* Bp, int K, int N,
+                          hipStream_t stream);
 hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
                           int K, int N, int group, hipStream_t stream);
 hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,

@@ -38,6 +38,30 @@ __host__ __device__ inline int64_t block_word_offset(int n16, int kb, int K) {
 
 // Word offset (within the whole buffer) that holds the eight codes
 // k0 .. k0+7 of column n, for k0 a multiple of 8.
+// 8-bit weights (layout version 1 for 8 bits): blocks of 16 columns x 64
+// in-features, 1 KiB each, column-block-major then along K.  In a block,
+// lane l = (n % 16) + 16 * ((k % 32) / 8) owns words 4l .. 4l+3, word
+// 2 * ((k % 64) / 32) + (k % 8) / 4 holds codes k0 .. k0+3 (k0 a multiple
+// of 4), code k0 + i at byte byte_of_code8(i).  A lane's 16-byte piece holds
+// its operands of two 32-deep steps; a 128-deep K block is two pieces.
+constexpr int kBlockK8 = 64;
+
+__host__ __device__ inline int byte_of_code8(int i) {
+  // {0,2,1,3}: codes k, k+1 in bytes 0 and 2 (one mask pairs them in the two
+  // halves of a register), codes k+2, k+3 in bytes 1 and 3
+  return (i >> 1) + ((i & 1) << 1);
+}
+
+__host__ __device__ inline int64_t block_word_offset8(int n16, int kb64, int K) {
+  return ((int64_t)n16 * (K / kBlockK8) + kb64) * kWordsPerBlock;
+}
+
+__host__ __device__ inline int64_t packed_word_of8(int k0, int n, int K) {
+  const int lane = (n % kBlockN) + kBlockN * ((k0 % 32) / 8);
+  const int j = 2 * ((k0 % kBlockK8) / 32) + (k0 % 8) / 4;
+  return block_word_offset8(n / kBlockN, k0 / kBlockK8, K) + lane * kWordsPerLane + j;
+}
+
 __host__ __device__ inline int64_t packed_word_of(int k0, int n, int K) {
   const int n16 = n / kBlockN;
   const int kb = k0 / kBlockK;

@@ -34,6 +34,38 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t* __restrict_
   }
 }
 
+// 8 bits: canonical byte i (code k0 + i) -> byte byte_of_code8(i); every
+// canonical word is exactly one permuted word.
+__device__ __forceinline__ uint32_t shuffle_bytes(uint32_t w) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out |= ((w >> (8 * i)) & 0xFFu) << (8 * byte_of_code8(i));
+  return out;
+}
+
+__global__ __launch_bounds__(256) void repack8_kernel(const uint32_t* __restrict__ Bq,
+                                                      uint32_t* __restrict__ Bp,
+                                                      int K, int N) {
+  const int64_t total = (int64_t)(K / 4) * N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += stride) {
+    const int j = (int)(idx / N);   // canonical word row: codes 4j .. 4j+3
+    const int n = (int)(idx % N);
+    Bp[packed_word_of8(4 * j, n, K)] = shuffle_bytes(Bq[idx]);
+  }
+}
+
+hipError_t launch_repack8(const uint32_t* Bq, uint32_t* Bp, int K, int N,
+                          hipStream_t stream) {
+  const int64_t total = (int64_t)(K / 4) * N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(repack8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     Bq, Bp, K, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream) {
   const int64_t total = (int64_t)(K / 8) * N;
