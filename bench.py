@@ -629,9 +629,9 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
         os.path.relpath(out_path, ROOT) + "`",
         "",
         f"Kernel source hash: `{kernel_source_hash()}`. Each format through `w4a16_gemm_awq` "
-        f"(FP16 without zero points is the plain kernel), hipEvents around {launches} "
+        f"(FP16 without zero points is the plain kernel) or `w8a16_gemm`, hipEvents around {launches} "
         f"back-to-back calls cycling over weight copies beyond 512 MB; the four formats are "
-        f"timed in turn, {repeats} rounds, median per format. Zero points: uint8 per group "
+        f"timed in turn, {repeats} rounds, median per format (the five formats interleaved). Zero points: uint8 per group "
         "and column (one more byte per 64 code bytes at group 128). 8-bit weights: "
         "`w8a16_gemm` (twice the code bytes of 4-bit).",
         "",

@@ -64,8 +64,12 @@ struct Slot<MB, NB, false, true> {
 // FMT: the weight format (format.hpp); formats other than 0 are compiled
 // without the fused epilogue.  A, S and C hold raw 16-bit values (FP16, or
 // BF16 for formats 2 and 3); Z the zero points of formats 1 and 3.
+// (BF16 without zero points: the compiler's own choice for the deepest
+// variant kept one wave per SIMD; the hint asks for the two it gets in the
+// other formats.)
 template <int MB, int NB, int WK, int D, bool EPI, int FMT>
-__global__ __launch_bounds__(64 * WK) void gemm_kernel(
+__global__ __launch_bounds__(64 * WK)
+__attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
