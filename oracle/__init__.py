@@ -24,6 +24,9 @@ plain numpy, with no blocking, fusion or reordering beyond that description:
   (BF16): zero points and BF16 (``dequant_awq``, ``gemm_awq``); section 1
   and the same table (4-bit and 8-bit checkpoints): 8-bit weights
   (``dequant8``, ``gemm8``, ``repack8``).
+* "The anthology of the SOTA" (dmarx.github.io), the MARLIN note, "Key
+  results" (Figure 15, Sparse-MARLIN): the 2:4 sparse variant
+  (``dequant_sparse24``, ``gemm_sparse24``, ``repack_sparse24``).
 
 Readings where the pages leave a step open (zero point 8, LSB-first nibble
 order along K, scale layout ``[K/group][N]``, single RNE rounding of the
@@ -61,4 +64,8 @@ from .w4a16_ref import (  # noqa: F401
     gemm8,
     repack8,
     unrepack8,
+    sparse24_keep,
+    dequant_sparse24,
+    gemm_sparse24,
+    repack_sparse24,
 )

@@ -487,3 +487,106 @@ def unrepack8(Bp: np.ndarray, K: int, N: int) -> np.ndarray:
     byte = np.array(_BYTE_OF_CODE8, dtype=np.uint32)[k % 4]
     q = (Bp[word] >> (np.uint32(8) * byte)) & np.uint32(0xFF)
     return pack_codes8(q)
+
+
+# ---------------------------------------------------------------------------
+# 2:4 structured sparsity (Sparse-MARLIN).  "The anthology of the SOTA"
+# (dmarx.github.io), the MARLIN note, section "Key results" (the serving
+# benchmark of Figure 15: a Sparse-MARLIN variant beside MARLIN).
+#
+# Readings (the pages give no format):
+# 15. In every group of four consecutive in-features of a column at most two
+#     weights are kept; the others are exactly zero.  The input is the dense
+#     canonical codes Bq [K/8][N] plus a mask uint8 [K/4][N] whose bits 0..3
+#     mark the kept in-features 4g + i.  The two kept positions are the two
+#     lowest set bits; with fewer than two bits set the missing slots take
+#     the lowest unset positions and code 8 (weight 0); bits beyond the two
+#     lowest are ignored.  Kept weights are fp16_rne((q - 8) * s) as before.
+# 16. The permuted layout (this library's own, version 1 for 2:4): per block
+#     of 16 columns x 128 in-features, 768 bytes: first 64 lanes x 8 bytes of
+#     codes, then 64 lanes x 4 bytes of positions.  Lane l = (n % 16) +
+#     16 * ((k % 64) // 16) of a block holds, for the 64-deep half t = (k %
+#     128) // 64, the eight kept codes of in-features 64t + 16 * (l // 16)
+#     .. +15 (two per group of four, ascending) in code word t, slot i at
+#     nibble {0,4,1,5,2,6,3,7}[i], and their positions in the group (0..3)
+#     at bits 16t + 2i .. +1 of its position word.
+# ---------------------------------------------------------------------------
+
+def _kept_positions(mask: np.ndarray):
+    """(p0, p1, valid0, valid1) for each group: the two kept positions and
+    whether each comes from a set mask bit (reading 15)."""
+    m = np.asarray(mask, dtype=np.uint8) & np.uint8(0xF)
+    bits = np.stack([(m >> np.uint8(i)) & np.uint8(1) for i in range(4)], axis=-1).astype(bool)
+    order = np.argsort(~bits, axis=-1, kind="stable")     # set bits first, ascending
+    p0, p1 = order[..., 0], order[..., 1]
+    v0 = np.take_along_axis(bits, p0[..., None], -1)[..., 0]
+    v1 = np.take_along_axis(bits, p1[..., None], -1)[..., 0]
+    lo = np.minimum(p0, p1)
+    hi = np.maximum(p0, p1)
+    vlo = np.where(p0 < p1, v0, v1)
+    vhi = np.where(p0 < p1, v1, v0)
+    return lo, hi, vlo, vhi
+
+
+def sparse24_keep(mask: np.ndarray) -> np.ndarray:
+    """Boolean keep[K][N]: the weights that are not pruned (reading 15)."""
+    lo, hi, vlo, vhi = _kept_positions(mask)
+    G, N = lo.shape
+    keep = np.zeros((G, 4, N), dtype=bool)
+    gi, ni = np.meshgrid(np.arange(G), np.arange(N), indexing="ij")
+    keep[gi, lo, ni] = vlo
+    keep[gi, hi, ni] = vhi
+    return keep.reshape(G * 4, N)
+
+
+def dequant_sparse24(Bq: np.ndarray, mask: np.ndarray, S: np.ndarray, group: int) -> np.ndarray:
+    """FP16 weights with the pruned ones exactly zero (+0)."""
+    W = dequant(Bq, S, group)
+    return np.where(sparse24_keep(mask), W, np.float16(0.0)).astype(np.float16)
+
+
+def gemm_sparse24(A, Bq, mask, S, group: int, cols=None):
+    """``(C16, C64)`` of the 2:4-sparse product; with ``cols``, only those
+    output columns."""
+    if cols is not None:
+        cols = np.asarray(cols, dtype=np.int64)
+        Bq = np.ascontiguousarray(Bq[:, cols])
+        mask = np.ascontiguousarray(np.asarray(mask)[:, cols])
+        S = np.ascontiguousarray(np.asarray(S)[:, cols])
+    W = dequant_sparse24(Bq, mask, S, group)
+    C64 = np.asarray(A, dtype=np.float16).astype(np.float64) @ W.astype(np.float64)
+    return C64.astype(np.float16), C64
+
+
+def repack_sparse24(Bq: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Permuted 2:4 words (flat uint32, K*N*3/32 of them: 192 per block of 16
+    columns x 128 in-features) from dense codes and mask (readings 15, 16)."""
+    q = unpack_codes(Bq)
+    K, N = q.shape
+    if K % 128 or N % 16:
+        raise ValueError("K must be a multiple of 128 and N of 16")
+    lo, hi, vlo, vhi = _kept_positions(mask)          # [K/4][N]
+    G = K // 4
+    gi = np.arange(G)[:, None]
+    ni = np.arange(N)[None, :]
+    c_lo = np.where(vlo, q[4 * gi + lo, ni], ZERO_POINT).astype(np.uint32)
+    c_hi = np.where(vhi, q[4 * gi + hi, ni], ZERO_POINT).astype(np.uint32)
+    KB = K // 128
+    out = np.zeros((N // 16) * KB * 192, dtype=np.uint32)
+    g = np.arange(G)[:, None] * np.ones((1, N), dtype=np.int64)
+    n = np.ones((G, 1), dtype=np.int64) * np.arange(N)[None, :]
+    k0 = 4 * g                                  # first in-feature of the group
+    base = ((n // 16) * KB + k0 // 128) * 192
+    lane = (n % 16) + 16 * ((k0 % 64) // 16)
+    t = (k0 % 128) // 64
+    slot0 = 2 * ((k0 % 16) // 4)                # slots 2r, 2r+1 of group r of the lane
+    nib = np.array([0, 4, 1, 5, 2, 6, 3, 7], dtype=np.uint32)
+    code_word = base + 2 * lane + t
+    pos_word = base + 128 + lane
+    for slot_off, code, pos in ((0, c_lo, lo), (1, c_hi, hi)):
+        sl = (slot0 + slot_off).astype(np.int64)
+        np.bitwise_or.at(out, code_word.ravel(), (code << (np.uint32(4) * nib[sl])).ravel())
+        np.bitwise_or.at(out, pos_word.ravel(),
+                         (pos.astype(np.uint32) << (np.uint32(16) * t.astype(np.uint32) +
+                                                    np.uint32(2) * sl.astype(np.uint32))).ravel())
+    return out

@@ -783,3 +783,101 @@ def test_gemm8_all_codes_128_is_zero_and_one_hot_rows():
     C, _ = oracle.gemm8(A1, Bq8, S, 128)
     for m, k in enumerate(ks):
         assert np.array_equal(C[m].view(np.uint16), W[k].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# 2:4 sparsity
+# ---------------------------------------------------------------------------
+
+def test_sparse24_keep_worked_masks():
+    """Hand-worked masks: two set bits keep exactly those; more than two keep
+    the lowest two; fewer keep only what is set."""
+    cases = {0b0011: [1, 1, 0, 0], 0b1010: [0, 1, 0, 1], 0b1100: [0, 0, 1, 1],
+             0b1111: [1, 1, 0, 0], 0b1110: [0, 1, 1, 0], 0b0100: [0, 0, 1, 0],
+             0b0000: [0, 0, 0, 0], 0b1001: [1, 0, 0, 1], 0xF5: [1, 0, 1, 0]}
+    for m, want in cases.items():
+        keep = oracle.sparse24_keep(np.array([[m]], dtype=np.uint8))
+        assert list(keep[:, 0].astype(int)) == want, bin(m)
+
+
+def test_dequant_sparse24_zeros_the_pruned_weights():
+    from synth import make_inputs
+    _, Bq, S = make_inputs(1, 256, 32, 128, seed=40)
+    mask = np.random.default_rng(41).integers(0, 16, size=(64, 32)).astype(np.uint8)
+    W = oracle.dequant(Bq, S, 128)
+    Ws = oracle.dequant_sparse24(Bq, mask, S, 128)
+    keep = oracle.sparse24_keep(mask)
+    assert keep.sum(axis=0).max() <= 128            # at most two of four
+    assert np.array_equal(Ws[keep].view(np.uint16), W[keep].view(np.uint16))
+    assert np.all(Ws[~keep].view(np.uint16) == 0)
+    assert np.all(keep.reshape(64, 4, 32).sum(axis=1) <= 2)
+
+
+def test_repack_sparse24_feeds_the_sparse_instruction():
+    """Consume the 2:4 words the way a wave does and recover A . W.
+
+    The sparse 16x16x64 instruction, as the hardware computes it: operand S
+    (16 x 64) from 64 lanes of eight values and a position word -- lane L
+    gives row L % 16, slot i lands at column 16 (L // 16) + 4 (i // 2) + p,
+    p = bits 2i..2i+1 of its position word; operand D (64 x 16): lane l gives
+    column l % 16, element j at row 32 (j // 8) + 8 (l // 16) + j % 8.  Here
+    S is the weights' transposed block (rows = output columns) and D the
+    activations' (columns = batch rows), so the result is C transposed."""
+    from synth import make_inputs
+    M, K, N = 16, 256, 32
+    A, Bq, S = make_inputs(M, K, N, 128, seed=42)
+    mask = np.random.default_rng(43).integers(0, 16, size=(K // 4, N)).astype(np.uint8)
+    Bp = oracle.repack_sparse24(Bq, mask).reshape(N // 16, K // 128, 192)
+    Af = A.astype(np.float64)
+    Ct = np.zeros((N, M))
+    for n16 in range(N // 16):
+        for kb in range(K // 128):
+            blk = Bp[n16, kb]
+            for t in range(2):
+                Sm = np.zeros((16, 64))
+                for L in range(64):
+                    code_word = int(blk[2 * L + t])
+                    pos_word = int(blk[128 + L]) >> (16 * t)
+                    s = float(S[kb, 16 * n16 + L % 16])
+                    for i in range(8):
+                        nib = (i >> 1) + ((i & 1) << 2)
+                        q = (code_word >> (4 * nib)) & 0xF
+                        p = (pos_word >> (2 * i)) & 3
+                        Sm[L % 16, 16 * (L // 16) + 4 * (i // 2) + p] += _fp16_struct((q - 8) * s)
+                Dm = np.zeros((64, 16))
+                for l in range(64):
+                    for j in range(16):
+                        Dm[32 * (j // 8) + 8 * (l // 16) + j % 8, l % 16] = \
+                            Af[l % 16, 128 * kb + 64 * t + 32 * (j // 8) + 8 * (l // 16) + j % 8]
+                Ct[16 * n16:16 * n16 + 16, :] += Sm @ Dm
+    _, C64 = oracle.gemm_sparse24(A, Bq, mask, S, 128)
+    assert np.allclose(Ct.T, C64, rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(2, 128, 16, 1), (3, 256, 16, 2)])
+def test_gemm_sparse24_brute_force(M, K, N, seed):
+    from synth import make_inputs
+    A, Bq, S = make_inputs(M, K, N, 128, seed)
+    mask = np.random.default_rng(seed + 60).integers(0, 16, size=(K // 4, N)).astype(np.uint8)
+    C16, C64 = oracle.gemm_sparse24(A, Bq, mask, S, 128)
+    for m in range(M):
+        for n in range(N):
+            total = Fraction(0)
+            for g in range(K // 4):
+                bits = [b for b in range(4) if (int(mask[g, n]) >> b) & 1][:2]
+                for b in bits:
+                    k = 4 * g + b
+                    q = (int(Bq[k // 8, n]) >> (4 * (k % 8))) & 0xF
+                    total += Fraction(float(A[m, k])) * Fraction(_fp16_struct((q - 8) * float(S[k // 128, n])))
+            assert float(C16[m, n]) == _fp16_exact(total)
+
+
+def test_gemm_sparse24_empty_mask_is_zero_and_full_mask_keeps_two():
+    from synth import make_inputs
+    A, Bq, S = make_inputs(4, 256, 32, 128, seed=44)
+    zero = np.zeros((64, 32), dtype=np.uint8)
+    assert not np.any(oracle.gemm_sparse24(A, Bq, zero, S, 128)[1])
+    full = np.full((64, 32), 0xF, dtype=np.uint8)
+    two = np.full((64, 32), 0b0011, dtype=np.uint8)
+    assert np.array_equal(oracle.gemm_sparse24(A, Bq, full, S, 128)[1],
+                          oracle.gemm_sparse24(A, Bq, two, S, 128)[1])
