@@ -258,6 +258,70 @@ int w8a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_
                         int N, int group, void* stream);
 
 /*
+ * 2:4 structured sparsity (Sparse-MARLIN).  The pages report a Sparse-MARLIN
+ * variant serving beside MARLIN ("The anthology of the SOTA", the MARLIN
+ * note, section "Key results"); they give no format, so this one is the
+ * library's own:
+ *
+ *   in every group of four consecutive in-features k = 4g .. 4g+3 of a
+ *   column at most two weights are kept, the others are exactly zero; the
+ *   kept ones are fp16_rne((q - 8) * s) as in w4a16_gemm.
+ *
+ * Input: the dense canonical codes Bq uint32 [K/8][N] (as for w4a16_repack)
+ * and a mask uint8 [K/4][N] whose bits 0..3 mark the kept in-features
+ * 4g + i.  A group keeps its two lowest set bits; with fewer than two bits
+ * set it keeps only those (bits above the lowest two are ignored).
+ *
+ * Permuted layout (version 1 for 2:4), 768 bytes per block of 16 columns x
+ * 128 in-features, block(n16, kb) = n16 * K/128 + kb: words 0..127 of a
+ * block hold codes, words 128..191 positions.  Lane l = (n % 16) +
+ * 16 * ((k % 64) / 16) owns code words 2l + t (t = (k % 128) / 64) and
+ * position word 128 + l.  Code word t holds the two kept codes of each of
+ * the lane's four groups (slots 2r, 2r+1 for group r, lower in-feature
+ * first) with slot i at nibble {0,4,1,5,2,6,3,7}[i]; bits 16t + 2i .. +1 of
+ * the position word hold slot i's position in its group (0..3).  A group
+ * with fewer than two kept weights fills its free slot with code 8 at its
+ * lowest unused position.  K * N * 3 / 8 bytes: three quarters of the dense
+ * 4-bit layout.
+ */
+
+/* Bytes of the permuted 2:4 layout: K * N * 3 / 8 (0 for non-positive sizes). */
+size_t w4a16_sparse24_packed_bytes(int K, int N);
+
+/* The offline compression and permutation: Bq uint32 [K/8][N] and mask
+ * uint8 [K/4][N] (device, read) -> Bpacked (device, write,
+ * w4a16_sparse24_packed_bytes(K, N) bytes) on `stream`.  K a positive
+ * multiple of 128, N of 16; all three pointers 16-byte aligned; Bpacked
+ * must not overlap Bq or mask (W4A16_ERR_SHAPE).  Other errors as
+ * w4a16_repack. */
+int w4a16_sparse24_repack(const uint32_t* Bq, const uint8_t* mask, uint32_t* Bpacked, int K,
+                          int N, void* stream);
+
+/* Workspace bytes of w4a16_sparse24_gemm for this shape (its plans differ
+ * from the dense ones); contract as w4a16_workspace_bytes. */
+size_t w4a16_sparse24_workspace_bytes(int M, int K, int N, int group);
+
+/* The plan of w4a16_sparse24_gemm for this shape, as w4a16_describe. */
+int w4a16_sparse24_describe(int M, int K, int N, int group, char* buf, size_t len);
+
+/* C = A . W with W the 2:4-sparse weights of Bpacked (pruned weights 0),
+ * computed by the sparse matrix instruction (half the multiplies of the
+ * dense product).  Arguments, layouts, numerics, alignment and errors as
+ * w4a16_gemm, with Bpacked from w4a16_sparse24_repack and the workspace
+ * sized by w4a16_sparse24_workspace_bytes. */
+int w4a16_sparse24_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                        uint16_t* C, int M, int K, int N, int group, void* workspace,
+                        void* stream);
+
+/* The weights of w4a16_sparse24_gemm, written out densely: W FP16 [K][N],
+ * each kept weight as the GEMM's own unpack routine makes it, +0 at every
+ * position no slot names.  (A free slot, code 8 at an unused position,
+ * gives (8 - 8) * s: -0 there when s < 0.)  Arguments and errors as
+ * w4a16_dequant_debug. */
+int w4a16_sparse24_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_t* W,
+                                 int K, int N, int group, void* stream);
+
+/*
  * w4a16_dequant_debug -- W = dequant(Bpacked, scales), written out.
  *
  * Uses the same device unpack-and-scale routine as w4a16_gemm, so it shows

@@ -25,6 +25,12 @@ Recipe (the same for every shape):
   rounding rule is shared with the code under test); values are carried as
   uint16 bit patterns.
 
+* 2:4 masks (``make_mask24``, its own generator): uint8 ``[K/4][N]``.  By
+  default each byte is one of the six patterns with exactly two of bits
+  0..3 set, uniformly (the pruning the sparse format stores); with
+  ``exact=False`` any byte 0..255 (groups with fewer or more set bits, and
+  set bits above bit 3).
+
 The value distributions are the ones the workload description gives: a
 Gaussian activation, uniform codes, and small positive scales, one per group
 of 128 (or one per column when the group is the whole of K).
@@ -90,3 +96,18 @@ def make_inputs_awq(M: int, K: int, N: int, group: int = 128, seed: int = 0,
         A = A32.astype(np.float16)
         S = S64.astype(np.float16)
     return A, Bq, S, Z
+
+
+# The six 4-bit patterns with exactly two bits set, in increasing order.
+TWO_OF_FOUR = np.array([0b0011, 0b0101, 0b0110, 0b1001, 0b1010, 0b1100], dtype=np.uint8)
+
+
+def make_mask24(K: int, N: int, seed: int = 0, exact: bool = True):
+    """A 2:4 mask ``uint8[K/4][N]``: uniform over the six two-of-four
+    patterns, or (``exact=False``) uniform bytes."""
+    if K % 4:
+        raise ValueError(f"bad shape K={K}")
+    rng = np.random.default_rng(seed)
+    if exact:
+        return TWO_OF_FOUR[rng.integers(0, 6, size=(K // 4, N))]
+    return rng.integers(0, 256, size=(K // 4, N), dtype=np.uint8)

@@ -115,3 +115,25 @@ def run_gemm8(A: np.ndarray, Bq8: np.ndarray, S: np.ndarray, group: int, workspa
     w4.w8a16_gemm(A_d, Bp, S_d, C_d, M, K, N, group, ws)
     torch.cuda.synchronize()
     return host_f16(C_d)
+
+
+def repack_sp24_on_device(Bq_d, mask_d, K: int, N: int):
+    Bp = w4.alloc_packed_sparse24(K, N)
+    w4.w4a16_sparse24_repack(Bq_d, mask_d, Bp, K, N)
+    return Bp
+
+
+def run_gemm_sp24(A: np.ndarray, Bq: np.ndarray, mask: np.ndarray, S: np.ndarray, group: int,
+                  workspace=None, Bp=None):
+    """C (numpy float16) from w4a16_sparse24_gemm on the given host inputs."""
+    import torch
+    M, K = A.shape
+    N = Bq.shape[1]
+    if Bp is None:
+        Bp = repack_sp24_on_device(dev(Bq), dev(mask), K, N)
+    A_d, S_d = dev(A), dev(S)
+    C_d = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    ws = workspace if workspace is not None else w4.alloc_workspace_sparse24(M, K, N, group)
+    w4.w4a16_sparse24_gemm(A_d, Bp, S_d, C_d, M, K, N, group, ws)
+    torch.cuda.synchronize()
+    return host_f16(C_d)

@@ -168,6 +168,39 @@ def test_w8a16_entry_points(lib):
     assert lib.w8a16_dequant_debug(P_B, P_S, P_W, 256, 64, 96, None) == ERR_GROUP
 
 
+def test_sparse24_entry_points(lib):
+    P_MASK = 0x70000000
+    assert w4.w4a16_sparse24_packed_bytes(4096, 4096) == 4096 * 4096 * 3 // 8
+    assert w4.w4a16_sparse24_packed_bytes(0, 16) == 0
+    r = lib.w4a16_sparse24_repack
+    assert r(None, P_MASK, P_B, 256, 64, None) == ERR_NULL
+    assert r(P_A, None, P_B, 256, 64, None) == ERR_NULL
+    assert r(P_A, P_MASK, None, 256, 64, None) == ERR_NULL
+    assert r(P_A, P_MASK, P_B, 200, 64, None) == ERR_SHAPE
+    assert r(P_A, P_MASK, P_B, 256, 8, None) == ERR_SHAPE
+    assert r(P_A, P_MASK + 4, P_B, 256, 64, None) == ERR_ALIGN
+    # the packed words overlapping the codes or the mask
+    assert r(P_A, P_MASK, P_A + 16, 256, 64, None) == ERR_SHAPE
+    assert r(P_A, P_MASK, P_MASK + 4096 - 16, 256, 64, None) == ERR_SHAPE
+    g = lib.w4a16_sparse24_gemm
+    assert g(P_A, P_B, P_S, P_C, 4, 100, 64, 128, None, None) == ERR_SHAPE
+    assert g(P_A, P_B, P_S, P_C, 4, 256, 64, 96, None, None) == ERR_GROUP
+    assert g(None, P_B, P_S, P_C, 4, 256, 64, 128, None, None) == ERR_NULL
+    assert g(P_A, P_B, P_S, P_C + 2, 4, 256, 64, 128, None, None) == ERR_ALIGN
+    # C overlapping the packed 2:4 codes (K * N * 3 / 8 bytes)
+    assert g(P_A, P_B, P_S, P_B + 256 * 64 * 3 // 8 - 64, 4, 256, 64, 128, None,
+             None) == ERR_SHAPE
+    assert g(None, None, None, None, 0, 256, 64, 128, None, None) == OK
+    d = lib.w4a16_sparse24_dequant_debug
+    assert d(None, P_S, P_W, 256, 64, 128, None) == ERR_NULL
+    assert d(P_B, P_S, P_W, 256, 64, 96, None) == ERR_GROUP
+    assert d(P_B, P_S + 2, P_W, 256, 64, 128, None) == ERR_ALIGN
+    assert lib.w4a16_sparse24_workspace_bytes(4, 100, 64, 128) == 0
+    buf = ctypes.create_string_buffer(64)
+    assert lib.w4a16_sparse24_describe(4, 100, 64, 128, buf, 64) == ERR_SHAPE
+    assert lib.w4a16_sparse24_describe(4, 256, 64, 128, None, 64) == ERR_NULL
+
+
 def test_repack_and_dequant_reject_bad_arguments(lib):
     assert lib.w4a16_repack(None, P_B, 256, 64, None) == ERR_NULL
     assert lib.w4a16_repack(P_A, P_B, 200, 64, None) == ERR_SHAPE

@@ -17,6 +17,13 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
     w8a16_gemm(A, Bpacked, scales, C, M, K, N, group, workspace, stream=None)
     w8a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
     w8a16_packed_bytes(K, N)
+    w4a16_sparse24_repack(Bq, mask, Bpacked, K, N, stream=None)
+    w4a16_sparse24_gemm(A, Bpacked, scales, C, M, K, N, group, workspace,
+                        stream=None)
+    w4a16_sparse24_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
+    w4a16_sparse24_packed_bytes(K, N)
+    w4a16_sparse24_workspace_bytes(M, K, N, group)
+    w4a16_sparse24_describe(M, K, N, group)
     w4a16_workspace_bytes(M, K, N, group)
     w4a16_packed_bytes(K, N)
     w4a16_layout_version()
@@ -36,6 +43,8 @@ __all__ = [
     "W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU",
     "w4a16_gemm_awq", "w4a16_dequant_awq_debug", "W4A16_DTYPE_F16", "W4A16_DTYPE_BF16",
     "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug", "w8a16_packed_bytes",
+    "w4a16_sparse24_repack", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
+    "w4a16_sparse24_packed_bytes", "w4a16_sparse24_workspace_bytes", "w4a16_sparse24_describe",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
     "w4a16_status_string", "w4a16_describe", "EXPORTED_SYMBOLS",
 ]
@@ -56,6 +65,8 @@ EXPORTED_SYMBOLS = (
     "w4a16_workspace_bytes", "w4a16_repack", "w4a16_gemm", "w4a16_dequant_debug",
     "w4a16_describe", "w4a16_gemm_fused", "w4a16_gemm_awq", "w4a16_dequant_awq_debug",
     "w8a16_packed_bytes", "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug",
+    "w4a16_sparse24_packed_bytes", "w4a16_sparse24_repack", "w4a16_sparse24_workspace_bytes",
+    "w4a16_sparse24_describe", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
 )
 
 
@@ -118,6 +129,18 @@ def load():
     lib.w4a16_dequant_debug.restype = i
     lib.w4a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
     lib.w4a16_describe.restype = i
+    lib.w4a16_sparse24_packed_bytes.argtypes = [i, i]
+    lib.w4a16_sparse24_packed_bytes.restype = sz
+    lib.w4a16_sparse24_repack.argtypes = [vp, vp, vp, i, i, vp]
+    lib.w4a16_sparse24_repack.restype = i
+    lib.w4a16_sparse24_workspace_bytes.argtypes = [i, i, i, i]
+    lib.w4a16_sparse24_workspace_bytes.restype = sz
+    lib.w4a16_sparse24_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
+    lib.w4a16_sparse24_describe.restype = i
+    lib.w4a16_sparse24_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp]
+    lib.w4a16_sparse24_gemm.restype = i
+    lib.w4a16_sparse24_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.w4a16_sparse24_dequant_debug.restype = i
     _lib = lib
     return lib
 
@@ -302,6 +325,55 @@ def w4a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,
                                       int(group), _stream(stream)))
 
 
+def w4a16_sparse24_packed_bytes(K: int, N: int) -> int:
+    return load().w4a16_sparse24_packed_bytes(int(K), int(N))
+
+
+def w4a16_sparse24_workspace_bytes(M: int, K: int, N: int, group: int) -> int:
+    return load().w4a16_sparse24_workspace_bytes(int(M), int(K), int(N), int(group))
+
+
+def w4a16_sparse24_describe(M: int, K: int, N: int, group: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check("w4a16_sparse24_describe",
+           load().w4a16_sparse24_describe(int(M), int(K), int(N), int(group), buf, 256))
+    return buf.value.decode()
+
+
+def w4a16_sparse24_repack(Bq, mask, Bpacked, K: int, N: int, stream=None) -> None:
+    import torch
+    _expect(Bq, torch.int32, "Bq")
+    _expect(mask, torch.uint8, "mask")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _check("w4a16_sparse24_repack",
+           load().w4a16_sparse24_repack(_ptr(Bq), _ptr(mask), _ptr(Bpacked), int(K), int(N),
+                                        _stream(stream)))
+
+
+def w4a16_sparse24_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
+                        workspace=None, stream=None) -> None:
+    import torch
+    _expect(A, torch.float16, "A")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(C, torch.float16, "C")
+    _check("w4a16_sparse24_gemm",
+           load().w4a16_sparse24_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C), int(M),
+                                      int(K), int(N), int(group), _ptr(workspace),
+                                      _stream(stream)))
+
+
+def w4a16_sparse24_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,
+                                 stream=None) -> None:
+    import torch
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(W, torch.float16, "W")
+    _check("w4a16_sparse24_dequant_debug",
+           load().w4a16_sparse24_dequant_debug(_ptr(Bpacked), _ptr(scales), _ptr(W), int(K),
+                                               int(N), int(group), _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # allocation conveniences (torch owns the memory; the library allocates none)
 # ---------------------------------------------------------------------------
@@ -325,3 +397,18 @@ def alloc_packed8(K: int, N: int, device=None):
     """An int32 tensor of ``w8a16_packed_bytes(K, N)`` bytes for repacked 8-bit codes."""
     import torch
     return torch.empty(K * N // 4, dtype=torch.int32, device=device or "cuda")
+
+
+def alloc_packed_sparse24(K: int, N: int, device=None):
+    """An int32 tensor of ``w4a16_sparse24_packed_bytes(K, N)`` bytes for 2:4 codes."""
+    import torch
+    return torch.empty(K * N * 3 // 32, dtype=torch.int32, device=device or "cuda")
+
+
+def alloc_workspace_sparse24(M: int, K: int, N: int, group: int, device=None):
+    """A zero-filled workspace of ``w4a16_sparse24_workspace_bytes`` bytes, or None."""
+    import torch
+    nbytes = w4a16_sparse24_workspace_bytes(M, K, N, group)
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")

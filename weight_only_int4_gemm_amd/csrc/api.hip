@@ -63,7 +63,8 @@ int check_group(int K, int group) {
   return W4A16_OK;
 }
 
-bool variant_is_compiled(const Plan& q) {
+bool variant_is_compiled(const Plan& q, int fmt) {
+  if (fmt == kFmtSp24) return q.tile == 0 && q.wm == 1 && sp_is_compiled(q.mb, q.nb, q.wk, q.depth);
   if (q.tile >= 2)
     return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth, q.tile == 3 ? 32 : 16);
   if (q.wm != 1) return false;
@@ -79,7 +80,7 @@ bool variant_is_compiled(const Plan& q) {
 // the LDS kernel with 32 x 32 blocks).  It feeds the same kernels;
 // w4a16_workspace_bytes sees it too, so sizes stay consistent within a
 // process.
-void apply_forced_plan(Plan* p, int KB) {
+void apply_forced_plan(Plan* p, int KB, int fmt) {
   const char* env = std::getenv("W4A16_FORCE_PLAN");
   if (!env || !*env) return;
   int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0, bdepth = 0, wm = 0;
@@ -96,15 +97,55 @@ void apply_forced_plan(Plan* p, int KB) {
   if (depth > 0) q.depth = depth;
   q.bdepth = bdepth > 0 ? bdepth : (q.tile == 1 ? 4 : 0);
   q.wm = wm > 0 ? wm : 1;
-  if (!variant_is_compiled(q)) {
+  if (!variant_is_compiled(q, fmt)) {
     // keep the forced tile but take the first compiled depth for it
     for (int d : {4, 3, 2, 1}) {
       q.depth = d;
-      if (variant_is_compiled(q)) break;
+      if (variant_is_compiled(q, fmt)) break;
     }
   }
-  if (!variant_is_compiled(q)) return;
+  if (!variant_is_compiled(q, fmt)) return;
   *p = q;
+}
+
+// The plan of one call as one line of text (w4a16_describe).
+int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len) {
+  if (!buf || len == 0) return W4A16_ERR_NULL;
+  buf[0] = 0;
+  if (M <= 0 || N == 0) return W4A16_ERR_SHAPE;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  const int cus = current_cus(nullptr);
+  if (cus <= 0) return W4A16_ERR_DEVICE;
+  const Plan p = make_plan(M, K, N, group, cus, fmt);
+  if (p.tile >= 2)
+    std::snprintf(buf, len,
+                  "gemm_lds_kernel<%d,%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
+                  "workspace=%zu",
+                  p.mb, p.nb, p.wm, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
+                  p.splits, 64 * p.wm * p.wk, p.splits, p.workspace_bytes);
+  else if (p.tile)
+    std::snprintf(buf, len,
+                  "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
+                  "workspace=%zu",
+                  p.mb, p.nb, p.wk, p.depth, p.bdepth, p.tiles_n, p.tiles_m, p.splits,
+                  64 * p.wk, p.splits, p.workspace_bytes);
+  else
+    std::snprintf(buf, len,
+                  "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                  p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
+                  p.splits, p.workspace_bytes);
+  return W4A16_OK;
+}
+
+size_t workspace_fmt(int M, int K, int N, int group, int fmt) {
+  if (M <= 0 || N == 0) return 0;
+  if (check_kn(K, N, false) != W4A16_OK || check_group(K, group) != W4A16_OK) return 0;
+  const int cus = current_cus(nullptr);
+  if (cus <= 0) return 0;
+  return make_plan(M, K, N, group, cus, fmt).workspace_bytes;
 }
 
 }  // namespace
@@ -122,14 +163,25 @@ void apply_forced_plan(Plan* p, int KB) {
 // only as far as needed to give every compute unit work, keeping at least
 // two K blocks per wave.  Larger batches go to the LDS kernel with 64 or 128
 // rows per wave, so each weight is unpacked once for many rows.
-Plan make_plan(int M, int K, int N, int group, int cus) {
+//
+// 2:4-sparse weights (format 5) run the streaming kernel at every batch
+// size: the small-batch plans as for dense weights, and above that 32- to
+// 128-row tiles (wider row tiles re-read fewer activation fragments per
+// weight).
+Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   (void)group;
   Plan p{};
   p.wm = 1;
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
   if (cus <= 0) cus = 256;
-  if (M <= 4 || (M <= 16 && N < 8192)) {
+  const bool sparse = fmt == kFmtSp24;
+  if (sparse && !(M <= 4 || (M <= 16 && N < 8192))) {
+    p.mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    p.nb = p.mb >= 8 ? 2 : 4;
+    p.wk = 4;
+    p.depth = p.mb >= 4 ? 1 : 2;
+  } else if (M <= 4 || (M <= 16 && N < 8192)) {
     // streaming kernel: activations straight from global memory
     p.mb = 1;
     if (M <= 4) {
@@ -240,7 +292,7 @@ Plan make_plan(int M, int K, int N, int group, int cus) {
   if (want > cap) want = cap;
   if (want > 64) want = 64;
   p.splits = (int)(want < 1 ? 1 : want);
-  apply_forced_plan(&p, KB);
+  apply_forced_plan(&p, KB, fmt);
   shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
   p.workspace_bytes = 0;
@@ -281,42 +333,11 @@ size_t w4a16_packed_bytes(int K, int N) {
 }
 
 size_t w4a16_workspace_bytes(int M, int K, int N, int group) {
-  if (M <= 0 || N == 0) return 0;
-  if (check_kn(K, N, false) != W4A16_OK || check_group(K, group) != W4A16_OK) return 0;
-  const int cus = current_cus(nullptr);
-  if (cus <= 0) return 0;
-  return make_plan(M, K, N, group, cus).workspace_bytes;
+  return workspace_fmt(M, K, N, group, kFmtF16);
 }
 
 int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
-  if (!buf || len == 0) return W4A16_ERR_NULL;
-  buf[0] = 0;
-  if (M <= 0 || N == 0) return W4A16_ERR_SHAPE;
-  int rc = check_kn(K, N, false);
-  if (rc != W4A16_OK) return rc;
-  rc = check_group(K, group);
-  if (rc != W4A16_OK) return rc;
-  const int cus = current_cus(nullptr);
-  if (cus <= 0) return W4A16_ERR_DEVICE;
-  const Plan p = make_plan(M, K, N, group, cus);
-  if (p.tile >= 2)
-    std::snprintf(buf, len,
-                  "gemm_lds_kernel<%d,%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
-                  "workspace=%zu",
-                  p.mb, p.nb, p.wm, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
-                  p.splits, 64 * p.wm * p.wk, p.splits, p.workspace_bytes);
-  else if (p.tile)
-    std::snprintf(buf, len,
-                  "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
-                  "workspace=%zu",
-                  p.mb, p.nb, p.wk, p.depth, p.bdepth, p.tiles_n, p.tiles_m, p.splits,
-                  64 * p.wk, p.splits, p.workspace_bytes);
-  else
-    std::snprintf(buf, len,
-                  "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
-                  p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
-                  p.splits, p.workspace_bytes);
-  return W4A16_OK;
+  return describe_fmt(M, K, N, group, kFmtF16, buf, len);
 }
 
 int w4a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N, void* stream) {
@@ -373,7 +394,8 @@ namespace {
 
 // The GEMM behind every entry point: argument checks, then the plan and the
 // launch.  fmt is a weight format of format.hpp (0: FP16, 1: FP16 with zero
-// points, 2: BF16, 3: BF16 with zero points).
+// points, 2: BF16, 3: BF16 with zero points, 4: 8-bit codes, 5: 2:4-sparse
+// codes).
 int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
                  const uint8_t* zeros, const uint16_t* bias, int activation, uint16_t* C,
                  int M, int K, int N, int group, int fmt, void* workspace, void* stream) {
@@ -388,7 +410,9 @@ int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* sca
       (bias && !aligned16(bias)) || (zeros && !aligned16(zeros)))
     return W4A16_ERR_ALIGN;
   const size_t cbytes = (size_t)M * N * 2;
-  const size_t pbytes = fmt == kFmtW8 ? (size_t)K * N : w4a16_packed_bytes(K, N);
+  const size_t pbytes = fmt == kFmtW8     ? (size_t)K * N
+                        : fmt == kFmtSp24 ? w4a16_sparse24_packed_bytes(K, N)
+                                          : w4a16_packed_bytes(K, N);
   if (overlap(C, cbytes, A, (size_t)M * K * 2) ||
       overlap(C, cbytes, Bpacked, pbytes) ||
       overlap(C, cbytes, scales, (size_t)(K / group) * N * 2) ||
@@ -397,7 +421,7 @@ int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* sca
     return W4A16_ERR_SHAPE;
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
-  const Plan plan = make_plan(M, K, N, group, cus);
+  const Plan plan = make_plan(M, K, N, group, cus, fmt);
   if (plan.workspace_bytes > 0) {
     if (!workspace) return W4A16_ERR_WORKSPACE;
     if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
@@ -478,6 +502,59 @@ int w4a16_gemm_awq(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* s
   const int fmt = (dtype == W4A16_DTYPE_BF16 ? 2 : 0) + (zeros ? 1 : 0);
   return gemm_checked(A, Bpacked, scales, zeros, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
                       fmt, workspace, stream);
+}
+
+size_t w4a16_sparse24_packed_bytes(int K, int N) {
+  if (K <= 0 || N <= 0) return 0;
+  return (size_t)K * (size_t)N / 8 * 3;
+}
+
+int w4a16_sparse24_repack(const uint32_t* Bq, const uint8_t* mask, uint32_t* Bpacked, int K,
+                          int N, void* stream) {
+  if (!Bq || !mask || !Bpacked) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bq) || !aligned16(mask) || !aligned16(Bpacked)) return W4A16_ERR_ALIGN;
+  const size_t qbytes = w4a16_packed_bytes(K, N);
+  const size_t mbytes = (size_t)K * N / 4;
+  const size_t pbytes = w4a16_sparse24_packed_bytes(K, N);
+  if (overlap(Bq, qbytes, Bpacked, pbytes) || overlap(mask, mbytes, Bpacked, pbytes))
+    return W4A16_ERR_SHAPE;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  if (launch_repack_sp24(Bq, mask, Bpacked, K, N, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
+}
+
+size_t w4a16_sparse24_workspace_bytes(int M, int K, int N, int group) {
+  return workspace_fmt(M, K, N, group, kFmtSp24);
+}
+
+int w4a16_sparse24_describe(int M, int K, int N, int group, char* buf, size_t len) {
+  return describe_fmt(M, K, N, group, kFmtSp24, buf, len);
+}
+
+int w4a16_sparse24_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                        uint16_t* C, int M, int K, int N, int group, void* workspace,
+                        void* stream) {
+  return gemm_checked(A, Bpacked, scales, nullptr, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
+                      kFmtSp24, workspace, stream);
+}
+
+int w4a16_sparse24_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_t* W,
+                                 int K, int N, int group, void* stream) {
+  if (!Bpacked || !scales || !W) return W4A16_ERR_NULL;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  if (!aligned16(Bpacked) || !aligned16(scales) || !aligned16(W)) return W4A16_ERR_ALIGN;
+  if (current_cus(nullptr) <= 0) return W4A16_ERR_DEVICE;
+  if (launch_dequant_fmt(Bpacked, scales, nullptr, W, K, N, group, kFmtSp24,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4A16_ERR_LAUNCH;
+  return W4A16_OK;
 }
 
 }  // extern "C"

@@ -76,6 +76,48 @@ __global__ __launch_bounds__(256) void dequant8_kernel(const uint32_t* __restric
   }
 }
 
+// 2:4 sparsity: one wave per 768-byte block; lane l reads its two code
+// words and its position word as the GEMM does, unpacks each code word with
+// the GEMM's routine and writes its column's sixteen in-features of each
+// 64-deep half: slot i's weight at position 4 (i / 2) + p_i, +0 at the two
+// positions of each group of four that hold no slot.
+__global__ __launch_bounds__(256) void dequant_sp24_kernel(const uint32_t* __restrict__ Bp,
+                                                           const _Float16* __restrict__ S,
+                                                           _Float16* __restrict__ W, int K,
+                                                           int N, int group) {
+  const int KB = K / kBlockK;
+  const int64_t blocks = (int64_t)(N / kBlockN) * KB;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t wstride = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t blk = wave0; blk < blocks; blk += wstride) {
+    const int n16 = (int)(blk / KB);
+    const int kb = (int)(blk % KB);
+    const int n = n16 * kBlockN + (lane & 15);
+    const uint32_t* base = Bp + block_word_offset_sp(n16, kb, K);
+    const uint2 codes = *reinterpret_cast<const uint2*>(base + 2 * lane);
+    const uint32_t pos = base[kCodeWordsSp + lane];
+    const _Float16 s = S[(int64_t)(kb * kBlockK / group) * N + n];
+    const half2_t s2 = {s, s};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      Half8 h;
+      h.v = unpack_col<kFmtSp24>(t ? codes.y : codes.x, make_col<kFmtSp24>(s2, 8u));
+      const uint32_t p = pos >> (16 * t);
+      const int k0 = kb * kBlockK + 64 * t + 16 * (lane >> 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int plo = (p >> (4 * r)) & 3, phi = (p >> (4 * r + 2)) & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const _Float16 v = plo == j ? h.v[2 * r] : phi == j ? h.v[2 * r + 1] : (_Float16)0.f;
+          W[(int64_t)(k0 + 4 * r + j) * N + n] = v;
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8_t* Z,
                               uint16_t* W, int K, int N, int group, int fmt,
                               hipStream_t stream) {
@@ -103,6 +145,9 @@ hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8
       break;
     case kFmtW8:
       hipLaunchKernelGGL(dequant8_kernel, grid, block, 0, stream, Bp, s, w, K, N, group);
+      break;
+    case kFmtSp24:
+      hipLaunchKernelGGL(dequant_sp24_kernel, grid, block, 0, stream, Bp, s, w, K, N, group);
       break;
     default:
       return hipErrorInvalidValue;

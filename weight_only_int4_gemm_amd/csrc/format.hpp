@@ -15,6 +15,11 @@
 //   3  BF16 with zero points:                    w = bf16_rne((q - z) * s)
 //   4  FP16, 8-bit codes centred on 128:         w = fp16_rne((q - 128) * s)
 //      (same page, section 1: the kernel serves 4-bit and 8-bit checkpoints)
+//   5  FP16, 2:4-sparse 4-bit codes: at most two kept weights in every four
+//      consecutive in-features of a column, w = fp16_rne((q - 8) * s) for
+//      the kept ones ("The anthology of the SOTA", the MARLIN note, "Key
+//      results": the Sparse-MARLIN variant), multiplied by the sparse matrix
+//      instruction with the weights as its compressed operand
 //
 // In every format (q - z) is an integer in -15..15 and the product with the
 // scale is exact before its one rounding to the 16-bit type.
@@ -42,14 +47,15 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_fmt_t __attribute__((ext_vector_type(4)));
 
-enum : int { kFmtF16 = 0, kFmtF16Zp = 1, kFmtBf16 = 2, kFmtBf16Zp = 3, kFmtW8 = 4 };
+enum : int { kFmtF16 = 0, kFmtF16Zp = 1, kFmtBf16 = 2, kFmtBf16Zp = 3, kFmtW8 = 4, kFmtSp24 = 5 };
 
 template <int FMT>
 struct Format {
-  static_assert(FMT >= 0 && FMT <= 4, "five formats");
+  static_assert(FMT >= 0 && FMT <= 5, "six formats");
   static constexpr bool kBf16 = FMT == kFmtBf16 || FMT == kFmtBf16Zp;
   static constexpr bool kZp = FMT == kFmtF16Zp || FMT == kFmtBf16Zp;
   static constexpr bool kW8 = FMT == kFmtW8;  // two code words per 32-deep step
+  static constexpr bool kSp = FMT == kFmtSp24;  // compressed 2:4 codes + positions
 };
 
 // What the unpack of one (group, column) needs, made once per K block and
@@ -65,7 +71,7 @@ template <int FMT>
 __device__ __forceinline__ ColParams make_col(half2_t s2, uint32_t z) {
   ColParams p;
   p.s2 = s2;
-  if constexpr (FMT != kFmtF16 && FMT != kFmtW8) {
+  if constexpr (FMT != kFmtF16 && FMT != kFmtW8 && FMT != kFmtSp24) {
     const _Float16 lo = (_Float16)(float)(1024u + z);  // exact: integers to 2048
     const _Float16 hi = (_Float16)(float)(64u + z);    // exact: quarter units above 256
     p.zlo = half2_t{lo, lo};
@@ -126,7 +132,7 @@ __device__ __forceinline__ half8_t unpack_scale_bf16(uint32_t word, float s, hal
 
 template <int FMT>
 __device__ __forceinline__ half8_t unpack_col(uint32_t word, const ColParams& p) {
-  if constexpr (FMT == kFmtF16)
+  if constexpr (FMT == kFmtF16 || FMT == kFmtSp24)
     return unpack_scale(word, p.s2);
   else if constexpr (FMT == kFmtF16Zp)
     return unpack_scale_zp(word, p.s2, p.zlo, p.zhi);
@@ -163,6 +169,29 @@ __device__ __forceinline__ float4_fmt_t mma16(half8_t a, half8_t b, float4_fmt_t
                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+
+// 2:4 sparsity.  One sparse 16x16x64 FP16 matrix instruction,
+// D (16 x 16) += S (16 x 64, 2:4-sparse along its 64) . B (64 x 16).  The
+// sparse operand comes compressed: lane L gives row L % 16 of S as eight
+// values, slot i of which sits at column 16 (L / 16) + 4 (i / 2) + p_i of S,
+// p_i = bits 2i .. 2i+1 of `pos` (the two slots of one group of four must
+// name different positions).  The dense operand: lane l gives column l % 16
+// of B, element j at row 32 (j / 8) + 8 (l / 16) + j % 8 -- i.e. the
+// activation fragments of two consecutive 32-deep steps of the dense
+// instruction, side by side.  The result lands as in the dense
+// instruction: lane l holds D rows 4 (l / 16) .. +3 of column l % 16.  (The
+// lane maps were read off the hardware with one-hot operands.)
+// Here S is a block of transposed weights (rows = output columns) and B a
+// block of transposed activations (columns = batch rows), so D is a block of
+// C transposed.
+typedef _Float16 half16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float4_fmt_t smma16(half8_t s, half8_t b_lo, half8_t b_hi,
+                                               uint32_t pos, float4_fmt_t acc) {
+  const half16_t b = __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                             12, 13, 14, 15);
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(s, b, acc, (int)pos, 0, 0);
 }
 
 // An FP32 result rounded to the output type (to nearest even), as the raw

@@ -18,6 +18,11 @@
 // loads for the partials (coherent.hpp), a wait for those stores to complete
 // before the arrival count, and no device-wide fence.
 //
+// 2:4-sparse weights (format 5) use the sparse 16x16x64 matrix instruction
+// with the weights as its compressed operand: per K block and column block
+// a lane loads its two code words and its position word (12 bytes instead
+// of 16), and the accumulators hold C transposed (format.hpp, smma16).
+//
 // Per 128-deep K block a wave issues, for each of its NB column blocks, one
 // 16-byte load per lane of permuted codes (the lane's own operand fragments
 // for four 32-deep steps) and one scale load; it unpacks each word in
@@ -37,7 +42,7 @@ namespace w4a16 {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-template <int MB, int NB, bool ZP, bool W8>
+template <int MB, int NB, bool ZP, bool W8, bool SP = false>
 struct Slot {
   uint4 b[NB];         // permuted codes: one 128-deep K block per column block
   half2_t s[NB];       // the group scale of this lane's column, in both halves
@@ -61,6 +66,16 @@ struct Slot<MB, NB, false, true> {
   uint4 b2[NB];
 };
 
+// 2:4-sparse codes: the two compressed code words (64-deep halves 0 and 1)
+// and the position word of this lane, per column block.
+template <int MB, int NB>
+struct Slot<MB, NB, false, false, true> {
+  uint2 b[NB];
+  half2_t s[NB];
+  half8_t a[MB][4];
+  uint32_t p[NB];
+};
+
 // FMT: the weight format (format.hpp); formats other than 0 are compiled
 // without the fused epilogue.  A, S and C hold raw 16-bit values (FP16, or
 // BF16 for formats 2 and 3); Z the zero points of formats 1 and 3.
@@ -77,6 +92,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   static_assert(!EPI || FMT == kFmtF16, "the fused epilogue is FP16 only");
   constexpr bool ZP = Format<FMT>::kZp;
   constexpr bool W8 = Format<FMT>::kW8;
+  constexpr bool SP = Format<FMT>::kSp;
+  typedef Slot<MB, NB, ZP, W8, SP> SlotT;
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
@@ -129,8 +146,11 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n16 = n16_0 + (nb < nvalid ? nb : nvalid - 1);
-    bcol[nb] = Bp + (W8 ? block_word_offset8(n16, 0, K) : block_word_offset(n16, 0, K)) +
-               lane * kWordsPerLane;
+    if constexpr (SP)
+      bcol[nb] = Bp + block_word_offset_sp(n16, 0, K);
+    else
+      bcol[nb] = Bp + (W8 ? block_word_offset8(n16, 0, K) : block_word_offset(n16, 0, K)) +
+                 lane * kWordsPerLane;
     scol[nb] = S + n16 * kBlockN + l16;
     if constexpr (ZP) zcol[nb] = Z + n16 * kBlockN + l16;
   }
@@ -141,11 +161,15 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   auto scale_row = [&](int kb) -> int {
     return (int)(((uint64_t)(uint32_t)kb * group_magic) >> 32);
   };
-  auto load = [&](Slot<MB, NB, ZP, W8>& sl, int kb) {
+  auto load = [&](SlotT& sl, int kb) {
     const int srow = scale_row(kb) * N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if constexpr (W8) {
+      if constexpr (SP) {
+        const uint32_t* blk = bcol[nb] + kb * kWordsPerBlockSp;
+        sl.b[nb] = *reinterpret_cast<const uint2*>(blk + 2 * lane);
+        sl.p[nb] = blk[kCodeWordsSp + lane];
+      } else if constexpr (W8) {
         // the two 64-deep blocks of this 128-deep K block
         sl.b[nb] = *reinterpret_cast<const uint4*>(bcol[nb] + 2 * kb * kWordsPerBlock);
         sl.b2[nb] =
@@ -163,26 +187,41 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
       for (int j = 0; j < 4; ++j)
         sl.a[mb][j] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
   };
-  auto compute = [&](const Slot<MB, NB, ZP, W8>& sl) {
+  auto compute = [&](const SlotT& sl) {
+    if constexpr (SP) {
+      // two 64-deep sparse steps; the accumulators hold C transposed
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // (column blocks past N recompute the last valid block; the store
-        // drops them -- a branch here would stall the load pipeline)
-        half8_t b;
-        if constexpr (W8) {
-          const uint4& pc = j < 2 ? sl.b[nb] : sl.b2[nb];
-          b = unpack8_scale((j & 1) ? pc.z : pc.x, (j & 1) ? pc.w : pc.y, sl.s[nb]);
-        } else {
-          const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
-                           : j == 2 ? sl.b[nb].z : sl.b[nb].w;
-          uint32_t z = 8;
-          if constexpr (ZP) z = sl.z[nb];
-          b = unpack_col<FMT>(w, make_col<FMT>(sl.s[nb], z));
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t pos = t ? sl.p[nb] >> 16 : sl.p[nb];
+          const half8_t w = unpack_scale(t ? sl.b[nb].y : sl.b[nb].x, sl.s[nb]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][nb] = smma16(w, sl.a[mb][2 * t], sl.a[mb][2 * t + 1], pos, acc[mb][nb]);
         }
+      }
+    } else {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mma16<FMT>(sl.a[mb][j], b, acc[mb][nb]);
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // (column blocks past N recompute the last valid block; the store
+          // drops them -- a branch here would stall the load pipeline)
+          half8_t b;
+          if constexpr (W8) {
+            const uint4& pc = j < 2 ? sl.b[nb] : sl.b2[nb];
+            b = unpack8_scale((j & 1) ? pc.z : pc.x, (j & 1) ? pc.w : pc.y, sl.s[nb]);
+          } else {
+            const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
+                             : j == 2 ? sl.b[nb].z : sl.b[nb].w;
+            uint32_t z = 8;
+            if constexpr (ZP) z = sl.z[nb];
+            b = unpack_col<FMT>(w, make_col<FMT>(sl.s[nb], z));
+          }
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mma16<FMT>(sl.a[mb][j], b, acc[mb][nb]);
+        }
       }
     }
   };
@@ -195,7 +234,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   const int nblk = first < kb1 ? (kb1 - first + WK - 1) / WK : 0;
   if (nblk > 0) {
     const int last = first + (nblk - 1) * WK;
-    Slot<MB, NB, ZP, W8> slot[D];
+    SlotT slot[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int kb = first + u * WK;
@@ -220,7 +259,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   }
 
   // Sum the waves' tiles in LDS, wave 0 first.  Lane l holds rows
-  // 4*(l/16) .. +3 of column l % 16 of each 16x16 block.
+  // 4*(l/16) .. +3 of column l % 16 of each 16x16 block (with 2:4-sparse
+  // weights: row l % 16, columns 4*(l/16) .. +3).
 #pragma unroll 1
   for (int w = 0; w < WK; ++w) {
     if (wave == w) {
@@ -230,7 +270,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float* p = &red[(mb * 16 + (lane >> 4) * 4 + i) * LDT + nb * 16 + l16];
+            float* p = SP ? &red[(mb * 16 + l16) * LDT + nb * 16 + (lane >> 4) * 4 + i]
+                          : &red[(mb * 16 + (lane >> 4) * 4 + i) * LDT + nb * 16 + l16];
             *p = (w == 0) ? acc[mb][nb][i] : *p + acc[mb][nb][i];
           }
     }
@@ -353,6 +394,20 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
 #define W4A16_FMT_VARIANTS(X) \
   X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 8, 2) X(1, 1, 4, 2) X(1, 4, 4, 4) X(1, 4, 4, 2)
 
+// Variants compiled for 2:4-sparse weights: the plans' small-batch ones and
+// wider row tiles for larger batches.
+#define W4A16_SP_VARIANTS(X)                                                  \
+  X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 8, 2) X(1, 1, 4, 2) X(1, 4, 4, 4) X(1, 4, 4, 2) \
+  X(2, 2, 4, 2) X(2, 4, 4, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) X(8, 2, 4, 1)
+
+bool sp_is_compiled(int mb, int nb, int wk, int depth) {
+#define W4A16_SMATCH(MB_, NB_, WK_, D_) \
+  if (mb == MB_ && nb == NB_ && wk == WK_ && depth == D_) return true;
+  W4A16_SP_VARIANTS(W4A16_SMATCH)
+#undef W4A16_SMATCH
+  return false;
+}
+
 bool plan_is_compiled(int mb, int nb, int wk, int depth) {
 #define W4A16_MATCH(MB_, NB_, WK_, D_) \
   if (mb == MB_ && nb == NB_ && wk == WK_ && depth == D_) return true;
@@ -401,6 +456,14 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
   }
   W4A16_FMT_VARIANTS(W4A16_FCASE)
 #undef W4A16_FCASE
+  if (wf.fmt == kFmtSp24) {
+#define W4A16_SCASE(MB_, NB_, WK_, D_)                                                      \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                           \
+    return launch_one<MB_, NB_, WK_, D_, kFmtSp24>(p, A, Bp, S, C, M, K, N, gmagic, ep,     \
+                                                   nullptr, workspace, stream);
+    W4A16_SP_VARIANTS(W4A16_SCASE)
+#undef W4A16_SCASE
+  }
   return hipErrorInvalidValue;
 }
 

@@ -45,7 +45,8 @@ struct Epilogue {
 };
 
 // The weight format of a call (format.hpp): 0 FP16, 1 FP16 with zero
-// points, 2 BF16, 3 BF16 with zero points, 4 FP16 with 8-bit weights;
+// points, 2 BF16, 3 BF16 with zero points, 4 FP16 with 8-bit weights, 5 FP16
+// with 2:4-sparse 4-bit weights;
 // `zeros` are the zero points uint8[K/group][N] of formats 1 and 3 (null
 // otherwise).
 struct WeightFormat {
@@ -53,8 +54,9 @@ struct WeightFormat {
   const uint8_t* zeros;
 };
 
-Plan make_plan(int M, int K, int N, int group, int cus);
+Plan make_plan(int M, int K, int N, int group, int cus, int fmt = 0);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
+bool sp_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
 
@@ -62,6 +64,8 @@ hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);
 hipError_t launch_repack8(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                           hipStream_t stream);
+hipError_t launch_repack_sp24(const uint32_t* Bq, const uint8_t* mask, uint32_t* Bp, int K,
+                              int N, hipStream_t stream);
 hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
                           int K, int N, int group, hipStream_t stream);
 hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,

@@ -70,4 +70,22 @@ __host__ __device__ inline int64_t packed_word_of(int k0, int n, int K) {
   return block_word_offset(n16, kb, K) + lane * kWordsPerLane + j;
 }
 
+// 2:4-sparse 4-bit weights (layout version 1 for 2:4): blocks of 16 columns
+// x 128 in-features as for 4 bits, column-block-major then along K, but
+// 768 bytes (192 words) each: words 0 .. 127 hold the kept codes, words
+// 128 .. 191 their positions.  Lane l of a block owns code words 2l, 2l+1
+// (one per 64-deep half t of the block) and position word 128 + l.  Code
+// word t of lane l holds, for column l % 16, the two kept codes of each of
+// the four groups of four in-features 64t + 16 (l / 16) + 4r .. +3
+// (r = 0..3; slots 2r, 2r+1, lower position first), slot i at nibble
+// nibble_of_code(i); bits 16t + 2i .. +1 of the position word hold slot i's
+// position (0..3) in its group.  So one 8-byte and one 4-byte read hand a
+// lane the compressed sparse operand of both 64-deep steps of the block.
+constexpr int kWordsPerBlockSp = 192;
+constexpr int kCodeWordsSp = 128;  // code words at the start of a block
+
+__host__ __device__ inline int64_t block_word_offset_sp(int n16, int kb, int K) {
+  return ((int64_t)n16 * (K / kBlockK) + kb) * kWordsPerBlockSp;
+}
+
 }  // namespace w4a16
