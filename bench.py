@@ -535,7 +535,8 @@ FORMAT_SHAPES = [
     ("prefill 8192x28672", 8192, 28672, [1024]),
 ]
 FORMATS = [("FP16", 0, False), ("FP16 + zero points", 0, True), ("BF16", 1, False),
-           ("BF16 + zero points", 1, True), ("8-bit weights", None, False)]
+           ("BF16 + zero points", 1, True), ("8-bit weights", None, False),
+           ("2:4 sparse", "sp24", False)]
 
 
 def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
@@ -546,7 +547,7 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
 
     import weight_only_int4_gemm_amd as w4
     from weight_only_int4_gemm_amd import roofline
-    from synth import make_inputs_awq, make_words
+    from synth import make_inputs_awq, make_mask24, make_words
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -574,16 +575,38 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
         del Bq8_d, Bq8
         ncopy8 = max(1, -(-ROTATE_BYTES // (K * N)))
         copies8 = [first8] + [first8.clone() for _ in range(ncopy8 - 1)]
+        # 2:4-sparse codes: the 4-bit words under a two-of-four mask
+        _, Bqs, _, _ = make_inputs_awq(1, K, N, GROUP, seed=0)
+        Bqs_d = torch.from_numpy(Bqs.view(np.int32)).to(dev)
+        mask_d = torch.from_numpy(make_mask24(K, N, seed=1)).to(dev)
+        firsts = w4.alloc_packed_sparse24(K, N)
+        w4.w4a16_sparse24_repack(Bqs_d, mask_d, firsts, K, N)
+        del Bqs_d, Bqs, mask_d
+        ncopys = max(1, -(-ROTATE_BYTES // (K * N * 3 // 8)))
+        copiess = [firsts] + [firsts.clone() for _ in range(ncopys - 1)]
         for M in batches:
             A16, _, _, _ = make_inputs_awq(M, K, 8, GROUP, seed=M)
             Ab, _, _, _ = make_inputs_awq(M, K, 8, GROUP, seed=M, bf16=True)
             acts = {0: torch.from_numpy(A16.view(np.int16)).to(dev),
                     1: torch.from_numpy(Ab.view(np.int16)).to(dev)}
             C_d = torch.empty((M, N), dtype=torch.int16, device=dev)
-            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, GROUP), 256),
+            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, GROUP),
+                                 w4.w4a16_sparse24_workspace_bytes(M, K, N, GROUP), 256),
                              dtype=torch.uint8, device=dev)
 
             def form(dtype, zp):
+                if dtype == "sp24":     # 2:4-sparse weights, FP16 activations
+                    def calls(c):
+                        args = (acts[0].data_ptr(), c.data_ptr(), scales[0].data_ptr(),
+                                C_d.data_ptr(), M, K, N, GROUP, ws.data_ptr(), sh)
+
+                        def run():
+                            rc = lib.w4a16_sparse24_gemm(*args)
+                            if rc != 0:
+                                raise RuntimeError(
+                                    f"w4a16_sparse24_gemm: {w4.w4a16_status_string(rc)}")
+                        return run
+                    return [calls(c) for c in copiess]
                 if dtype is None:       # 8-bit weights, FP16 activations
                     def call8(c):
                         args = (acts[0].data_ptr(), c.data_ptr(), scales[0].data_ptr(),
@@ -617,13 +640,15 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
             flops = roofline.flops(M, K, N)
             rows.append(dict(shape=label, M=M, us=[t * 1e6 for t in med],
                              tflops=[flops / t / 1e12 for t in med],
-                             plan=w4.w4a16_describe(M, K, N, GROUP).split(" workspace")[0]))
+                             plan=w4.w4a16_describe(M, K, N, GROUP).split(" workspace")[0],
+                             plan_sp24=w4.w4a16_sparse24_describe(M, K, N, GROUP)
+                             .split(" workspace")[0]))
             print(json.dumps(rows[-1]), flush=True)
             del acts, C_d, ws
-        del copies, first, scales, zeros, copies8, first8
+        del copies, first, scales, zeros, copies8, first8, copiess, firsts
         torch.cuda.empty_cache()
     lines = [
-        "# Weight formats on one MI355X: FP16, zero points, BF16, 8-bit weights",
+        "# Weight formats on one MI355X: FP16, zero points, BF16, 8-bit weights, 2:4 sparsity",
         "",
         "Command (repository root, GPU box): `python3 bench.py --formats-report " +
         os.path.relpath(out_path, ROOT) + "`",
@@ -631,16 +656,19 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
         f"Kernel source hash: `{kernel_source_hash()}`. Each format through `w4a16_gemm_awq` "
         f"(FP16 without zero points is the plain kernel) or `w8a16_gemm`, hipEvents around {launches} "
         f"back-to-back calls cycling over weight copies beyond 512 MB; the four formats are "
-        f"timed in turn, {repeats} rounds, median per format (the five formats interleaved). Zero points: uint8 per group "
+        f"timed in turn, {repeats} rounds, median per format (the formats interleaved). Zero points: uint8 per group "
         "and column (one more byte per 64 code bytes at group 128). 8-bit weights: "
-        "`w8a16_gemm` (twice the code bytes of 4-bit).",
+        "`w8a16_gemm` (twice the code bytes of 4-bit). 2:4 sparse: `w4a16_sparse24_gemm` "
+        "on the same codes under a two-of-four mask (three quarters of the 4-bit bytes, "
+        "half the products; its own plan).",
         "",
-        "| shape | M | " + " | ".join(f"{n} us" for n, _, _ in FORMATS) + " | plan |",
-        "|---|---|" + "---|" * len(FORMATS) + "---|",
+        "| shape | M | " + " | ".join(f"{n} us" for n, _, _ in FORMATS) + " | plan | 2:4 plan |",
+        "|---|---|" + "---|" * len(FORMATS) + "---|---|",
     ]
     for r in rows:
         lines.append(f"| {r['shape']} | {r['M']} | " +
-                     " | ".join(f"{u:.1f}" for u in r["us"]) + f" | `{r['plan']}` |")
+                     " | ".join(f"{u:.1f}" for u in r["us"]) +
+                     f" | `{r['plan']}` | `{r['plan_sp24']}` |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 

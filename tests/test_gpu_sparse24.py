@@ -95,13 +95,15 @@ SP_CASES = [
     (1, 2048, 36864, "gemm_kernel<1,4,8,2>"),
     (3, 13824, 4096, "gemm_kernel<1,2,8,2>"),
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
-    (8, 11008, 1024, "gemm_kernel<1,4,4,4>"),
+    (8, 11008, 1024, "gemm_kernel<1,4,4,2>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),
-    (16, 1024, 8192, "gemm_kernel<1,4,4,2>"),
-    (32, 1024, 4096, "gemm_kernel<2,4,4,2>"),
-    (45, 1024, 208, "gemm_kernel<4,4,4,1>"),
-    (128, 1024, 1024, "gemm_kernel<8,2,4,1>"),
-    (300, 512, 512, "gemm_kernel<8,2,4,1>"),
+    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4,16>"),
+    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4,16>"),
+    (45, 1024, 208, "gemm_lds_kernel<4,2,1,4,3,16>"),
+    (128, 1024, 1024, "gemm_lds_kernel<4,2,1,4,3,16>"),
+    (128, 512, 36864, "gemm_lds_kernel<4,2,1,4,3,16>"),
+    (128, 256, 65536, "gemm_lds_kernel<4,2,1,4,3,16>"),
+    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3,16>"),
 ]
 
 
@@ -123,15 +125,22 @@ def test_gemm_sp24_matches_oracle(M, K, N, kernel):
 
 @pytest.mark.parametrize("plan", ["1,1,8,3,2", "1,2,8,4,2", "1,4,8,2,2", "1,1,4,5,2",
                                   "1,4,4,3,4", "1,4,4,2,2", "2,2,4,3,2", "2,4,4,2,2",
-                                  "4,2,4,3,1", "4,4,4,2,1", "8,2,4,4,1"])
+                                  "4,2,4,3,1", "4,4,4,2,1", "8,2,4,4,1",
+                                  "1,2,8,4,4,2", "2,2,8,2,4,2", "4,1,8,3,3,2",
+                                  "4,2,4,2,3,2,0,2", "8,2,8,2,3,2", "4,2,4,2,3,2",
+                                  "4,2,8,3,3,2", "8,1,8,2,3,2", "2,2,4,4,3,2,0,2",
+                                  "2,4,4,2,4,2", "8,4,4,2,3,2"])
 def test_gemm_sp24_forced_plans_split_k(monkeypatch, plan):
     M, K, N, group = 45, 3584, 208, 512
     A, Bq, S = make_inputs(M, K, N, group, seed=5)
     mask = make_mask24(K, N, seed=6, exact=False)
     monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
     desc = w4.w4a16_sparse24_describe(M, K, N, group)
-    mb, nb, wk, _, depth = plan.split(",")
-    assert desc.startswith(f"gemm_kernel<{mb},{nb},{wk},{depth}>"), desc
+    f = [int(x) for x in plan.split(",")] + [0, 0, 0]
+    mb, nb, wk, depth, tile, wm = f[0], f[1], f[2], f[4], f[5], f[7] or 1
+    want = (f"gemm_lds_kernel<{mb},{nb},{wm},{wk},{depth},16>" if tile == 2
+            else f"gemm_kernel<{mb},{nb},{wk},{depth}>")
+    assert desc.startswith(want), desc
     assert "splits=1 " not in desc, desc
     say("gemm sp24 forced", plan, desc)
     C = run_gemm_sp24(A, Bq, mask, S, group)

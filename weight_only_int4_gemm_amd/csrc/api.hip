@@ -64,7 +64,10 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q, int fmt) {
-  if (fmt == kFmtSp24) return q.tile == 0 && q.wm == 1 && sp_is_compiled(q.mb, q.nb, q.wk, q.depth);
+  if (fmt == kFmtSp24) {
+    if (q.tile == 2) return lds_sp_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth);
+    return q.tile == 0 && q.wm == 1 && sp_is_compiled(q.mb, q.nb, q.wk, q.depth);
+  }
   if (q.tile >= 2)
     return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth, q.tile == 3 ? 32 : 16);
   if (q.wm != 1) return false;
@@ -164,10 +167,14 @@ size_t workspace_fmt(int M, int K, int N, int group, int fmt) {
 // two K blocks per wave.  Larger batches go to the LDS kernel with 64 or 128
 // rows per wave, so each weight is unpacked once for many rows.
 //
-// 2:4-sparse weights (format 5) run the streaming kernel at every batch
-// size: the small-batch plans as for dense weights, and above that 32- to
-// 128-row tiles (wider row tiles re-read fewer activation fragments per
-// weight).
+// 2:4-sparse weights (format 5) take the same plans with three changes,
+// measured at the Llama-2-7B layer shapes: the streaming kernel keeps two
+// K blocks in flight (a slot is smaller; 11008 x 4096 at M = 16: 14.6 ->
+// 12.2 us); 32 < M <= 128 runs 64 x 128 tiles as four waves of 64 x 32 (half
+// the matrix instructions per activation fragment of the dense format, so
+// wider wave tiles: 4096 x 12288 at M = 128: 26.6 -> 21.1 us); and the K
+// split there is twice the dense one below a full wave of workgroups and
+// none above it.
 Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   (void)group;
   Plan p{};
@@ -175,13 +182,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
   if (cus <= 0) cus = 256;
-  const bool sparse = fmt == kFmtSp24;
-  if (sparse && !(M <= 4 || (M <= 16 && N < 8192))) {
-    p.mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    p.nb = p.mb >= 8 ? 2 : 4;
-    p.wk = 4;
-    p.depth = p.mb >= 4 ? 1 : 2;
-  } else if (M <= 4 || (M <= 16 && N < 8192)) {
+  if (M <= 4 || (M <= 16 && N < 8192)) {
     // streaming kernel: activations straight from global memory
     p.mb = 1;
     if (M <= 4) {
@@ -235,6 +236,15 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     p.wk = 8;
     p.depth = 3;
   }
+  const bool sparse = fmt == kFmtSp24;
+  if (sparse && p.tile == 0) p.depth = 2;
+  if (sparse && M > 32 && M <= 128) {
+    p.mb = 4;
+    p.nb = 2;
+    p.wm = 1;
+    p.wk = 4;
+    p.depth = 3;
+  }
   auto shape = [&](Plan& q) {
     const int f = q.tile == 3 ? 32 : 16;
     q.tm = f * q.mb * q.wm;
@@ -253,9 +263,12 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     // fewer tiles than compute units: split K as far as whole splits fill
     // the compute units (a partly filled extra wave of workgroups costs
     // more than idle compute units), a power of two
-    want = cus / tiles;
+    want = (sparse && M > 32 && M <= 128 ? 2 : 1) * cus / tiles;
     while (want & (want - 1)) want &= want - 1;
     cap = KB / 4 < 8 ? KB / 4 : 8;
+  } else if (p.tile && sparse && M > 32 && M <= 128) {
+    want = 1;
+    cap = 1;
   } else if (p.tile) {
     // more tiles than compute units: the last wave of workgroups may run
     // nearly empty (288 tiles on 256 CUs keep 56% of them busy on average).

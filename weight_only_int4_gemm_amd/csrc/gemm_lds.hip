@@ -29,6 +29,12 @@
 //    in the permuted layout's own order (lane l's four words at 16*l), so a
 //    wave reads its fragments with one conflict-free 16-byte read per block;
 //  * scales: the tile's 16*NB*WN FP16 scales of this K block's group.
+//
+// 2:4-sparse weights (format 5): a code block is 768 bytes (layout.hpp),
+// brought in by one 16-byte direct load on lanes 0..47; a wave reads its
+// two code words (8 bytes) and its position word from LDS and runs two
+// sparse 16x16x64 matrix instructions per K block and 16 x 16 output block
+// (format.hpp, smma16), whose results are C transposed.
 #include <type_traits>
 
 #include "layout.hpp"
@@ -54,8 +60,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
     float* __restrict__ partials, Epilogue ep, const uint8_t* __restrict__ Z) {
   static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
-  static_assert(FMT == kFmtF16 || (F == 16 && !EPI), "formats 1-3: 16 x 16 blocks, no epilogue");
+  static_assert(FMT == kFmtF16 || (F == 16 && !EPI), "formats 1-5: 16 x 16 blocks, no epilogue");
   constexpr bool ZP = Format<FMT>::kZp;
+  constexpr bool SP = Format<FMT>::kSp;
+  constexpr int BLOCK_PIECES = SP ? 48 : 64;     // 16-byte pieces of one code block
   constexpr int PPB = Format<FMT>::kW8 ? 2 : 1;  // 1 KiB pieces per code block and K block
   constexpr int WAVES = WM * WN;
   constexpr int TM = F * MB * WM;
@@ -69,7 +77,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // the same place), so every wave issues the same number of loads
   constexpr int ALOADS = (ACHUNKS + WAVES - 1) / WAVES;
   constexpr int BLOADS = (BLOCKS * PPB + WAVES - 1) / WAVES;
-  constexpr int BPIECES = BLOCKS * PPB * 64;   // 16-byte pieces of codes
+  constexpr int BPIECES = BLOCKS * PPB * BLOCK_PIECES;  // 16-byte pieces of codes
   constexpr int SDWORDS = TN / 2;              // scales of one K block, as 32-bit words
   constexpr int SLOADS = (SDWORDS + 63) / 64;  // 4-byte direct loads (every wave issues them)
   constexpr int ZLOADS = ZP ? (TN / 4 + 63) / 64 : 0;  // zero points: 4-byte loads, all waves
@@ -125,9 +133,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     bblk[i] = (wave + WAVES * i) % (BLOCKS * PPB);
     const int n16 = tile_n * BLOCKS + bblk[i] / PPB;
     const int n16c = n16 <= n16_last ? n16 : n16_last;
-    bsrc[i] = Bp +
-              (PPB == 2 ? block_word_offset8(n16c, bblk[i] % 2, K) : block_word_offset(n16c, 0, K)) +
-              lane * kWordsPerLane;
+    if constexpr (SP)
+      bsrc[i] = Bp + block_word_offset_sp(n16c, 0, K) + lane * 4;
+    else
+      bsrc[i] = Bp +
+                (PPB == 2 ? block_word_offset8(n16c, bblk[i] % 2, K) : block_word_offset(n16c, 0, K)) +
+                lane * kWordsPerLane;
   }
   // Scale source: word i*64 + lane of the stage holds columns 2w, 2w+1.
   const _Float16* ssrc[SLOADS];
@@ -161,8 +172,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     }
 #pragma unroll
     for (int i = 0; i < BLOADS; ++i) {
-      __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[i] + PPB * kb * kWordsPerBlock),
-                                       (lds_ptr_t)&sg.b[64 * bblk[i]], 16, 0, 0);
+      if constexpr (SP) {
+        // a 768-byte block: lanes 0..47 move it (one load instruction still)
+        if (lane < BLOCK_PIECES)
+          __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[i] + kb * kWordsPerBlockSp),
+                                           (lds_ptr_t)&sg.b[BLOCK_PIECES * bblk[i]], 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((global_ptr_t)(bsrc[i] + PPB * kb * kWordsPerBlock),
+                                         (lds_ptr_t)&sg.b[64 * bblk[i]], 16, 0, 0);
+      }
     }
     const int srow = scale_row(kb) * N;
 #pragma unroll
@@ -315,8 +333,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
         }
     }
   };
+  // ---- 2:4-sparse codes: two 64-deep sparse steps per K block ------------
+  // Step t multiplies the weights' compressed code word t (transposed: rows
+  // are output columns) by the activation fragments of 32-deep slices 2t
+  // and 2t+1 side by side; acc[mb][nb] holds C transposed.
+  auto compute_sp = [&](const Stage& sg) {
+    uint2 w[NB];
+    uint32_t pos[NB];
+    half2_t s2[NB];
+    const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
+    const uint2* bw2 = reinterpret_cast<const uint2*>(sg.b);
+    const uint32_t* bw = reinterpret_cast<const uint32_t*>(sg.b);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int blk = wn * NB + nb;
+      w[nb] = bw2[(kWordsPerBlockSp / 2) * blk + lane];
+      pos[nb] = bw[kWordsPerBlockSp * blk + kCodeWordsSp + lane];
+      const _Float16 sc = sh[wn * 16 * NB + nb * 16 + l16];
+      s2[nb] = half2_t{sc, sc};
+    }
+    half8_t a0[MB], a1[MB], a2[MB], a3[MB];
+    half8_t b0[NB], b1[NB];
+    read_a(sg, 0, a0);
+    read_a(sg, 1, a1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b0[nb] = unpack_scale(w[nb].x, s2[nb]);
+    read_a(sg, 2, a2);
+    read_a(sg, 3, a3);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b1[nb] = unpack_scale(w[nb].y, s2[nb]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (F == 16) acc[mb][nb] = smma16(b0[nb], a0[mb], a1[mb], pos[nb], acc[mb][nb]);
+      }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (F == 16)
+          acc[mb][nb] = smma16(b1[nb], a2[mb], a3[mb], pos[nb] >> 16, acc[mb][nb]);
+      }
+  };
   auto compute = [&](const Stage& sg) {
-    if constexpr (F == 16)
+    if constexpr (SP)
+      compute_sp(sg);
+    else if constexpr (F == 16)
       compute16(sg);
     else
       compute32(sg);
@@ -339,7 +402,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // from four waves stalls each wave for hundreds of cycles).  So the
   // step's loads are spread between its matrix instructions: one load
   // after every MFMA_PER_LOAD of them.
-  constexpr int NMFMA = (F == 16 ? 4 : 8) * MB * NB;
+  constexpr int NMFMA = (SP ? 2 : F == 16 ? 4 : 8) * MB * NB;
   constexpr int MFMA_PER_LOAD = NMFMA / (LOADS + 1) > 0 ? NMFMA / (LOADS + 1) : 1;
   auto step = [&](int u, int kb) {  // u = t % NS
     stage_barrier<(NS - 2) * LOADS>();
@@ -365,7 +428,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   if constexpr (F == 16)
-    store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, splits,
+    store_output_tile<MB, NB, WAVES, EPI, FMT, SP>(acc, C, M, N, wrow0, wcol0, split, splits,
                                                counters, partials,
                                                reinterpret_cast<int*>(&st0.s[0]), ep, bias);
   else
@@ -431,6 +494,21 @@ bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f) {
   return false;
 }
 
+// Variants compiled for 2:4-sparse codes: the plans' ones and wider wave
+// tiles (with half the matrix instructions per activation fragment, wider
+// column blocks per wave keep more of them in flight).
+#define W4A16_LDS_SP_VARIANTS(X)                                                       \
+  W4A16_LDS_FMT_VARIANTS(X) X(4, 2, 1, 4, 3) X(4, 2, 1, 8, 3) X(8, 1, 1, 8, 3)          \
+  X(2, 2, 2, 4, 3) X(2, 4, 1, 4, 4) X(8, 4, 1, 4, 3)
+
+bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns) {
+#define W4A16_LSMATCH(MB_, NB_, WM_, WN_, NS_) \
+  if (mb == MB_ && nb == NB_ && wm == WM_ && wn == WN_ && ns == NS_) return true;
+  W4A16_LDS_SP_VARIANTS(W4A16_LSMATCH)
+#undef W4A16_LSMATCH
+  return false;
+}
+
 // Stages for 8-bit codes, whose code pieces are twice the size: as many of
 // the plan's NS as fit in the 160 KiB of LDS (the same tiles, splits and
 // workspace; only the pipeline depth differs).
@@ -456,6 +534,16 @@ hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
     return hipErrorInvalidValue;
   }
   if (f != 16) return hipErrorInvalidValue;
+  if (wf.fmt == kFmtSp24) {
+#define W4A16_LSCASE(MB_, NB_, WM_, WN_, NS_)                                                 \
+  if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_)             \
+    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtSp24>(p, A, Bp, S, C, M, K, N,     \
+                                                                 gmagic, ep, nullptr,         \
+                                                                 workspace, stream);
+    W4A16_LDS_SP_VARIANTS(W4A16_LSCASE)
+#undef W4A16_LSCASE
+    return hipErrorInvalidValue;
+  }
 #define W4A16_LFCASE(MB_, NB_, WM_, WN_, NS_)                                                 \
   if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_) {           \
     if (wf.fmt == kFmtF16Zp)                                                                  \

@@ -59,6 +59,7 @@ bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
 bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
+bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);

@@ -84,7 +84,10 @@ struct LaneBias {
 // that sums finds its own fragments at the same places.  `flag` is an int in
 // LDS no wave touches any more.  The epilogue is applied to the final sums
 // only; FMT sets the output type (FP16, or BF16 for formats 2 and 3).
-template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16>
+// TRANS: acc[mb][nb] holds the block transposed (the sparse instruction's
+// result): lane l has row l % 16, columns 4*(l/16) .. +3, stored as one
+// 8-byte vector.
+template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16, bool TRANS = false>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
                                                   int wrow0, int wcol0, int split, int splits,
@@ -96,6 +99,26 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
   const int wave = threadIdx.x >> 6;
   const int col_base = wcol0 + (lane & 15);
   auto write_c = [&]() {
+    if constexpr (TRANS) {
+      static_assert(!EPI, "no fused epilogue on the transposed path");
+      typedef _Float16 half4_vt __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int gr = wrow0 + mb * 16 + (lane & 15);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // N is a multiple of 16: four columns from a multiple of 4 fit
+          const int gc = wcol0 + nb * 16 + (lane >> 4) * 4;
+          if (gr < M && gc < N) {
+            half4_vt h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = out16<FMT>(acc[mb][nb][i]);
+            *reinterpret_cast<half4_vt*>(C + (int64_t)gr * N + gc) = h;
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
