@@ -333,7 +333,7 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
 
     import weight_only_int4_gemm_amd as w4
     from weight_only_int4_gemm_amd import roofline
-    from synth import make_activations, make_inputs
+    from synth import make_activations, make_inputs, make_mask24
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -347,6 +347,12 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
         first = w4.alloc_packed(K, N)
         w4.w4a16_repack(Bq_d, first, K, N)
+        # the same codes under a two-of-four mask, for the 2:4-sparse column
+        sfirst = w4.alloc_packed_sparse24(K, N)
+        w4.w4a16_sparse24_repack(Bq_d, torch.from_numpy(make_mask24(K, N, seed=1)).to(dev),
+                                 sfirst, K, N)
+        nsp = max(1, -(-ROTATE_BYTES // (K * N * 3 // 8)))
+        scopies = [sfirst] + [sfirst.clone() for _ in range(nsp - 1)]
         del Bq_d, Bq
         ncopy = max(1, -(-ROTATE_BYTES // (K * N // 2)))
         copies = [first] + [first.clone() for _ in range(ncopy - 1)]
@@ -359,8 +365,20 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         for M in batches:
             A_d = torch.from_numpy(make_activations(M, K, seed=M)).to(dev)
             C_d = torch.empty((M, N), dtype=torch.float16, device=dev)
-            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, group), 256),
+            ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, group),
+                                 w4.w4a16_sparse24_workspace_bytes(M, K, N, group), 256),
                              dtype=torch.uint8, device=dev)
+
+            def sparse_call(c):
+                args = (A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K, N,
+                        group, ws.data_ptr(), sh)
+
+                def run():
+                    rc = lib.w4a16_sparse24_gemm(*args)
+                    if rc != 0:
+                        raise RuntimeError(
+                            f"w4a16_sparse24_gemm failed: {w4.w4a16_status_string(rc)}")
+                return run
 
             def gemm_call(c):
                 args = (A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K, N,
@@ -376,9 +394,13 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
             C16 = torch.empty((M, N), dtype=torch.float16, device=dev)
             t16 = _time_calls([(lambda w=w: torch.matmul(A_d, w, out=C16)) for w in wcopies],
                               launches, repeats)
+            tsp = _time_calls([sparse_call(c) for c in scopies], launches, repeats)
             flops = roofline.flops(M, K, N)
             nbytes = roofline.algorithmic_bytes(M, K, N, group)
+            # 2:4: three quarters of the code bytes, the rest unchanged
+            sbytes = nbytes - K * N // 2 + K * N * 3 // 8
             rows.append(dict(shape=label, M=M, K=K, N=N, group=group, us=t * 1e6,
+                             sp24_us=tsp * 1e6, sp24_tbps=sbytes / tsp / 1e12,
                              tflops=flops / t / 1e12, tbps=nbytes / t / 1e12,
                              bound=roofline.bound(M, K, N, group),
                              frac=roofline.roofline_seconds(M, K, N, group) / t,
@@ -386,7 +408,7 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
                              plan=w4.w4a16_describe(M, K, N, group).split(" workspace")[0]))
             print(json.dumps(rows[-1]), flush=True)
             del A_d, C_d, ws, C16
-        del copies, first, S_d, W, wcopies
+        del copies, first, S_d, W, wcopies, scopies, sfirst
         torch.cuda.empty_cache()
     clocks_after = _gpu_clocks()
 
@@ -403,20 +425,25 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         "(weights seed 0, activations seed M). Roofline: HBM 8 TB/s, dense FP16 MFMA "
         "2.5 PFLOP/s; `frac` is the bound's time over the measured time. `FP16 us` is "
         "torch.matmul (hipBLASLt) on the same weights dequantised to FP16, timed the same "
-        "way with its own rotation of weight copies; `x FP16` is its time over ours.",
+        "way with its own rotation of weight copies; `x FP16` is its time over ours. "
+        "`2:4 us` is `w4a16_sparse24_gemm` on the same codes under a two-of-four mask (seed 1), "
+        "with its own rotation and plan; `2:4 TB/s` counts its bytes (three quarters of the "
+        "code bytes).",
         "",
         f"Clocks after a one-second warm-up, before the first shape (rocm-smi): "
         f"{clocks_before or 'n/a'}",
         "",
         f"Clocks after: {clocks_after or 'n/a'}",
         "",
-        "| shape | M | us | TFLOP/s | HBM TB/s | bound | frac | FP16 us | x FP16 | plan |",
-        "|---|---|---|---|---|---|---|---|---|---|",
+        "| shape | M | us | TFLOP/s | HBM TB/s | bound | frac | FP16 us | x FP16 | 2:4 us | "
+        "2:4 TB/s | plan |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
     ]
     for r in rows:
         lines.append(f"| {r['shape']} | {r['M']} | {r['us']:.1f} | {r['tflops']:.1f} | "
                      f"{r['tbps']:.2f} | {r['bound']} | {r['frac']:.3f} | {r['fp16_us']:.1f} | "
-                     f"{r['speedup']:.2f} | `{r['plan']}` |")
+                     f"{r['speedup']:.2f} | {r['sp24_us']:.1f} | {r['sp24_tbps']:.2f} | "
+                     f"`{r['plan']}` |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 

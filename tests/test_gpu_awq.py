@@ -100,8 +100,9 @@ def test_awq_dequant_exhaustive_codes_zero_points_scales(fmt, dtype, zp):
 # (M, K, N, the plan's kernel and template arguments as w4a16_describe prints them)
 AWQ_CASES = [
     (1, 4096, 4096, "gemm_kernel<1,1,8,2>"),
+    (1, 4096, 12288, "gemm_kernel<1,1,4,2>"),
     (1, 4096, 22016, "gemm_kernel<1,2,8,2>"),
-    (1, 2048, 36864, "gemm_kernel<1,4,8,2>"),
+    (1, 2048, 36864, "gemm_kernel<1,4,4,2>"),
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,4>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),

@@ -91,8 +91,9 @@ def test_dequant_sp24_keeps_exactly_the_mask():
 # the plans' kernels (as w4a16_sparse24_describe prints them), one shape each
 SP_CASES = [
     (1, 4096, 4096, "gemm_kernel<1,1,8,2>"),
+    (1, 4096, 12288, "gemm_kernel<1,1,4,2>"),
     (1, 4096, 22016, "gemm_kernel<1,2,8,2>"),
-    (1, 2048, 36864, "gemm_kernel<1,4,8,2>"),
+    (1, 2048, 36864, "gemm_kernel<1,4,4,2>"),
     (3, 13824, 4096, "gemm_kernel<1,2,8,2>"),
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,2>"),

@@ -78,8 +78,9 @@ def test_dequant8_all_codes_against_every_scale():
 # the plans' kernels (as w4a16_describe prints them), one shape each
 W8_CASES = [
     (1, 4096, 4096, "gemm_kernel<1,1,8,2>"),
+    (1, 4096, 12288, "gemm_kernel<1,1,4,2>"),
     (1, 4096, 22016, "gemm_kernel<1,2,8,2>"),
-    (1, 2048, 36864, "gemm_kernel<1,4,8,2>"),
+    (1, 2048, 36864, "gemm_kernel<1,4,4,2>"),
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,4>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),

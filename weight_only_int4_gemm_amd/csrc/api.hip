@@ -187,9 +187,14 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     p.mb = 1;
     if (M <= 4) {
       // 16-column tiles; 32 for wide N or deep K (there split three ways
-      // below), 64 for very wide N
+      // below), 64 for very wide N.  Four waves per workgroup with 16- and
+      // 64-column tiles when there are at least two tiles per compute unit,
+      // else eight (measured: 18432 x 73728 at M = 1..4 126-131 us against
+      // 130-142 us with eight; 4096 x 12288 at M = 1 9.4 against 10.0 us;
+      // but 11008 x 4096, 256 tiles, 9.6 against 8.3 us; and 4096 x 22016
+      // at M = 1 keeps eight waves of 32 columns, 14.1 against 14.7 us)
       p.nb = n16 >= 8 * cus ? 4 : (n16 >= 4 * cus || KB >= 96) ? 2 : 1;
-      p.wk = 8;
+      p.wk = p.nb != 2 && n16 / p.nb >= 2 * cus ? 4 : 8;
       p.depth = 2;
     } else {
       p.nb = n16 >= 2 * cus || KB >= 64 ? 4 : 1;
