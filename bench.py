@@ -60,6 +60,8 @@ GROUP = 128
 WEIGHT_COPIES = 8   # 8 x 101 MB of packed weights: far beyond the 256 MB MALL
 COPY_PROBE_BYTES = 512 * 2**20   # one-dispatch device copy of known size, counter calibration
 COPY_PROBE_RUNS = 4
+SIMDS = 256 * 4                 # MI355X: 256 compute units of four SIMDs
+XCDS = 8                        # accelerator complex dies
 WARMUP_MIN_S = 0.5   # untimed steps run at least this long before timing
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama7b_step.json")
 
@@ -104,6 +106,14 @@ def parse():
                     help="time the weight formats (FP16, FP16 with zero points, BF16, BF16 "
                          "with zero points, 8-bit weights) side by side, write a markdown "
                          "table to OUT and exit")
+    ap.add_argument("--single", nargs=3, type=int, metavar=("M", "K", "N"),
+                    help="time one GEMM shape (group 128) with rotating weight copies, "
+                         "print one JSON line and exit: a short program for counter runs")
+    ap.add_argument("--sparse24", action="store_true",
+                    help="with --single: the 2:4-sparse GEMM on the same codes")
+    ap.add_argument("--pmc-kernels", nargs="+", metavar=("OUT", "DIR"),
+                    help="summarise rocprofv3 --pmc runs (one DIR each) into OUT (JSON): "
+                         "per GEMM kernel and counter, the value per dispatch")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script into a traffic file and exit")
@@ -227,6 +237,60 @@ def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
         json.dump(summary, f, indent=1)
         f.write("\n")
     print(json.dumps(summary, indent=1))
+
+
+def pmc_kernels(out_path: str, run_dirs) -> None:
+    """Per GEMM kernel and counter of each rocprofv3 --pmc run: the value per
+    dispatch (rows of one dispatch summed; and their maximum), averaged over
+    dispatches.  rocprofv3 stores one value per dispatch, already summed over
+    the counter's instances.  MFMA utilisation as rocprofv3's own derived
+    MfmaUtil defines it: SQ_VALU_MFMA_BUSY_CYCLES summed over SIMDs, over
+    (GRBM_GUI_ACTIVE of one XCD times the SIMD count); GRBM_GUI_ACTIVE comes
+    summed over the eight XCDs, which are active over the same span, so one
+    XCD's value is that sum over eight."""
+    out = {"commands": "rocprofv3 --pmc <counters> -d DIR -o run -- python3 bench.py "
+                       "--single M K N [--sparse24]; python3 bench.py --pmc-kernels OUT DIR...",
+           "kernel_source_hash": kernel_source_hash(), "runs": {}}
+    for d in run_dirs:
+        dbs = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
+        if not dbs:
+            raise SystemExit(f"no rocprofv3 results database under {d}")
+        per = {}
+        cols = None
+        for db in dbs:
+            con = sqlite3.connect(db)
+            cur = con.execute("select * from counters_collection")
+            cols = [c[0] for c in cur.description]
+            disp = next((c for c in cols if "dispatch" in c.lower() and "id" in c.lower()), None)
+            for row in cur:
+                r = dict(zip(cols, row))
+                k = _short_kernel_name(str(r["kernel_name"]))
+                if "gemm" not in k:
+                    continue
+                key = (db, r[disp]) if disp else (db, id(row))
+                per.setdefault(k, {}).setdefault(r["counter_name"], {}).setdefault(
+                    key, []).append(float(r["value"]))
+            con.close()
+        kern = {}
+        for k, ctrs in per.items():
+            entry = {}
+            for c, bydisp in ctrs.items():
+                vals = list(bydisp.values())
+                entry[c] = {"dispatches": len(vals),
+                            "sum_per_dispatch": sum(sum(v) for v in vals) / len(vals),
+                            "max_per_dispatch": sum(max(v) for v in vals) / len(vals),
+                            "rows_per_dispatch": sum(len(v) for v in vals) / len(vals)}
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in entry and "GRBM_GUI_ACTIVE" in entry:
+                gui_one_xcd = entry["GRBM_GUI_ACTIVE"]["sum_per_dispatch"] / XCDS
+                entry["mfma_util_percent"] = (100 * entry["SQ_VALU_MFMA_BUSY_CYCLES"]["sum_per_dispatch"]
+                                              / (gui_one_xcd * SIMDS))
+            if "MfmaUtil" in entry:
+                entry["mfma_util_percent_rocprof"] = entry["MfmaUtil"]["sum_per_dispatch"]
+            kern[k] = entry
+        out["runs"][os.path.basename(os.path.normpath(d))] = {"columns": cols, "kernels": kern}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
 
 
 def measured_traffic(kernel: str):
@@ -700,10 +764,68 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+def single_gemm(M: int, K: int, N: int, sparse: bool = False, launches: int = 20,
+                repeats: int = 3) -> None:
+    """One GEMM shape, group 128: warm clocks, then ``repeats`` batches of
+    ``launches`` back-to-back calls over weight copies beyond the Infinity
+    Cache; prints the median time per call and the plan as one JSON line."""
+    import numpy as np
+    import torch
+
+    import weight_only_int4_gemm_amd as w4
+    from weight_only_int4_gemm_amd import roofline
+    from synth import make_activations, make_inputs, make_mask24
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = w4.load()
+    sh = torch.cuda.current_stream().cuda_stream
+    _, Bq, S = make_inputs(1, K, N, GROUP, seed=0)
+    Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
+    if sparse:
+        first = w4.alloc_packed_sparse24(K, N)
+        w4.w4a16_sparse24_repack(Bq_d, torch.from_numpy(make_mask24(K, N, seed=1)).to(dev),
+                                 first, K, N)
+        wbytes = K * N * 3 // 8
+        ws_bytes = w4.w4a16_sparse24_workspace_bytes(M, K, N, GROUP)
+        fn, desc = lib.w4a16_sparse24_gemm, w4.w4a16_sparse24_describe(M, K, N, GROUP)
+    else:
+        first = w4.alloc_packed(K, N)
+        w4.w4a16_repack(Bq_d, first, K, N)
+        wbytes = K * N // 2
+        ws_bytes = w4.w4a16_workspace_bytes(M, K, N, GROUP)
+        fn, desc = lib.w4a16_gemm, w4.w4a16_describe(M, K, N, GROUP)
+    del Bq_d
+    copies = [first] + [first.clone() for _ in range(max(1, -(-ROTATE_BYTES // wbytes)) - 1)]
+    S_d = torch.from_numpy(S).to(dev)
+    A_d = torch.from_numpy(make_activations(M, K, seed=M)).to(dev)
+    C_d = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def call(c):
+        args = (A_d.data_ptr(), c.data_ptr(), S_d.data_ptr(), C_d.data_ptr(), M, K, N, GROUP,
+                ws.data_ptr(), sh)
+
+        def run():
+            rc = fn(*args)
+            if rc != 0:
+                raise RuntimeError(f"GEMM failed: {w4.w4a16_status_string(rc)}")
+        return run
+
+    _warm_clocks(0.5)
+    t = _time_calls([call(c) for c in copies], launches, repeats)
+    print(json.dumps(dict(M=M, K=K, N=N, group=GROUP, sparse24=sparse, us=t * 1e6,
+                          tflops=roofline.flops(M, K, N) / t / 1e12, plan=desc,
+                          calls=max(5, len(copies)) + launches * repeats)), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.pmc_kernels:
+        pmc_kernels(args.pmc_kernels[0], args.pmc_kernels[1:])
         return
     if args.configs_report:
         configs_report(args.configs_report)
@@ -713,6 +835,9 @@ def main():
         return
     if args.formats_report:
         formats_report(args.formats_report)
+        return
+    if args.single:
+        single_gemm(*args.single, sparse=args.sparse24)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
