@@ -109,5 +109,5 @@ def make_mask24(K: int, N: int, seed: int = 0, exact: bool = True):
         raise ValueError(f"bad shape K={K}")
     rng = np.random.default_rng(seed)
     if exact:
-        return TWO_OF_FOUR[rng.integers(0, 6, size=(K // 4, N))]
+        return TWO_OF_FOUR[rng.integers(0, 6, size=(K // 4, N), dtype=np.uint8)]
     return rng.integers(0, 256, size=(K // 4, N), dtype=np.uint8)

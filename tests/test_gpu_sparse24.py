@@ -217,3 +217,43 @@ def test_gemm_sp24_llama_shapes_sampled(M, K, N):
                                    [0, 15, 16, N - 1]]))
     _, C64 = oracle.gemm_sparse24(A, Bq, mask, S, 128, cols=cols)
     assert_gemm_close(C[:, cols], C64, f"M={M} K={K} N={N}")
+
+
+# The workload's other shapes at full size, in the plans the benchmark times:
+# every row, a sample of output columns (first, middle and last column tiles
+# and random ones), each computed by the oracle.
+def _sample_cols(N, count, seed):
+    rng = np.random.default_rng(seed)
+    cols = set(range(0, 16)) | set(range(N - 16, N)) | set(range(N // 2, N // 2 + 16))
+    cols |= set(rng.choice(N, size=count, replace=False).tolist())
+    return np.array(sorted(cols))
+
+
+def _sampled_sp24(K, N, group, Ms, seed, count=64):
+    import torch
+    _, Bq, S = make_inputs(1, K, N, group, seed=seed)
+    mask = make_mask24(K, N, seed=seed + 1)
+    Bp = repack_sp24_on_device(dev(Bq), dev(mask), K, N)
+    cols = _sample_cols(N, count, seed)
+    for M in Ms:
+        A, _, _ = make_inputs(M, K, 8, group, seed=seed + M)
+        say("sp24 sampled", K, N, group, "M", M, w4.w4a16_sparse24_describe(M, K, N, group))
+        C = run_gemm_sp24(A, Bq, mask, S, group, Bp=Bp)
+        _, C64 = oracle.gemm_sparse24(A, Bq, mask, S, group, cols=cols)
+        assert_gemm_close(C[:, cols], C64, f"K={K} N={N} g={group} M={M}")
+    del Bp
+    torch.cuda.empty_cache()
+
+
+def test_gemm_sp24_large_layer_batch_sweep():
+    _sampled_sp24(18432, 73728, 128, (1, 2, 4, 8, 16, 32, 64, 128), seed=0)
+
+
+def test_gemm_sp24_prefill_layer():
+    _sampled_sp24(8192, 28672, 128, (512, 1024, 4096), seed=0, count=32)
+
+
+@pytest.mark.parametrize("K,N", [(28672, 8192), (13824, 5120)])
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_gemm_sp24_deep_k_layers(K, N, per_channel):
+    _sampled_sp24(K, N, K if per_channel else 128, (1, 8, 32), seed=0)
