@@ -59,3 +59,35 @@ def test_more_than_one_gpu_is_refused():
     assert proc.returncode == 2
     assert "one GPU" in proc.stderr
     assert proc.stdout == ""
+
+
+def _fake_pmc_db(path, rows):
+    import sqlite3
+    path.parent.mkdir(parents=True, exist_ok=True)
+    con = sqlite3.connect(str(path))
+    con.execute("create table counters_collection (dispatch_id integer, kernel_name text, "
+                "counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_pmc_kernels_summary(tmp_path):
+    k = "_ZN5w4a1615gemm_lds_kernelILi8ELi2ELi1ELi8ELi3ELi16ELb0ELi0EEEvPKDF16_"
+    # two dispatches of one GEMM kernel and one of another kernel (ignored)
+    rows = []
+    for d, busy, gui in ((1, 1024 * 500.0, 8 * 1000.0), (2, 1024 * 700.0, 8 * 1000.0)):
+        rows += [(d, k, "SQ_VALU_MFMA_BUSY_CYCLES", busy), (d, k, "GRBM_GUI_ACTIVE", gui),
+                 (d, k, "SQ_INSTS_VALU_MFMA_MOPS_F16", 32.0)]
+    rows.append((3, "elementwise_kernel", "GRBM_GUI_ACTIVE", 5.0))
+    _fake_pmc_db(tmp_path / "run_a" / "x" / "run_results.db", rows)
+    out = tmp_path / "out.json"
+    bench.pmc_kernels(str(out), [str(tmp_path / "run_a")])
+    summ = json.loads(out.read_text())
+    e = summ["runs"]["run_a"]["kernels"]["gemm_lds_kernel<8,2,1,8,3,16>"]
+    assert list(summ["runs"]["run_a"]["kernels"]) == ["gemm_lds_kernel<8,2,1,8,3,16>"]
+    assert e["GRBM_GUI_ACTIVE"]["dispatches"] == 2
+    assert e["SQ_VALU_MFMA_BUSY_CYCLES"]["sum_per_dispatch"] == 1024 * 600.0
+    # busy cycles over (one XCD's active cycles x 1024 SIMDs): 600 / 1000
+    assert abs(e["mfma_util_percent"] - 60.0) < 1e-9
+    assert summ["kernel_source_hash"] == bench.kernel_source_hash()
