@@ -98,7 +98,11 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
-  __shared__ float red[TM * LDT];
+  // The waves' partial tiles: one LDS slot per wave where they fit (one
+  // barrier, then every thread adds the slots in wave order), else one slot
+  // the waves add into in turn (a barrier per wave).
+  constexpr bool SLOTS = (size_t)WK * TM * LDT * sizeof(float) <= 40 * 1024;
+  __shared__ float red[(SLOTS ? WK : 1) * TM * LDT];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
@@ -273,22 +277,48 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   // Sum the waves' tiles in LDS, wave 0 first.  Lane l holds rows
   // 4*(l/16) .. +3 of column l % 16 of each 16x16 block (with 2:4-sparse
   // weights: row l % 16, columns 4*(l/16) .. +3).
-#pragma unroll 1
-  for (int w = 0; w < WK; ++w) {
-    if (wave == w) {
+  auto red_index = [&](int mb, int nb, int i) {
+    return SP ? (mb * 16 + l16) * LDT + nb * 16 + (lane >> 4) * 4 + i
+              : (mb * 16 + (lane >> 4) * 4 + i) * LDT + nb * 16 + l16;
+  };
+  if constexpr (SLOTS) {
+    float* mine = red + wave * TM * LDT;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* p = SP ? &red[(mb * 16 + l16) * LDT + nb * 16 + (lane >> 4) * 4 + i]
-                          : &red[(mb * 16 + (lane >> 4) * 4 + i) * LDT + nb * 16 + l16];
-            *p = (w == 0) ? acc[mb][nb][i] : *p + acc[mb][nb][i];
-          }
-    }
+        for (int i = 0; i < 4; ++i) mine[red_index(mb, nb, i)] = acc[mb][nb][i];
     __syncthreads();
+  } else {
+#pragma unroll 1
+    for (int w = 0; w < WK; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float* p = &red[red_index(mb, nb, i)];
+              *p = (w == 0) ? acc[mb][nb][i] : *p + acc[mb][nb][i];
+            }
+      }
+      __syncthreads();
+    }
   }
+  // Four consecutive columns (c a multiple of 4) of row r of the summed
+  // tile: the waves' values added in wave order 0, 1, ..., the same order
+  // either way.
+  auto tile_value = [&](int r, int c) -> float4_t {
+    float4_t x = *reinterpret_cast<const float4_t*>(&red[r * LDT + c]);
+    if constexpr (SLOTS) {
+#pragma unroll
+      for (int w = 1; w < WK; ++w)
+        x = x + *reinterpret_cast<const float4_t*>(&red[w * TM * LDT + r * LDT + c]);
+    }
+    return x;
+  };
 
   constexpr int VEC = 4;
   constexpr int VPR = TN / VEC;  // float4 vectors per tile row
@@ -309,7 +339,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
       const int r = v / VPR, c = (v % VPR) * VEC;
       const int gr = row0 + r, gc = col0 + c;
       if (gr < M && gc < N) {
-        const float4_t x = *reinterpret_cast<const float4_t*>(&red[r * LDT + c]);
+        const float4_t x = tile_value(r, c);
         *reinterpret_cast<half4_t*>(C + (int64_t)gr * N + gc) = finish(x);
       }
     }
@@ -327,7 +357,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
     for (int v = threadIdx.x; v < rows * VPR; v += blockDim.x) {
       const int r = v / VPR, c = (v % VPR) * VEC;
-      store_coherent(mine, v, *reinterpret_cast<const float4_t*>(&red[r * LDT + c]));
+      store_coherent(mine, v, tile_value(r, c));
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
