@@ -100,8 +100,11 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
   // The waves' partial tiles: one LDS slot per wave where they fit (one
   // barrier, then every thread adds the slots in wave order), else one slot
-  // the waves add into in turn (a barrier per wave).
-  constexpr bool SLOTS = (size_t)WK * TM * LDT * sizeof(float) <= 40 * 1024;
+  // the waves add into in turn (a barrier per wave).  2:4-sparse codes keep
+  // the second form: with the first, the compiler gave the 64-column
+  // variant a shallower load schedule (the 18432 x 73728 layer at M = 1:
+  // 159 against 107 us).
+  constexpr bool SLOTS = !SP && (size_t)WK * TM * LDT * sizeof(float) <= 40 * 1024;
   __shared__ float red[(SLOTS ? WK : 1) * TM * LDT];
   __shared__ int s_last;
 
