@@ -182,8 +182,10 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
   if (cus <= 0) cus = 256;
-  if (M <= 4 || (M <= 16 && N < 8192)) {
-    // streaming kernel: activations straight from global memory
+  if (M <= 4 || (M <= 16 && N < 8192) || (M <= 8 && n16 >= 8 * cus)) {
+    // streaming kernel: activations straight from global memory (up to
+    // M = 8 on very wide layers too: 18432 x 73728 at M = 8 took 128 us
+    // against 145 us in the LDS kernel; at M = 16 the LDS kernel is ahead)
     p.mb = 1;
     if (M <= 4) {
       // 16-column tiles; 32 for wide N or deep K (there split three ways
@@ -295,7 +297,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     // 13824 x 5120: 1.2-1.25x over unsplit 16-column tiles)
     want = 3;
     cap = KB / (2 * p.wk);
-  } else if (M > 4 && KB >= 96) {
+  } else if (M > 4 && KB >= 96 && tiles < 2 * (int64_t)cus) {
     // streaming, five to sixteen rows, deep K: eight K ranges per 64-column
     // tile (13824 x 5120: 1.3x over the default below)
     want = 8;
