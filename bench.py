@@ -35,7 +35,10 @@ to the value recorded with the counters:
 time (the single 4096 x 4096 layer, the Llama-2-7B layers, the 18432 x 73728
 batch sweep, the 8192 x 28672 prefill layer and the deep-K layers with group
 128 and group K) and writes a table of time, TFLOP/s, HBM TB/s and roofline
-fraction per call.
+fraction per call, with the 2:4-sparse GEMM on the same codes beside it.
+``--single M K N [--sparse24]`` times one GEMM and prints one JSON line: the
+short program for counter runs, summarised by ``--pmc-kernels OUT DIR...``
+(MFMA utilisation, HBM bytes per dispatch).
 """
 
 from __future__ import annotations
