@@ -1,5 +1,5 @@
-// The W4A16 GEMM for batches of more than 32 rows, with every operand
-// staged through LDS: C = A . dequant(Bpacked).
+// The W4A16 GEMM for all but the smallest batches (the plans in api.hip),
+// with every operand staged through LDS: C = A . dequant(Bpacked).
 //
 // A workgroup of WM x WN waves owns an F*MB*WM x F*NB*WN output tile and one
 // K range; wave (wm, wn) owns the F*MB x F*NB block at row block wm, column

@@ -1,4 +1,4 @@
-// The W4A16 GEMM for batches of more than 32 rows: C = A . dequant(Bpacked).
+// A W4A16 GEMM for larger batches (forced plans only): C = A . dequant(Bpacked).
 //
 // Once a batch has dozens of rows the matrix instructions, not the weight
 // stream, set the pace ("Quant Marlin kernel" explainer, "Why architecture
