@@ -1,35 +1,39 @@
 """W4A16 GEMM throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sweep|llama7b]
 
-Workload: the Llama-2-7B-shaped linear layers as W4A16 GEMMs (K x N =
-4096 x 12288 fused qkv, 4096 x 4096 o, 4096 x 22016 fused gate/up,
-11008 x 4096 down), group 128, at batch M = 1, 16 and 128.  One step runs
-all twelve GEMMs once.  Inputs are seeded synthetic data (A ~ N(0,1) in
-FP16, uniform codes, FP16 scales uniform on [0.005, 0.02]), resident in HBM
-before timing starts.  Each of the twelve GEMMs of a step reads its own copy
-of the layer's weights, and the copies rotate over steps, so that no weight
-read is served by the 256 MB Infinity Cache from an earlier launch.
+Default workload (the one the metric is quoted on): the large single layer
+K = 18432, N = 73728 (the 72k x 18k layer of the MARLIN note's first figure),
+group 128, at every batch size M = 1, 2, 4, 8, 16, 32, 64, 128.  One step runs
+the eight GEMMs once.  Inputs are seeded synthetic data (A ~ N(0,1) in FP16,
+uniform codes, FP16 scales uniform on [0.005, 0.02]), resident in HBM before
+timing starts.  Weights, scales and activations exist in several copies and
+the copy a launch reads rotates, so that no launch finds its operands in the
+256 MB Infinity Cache from an earlier one.
 
 Warmup runs the W steps asked for and continues until at least half a
-second of steps has run (the GPU's clocks ramp up from idle); the JSON line
-gives both W and the number of warmup steps run.  The timed region is
-exactly K steps.  The same K steps are then replayed from HIP graphs (one
-graph per weight-copy rotation) and reported under ``graph``.
+second of steps has run (the GPU's clocks ramp up from idle).  Then five
+timed regions of exactly K steps each, synchronised on both sides; the
+median is ``value`` (all five are listed).  The Llama-2-7B layer step (four
+layers at M = 1, 16, 128) is timed the same way and reported under
+``secondary``.
 
 Prints one JSON line: whole-step TFLOP/s (the metric), achieved HBM TB/s,
-the roofline object of the dominant kernel (per-launch durations from HIP
-events around back-to-back batches of each GEMM on the launch stream), and
-the CPU oracle timed on the host.
+per-GEMM times, the roofline object of the dominant kernel (per-launch
+durations from HIP events around back-to-back batches of each GEMM on the
+launch stream), measured ceilings (a plain 2 GiB read and an FP16
+matrix-instruction loop, libw4a16_probes.so) beside the published peaks,
+the clocks under load (rocm-smi) and the CPU oracle timed on the host on a
+bounded slice of the same workload.
 
 Counter-based HBM traffic (``roofline.traffic``) comes from two rocprofv3
 counter runs of this script, summarised into profiles/ by
 ``--pmc-summary``; it is reported only while the kernel sources still hash
 to the value recorded with the counters:
 
-    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-graph --copy-probe
-    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-graph --copy-probe
-    python3 bench.py --pmc-summary OUT/fetch OUT/write profiles/pmc_traffic_llama7b_step.json
+    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-graph --no-secondary --no-probes --no-clocks --copy-probe
+    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-graph --no-secondary --no-probes --no-clocks --copy-probe
+    python3 bench.py --pmc-summary OUT/fetch OUT/write profiles/pmc_traffic_large_layer_sweep.json
 
 ``--configs-report OUT.md`` instead times every workload shape one GEMM at a
 time (the single 4096 x 4096 layer, the Llama-2-7B layers, the 18432 x 73728
@@ -66,7 +70,31 @@ COPY_PROBE_RUNS = 4
 SIMDS = 256 * 4                 # MI355X: 256 compute units of four SIMDs
 XCDS = 8                        # accelerator complex dies
 WARMUP_MIN_S = 0.5   # untimed steps run at least this long before timing
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama7b_step.json")
+REPEATS = 5          # timed regions of exactly --steps steps; the median is reported
+PROBE_READ_BYTES = 2 * 2**30    # the stream-read ceiling: a 2 GiB buffer read once per launch
+PROBE_MFMA_ITERS = 4096
+
+# The workloads.  "sweep" is the one the metric is quoted on: the large
+# single layer at every batch size from 1 to 128.
+WORKLOADS = {
+    "sweep": {
+        "layers": [("large", 18432, 73728)],
+        "batches": [1, 2, 4, 8, 16, 32, 64, 128],
+        "copies": 2,     # 2 x 680 MB of packed weights
+        "workload": "Large single W4A16 layer K=18432, N=73728 (the 72k x 18k layer), group "
+                    "128, batch sweep M in {1,2,4,8,16,32,64,128}; one step = the 8 GEMMs",
+        "traffic": os.path.join(ROOT, "profiles", "pmc_traffic_large_layer_sweep.json"),
+    },
+    "llama7b": {
+        "layers": LAYERS,
+        "batches": BATCHES,
+        "copies": WEIGHT_COPIES,
+        "workload": "Llama-2-7B-shaped W4A16 linear layers (qkv 4096x12288, o 4096x4096, "
+                    "gate/up 4096x22016, down 11008x4096), group 128, M in {1,16,128}; "
+                    "one step = the 12 GEMMs",
+        "traffic": os.path.join(ROOT, "profiles", "pmc_traffic_llama7b_step.json"),
+    },
+}
 
 # Every workload shape, for --configs-report: (label, K, N, group, batch sizes).
 REPORT_SHAPES = [
@@ -88,13 +116,22 @@ ROTATE_BYTES = 512 * 10**6   # weight copies cycled per shape: beyond the 256 MB
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="sweep",
+                    help="the workload of the headline line (default: the large-layer "
+                         "batch sweep the metric is quoted on)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other workload (reported under 'secondary')")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the stream-read and MFMA-loop ceiling probes")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the rocm-smi clock readout under load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step (profiler runs)")
-    ap.add_argument("--cpu-sample-cols", type=int, default=0,
-                    help="columns per GEMM for the CPU oracle (0 = whole GEMMs)")
+    ap.add_argument("--cpu-sample-cols", type=int, default=4096,
+                    help="output columns per layer for the CPU oracle (0 = whole layers)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a one-dispatch elementwise copy (negation) "
                          "of 512 MiB a few times: calibrates the HBM byte counters")
@@ -296,11 +333,11 @@ def pmc_kernels(out_path: str, run_dirs) -> None:
         f.write("\n")
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, path: str):
     """Counter-measured HBM bytes per launch of `kernel`, or None when there
     is no summary or the kernel sources changed since it was taken."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path) as f:
             summ = json.load(f)
     except (OSError, ValueError):
         return None
@@ -310,9 +347,79 @@ def measured_traffic(kernel: str):
     return None if entry is None else entry["hbm_bytes_per_dispatch"]
 
 
-def cpu_baseline(sample_cols: int):
-    """The oracle, as it stands, on this host: the step's twelve GEMMs (or the
-    first ``sample_cols`` columns of each)."""
+def measured_ceilings(torch, dev):
+    """What this chip sustains (libw4a16_probes.so), beside the published
+    peaks: a plain read of a 2 GiB buffer with 16-byte non-temporal loads,
+    and independent FP16 matrix instructions on register operands in every
+    wave of a full grid.  Median of five timed launches each."""
+    import ctypes
+    import numpy as np
+    from weight_only_int4_gemm_amd import roofline
+    path = os.path.join(ROOT, "weight_only_int4_gemm_amd", "libw4a16_probes.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.w4a16_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p]
+    lib.w4a16_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    lib.w4a16_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.w4a16_probe_mfma_flops.restype = ctypes.c_double
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    buf = torch.ones(PROBE_READ_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def timed(launch, reps=5):
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    read_blocks = 256 * 8
+    t_read = timed(lambda: lib.w4a16_probe_read(buf.data_ptr(), PROBE_READ_BYTES,
+                                                sink.data_ptr(), read_blocks, sh))
+    del buf
+    mfma_blocks = 256 * 8   # 8192 waves: eight per SIMD
+    t_mfma = timed(lambda: lib.w4a16_probe_mfma(sink.data_ptr(), mfma_blocks, PROBE_MFMA_ITERS,
+                                                sh))
+    flops = lib.w4a16_probe_mfma_flops(mfma_blocks, PROBE_MFMA_ITERS)
+    read_gbps = PROBE_READ_BYTES / t_read / 1e9
+    mfma_tflops = flops / t_mfma / 1e12
+    return {
+        "hbm_read_gbps": read_gbps,
+        "hbm_read_frac_of_peak": read_gbps / (roofline.HBM_PEAK_BYTES_PER_S / 1e9),
+        "mfma_f16_tflops": mfma_tflops,
+        "mfma_frac_of_peak": mfma_tflops / (roofline.MFMA_F16_PEAK_FLOPS / 1e12),
+        "probe": "2 GiB read once with 16-byte non-temporal loads (2048 workgroups of 512); "
+                 f"{PROBE_MFMA_ITERS} rounds of 8 independent v_mfma_f32_16x16x32_f16 per wave, "
+                 "2048 workgroups of 4 waves; median of 5 launches each",
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, sample_cols: int):
+    """The oracle, as it stands, on this host: every GEMM of one step of the
+    workload on the first ``sample_cols`` output columns of each layer (full
+    K, every batch size; 0 = whole layers), timed call by call."""
     import numpy as np
     import oracle
     from synth import make_inputs
@@ -323,24 +430,26 @@ def cpu_baseline(sample_cols: int):
         threads = os.cpu_count() or 1
     total_flops = 0
     t_total = 0.0
-    for name, K, N in LAYERS:
+    for name, K, N in wl["layers"]:
         cols = N if sample_cols <= 0 else min(N, sample_cols)
         _, Bq, S = make_inputs(1, K, cols, GROUP, seed=0)
-        for M in BATCHES:
+        for M in wl["batches"]:
             A, _, _ = make_inputs(M, K, 8, GROUP, seed=M)
             t0 = time.perf_counter()
             oracle.gemm(A, Bq, S, GROUP)
             t_total += time.perf_counter() - t0
             total_flops += 2 * M * K * cols
-    what = "all twelve GEMMs of one step" if sample_cols <= 0 else \
-        f"the first {sample_cols} output columns of each of the twelve GEMMs"
+    what = "every GEMM of one step" if sample_cols <= 0 else \
+        f"every GEMM of one step on the first {sample_cols} output columns of each layer " \
+        f"(full K, all {len(wl['batches'])} batch sizes)"
     return {
         "value": total_flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{what} (float64 accumulation, numpy), {t_total:.1f} s on "
-                  f"{os.cpu_count()} logical CPUs",
+        "sample": f"{what}; float64 accumulation, numpy; {t_total:.1f} s",
+        "cpu_model": _cpu_model(),
+        "logical_cpus": os.cpu_count(),
     }
 
 
@@ -822,6 +931,243 @@ def single_gemm(M: int, K: int, N: int, sparse: bool = False, launches: int = 20
                           calls=max(5, len(copies)) + launches * repeats)), flush=True)
 
 
+def _build_workload(wl, dev, torch, w4, make_inputs, np):
+    """Inputs of a workload, resident in HBM: per layer `copies` copies of
+    the packed weights, the scales and every batch's activations (the copy a
+    launch reads rotates, so no launch finds its operands in the 256 MB
+    Infinity Cache from an earlier one), one output per GEMM, one workspace.
+    Returns the GEMMs of a step in launch order, the C-call arguments of the
+    first `copies` steps (the rotation repeats after that) and the plans."""
+    layers, batches, copies = wl["layers"], wl["batches"], wl["copies"]
+    packed, scales, acts = {}, {}, {}
+    for name, K, N in layers:
+        _, Bq, S = make_inputs(1, K, N, GROUP, seed=0)
+        Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
+        del Bq
+        first = w4.alloc_packed(K, N)
+        w4.w4a16_repack(Bq_d, first, K, N)
+        del Bq_d
+        packed[name] = [first] + [first.clone() for _ in range(copies - 1)]
+        s0 = torch.from_numpy(S).to(dev)
+        scales[name] = [s0] + [s0.clone() for _ in range(copies - 1)]
+        for M in batches:
+            A, _, _ = make_inputs(M, K, 8, GROUP, seed=M)
+            a0 = torch.from_numpy(A).to(dev)
+            acts[(name, M)] = [a0] + [a0.clone() for _ in range(copies - 1)]
+    outs, ws_bytes = {}, 0
+    for name, K, N in layers:
+        for M in batches:
+            outs[(name, M)] = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws_bytes = max(ws_bytes, w4.w4a16_workspace_bytes(M, K, N, GROUP))
+    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    gemms = [(name, K, N, M) for M in batches for (name, K, N) in layers]
+    plans = {g: w4.w4a16_describe(g[3], g[1], g[2], GROUP) for g in gemms}
+    uses = len(batches)   # uses of one layer per step
+
+    def args_for(g, copy, stream_handle):
+        name, K, N, M = g
+        return (acts[(name, M)][copy].data_ptr(), packed[name][copy].data_ptr(),
+                scales[name][copy].data_ptr(), outs[(name, M)].data_ptr(), M, K, N, GROUP,
+                workspace.data_ptr(), stream_handle)
+
+    # the t-th use of a layer over the run reads copy t % copies
+    def calls(stream_handle):
+        return [[args_for(g, (uses * s + batches.index(g[3])) % copies, stream_handle)
+                 for g in gemms] for s in range(copies)]
+    keep = (packed, scales, acts, outs, workspace)
+    return gemms, calls, plans, keep
+
+
+def _time_workload(wl, args, lib, torch, w4, roofline, stream, make_inputs, np, dev,
+                   graph: bool):
+    """Time one workload: warmup, then REPEATS timed regions of exactly
+    args.steps steps each (synchronised on both sides; the median is the
+    result), per-GEMM launch durations from HIP events on the launch stream,
+    and optionally the same steps replayed from HIP graphs."""
+    gemms, calls, plans, keep = _build_workload(wl, dev, torch, w4, make_inputs, np)
+    copies = wl["copies"]
+    sh = stream.cuda_stream
+    calls_per_step = calls(sh)
+
+    def run_step(s):
+        for a in calls_per_step[s % copies]:
+            rc = lib.w4a16_gemm(*a)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+
+    # Warmup: the W steps asked for, continued (untimed) until at least
+    # WARMUP_MIN_S of back-to-back steps have run: from idle the GPU takes a
+    # fraction of a second to reach its working clocks.
+    t_w = time.perf_counter()
+    warmup_run = 0
+    while warmup_run < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+        run_step(warmup_run)
+        warmup_run += 1
+        if warmup_run % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+    # ---- timed regions: launches only, exactly args.steps steps each ----
+    walls = []
+    s_next = warmup_run
+    for _ in range(REPEATS):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            run_step(s_next + s)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        s_next += args.steps
+    wall = sorted(walls)[len(walls) // 2]
+
+    # Per-GEMM launch durations: each GEMM launched n_rep times back to back
+    # (its copies rotating) between two HIP events on the launch stream;
+    # duration per launch = span / n_rep.
+    n_rep = max(args.steps, 2 * copies, 10)
+    spans = {}
+    torch.cuda.synchronize()
+    for gi, g in enumerate(gemms):
+        gcalls = [calls_per_step[s][gi] for s in range(copies)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(n_rep):
+            rc = lib.w4a16_gemm(*gcalls[r % copies])
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+        e1.record(stream)
+        spans[g] = (e0, e1)
+    torch.cuda.synchronize()
+    launch_s = {g: e0.elapsed_time(e1) / n_rep / 1e3 for g, (e0, e1) in spans.items()}
+
+    graph_wall = None
+    if graph:
+        # one graph per rotation step, captured once on a side stream
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graphs = []
+        cap_calls = calls(cap.cuda_stream)
+        with torch.cuda.stream(cap):
+            for s in range(copies):
+                gph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gph, stream=cap):
+                    for a in cap_calls[s]:
+                        rc = lib.w4a16_gemm(*a)
+                        if rc != 0:
+                            raise RuntimeError(
+                                f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
+                graphs.append(gph)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        n_warm = max(args.warmup, 2 * copies)
+        for s in range(n_warm):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[(n_warm + s) % copies].replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        del graphs
+
+    step_flops = sum(roofline.flops(M, K, N) for (_, K, N, M) in gemms)
+    step_bytes = sum(roofline.algorithmic_bytes(M, K, N, GROUP) for (_, K, N, M) in gemms)
+    step_roof_s = sum(roofline.roofline_seconds(M, K, N, GROUP) for (_, K, N, M) in gemms)
+    per_gemm = []
+    for g in gemms:
+        name, K, N, M = g
+        t = launch_s[g]
+        per_gemm.append({
+            "layer": name, "M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
+            "tflops": round(roofline.flops(M, K, N) / t / 1e12, 2),
+            "tbps": round(roofline.algorithmic_bytes(M, K, N, GROUP) / t / 1e12, 3),
+            "roofline_frac": round(roofline.roofline_seconds(M, K, N, GROUP) / t, 3),
+            "bound": roofline.bound(M, K, N, GROUP), "plan": plans[g],
+        })
+    res = {
+        "workload": wl["workload"],
+        "value": step_flops / (wall / args.steps) / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_step": wall * 1e3 / args.steps,
+        "repeat_ms_per_step": [round(w * 1e3 / args.steps, 4) for w in walls],
+        "hbm_tbps": step_bytes / (wall / args.steps) / 1e12,
+        "step_roofline_frac": step_roof_s / (wall / args.steps),
+        "warmup_steps_run": warmup_run,
+        "events_ms_per_step": sum(launch_s.values()) * 1e3,
+        "graph": None if graph_wall is None else {
+            "launch": f"one HIP graph per step ({len(gemms)} kernel nodes), replayed",
+            "ms_per_step": graph_wall * 1e3 / args.steps,
+            "value": step_flops / (graph_wall / args.steps) / 1e12, "unit": "TFLOP/s"},
+        "per_gemm": per_gemm,
+        "weight_copies": copies,
+    }
+    res["roofline"] = _dominant_roofline(gemms, plans, launch_s, roofline, wl["traffic"])
+    res["_run_step"] = run_step
+    res["_next_step"] = s_next
+    res["_keep"] = keep
+    return res
+
+
+def _dominant_roofline(gemms, plans, launch_s, roofline, traffic_path):
+    """The roofline object of the kernel variant with the most time in a
+    step: algorithmic flops (MFMA-bound) or bytes (HBM-bound) per launch over
+    its average launch duration."""
+    by_kernel = {}
+    for g in gemms:
+        name, K, N, M = g
+        kname = plans[g].split()[0]
+        d = by_kernel.setdefault(kname, {"s": 0.0, "launches": 0, "bytes": 0, "flops": 0,
+                                         "hbm": 0, "mfma": 0})
+        d["s"] += launch_s[g]
+        d["launches"] += 1
+        d["bytes"] += roofline.algorithmic_bytes(M, K, N, GROUP)
+        d["flops"] += roofline.flops(M, K, N)
+        d[roofline.bound(M, K, N, GROUP)] += 1
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["s"])
+    avg_s = dom["s"] / dom["launches"]
+    if dom["hbm"] >= dom["mfma"]:
+        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved,
+                "peak": roofline.HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s"}
+    else:
+        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved,
+                "peak": roofline.MFMA_F16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(dom_name, traffic_path)
+    roof["traffic_unit"] = "bytes per launch"
+    roof["algorithmic_bytes"] = dom["bytes"] / dom["launches"]
+    roof["algorithmic_flops"] = dom["flops"] / dom["launches"]
+    roof["kernel"] = dom_name
+    roof["avg_launch_us"] = avg_s * 1e6
+    roof["launches_per_step"] = dom["launches"]
+    return roof
+
+
+def _clocks_under_load(run_step, first_step: int, torch, seconds: float = 2.0) -> str:
+    """rocm-smi's clock readout taken while steps keep the GPU busy."""
+    import subprocess
+    import threading
+    out = {}
+
+    def read():
+        out["clocks"] = _gpu_clocks()
+
+    th = threading.Thread(target=read)
+    t0 = time.perf_counter()
+    th.start()
+    s = first_step
+    while th.is_alive() and time.perf_counter() - t0 < seconds + 30:
+        run_step(s)
+        s += 1
+        if s % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    th.join()
+    return out.get("clocks", "")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -860,179 +1206,27 @@ def main():
     torch.cuda.set_device(dev)
     lib = w4.load()
     stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
 
-    # ---- inputs, resident in HBM -------------------------------------------
-    packed = {}     # layer -> list of WEIGHT_COPIES packed buffers
-    scales = {}
-    for name, K, N in LAYERS:
-        _, Bq, S = make_inputs(1, K, N, GROUP, seed=0)
-        Bq_d = torch.from_numpy(Bq.view(np.int32)).to(dev)
-        first = w4.alloc_packed(K, N)
-        w4.w4a16_repack(Bq_d, first, K, N)
-        packed[name] = [first] + [first.clone() for _ in range(WEIGHT_COPIES - 1)]
-        scales[name] = torch.from_numpy(S).to(dev)
-        del Bq_d
-    acts, outs = {}, {}
-    ws_bytes = 0
-    for name, K, N in LAYERS:
-        for M in BATCHES:
-            A, _, _ = make_inputs(M, K, 8, GROUP, seed=M)
-            acts[(name, M)] = torch.from_numpy(A).to(dev)
-            outs[(name, M)] = torch.empty((M, N), dtype=torch.float16, device=dev)
-            ws_bytes = max(ws_bytes, w4.w4a16_workspace_bytes(M, K, N, GROUP))
-    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
+    primary = WORKLOADS[args.workload]
+    res = _time_workload(primary, args, lib, torch, w4, roofline, stream, make_inputs, np, dev,
+                         graph=not args.no_graph)
+    clocks = "" if args.no_clocks else _clocks_under_load(res["_run_step"], res["_next_step"],
+                                                          torch)
+    del res["_run_step"], res["_next_step"], res["_keep"]
+    torch.cuda.empty_cache()
 
-    # the twelve GEMMs of a step, in order; copy index rotates per launch
-    gemms = [(name, K, N, M) for M in BATCHES for (name, K, N) in LAYERS]
-    plans = {g: w4.w4a16_describe(g[3], g[1], g[2], GROUP) for g in gemms}
+    secondary = None
+    if not args.no_secondary:
+        other = WORKLOADS["llama7b" if args.workload == "sweep" else "sweep"]
+        sec = _time_workload(other, args, lib, torch, w4, roofline, stream, make_inputs, np,
+                             dev, graph=not args.no_graph)
+        del sec["_run_step"], sec["_next_step"], sec["_keep"]
+        torch.cuda.empty_cache()
+        secondary = sec
 
-    def args_for(g, copy):
-        name, K, N, M = g
-        return (acts[(name, M)].data_ptr(), packed[name][copy].data_ptr(),
-                scales[name].data_ptr(), outs[(name, M)].data_ptr(), M, K, N, GROUP,
-                workspace.data_ptr(), sh)
-
-    # A layer is used three times a step (once per batch); its t-th use over
-    # the run reads copy t % WEIGHT_COPIES, so between two reads of the same
-    # copy every layer has been read WEIGHT_COPIES - 1 more times (~700 MB).
-    n_launch = len(gemms)
-    calls_per_step = [[args_for(g, (len(BATCHES) * s + BATCHES.index(g[3])) % WEIGHT_COPIES)
-                       for g in gemms] for s in range(WEIGHT_COPIES)]
-
-    def run_step(s):
-        for a in calls_per_step[s % WEIGHT_COPIES]:
-            rc = lib.w4a16_gemm(*a)
-            if rc != 0:
-                raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
-
-    # Warmup: the W steps asked for, continued (untimed) until at least
-    # WARMUP_MIN_S of back-to-back steps have run: from idle the GPU takes a
-    # fraction of a second to reach its working clocks, and a few steps
-    # alone would time the ramp, not the kernels.
-    t_w = time.perf_counter()
-    warmup_run = 0
-    while warmup_run < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
-        run_step(warmup_run)
-        warmup_run += 1
-        if warmup_run % 64 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    # ---- timed region ------------------------------------------------------
-    # The step as a user runs it: launches only.  (Recording an event per
-    # launch costs host time comparable to the small kernels themselves.)
-    torch.cuda.synchronize()
-    # (the weight-copy rotation continues from the warmup)
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(warmup_run + s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Per-GEMM durations behind the roofline object: each of the step's GEMMs
-    # launched K times back to back (its weight copies rotating) between two
-    # HIP events on the launch stream; duration per launch = span / K.  An
-    # event pair around every single launch would add the event packets'
-    # own time (a few microseconds) to each kernel.
-    n_rep = max(args.steps, 20)
-    per_gemm_ms = {}
-    torch.cuda.synchronize()
-    for gi, g in enumerate(gemms):
-        calls = [calls_per_step[s][gi] for s in range(WEIGHT_COPIES)]
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(n_rep):
-            rc = lib.w4a16_gemm(*calls[r % WEIGHT_COPIES])
-            if rc != 0:
-                raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
-        e1.record(stream)
-        per_gemm_ms[g] = (e0, e1)
-    torch.cuda.synchronize()
-    per_gemm_ms = {g: [e0.elapsed_time(e1) / n_rep] * n_rep for g, (e0, e1) in per_gemm_ms.items()}
-    gpu_ms_total = sum(v[0] for v in per_gemm_ms.values()) * n_rep
-
-    # The same steps replayed from HIP graphs: one graph per weight-copy
-    # rotation, each holding the step's twelve launches, captured once on a
-    # side stream.  A replay submits the step in one call, which removes the
-    # host's per-launch cost and the gaps it leaves between small kernels.
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    graphs = []
-    with torch.cuda.stream(cap):
-        for s in range(0 if args.no_graph else WEIGHT_COPIES):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for a in calls_per_step[s]:
-                    rc = lib.w4a16_gemm(*a[:-1], cap.cuda_stream)
-                    if rc != 0:
-                        raise RuntimeError(f"w4a16_gemm failed: {w4.w4a16_status_string(rc)}")
-            graphs.append(g)
-    stream.wait_stream(cap)
-    torch.cuda.synchronize()
-    graph_wall = None
-    if graphs:
-        n_warm = max(args.warmup, 2 * WEIGHT_COPIES)
-        for s in range(n_warm):
-            graphs[s % WEIGHT_COPIES].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            graphs[(n_warm + s) % WEIGHT_COPIES].replay()
-        torch.cuda.synchronize()
-        graph_wall = time.perf_counter() - t0
-    del graphs
-
-
-    step_flops = sum(roofline.flops(M, K, N) for (_, K, N, M) in gemms)
-    step_bytes = sum(roofline.algorithmic_bytes(M, K, N, GROUP) for (_, K, N, M) in gemms)
-    step_roof_s = sum(roofline.roofline_seconds(M, K, N, GROUP) for (_, K, N, M) in gemms)
-    ms_per_step = wall * 1e3 / args.steps
-    value = step_flops / (wall / args.steps) / 1e12
-
-    # ---- the dominant kernel: the variant with the most time in the step ----
-    by_kernel = {}
-    for g in gemms:
-        kname = plans[g].split()[0]
-        d = by_kernel.setdefault(kname, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0,
-                                         "hbm": 0, "mfma": 0})
-        d["ms"] += sum(per_gemm_ms[g])
-        d["launches"] += len(per_gemm_ms[g])
-        name, K, N, M = g
-        d["bytes"] += roofline.algorithmic_bytes(M, K, N, GROUP) * len(per_gemm_ms[g])
-        d["flops"] += roofline.flops(M, K, N) * len(per_gemm_ms[g])
-        d[roofline.bound(M, K, N, GROUP)] += 1
-    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
-    avg_s = dom["ms"] / dom["launches"] / 1e3
-    if dom["hbm"] >= dom["mfma"]:
-        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_BYTES_PER_S / 1e9,
-                "unit": "GB/s"}
-    else:
-        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved,
-                "peak": roofline.MFMA_F16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom_name)
-    roof["traffic_unit"] = "bytes per launch"
-    roof["algorithmic_bytes"] = dom["bytes"] / dom["launches"]
-    roof["kernel"] = dom_name
-    roof["avg_launch_us"] = avg_s * 1e6
-    roof["launches_per_step"] = dom["launches"] // n_rep
-
-    per_gemm = []
-    for g in gemms:
-        name, K, N, M = g
-        t = sorted(per_gemm_ms[g])[len(per_gemm_ms[g]) // 2] / 1e3
-        per_gemm.append({
-            "layer": name, "M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
-            "tflops": round(roofline.flops(M, K, N) / t / 1e12, 2),
-            "gbps": round(roofline.algorithmic_bytes(M, K, N, GROUP) / t / 1e9, 1),
-            "roofline_frac": round(roofline.roofline_seconds(M, K, N, GROUP) / t, 3),
-            "bound": roofline.bound(M, K, N, GROUP), "plan": plans[g],
-        })
+    ceilings = None
+    if not args.no_probes:
+        ceilings = measured_ceilings(torch, dev)
 
     if args.copy_probe:
         # torch's elementwise negation: one dispatch that reads and writes
@@ -1048,39 +1242,40 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_sample_cols)
+        cpu = cpu_baseline(primary, args.cpu_sample_cols)
 
     line = {
         "metric": "W4A16 GEMM TFLOP/s + achieved HBM TB/s (% roofline) at M=1..128, 1 MI355X",
-        "value": value,
+        "value": res["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": warmup_run,
-        "ms_per_step": ms_per_step,
+        "warmup_steps_run": res["warmup_steps_run"],
+        "ms_per_step": res["ms_per_step"],
+        "repeats": REPEATS,
+        "repeat_ms_per_step": res["repeat_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "Llama-2-7B-shaped W4A16 linear layers (qkv 4096x12288, o 4096x4096, "
-                        "gate/up 4096x22016, down 11008x4096), group 128, M in {1,16,128}; "
-                        "one step = the 12 GEMMs",
-            "group": GROUP, "batches": BATCHES, "weight_copies": WEIGHT_COPIES,
+            "workload": primary["workload"],
+            "group": GROUP, "batches": primary["batches"],
+            "weight_copies": primary["copies"],
             "parallelism": "single GPU",
         },
-        "hbm_tbps": step_bytes / (wall / args.steps) / 1e12,
-        "step_roofline_frac": step_roof_s / (wall / args.steps),
-        "events_pass_ms_per_step": gpu_ms_total / n_rep,
-        "graph": None if graph_wall is None else {
-            "launch": f"one HIP graph per step ({n_launch} kernel nodes), replayed",
-            "ms_per_step": graph_wall * 1e3 / args.steps,
-            "value": step_flops / (graph_wall / args.steps) / 1e12, "unit": "TFLOP/s"},
-        "roofline": roof,
+        "hbm_tbps": res["hbm_tbps"],
+        "step_roofline_frac": res["step_roofline_frac"],
+        "events_ms_per_step": res["events_ms_per_step"],
+        "graph": res["graph"],
+        "roofline": res["roofline"],
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
-        "per_gemm": per_gemm,
+        "per_gemm": res["per_gemm"],
+        "secondary": secondary,
+        "sclk": clocks,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(line))

@@ -91,6 +91,20 @@ size_t w4a16_packed_bytes(int K, int N);
  * W4A16_ERR_DEVICE.  Launches nothing. */
 int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len);
 
+/* Tuning and testing only: replace the plan heuristic of every later call
+ * in this process with the text spec
+ *   "mb,nb,wk,splits[,depth[,tile[,unused[,wm]]]]"
+ * (a field <= 0 keeps the heuristic's value; tile 0 is the streaming
+ * kernel, 2 the LDS kernel with 16 x 16 blocks, 3 with 32 x 32 blocks).  A
+ * spec naming a variant that is not compiled leaves the heuristic's plan in
+ * place.  NULL or "" restores the heuristic.  The environment variable
+ * W4A16_FORCE_PLAN, read once when the library first plans a call, seeds the
+ * same setting.  w4a16_workspace_bytes and w4a16_describe follow it, so a
+ * caller that changes it between sizing a workspace and a call must size
+ * again.  Not to be called while another thread plans a call.
+ * Returns W4A16_OK, or W4A16_ERR_SHAPE for text that is not a spec. */
+int w4a16_set_forced_plan(const char* spec);
+
 /*
  * w4a16_repack -- offline permutation of canonical codes into the layout
  * the GEMM reads.
@@ -123,12 +137,16 @@ int w4a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N,
  * 0 means the call needs no workspace.  Returns 0 for shapes w4a16_gemm
  * rejects.
  *
+ * Layout: a fixed 64 KiB header of 32-bit arrival counters (one per output
+ * tile, at the same place for every shape), then the FP32 partial tiles.
+ *
  * Contract: the caller allocates at least this many bytes and fills them
  * with zeros once, after allocating.  Every call leaves the counters at zero
  * again, so one workspace serves any number of later calls of any shape
  * whose requirement it covers, as long as those calls are ordered (same
  * stream, or synchronised).  Two calls running at the same time must not
- * share a workspace.
+ * share a workspace.  The workspace may not overlap A, Bpacked, scales, C
+ * or any other buffer of the call (W4A16_ERR_SHAPE).
  */
 size_t w4a16_workspace_bytes(int M, int K, int N, int group);
 
@@ -158,7 +176,8 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group);
  *           products accumulate in FP32, C is rounded once to FP16
  *           (round to nearest even; overflow gives +-inf).
  * Errors:   W4A16_ERR_NULL, _SHAPE, _GROUP, _ALIGN, _WORKSPACE, _DEVICE,
- *           _LAUNCH.  C must not overlap A, Bpacked, scales or workspace.
+ *           _LAUNCH.  C must not overlap A, Bpacked, scales or workspace,
+ *           and the workspace none of the inputs.
  */
 int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked,
                const uint16_t* scales, uint16_t* C, int M, int K, int N,

@@ -234,3 +234,20 @@ def test_roofline_accounting():
     # the ridge between the two peaks sits near M = 80 for weight-dominated shapes
     assert roofline.bound(64, 18432, 73728, 128) == "hbm"
     assert roofline.bound(128, 18432, 73728, 128) == "mfma"
+
+
+def test_forced_plan_setter(lib):
+    """The tuning override parses its text and can be cleared; the launch
+    path never reads the environment."""
+    assert lib.w4a16_set_forced_plan(b"1,2,4,1") == OK
+    assert lib.w4a16_set_forced_plan(b"1,2,4,1,2,0,0,1") == OK
+    assert lib.w4a16_set_forced_plan(b"4,1,8,2,3,2") == OK
+    assert lib.w4a16_set_forced_plan(b"1,2") == ERR_SHAPE        # fewer than four fields
+    assert lib.w4a16_set_forced_plan(b"1,2,4,1,2,1") == ERR_SHAPE  # no tile kernel 1
+    assert lib.w4a16_set_forced_plan(b"x") == ERR_SHAPE
+    assert lib.w4a16_set_forced_plan(None) == OK
+    assert lib.w4a16_set_forced_plan(b"") == OK
+    w4.w4a16_set_forced_plan("4,1,8,2,3,2")
+    w4.w4a16_set_forced_plan(None)
+    with pytest.raises(w4.W4A16Error):
+        w4.w4a16_set_forced_plan("1,2")

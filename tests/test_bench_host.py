@@ -44,12 +44,24 @@ def test_traffic_is_null_for_other_sources(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps({"kernel_source_hash": "0" * 16,
                              "kernels": {"k<1>": {"hbm_bytes_per_dispatch": 5.0}}}))
-    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(f))
-    assert bench.measured_traffic("k<1>") is None
+    assert bench.measured_traffic("k<1>", str(f)) is None
     f.write_text(json.dumps({"kernel_source_hash": bench.kernel_source_hash(),
                              "kernels": {"k<1>": {"hbm_bytes_per_dispatch": 5.0}}}))
-    assert bench.measured_traffic("k<1>") == 5.0
-    assert bench.measured_traffic("k<2>") is None
+    assert bench.measured_traffic("k<1>", str(f)) == 5.0
+    assert bench.measured_traffic("k<2>", str(f)) is None
+    assert bench.measured_traffic("k<1>", str(tmp_path / "absent.json")) is None
+
+
+def test_headline_workload_is_the_large_layer_sweep(monkeypatch):
+    """The default line times the batch sweep M = 1..128 on the 18432 x 73728
+    layer, the configuration the metric is quoted on."""
+    wl = bench.WORKLOADS["sweep"]
+    assert wl["layers"] == [("large", 18432, 73728)]
+    assert wl["batches"] == [1, 2, 4, 8, 16, 32, 64, 128]
+    # two copies of 680 MB of packed weights: well past the 256 MB cache
+    assert wl["copies"] * 18432 * 73728 // 2 > 2 * 256 * 10**6
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    assert bench.parse().workload == "sweep"
 
 
 def test_more_than_one_gpu_is_refused():

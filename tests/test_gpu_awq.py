@@ -25,8 +25,10 @@ FORMATS = [("f16+zp", 0, True), ("bf16", 1, False), ("bf16+zp", 1, True)]
 
 
 @pytest.fixture(autouse=True)
-def _no_forced_plan(monkeypatch):
-    monkeypatch.delenv("W4A16_FORCE_PLAN", raising=False)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
 
 
 def _inputs(M, K, N, group, seed, dtype, zp):
@@ -141,7 +143,7 @@ def test_awq_forced_plans_split_k(monkeypatch, fmt, dtype, zp, plan):
     N = 208 a ragged column tile, group 512."""
     M, K, N, group = 45, 3584, 208, 512
     A, Bq, S, Z = _inputs(M, K, N, group, 5, dtype, zp)
-    monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
+    w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_describe(M, K, N, group)
     assert "splits=1 " not in desc, desc
     say("awq forced", fmt, plan, desc)
@@ -202,7 +204,7 @@ def test_awq_plan_outside_the_compiled_variants_is_rejected(monkeypatch):
     import torch
     M, K, N = 45, 1024, 208
     A, Bq, S, Z = make_inputs_awq(M, K, N, 128, seed=3, bf16=True)
-    monkeypatch.setenv("W4A16_FORCE_PLAN", "4,2,4,1,3,2")
+    w4.w4a16_set_forced_plan("4,2,4,1,3,2")
     assert w4.w4a16_describe(M, K, N, 128).startswith("gemm_lds_kernel<4,2,1,4,3,16>")
     say("awq rejected plan")
     with pytest.raises(w4.W4A16Error) as e:

@@ -25,8 +25,10 @@ LLAMA_LAYERS = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)]
 
 
 @pytest.fixture(autouse=True)
-def _no_forced_plan(monkeypatch):
-    monkeypatch.delenv("W4A16_FORCE_PLAN", raising=False)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
 
 
 def _sample_cols(N, count, seed):

@@ -26,8 +26,10 @@ ACTS = {"none": w4.W4A16_ACT_NONE, "relu": w4.W4A16_ACT_RELU, "silu": w4.W4A16_A
 
 
 @pytest.fixture(autouse=True)
-def _no_forced_plan(monkeypatch):
-    monkeypatch.delenv("W4A16_FORCE_PLAN", raising=False)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
 
 
 @functools.lru_cache(maxsize=None)
@@ -47,10 +49,9 @@ def _check(C, C64, bias, act, what):
 # One variant of each kernel family, with and without split-K; M = 45 and
 # N = 208 leave ragged row and column tiles.
 FUSED_PLANS = ["1,2,4,1,2", "1,4,4,7,2",            # streaming kernel
-               "4,2,4,1,4,1", "4,2,4,3,2,1",        # tile kernel
                "4,1,8,1,3,2", "8,2,8,2,3,2", "1,4,8,1,4,2",   # LDS kernel, 16 x 16
                "4,1,8,1,3,3", "4,1,8,3,3,3"]        # LDS kernel, 32 x 32
-KERNEL_OF_TILE = {0: "gemm_kernel", 1: "gemm_tile_kernel", 2: "gemm_lds_kernel",
+KERNEL_OF_TILE = {0: "gemm_kernel", 2: "gemm_lds_kernel",
                   3: "gemm_lds_kernel"}
 
 
@@ -61,7 +62,7 @@ def test_fused_forced_plans(monkeypatch, plan, act, with_bias):
     M, K, N, group = 45, 3584, 208, 128
     A, Bq, S, bias, C64 = _case(M, K, N, group, 5)
     b = bias if with_bias else None
-    monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
+    w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_describe(M, K, N, group)
     fields = [int(x) for x in plan.split(",")]
     assert desc.startswith(KERNEL_OF_TILE[fields[5] if len(fields) > 5 else 0] + "<"), desc

@@ -23,8 +23,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True)
-def _no_forced_plan(monkeypatch):
-    monkeypatch.delenv("W4A16_FORCE_PLAN", raising=False)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
 
 
 # ---------------------------------------------------------------------------
@@ -142,10 +144,6 @@ def test_gemm_matches_oracle(M, K, N, group):
 
 STREAM_PLANS = ["1,1,4,1,2", "1,1,8,3,4", "1,2,4,2,2", "1,2,8,1,4", "1,4,4,7,2", "1,4,8,2,2",
                 "2,2,4,3,2", "2,4,4,1,2", "4,2,4,5,1", "4,4,4,1,1", "8,2,4,2,1", "8,4,4,1,1"]
-TILE_PLANS = ["4,2,2,1,4,1", "4,2,4,3,2,1", "4,2,4,1,4,1", "4,2,4,6,4,1", "4,4,2,2,4,1",
-              "4,4,4,1,4,1", "8,1,4,2,2,1", "8,2,2,1,2,1", "8,2,4,5,2,1", "8,4,2,1,2,1",
-              "8,4,4,2,2,1", "8,4,4,1,2,1", "8,4,4,3,4,1", "4,2,4,2,2,1,8", "8,1,4,3,2,1,8",
-              "4,2,4,1,4,1,8"]
 LDS_PLANS = ["4,2,2,1,3,2", "4,2,4,3,3,2", "4,2,4,1,4,2", "4,2,4,6,4,2", "4,4,4,2,3,2",
              "8,1,4,3,3,2", "8,2,4,1,2,2", "8,2,4,5,3,2", "8,4,4,2,2,2", "8,4,4,1,3,2",
              "4,1,8,2,3,2", "4,2,8,1,3,2", "8,1,8,3,3,2", "8,2,8,1,3,2",
@@ -158,7 +156,7 @@ LDS32_PLANS = ["4,1,8,1,3,3", "4,1,8,3,3,3", "2,1,8,3,3,3", "4,1,4,1,3,3", "2,2,
 LDS_GRID_PLANS = ["4,4,4,1,3,2,0,2", "2,4,2,3,3,2,0,4", "4,2,4,1,3,2,0,2", "2,2,2,2,3,2,0,4",
                   "2,2,4,5,3,2,0,2", "2,4,4,1,3,2,0,2", "4,4,2,2,3,2,0,2", "2,4,2,1,3,2,0,2",
                   "1,2,2,1,3,3,0,4", "1,4,2,3,3,3,0,4", "2,2,4,1,3,3,0,2"]
-KERNEL_OF_TILE = {0: "gemm_kernel", 1: "gemm_tile_kernel", 2: "gemm_lds_kernel",
+KERNEL_OF_TILE = {0: "gemm_kernel", 2: "gemm_lds_kernel",
                   3: "gemm_lds_kernel"}
 
 
@@ -167,7 +165,7 @@ def _forced_plan_case(monkeypatch, plan, group):
     M, K, N = 45, 3584, 208
     A, Bq, S = make_inputs(M, K, N, group, seed=5)
     _, C64 = oracle.gemm(A, Bq, S, group)
-    monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
+    w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_describe(M, K, N, group)
     fields = [int(x) for x in plan.split(",")]
     kernel = KERNEL_OF_TILE[fields[5] if len(fields) > 5 else 0]
@@ -183,23 +181,65 @@ def _forced_plan_case(monkeypatch, plan, group):
     assert_gemm_close(C, C64, f"plan {plan} group {group}")
 
 
-@pytest.mark.parametrize("plan", STREAM_PLANS + TILE_PLANS + LDS_PLANS + LDS32_PLANS +
+@pytest.mark.parametrize("plan", STREAM_PLANS + LDS_PLANS + LDS32_PLANS +
                          LDS_GRID_PLANS)
 def test_gemm_forced_plans_agree(monkeypatch, plan):
     """Every compiled variant and split count gives the oracle's answer."""
     _forced_plan_case(monkeypatch, plan, 128)
 
 
-@pytest.mark.parametrize("plan", ["1,2,4,3,2", "4,2,4,3,2,1", "4,2,4,3,3,2", "8,4,4,2,2,2",
+@pytest.mark.parametrize("plan", ["1,2,4,3,2", "4,2,4,3,3,2", "8,4,4,2,2,2",
                                   "4,1,8,2,3,3", "2,4,2,2,3,2,0,4", "1,2,2,2,3,3,0,4"])
 def test_gemm_forced_plans_coarse_groups(monkeypatch, plan):
     """A scale group of four K blocks (512): each K block finds its group row."""
     _forced_plan_case(monkeypatch, plan, 512)
 
 
-def test_gemm_deterministic_and_workspace_reuse():
+# Forced split-K plans for the workspace-reuse test: the streaming kernel
+# with 16-column tiles and the LDS kernel with 64 x 128 tiles, both split.
+REUSE_PLANS = ["1,1,4,2,2", "4,1,8,2,3,2"]
+
+
+@pytest.mark.parametrize("plan", REUSE_PLANS)
+def test_gemm_workspace_reuse_across_shapes(plan):
+    """One workspace, zero-filled once, serves split-K calls of two shapes in
+    turn: the second shape has more output tiles than the first, so with
+    counters placed after the first call's tile count its counters would
+    land on the first call's partial sums.  Both outputs match the oracle
+    and repeat bit for bit."""
+    import torch
+    w4.w4a16_set_forced_plan(plan)
+    shapes = [(16, 2048, 1024), (16, 2048, 4096)]
+    cases = []
+    for i, (M, K, N) in enumerate(shapes):
+        A, Bq, S = make_inputs(M, K, N, 128, seed=20 + i)
+        desc = w4.w4a16_describe(M, K, N, 128)
+        assert "splits=1 " not in desc, desc
+        cases.append((A, Bq, S, repack_on_device(dev(Bq), K, N), desc))
+    tiles = [int(c[4].split("grid=")[1].split("x")[0]) for c in cases]
+    assert tiles[1] > tiles[0], tiles
+    need = max(w4.w4a16_workspace_bytes(M, K, N, 128) for M, K, N in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    firsts = []
+    for (A, Bq, S, Bp, desc) in cases:
+        say("workspace reuse", plan, desc)
+        C = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)
+        _, C64 = oracle.gemm(A, Bq, S, 128)
+        assert_gemm_close(C, C64, desc)
+        firsts.append(C)
+    for rnd in range(3):
+        for i, (A, Bq, S, Bp, desc) in enumerate(cases):
+            again = run_gemm(A, Bq, S, 128, workspace=ws, Bp=Bp)
+            assert np.array_equal(firsts[i].view(np.uint16), again.view(np.uint16)), \
+                f"round {rnd} shape {shapes[i]}"
+    # every counter is back at zero after the calls
+    torch.cuda.synchronize()
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
+def test_gemm_deterministic_repeats():
     """Bit-identical output over repeated calls sharing one workspace, with a
-    call of another shape in between (the counters must be back at zero)."""
+    call of another shape in between."""
     import torch
     M, K, N = 16, 4096, 4096
     A, Bq, S = make_inputs(M, K, N, 128, seed=0)
@@ -307,3 +347,55 @@ def test_gemm_graph_capture_replays():
         assert torch.equal(C_g.view(torch.int16), C_eager.view(torch.int16)), f"replay {i}"
         w4.w4a16_gemm(A_d, Bp, S_d, C_eager, M, K, N, 128, ws)   # eager work in between
         torch.cuda.synchronize()
+
+
+def test_workspace_aliasing_an_input_is_rejected():
+    """Partial tiles are written while other workgroups read the inputs: a
+    workspace overlapping A, the weights or the scales is refused before any
+    launch."""
+    import ctypes
+    import torch
+    w4.w4a16_set_forced_plan("1,1,4,2,2")
+    M, K, N, g = 16, 2048, 1024, 128
+    A, Bq, S = make_inputs(M, K, N, g, seed=3)
+    need = w4.w4a16_workspace_bytes(M, K, N, g)
+    assert need > 0
+    big = torch.zeros(need + M * K * 2, dtype=torch.uint8, device="cuda")
+    A_d = big[: M * K * 2].view(torch.float16)
+    A_d.copy_(dev(A).view(-1))
+    Bp = repack_on_device(dev(Bq), K, N)
+    S_d = dev(S)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    lib = w4.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    for ws_ptr in (A_d.data_ptr(), Bp.data_ptr(), S_d.data_ptr()):
+        rc = lib.w4a16_gemm(A_d.data_ptr(), Bp.data_ptr(), S_d.data_ptr(), C.data_ptr(), M, K, N,
+                            g, ctypes.c_void_p(ws_ptr), stream)
+        assert rc == -2, rc   # W4A16_ERR_SHAPE
+    # a separate workspace is accepted
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    w4.w4a16_gemm(A_d, Bp, S_d, C, M, K, N, g, ws)
+    torch.cuda.synchronize()
+
+
+def test_binding_refuses_buffers_too_small():
+    """The C interface takes no sizes: the binding checks every tensor's
+    bytes before a pointer reaches the library."""
+    import torch
+    M, K, N, g = 4, 256, 64, 128
+    A, Bq, S = make_inputs(M, K, N, g, seed=4)
+    Bp = repack_on_device(dev(Bq), K, N)
+    A_d, S_d = dev(A), dev(S)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    short = torch.empty((M - 1, N), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="C"):
+        w4.w4a16_gemm(A_d, Bp, S_d, short, M, K, N, g, None)
+    with pytest.raises(ValueError, match="A"):
+        w4.w4a16_gemm(A_d[:2], Bp, S_d, C, M, K, N, g, None)
+    with pytest.raises(ValueError, match="scales"):
+        w4.w4a16_gemm(A_d, Bp, S_d[:1, :32].contiguous(), C, M, K, N, g, None)
+    with pytest.raises(ValueError, match="Bpacked"):
+        w4.w4a16_gemm(A_d, Bp[:16], S_d, C, M, K, N, g, None)
+    W = torch.empty((K - 128, N), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="W"):
+        w4.w4a16_dequant_debug(Bp, S_d, W, K, N, g)

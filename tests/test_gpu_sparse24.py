@@ -24,8 +24,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True)
-def _no_forced_plan(monkeypatch):
-    monkeypatch.delenv("W4A16_FORCE_PLAN", raising=False)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
 
 
 @pytest.mark.parametrize("K,N,exact", [(128, 16, True), (256, 64, False), (640, 48, True),
@@ -135,7 +137,7 @@ def test_gemm_sp24_forced_plans_split_k(monkeypatch, plan):
     M, K, N, group = 45, 3584, 208, 512
     A, Bq, S = make_inputs(M, K, N, group, seed=5)
     mask = make_mask24(K, N, seed=6, exact=False)
-    monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
+    w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_sparse24_describe(M, K, N, group)
     f = [int(x) for x in plan.split(",")] + [0, 0, 0]
     mb, nb, wk, depth, tile, wm = f[0], f[1], f[2], f[4], f[5], f[7] or 1

@@ -22,8 +22,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True)
-def _no_forced_plan(monkeypatch):
-    monkeypatch.delenv("W4A16_FORCE_PLAN", raising=False)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
 
 
 def _words8(K, N, seed):
@@ -116,7 +118,7 @@ def test_gemm8_forced_plans_split_k(monkeypatch, plan):
     M, K, N, group = 45, 3584, 208, 512
     A, _, S = make_inputs(M, K, N, group, seed=5)
     Bq8 = _words8(K, N, 9)
-    monkeypatch.setenv("W4A16_FORCE_PLAN", plan)
+    w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_describe(M, K, N, group)
     assert "splits=1 " not in desc, desc
     say("gemm8 forced", plan, desc)

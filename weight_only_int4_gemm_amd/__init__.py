@@ -28,6 +28,7 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
     w4a16_packed_bytes(K, N)
     w4a16_layout_version()
     w4a16_status_string(status)
+    w4a16_set_forced_plan(spec)          (tuning and testing only)
 
 A missing library is an error (``LibraryNotBuilt``); there is no fallback.
 """
@@ -46,7 +47,7 @@ __all__ = [
     "w4a16_sparse24_repack", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_workspace_bytes", "w4a16_sparse24_describe",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
-    "w4a16_status_string", "w4a16_describe", "EXPORTED_SYMBOLS",
+    "w4a16_status_string", "w4a16_describe", "w4a16_set_forced_plan", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,7 @@ EXPORTED_SYMBOLS = (
     "w8a16_packed_bytes", "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_repack", "w4a16_sparse24_workspace_bytes",
     "w4a16_sparse24_describe", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
+    "w4a16_set_forced_plan",
 )
 
 
@@ -141,6 +143,8 @@ def load():
     lib.w4a16_sparse24_gemm.restype = i
     lib.w4a16_sparse24_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.w4a16_sparse24_dequant_debug.restype = i
+    lib.w4a16_set_forced_plan.argtypes = [ctypes.c_char_p]
+    lib.w4a16_set_forced_plan.restype = i
     _lib = lib
     return lib
 
@@ -183,6 +187,52 @@ def _expect(t, dtype, what):
         raise ValueError(f"{what}: must be a device tensor")
 
 
+def _need(t, nbytes: int, what: str):
+    """The C interface takes no buffer sizes: a tensor smaller than the call
+    reads or writes, or one on another device than the current one, is
+    refused here, before any pointer reaches the library."""
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, the call needs {nbytes}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what}: on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
+def _shape_ok(M: int, K: int, N: int, group: int) -> bool:
+    """Shapes whose buffer sizes are defined; the library rejects the rest
+    with its own status code."""
+    return M >= 0 and K > 0 and N >= 0 and group > 0 and K % group == 0
+
+
+def _need_gemm(M, K, N, group, A, Bpacked, packed_bytes, scales, C, workspace, ws_bytes,
+               zeros=None, bias=None):
+    M, K, N, group = int(M), int(K), int(N), int(group)
+    if not _shape_ok(M, K, N, group) or M == 0 or N == 0:
+        return
+    _need(A, M * K * 2, "A")
+    _need(Bpacked, packed_bytes, "Bpacked")
+    _need(scales, (K // group) * N * 2, "scales")
+    _need(zeros, (K // group) * N, "zeros")
+    _need(bias, N * 2, "bias")
+    _need(C, M * N * 2, "C")
+    if ws_bytes:
+        _need(workspace, ws_bytes, "workspace")
+
+
+def _need_weights(K, N, group, Bpacked, packed_bytes, scales, W, zeros=None):
+    K, N, group = int(K), int(N), int(group)
+    if not _shape_ok(0, K, N, group) or N == 0:
+        return
+    _need(Bpacked, packed_bytes, "Bpacked")
+    _need(scales, (K // group) * N * 2, "scales")
+    _need(zeros, (K // group) * N, "zeros")
+    _need(W, K * N * 2, "W")
+
+
 # ---------------------------------------------------------------------------
 # the C interface, name for name
 # ---------------------------------------------------------------------------
@@ -209,10 +259,20 @@ def w4a16_describe(M: int, K: int, N: int, group: int) -> str:
     return buf.value.decode()
 
 
+def w4a16_set_forced_plan(spec=None) -> None:
+    """Tuning and testing only: force the plan of later calls (see the
+    header for the text); None restores the heuristic."""
+    arg = None if not spec else str(spec).encode()
+    _check("w4a16_set_forced_plan", load().w4a16_set_forced_plan(arg))
+
+
 def w4a16_repack(Bq, Bpacked, K: int, N: int, stream=None) -> None:
     import torch
     _expect(Bq, torch.int32, "Bq")
     _expect(Bpacked, torch.int32, "Bpacked")
+    if int(K) > 0 and int(N) > 0:
+        _need(Bq, int(K) * int(N) // 2, "Bq")
+        _need(Bpacked, w4a16_packed_bytes(K, N), "Bpacked")
     _check("w4a16_repack", load().w4a16_repack(_ptr(Bq), _ptr(Bpacked), int(K), int(N),
                                                _stream(stream)))
 
@@ -224,6 +284,8 @@ def w4a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
     _expect(Bpacked, torch.int32, "Bpacked")
     _expect(scales, torch.float16, "scales")
     _expect(C, torch.float16, "C")
+    _need_gemm(M, K, N, group, A, Bpacked, w4a16_packed_bytes(K, N), scales, C, workspace,
+               w4a16_workspace_bytes(M, K, N, group))
     _check("w4a16_gemm", load().w4a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
                                            int(M), int(K), int(N), int(group),
                                            _ptr(workspace), _stream(stream)))
@@ -237,6 +299,8 @@ def w4a16_gemm_fused(A, Bpacked, scales, bias, activation: int, C, M: int, K: in
     _expect(scales, torch.float16, "scales")
     _expect(bias, torch.float16, "bias")
     _expect(C, torch.float16, "C")
+    _need_gemm(M, K, N, group, A, Bpacked, w4a16_packed_bytes(K, N), scales, C, workspace,
+               w4a16_workspace_bytes(M, K, N, group), bias=bias)
     _check("w4a16_gemm_fused",
            load().w4a16_gemm_fused(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(bias),
                                    int(activation), _ptr(C), int(M), int(K), int(N),
@@ -261,6 +325,8 @@ def w4a16_gemm_awq(A, Bpacked, scales, zeros, C, M: int, K: int, N: int, group: 
     _expect16(scales, "scales")
     _expect(zeros, torch.uint8, "zeros")
     _expect16(C, "C")
+    _need_gemm(M, K, N, group, A, Bpacked, w4a16_packed_bytes(K, N), scales, C, workspace,
+               w4a16_workspace_bytes(M, K, N, group), zeros=zeros)
     _check("w4a16_gemm_awq",
            load().w4a16_gemm_awq(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(zeros), _ptr(C),
                                  int(M), int(K), int(N), int(group), int(dtype),
@@ -274,6 +340,7 @@ def w4a16_dequant_awq_debug(Bpacked, scales, zeros, W, K: int, N: int, group: in
     _expect16(scales, "scales")
     _expect(zeros, torch.uint8, "zeros")
     _expect16(W, "W")
+    _need_weights(K, N, group, Bpacked, w4a16_packed_bytes(K, N), scales, W, zeros=zeros)
     _check("w4a16_dequant_awq_debug",
            load().w4a16_dequant_awq_debug(_ptr(Bpacked), _ptr(scales), _ptr(zeros), _ptr(W),
                                           int(K), int(N), int(group), int(dtype),
@@ -288,6 +355,9 @@ def w8a16_repack(Bq8, Bpacked, K: int, N: int, stream=None) -> None:
     import torch
     _expect(Bq8, torch.int32, "Bq8")
     _expect(Bpacked, torch.int32, "Bpacked")
+    if int(K) > 0 and int(N) > 0:
+        _need(Bq8, int(K) * int(N), "Bq8")
+        _need(Bpacked, w8a16_packed_bytes(K, N), "Bpacked")
     _check("w8a16_repack", load().w8a16_repack(_ptr(Bq8), _ptr(Bpacked), int(K), int(N),
                                                _stream(stream)))
 
@@ -299,6 +369,8 @@ def w8a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
     _expect(Bpacked, torch.int32, "Bpacked")
     _expect(scales, torch.float16, "scales")
     _expect(C, torch.float16, "C")
+    _need_gemm(M, K, N, group, A, Bpacked, w8a16_packed_bytes(K, N), scales, C, workspace,
+               w4a16_workspace_bytes(M, K, N, group))
     _check("w8a16_gemm", load().w8a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
                                            int(M), int(K), int(N), int(group),
                                            _ptr(workspace), _stream(stream)))
@@ -309,6 +381,7 @@ def w8a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int, stream=N
     _expect(Bpacked, torch.int32, "Bpacked")
     _expect(scales, torch.float16, "scales")
     _expect(W, torch.float16, "W")
+    _need_weights(K, N, group, Bpacked, w8a16_packed_bytes(K, N), scales, W)
     _check("w8a16_dequant_debug",
            load().w8a16_dequant_debug(_ptr(Bpacked), _ptr(scales), _ptr(W), int(K), int(N),
                                       int(group), _stream(stream)))
@@ -320,6 +393,7 @@ def w4a16_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,
     _expect(Bpacked, torch.int32, "Bpacked")
     _expect(scales, torch.float16, "scales")
     _expect(W, torch.float16, "W")
+    _need_weights(K, N, group, Bpacked, w4a16_packed_bytes(K, N), scales, W)
     _check("w4a16_dequant_debug",
            load().w4a16_dequant_debug(_ptr(Bpacked), _ptr(scales), _ptr(W), int(K), int(N),
                                       int(group), _stream(stream)))
@@ -345,6 +419,10 @@ def w4a16_sparse24_repack(Bq, mask, Bpacked, K: int, N: int, stream=None) -> Non
     _expect(Bq, torch.int32, "Bq")
     _expect(mask, torch.uint8, "mask")
     _expect(Bpacked, torch.int32, "Bpacked")
+    if int(K) > 0 and int(N) > 0:
+        _need(Bq, int(K) * int(N) // 2, "Bq")
+        _need(mask, int(K) * int(N) // 4, "mask")
+        _need(Bpacked, w4a16_sparse24_packed_bytes(K, N), "Bpacked")
     _check("w4a16_sparse24_repack",
            load().w4a16_sparse24_repack(_ptr(Bq), _ptr(mask), _ptr(Bpacked), int(K), int(N),
                                         _stream(stream)))
@@ -357,6 +435,8 @@ def w4a16_sparse24_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: in
     _expect(Bpacked, torch.int32, "Bpacked")
     _expect(scales, torch.float16, "scales")
     _expect(C, torch.float16, "C")
+    _need_gemm(M, K, N, group, A, Bpacked, w4a16_sparse24_packed_bytes(K, N), scales, C,
+               workspace, w4a16_sparse24_workspace_bytes(M, K, N, group))
     _check("w4a16_sparse24_gemm",
            load().w4a16_sparse24_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C), int(M),
                                       int(K), int(N), int(group), _ptr(workspace),
@@ -369,6 +449,7 @@ def w4a16_sparse24_dequant_debug(Bpacked, scales, W, K: int, N: int, group: int,
     _expect(Bpacked, torch.int32, "Bpacked")
     _expect(scales, torch.float16, "scales")
     _expect(W, torch.float16, "W")
+    _need_weights(K, N, group, Bpacked, w4a16_sparse24_packed_bytes(K, N), scales, W)
     _check("w4a16_sparse24_dequant_debug",
            load().w4a16_sparse24_dequant_debug(_ptr(Bpacked), _ptr(scales), _ptr(W), int(K),
                                                int(N), int(group), _stream(stream)))

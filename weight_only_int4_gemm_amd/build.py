@@ -3,7 +3,8 @@
     python -m weight_only_int4_gemm_amd.build
 
 Compiles each translation unit with hipcc (in parallel) into ``_build/`` at
-the repository root and links ``weight_only_int4_gemm_amd/libw4a16.so``.
+the repository root and links ``weight_only_int4_gemm_amd/libw4a16.so``, then
+the measurement probes (``csrc/probes.hip``) into ``libw4a16_probes.so``.
 Cross-compiles without a GPU.  Always rebuilds.
 """
 
@@ -20,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm_tile.hip", "gemm_lds.hip", "repack.hip", "dequant.hip"]
+PROBES_LIB = os.path.join(PKG, "libw4a16_probes.so")
+SOURCES = ["api.hip", "gemm.hip", "gemm_lds.hip", "repack.hip", "dequant.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -71,6 +73,12 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the measurement probes: a library of their own, loaded by bench.py only
+    pobj = os.path.join(BUILD, "probes.o")
+    _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, "probes.hip"), "-o", pobj])
+    tmp = PROBES_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, pobj])
+    os.replace(tmp, PROBES_LIB)
     return LIB
 
 

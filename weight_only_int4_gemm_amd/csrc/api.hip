@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/w4a16.h"
 #include "format.hpp"
@@ -70,36 +71,71 @@ bool variant_is_compiled(const Plan& q, int fmt) {
   }
   if (q.tile >= 2)
     return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth, q.tile == 3 ? 32 : 16);
-  if (q.wm != 1) return false;
-  return q.tile ? tile_is_compiled(q.mb, q.nb, q.wk, q.depth, q.bdepth)
-                : plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
+  if (q.wm != 1 || q.tile != 0) return false;
+  return plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
 }
 
-// Test and tuning override:
-// W4A16_FORCE_PLAN="mb,nb,wk,splits[,depth[,tile[,bdepth[,wm]]]]" replaces the
-// heuristic's choice when it names a compiled variant (a field <= 0 keeps
-// the heuristic's value; tile is 0, the default, for the streaming kernel,
-// 1 for the tile kernel, 2 for the LDS kernel with 16 x 16 blocks or 3 for
-// the LDS kernel with 32 x 32 blocks).  It feeds the same kernels;
-// w4a16_workspace_bytes sees it too, so sizes stay consistent within a
-// process.
+// Test and tuning override of the plan heuristic: a process-wide setting,
+// seeded once from the environment variable W4A16_FORCE_PLAN when the
+// library first plans a call, and replaced by w4a16_set_forced_plan.  The
+// text is "mb,nb,wk,splits[,depth[,tile[,unused[,wm]]]]": a field <= 0 keeps
+// the heuristic's value; tile is 0 (the default) for the streaming kernel,
+// 2 for the LDS kernel with 16 x 16 blocks, 3 for the LDS kernel with
+// 32 x 32 blocks.  The override feeds the same kernels, and
+// w4a16_workspace_bytes sees it as well, so sizes agree as long as it is
+// not changed between the two calls.
+struct ForcedPlan {
+  bool set;
+  int mb, nb, wk, splits, depth, tile, wm;
+};
+
+std::mutex g_force_mu;
+ForcedPlan g_force{};
+std::atomic<bool> g_force_any{false};
+std::once_flag g_force_env_once;
+
+// Parse an override; false if the text is not one.
+bool parse_forced_plan(const char* text, ForcedPlan* out) {
+  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0, unused = 0, wm = 0;
+  if (std::sscanf(text, "%d,%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
+                  &unused, &wm) < 4)
+    return false;
+  if (tile != 0 && tile != 2 && tile != 3) return false;
+  *out = ForcedPlan{true, mb, nb, wk, splits, depth, tile, wm};
+  return true;
+}
+
+void set_forced(const ForcedPlan& f) {
+  std::lock_guard<std::mutex> lock(g_force_mu);
+  g_force = f;
+  g_force_any.store(f.set, std::memory_order_release);
+}
+
+void seed_forced_from_env() {
+  std::call_once(g_force_env_once, [] {
+    const char* env = std::getenv("W4A16_FORCE_PLAN");
+    ForcedPlan f{};
+    if (env && *env && parse_forced_plan(env, &f)) set_forced(f);
+  });
+}
+
 void apply_forced_plan(Plan* p, int KB, int fmt) {
-  const char* env = std::getenv("W4A16_FORCE_PLAN");
-  if (!env || !*env) return;
-  int mb = 0, nb = 0, wk = 0, splits = 0, depth = 0, tile = 0, bdepth = 0, wm = 0;
-  if (std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
-                  &bdepth, &wm) < 4)
-    return;
-  if (tile < 0 || tile > 3) return;
+  seed_forced_from_env();
+  if (!g_force_any.load(std::memory_order_acquire)) return;
+  ForcedPlan f;
+  {
+    std::lock_guard<std::mutex> lock(g_force_mu);
+    f = g_force;
+  }
+  if (!f.set) return;
   Plan q = *p;
-  q.tile = tile;  // absent: the streaming kernel
-  if (mb > 0) q.mb = mb;
-  if (nb > 0) q.nb = nb;
-  if (wk > 0) q.wk = wk;
-  if (splits > 0) q.splits = splits > KB ? KB : splits;
-  if (depth > 0) q.depth = depth;
-  q.bdepth = bdepth > 0 ? bdepth : (q.tile == 1 ? 4 : 0);
-  q.wm = wm > 0 ? wm : 1;
+  q.tile = f.tile;
+  if (f.mb > 0) q.mb = f.mb;
+  if (f.nb > 0) q.nb = f.nb;
+  if (f.wk > 0) q.wk = f.wk;
+  if (f.splits > 0) q.splits = f.splits > KB ? KB : f.splits;
+  if (f.depth > 0) q.depth = f.depth;
+  q.wm = f.wm > 0 ? f.wm : 1;
   if (!variant_is_compiled(q, fmt)) {
     // keep the forced tile but take the first compiled depth for it
     for (int d : {4, 3, 2, 1}) {
@@ -129,12 +165,6 @@ int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len)
                   "workspace=%zu",
                   p.mb, p.nb, p.wm, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
                   p.splits, 64 * p.wm * p.wk, p.splits, p.workspace_bytes);
-  else if (p.tile)
-    std::snprintf(buf, len,
-                  "gemm_tile_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
-                  "workspace=%zu",
-                  p.mb, p.nb, p.wk, p.depth, p.bdepth, p.tiles_n, p.tiles_m, p.splits,
-                  64 * p.wk, p.splits, p.workspace_bytes);
   else
     std::snprintf(buf, len,
                   "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
@@ -315,9 +345,10 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   apply_forced_plan(&p, KB, fmt);
   shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
+  if (ftiles > kMaxSplitTiles) p.splits = 1;  // the counter header holds one per tile
   p.workspace_bytes = 0;
   if (p.splits > 1) {
-    p.workspace_bytes = counters_bytes((int)ftiles) +
+    p.workspace_bytes = kCounterHeaderBytes +
                         (size_t)ftiles * p.splits * p.tm * p.tn * sizeof(float);
   }
   return p;
@@ -330,6 +361,18 @@ using namespace w4a16;
 extern "C" {
 
 int w4a16_layout_version(void) { return kLayoutVersion; }
+
+int w4a16_set_forced_plan(const char* spec) {
+  seed_forced_from_env();  // a later first plan must not overwrite this
+  if (!spec || !*spec) {
+    set_forced(ForcedPlan{});
+    return W4A16_OK;
+  }
+  ForcedPlan f{};
+  if (!parse_forced_plan(spec, &f)) return W4A16_ERR_SHAPE;
+  set_forced(f);
+  return W4A16_OK;
+}
 
 const char* w4a16_status_string(int status) {
   switch (status) {
@@ -445,7 +488,15 @@ int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* sca
   if (plan.workspace_bytes > 0) {
     if (!workspace) return W4A16_ERR_WORKSPACE;
     if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
-    if (overlap(C, cbytes, workspace, plan.workspace_bytes)) return W4A16_ERR_SHAPE;
+    // partial tiles are written while other workgroups still read the
+    // inputs: the workspace may alias none of the buffers
+    const size_t wb = plan.workspace_bytes;
+    if (overlap(workspace, wb, C, cbytes) || overlap(workspace, wb, A, (size_t)M * K * 2) ||
+        overlap(workspace, wb, Bpacked, pbytes) ||
+        overlap(workspace, wb, scales, (size_t)(K / group) * N * 2) ||
+        (bias && overlap(workspace, wb, bias, (size_t)N * 2)) ||
+        (zeros && overlap(workspace, wb, zeros, (size_t)(K / group) * N)))
+      return W4A16_ERR_SHAPE;
   }
   const Epilogue ep{reinterpret_cast<const _Float16*>(bias), activation};
   const WeightFormat wf{fmt, zeros};

@@ -24,7 +24,8 @@
 // In every format (q - z) is an integer in -15..15 and the product with the
 // scale is exact before its one rounding to the 16-bit type.
 //
-// FP16 with a zero point uses the FP16 trick of unpack.hpp with the
+// FP16 with a zero point uses the magic-number conversion of unpack.hpp
+// (FasterTransformer; Kim et al. 2022) with the
 // subtrahends 1024 + z and 64 + z instead of 1032 and 72: both are exact in
 // FP16, so the difference is the exact integer q - z.  The BF16 formats take
 // that same exact q - z in FP16, widen each half to FP32, multiply by the

@@ -406,8 +406,7 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
   float* partials = nullptr;
   if (p.splits > 1) {
     counters = static_cast<unsigned*>(workspace);
-    partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        counters_bytes(p.tiles_n * p.tiles_m));
+    partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterHeaderBytes);
   }
   const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WK);
   auto a = reinterpret_cast<const _Float16*>(A);
@@ -471,10 +470,7 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
   const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
   if (p.tile >= 2)
     return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, ep, wf, workspace, stream);
-  if (p.tile) {
-    if (wf.fmt != kFmtF16) return hipErrorInvalidValue;  // the tile kernel is FP16 only
-    return launch_tile(p, A, Bp, S, C, M, K, N, gmagic, ep, workspace, stream);
-  }
+  if (p.tile) return hipErrorInvalidValue;
   if (wf.fmt == kFmtF16) {
 #define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \

@@ -4,15 +4,16 @@
 // A workgroup of WM x WN waves owns an F*MB*WM x F*NB*WN output tile and one
 // K range; wave (wm, wn) owns the F*MB x F*NB block at row block wm, column
 // block wn.  With WM = 1 every wave spans all rows and each weight is
-// unpacked once per workgroup (the tile kernel's decomposition); with
-// WM > 1 each weight is unpacked by WM waves, but a wave reads only its own
-// rows of the activation stage, which divides the LDS bytes read per matrix
-// instruction (each wave re-reads its activation rows for every K block).
-// The difference from the tile kernel (gemm_tile.hip) is the load pipeline.  Vector-memory loads of a
-// wave complete in issue order, so in the tile kernel the wait for an
-// activation stage also waits for every code load issued before it, and the
-// codes (which come from HBM) never get more than a couple of K blocks of
-// latency allowance however early they are issued.  Here one K block's
+// unpacked once per workgroup; with WM > 1 each weight is unpacked by WM
+// waves, but a wave reads only its own rows of the activation stage, which
+// divides the LDS bytes read per matrix instruction (each wave re-reads its
+// activation rows for every K block).
+//
+// Vector-memory loads of a wave complete in issue order, so if the codes
+// went to registers and the activations to LDS, the wait for an activation
+// stage would also wait for every code load issued before it, and the codes
+// (which come from HBM) would never get more than a couple of K blocks of
+// latency allowance however early they were issued.  Here one K block's
 // activations, codes and scales form one LDS stage and are all brought in by
 // the direct 16-byte global -> LDS load ("Quant Marlin kernel" explainer,
 // "The architecture", top row: async copies of the next tile into shared
@@ -24,7 +25,7 @@
 //
 // Stage layout (per K block):
 //  * activations: 16*MB rows x 16 pieces of 16 bytes, piece c of row r at
-//    slot c ^ (r & 15) (conflict-free fragment reads, as in the tile kernel);
+//    slot c ^ (r & 15) (conflict-free fragment reads);
 //  * codes: the NB*WN (16-column) fragment blocks of the tile, 1 KiB each,
 //    in the permuted layout's own order (lane l's four words at 16*l), so a
 //    wave reads its fragments with one conflict-free 16-byte read per block;
@@ -446,8 +447,7 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
   float* partials = nullptr;
   if (p.splits > 1) {
     counters = static_cast<unsigned*>(workspace);
-    partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        counters_bytes(p.tiles_n * p.tiles_m));
+    partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterHeaderBytes);
   }
   const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WM * WN);
   auto a = reinterpret_cast<const _Float16*>(A);

@@ -8,29 +8,26 @@
 namespace w4a16 {
 
 // How one w4a16_gemm call is cut into work.
-//  tile   0: the streaming kernel (small batches), 1: the tile kernel
-//         (codes through registers), 2: the LDS kernel (every operand
-//         through LDS stages) with 16 x 16 matrix blocks, 3: the LDS kernel
-//         with 32 x 32 blocks (mb and nb then count 32-row / 32-column
-//         blocks)
+//  tile   0: the streaming kernel (small batches), 2: the LDS kernel
+//         (every operand through LDS stages) with 16 x 16 matrix blocks,
+//         3: the LDS kernel with 32 x 32 blocks (mb and nb then count
+//         32-row / 32-column blocks)
 //  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
 //  nb     16-column blocks per wave
 //  wk     waves per workgroup (LDS kernel: waves along N).  Streaming
 //         kernel: they split the workgroup's K range (every wk-th 128-deep
 //         K block each) and their sums are added in wave order through LDS;
-//         the N tile is 16 * nb.  Tile and LDS kernels: they split the N
-//         tile, which is 16 * nb * wk.
+//         the N tile is 16 * nb.  LDS kernel: they split the N tile, which
+//         is 16 * nb * wk.
 //  wm     LDS kernel: waves along M (1 elsewhere); the M tile is
 //         16 * mb * wm (32 * ... with 32 x 32 blocks), the workgroup
 //         wm * wk waves
 //  splits K ranges per output tile, one workgroup each; their FP32
 //         partials go through the workspace and are added in split order
-//  depth  streaming kernel: K blocks each wave keeps in flight; tile
-//         kernel: activation stages in LDS (K blocks of activations in
-//         flight + 1); LDS kernel: stages of activations, codes and scales
-//  bdepth tile kernel: K blocks of codes in flight (register slots)
+//  depth  streaming kernel: K blocks each wave keeps in flight; LDS
+//         kernel: stages of activations, codes and scales
 struct Plan {
-  int tile, mb, nb, wk, splits, depth, bdepth, wm;
+  int tile, mb, nb, wk, splits, depth, wm;
   int tm, tn;              // output tile of one workgroup
   int tiles_n, tiles_m;
   size_t workspace_bytes;  // 0 when splits == 1
@@ -57,7 +54,6 @@ struct WeightFormat {
 Plan make_plan(int M, int K, int N, int group, int cus, int fmt = 0);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
-bool tile_is_compiled(int mb, int nb, int wn, int ns, int db);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
 bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns);
 
@@ -69,9 +65,6 @@ hipError_t launch_repack_sp24(const uint32_t* Bq, const uint8_t* mask, uint32_t*
                               int N, hipStream_t stream);
 hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
                           int K, int N, int group, hipStream_t stream);
-hipError_t launch_tile(const Plan& p, const uint16_t* A, const uint32_t* Bp,
-                       const uint16_t* S, uint16_t* C, int M, int K, int N,
-                       uint64_t gmagic, Epilogue ep, void* workspace, hipStream_t stream);
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
                       Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream);
@@ -83,11 +76,15 @@ hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8
                               uint16_t* W, int K, int N, int group, int fmt,
                               hipStream_t stream);
 
-// Workspace layout for a plan with splits > 1: one 32-bit arrival counter
-// per output tile (padded to 256 bytes), then FP32 partial tiles
-// [tile][split][16*mb rows][16*nb cols].
-inline size_t counters_bytes(int tiles) {
-  return ((size_t)tiles * 4 + 255) / 256 * 256;
-}
+// Workspace layout for a plan with splits > 1: a fixed header of
+// kMaxSplitTiles 32-bit arrival counters (one per output tile; 64 KiB
+// whatever the shape), then the FP32 partial tiles
+// [tile][split][tile rows][tile cols].  The header's size does not depend on
+// the call, so the counters of one call never sit where an earlier call of
+// another shape left partial sums: every call leaves the counters it used at
+// zero, and a workspace zero-filled once serves calls of any shape in turn.
+// Plans split K only when the output has at most kMaxSplitTiles tiles.
+constexpr int kMaxSplitTiles = 16384;
+constexpr size_t kCounterHeaderBytes = (size_t)kMaxSplitTiles * sizeof(unsigned);
 
 }  // namespace w4a16

@@ -1,5 +1,4 @@
-// Pieces shared by the two LDS-staged GEMM kernels (gemm_tile.hip,
-// gemm_lds.hip): address-space casts for the direct global -> LDS load, a
+// Pieces of the LDS-staged GEMM kernel (gemm_lds.hip): address-space casts for the direct global -> LDS load, a
 // count-based wait, and the output stage with its split-K hand-off.
 #pragma once
 

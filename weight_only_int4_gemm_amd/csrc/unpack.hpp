@@ -2,14 +2,18 @@
 // weights (q - 8) * s, in the order the 16x16x32 FP16 matrix instruction
 // takes its B operand.
 //
-// The pages: each thread unpacks INT4 codes to FP16 with bitwise operations
-// and a small lookup trick, then multiplies by the group scale ("Quant
-// Marlin kernel" explainer, "The architecture: every piece explained",
-// middle row), a handful of instructions per group of weights ("Why
-// architecture matters here").
+// The pages have every thread turn its 4-bit codes into FP16 values with a
+// few bit operations and then apply the group scale ("Quant Marlin kernel"
+// explainer, "The architecture: every piece explained", middle row; "Why
+// architecture matters here" on keeping it to a handful of instructions).
 //
-// The trick used here: OR-ing a 4-bit code into the mantissa of a suitable
-// FP16 constant yields "constant + code" with no conversion instruction.
+// The conversion is the published FP16 "magic number" method for 4-bit
+// integers (NVIDIA FasterTransformer's mixed-precision GEMM; Kim et al.,
+// "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud
+// Scale Production", 2022): OR-ing a small integer into the low mantissa
+// bits of a suitable FP16 constant gives "constant + integer" with no
+// conversion instruction, and one exact subtraction removes the constant.
+// This routine restates it for this library's nibble order:
 //  * A code in bits 0..3 of a 16-bit half, OR-ed into 1024.0 (0x6400,
 //    mantissa unit 1), gives 1024 + q.
 //  * A code in bits 4..7, OR-ed into 64.0 (0x5400, mantissa unit 1/16),
