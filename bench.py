@@ -72,7 +72,8 @@ XCDS = 8                        # accelerator complex dies
 WARMUP_MIN_S = 0.5   # untimed steps run at least this long before timing
 REPEATS = 5          # timed regions of exactly --steps steps; the median is reported
 PROBE_READ_BYTES = 2 * 2**30    # the stream-read ceiling: a 2 GiB buffer read once per launch
-PROBE_MFMA_ITERS = 4096
+PROBE_MFMA_ITERS = 2048
+PROBE_MFMA_BLOCKS = 1024         # four waves per SIMD
 
 # The workloads.  "sweep" is the one the metric is quoted on: the large
 # single layer at every batch size from 1 to 128.
@@ -388,7 +389,7 @@ def measured_ceilings(torch, dev):
     t_read = timed(lambda: lib.w4a16_probe_read(buf.data_ptr(), PROBE_READ_BYTES,
                                                 sink.data_ptr(), read_blocks, sh))
     del buf
-    mfma_blocks = 256 * 8   # 8192 waves: eight per SIMD
+    mfma_blocks = PROBE_MFMA_BLOCKS
     t_mfma = timed(lambda: lib.w4a16_probe_mfma(sink.data_ptr(), mfma_blocks, PROBE_MFMA_ITERS,
                                                 sh))
     flops = lib.w4a16_probe_mfma_flops(mfma_blocks, PROBE_MFMA_ITERS)
@@ -400,8 +401,8 @@ def measured_ceilings(torch, dev):
         "mfma_f16_tflops": mfma_tflops,
         "mfma_frac_of_peak": mfma_tflops / (roofline.MFMA_F16_PEAK_FLOPS / 1e12),
         "probe": "2 GiB read once with 16-byte non-temporal loads (2048 workgroups of 512); "
-                 f"{PROBE_MFMA_ITERS} rounds of 8 independent v_mfma_f32_16x16x32_f16 per wave, "
-                 "2048 workgroups of 4 waves; median of 5 launches each",
+                 f"{PROBE_MFMA_ITERS} rounds of 16 independent v_mfma_f32_16x16x32_f16 per wave, "
+                 f"{PROBE_MFMA_BLOCKS} workgroups of 4 waves; median of 5 launches each",
     }
 
 
@@ -794,6 +795,7 @@ def formats_report(out_path: str, repeats: int = 7, launches: int = 50) -> None:
                     1: torch.from_numpy(Ab.view(np.int16)).to(dev)}
             C_d = torch.empty((M, N), dtype=torch.int16, device=dev)
             ws = torch.zeros(max(w4.w4a16_workspace_bytes(M, K, N, GROUP),
+                                 w4.w8a16_workspace_bytes(M, K, N, GROUP),
                                  w4.w4a16_sparse24_workspace_bytes(M, K, N, GROUP), 256),
                              dtype=torch.uint8, device=dev)
 

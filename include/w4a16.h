@@ -51,7 +51,7 @@ enum w4a16_status {
     W4A16_ERR_SHAPE = -2,     /* M, K or N out of range or not a multiple    */
     W4A16_ERR_GROUP = -3,     /* group not a multiple of 128 dividing K      */
     W4A16_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned            */
-    W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed       */
+    W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed      */
     W4A16_ERR_LAUNCH = -6,    /* the kernel launch failed                    */
     W4A16_ERR_DEVICE = -7,    /* no usable current HIP device                */
     W4A16_ERR_EPILOGUE = -8,  /* unknown activation for w4a16_gemm_fused     */
@@ -265,9 +265,16 @@ size_t w8a16_packed_bytes(int K, int N);
  * device to device on `stream`.  Requirements and errors as w4a16_repack. */
 int w8a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N, void* stream);
 
-/* C = A . dequant8(Bpacked, scales): arguments, layouts, workspace (the
- * same plan and size as w4a16_workspace_bytes), alignment and errors as
- * w4a16_gemm. */
+/* Workspace bytes of w8a16_gemm for this shape: its plans differ from the
+ * 4-bit ones from 16 rows on, so its workspace is sized here (contract as
+ * w4a16_workspace_bytes). */
+size_t w8a16_workspace_bytes(int M, int K, int N, int group);
+
+/* The plan of w8a16_gemm for this shape, as w4a16_describe. */
+int w8a16_describe(int M, int K, int N, int group, char* buf, size_t len);
+
+/* C = A . dequant8(Bpacked, scales): arguments, layouts, alignment and
+ * errors as w4a16_gemm; the workspace is sized by w8a16_workspace_bytes. */
 int w8a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales, uint16_t* C,
                int M, int K, int N, int group, void* workspace, void* stream);
 

@@ -30,7 +30,7 @@ extern "C" {
  * the reads cannot be expected to produce; it must be valid device memory. */
 int w4a16_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream);
 
-/* Run `iters` rounds of eight independent v_mfma_f32_16x16x32_f16 in each
+/* Run `iters` rounds of sixteen independent v_mfma_f32_16x16x32_f16 in each
  * of the four waves of `blocks` workgroups, on register operands.  `sink`
  * (device, one float) as above. */
 int w4a16_probe_mfma(float* sink, int blocks, int iters, void* stream);

@@ -111,7 +111,7 @@ def run_gemm8(A: np.ndarray, Bq8: np.ndarray, S: np.ndarray, group: int, workspa
         Bp = repack8_on_device(dev(Bq8), K, N)
     A_d, S_d = dev(A), dev(S)
     C_d = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
-    ws = workspace if workspace is not None else w4.alloc_workspace(M, K, N, group)
+    ws = workspace if workspace is not None else w4.alloc_workspace8(M, K, N, group)
     w4.w8a16_gemm(A_d, Bp, S_d, C_d, M, K, N, group, ws)
     torch.cuda.synchronize()
     return host_f16(C_d)

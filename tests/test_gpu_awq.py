@@ -137,10 +137,13 @@ def test_awq_gemm_matches_oracle(fmt, dtype, zp, M, K, N, kernel):
 
 @pytest.mark.parametrize("fmt,dtype,zp", FORMATS)
 @pytest.mark.parametrize("plan", ["1,4,4,5,4", "1,2,8,3,2", "1,2,8,4,4,2", "2,2,8,2,4,2",
-                                  "4,1,8,3,3,2", "4,2,4,2,3,2,0,2", "8,2,8,2,3,2"])
+                                  "4,1,8,3,3,2", "4,2,4,2,3,2,0,2", "8,2,8,2,3,2",
+                                  "8,4,4,3,3,4", "4,4,4,5,4,4", "2,4,4,4,6,4", "1,4,4,7,6,4",
+                                  "4,4,4,5,3,4,0,2", "2,4,4,4,4,4,0,2", "1,4,4,7,6,4,0,2"])
 def test_awq_forced_plans_split_k(monkeypatch, fmt, dtype, zp, plan):
-    """The compiled variants with split-K (forced), M = 45 ragged rows,
-    N = 208 a ragged column tile, group 512."""
+    """The compiled variants with split-K (forced; for the stream-K kernel,
+    grids that share tiles between workgroups), M = 45 ragged rows, N = 208
+    a ragged column tile, group 512."""
     M, K, N, group = 45, 3584, 208, 512
     A, Bq, S, Z = _inputs(M, K, N, group, 5, dtype, zp)
     w4.w4a16_set_forced_plan(plan)

@@ -258,12 +258,15 @@ def test_gemm_deterministic_repeats():
     assert_gemm_close(first, C64)
 
 
-@pytest.mark.parametrize("M,K,N", [(128, 4096, 4096), (64, 11008, 1024), (300, 2048, 512)])
-def test_lds_kernel_split_k_deterministic(M, K, N):
-    """The LDS kernel's split-K path, as the heuristic picks it: bit-identical
-    repeats on one workspace."""
+@pytest.mark.parametrize("M,K,N,plan", [(128, 4096, 4096, "4,1,8,4,3,2"),
+                                        (64, 11008, 1024, "4,1,8,4,3,2"),
+                                        (300, 2048, 512, "8,2,8,2,3,2")])
+def test_lds_kernel_split_k_deterministic(M, K, N, plan):
+    """The LDS kernel's split-K path (forced): bit-identical repeats on one
+    workspace."""
     import torch
     A, Bq, S = make_inputs(M, K, N, 128, seed=M + K)
+    w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_describe(M, K, N, 128)
     assert desc.startswith("gemm_lds_kernel<") and "splits=1 " not in desc, desc
     ws = w4.alloc_workspace(M, K, N, 128)

@@ -1,0 +1,162 @@
+"""The stream-K kernel (gemm_sk.hip) against the oracle: every compiled
+variant, grids that cut tiles between workgroups anywhere (so partial tiles
+go through the workspace and the last arriver adds them in K order), tile
+padding when the K blocks are not a multiple of the pipeline depth, ragged
+rows and columns, determinism, workspace reuse and the fused output stage."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_int4_gemm_amd as w4
+from synth import make_bias, make_inputs
+from tests.gpu_util import dev, repack_on_device, run_gemm, run_gemm_fused, say
+from tests.tolerance import assert_epilogue_close, assert_gemm_close
+
+pytestmark = pytest.mark.gpu
+
+# compiled variants (16*mb rows per wave, pipeline depth ns, wm waves along M)
+VARIANTS = [(8, 3, 1), (4, 4, 1), (2, 6, 1), (1, 6, 1), (4, 3, 2), (2, 4, 2), (1, 6, 2)]
+
+
+@pytest.fixture(autouse=True)
+def _no_forced_plan():
+    w4.w4a16_set_forced_plan(None)
+    yield
+    w4.w4a16_set_forced_plan(None)
+
+
+def _plan(mb, ns, grid, wm=1):
+    return f"{mb},4,4,{grid},{ns},4,0,{wm}"
+
+
+def _name(mb, ns, wm):
+    return f"gemm_sk_kernel<{mb},4,{ns},{wm}>"
+
+
+@pytest.mark.parametrize("mb,ns,wm", VARIANTS)
+@pytest.mark.parametrize("grid", [1, 3, 7, 0])
+def test_sk_forced_grids_agree(mb, ns, wm, grid):
+    """M = 45 and N = 208 leave ragged row and column tiles; K = 3584 is 28
+    K blocks (padded to a multiple of ns where needed); grids of 3 and 7
+    workgroups cut tiles in the middle."""
+    M, K, N, g = 45, 3584, 208, 128
+    A, Bq, S = make_inputs(M, K, N, g, seed=11)
+    w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm))
+    desc = w4.w4a16_describe(M, K, N, g)
+    assert desc.startswith(_name(mb, ns, wm)), desc
+    say("sk forced", mb, ns, wm, grid, desc)
+    C = run_gemm(A, Bq, S, g)
+    _, C64 = oracle.gemm(A, Bq, S, g)
+    assert_gemm_close(C, C64, desc)
+
+
+@pytest.mark.parametrize("M,K,N,mb,ns,wm", [(200, 4096, 1024, 8, 3, 1), (64, 3840, 768, 2, 4, 2),
+                                            (16, 2048, 4160, 1, 6, 1), (130, 1152, 2048, 4, 3, 2)])
+def test_sk_default_and_split_grids(M, K, N, mb, ns, wm):
+    """Several column and row tiles; the default grid (one workgroup per
+    compute unit, at least eight K blocks each) and a 5-workgroup grid whose
+    runs end inside tiles."""
+    A, Bq, S = make_inputs(M, K, N, 128, seed=M + N)
+    _, C64 = oracle.gemm(A, Bq, S, 128)
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 0, wm))
+    desc = w4.w4a16_describe(M, K, N, 128)
+    assert desc.startswith(_name(mb, ns, wm)), desc
+    say("sk default grid", M, K, N, desc)
+    assert_gemm_close(run_gemm(A, Bq, S, 128), C64, desc)
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 5, wm))
+    desc5 = w4.w4a16_describe(M, K, N, 128)
+    assert "workspace=0" not in desc5, desc5
+    say("sk grid 5", M, K, N, desc5)
+    assert_gemm_close(run_gemm(A, Bq, S, 128), C64, desc5)
+
+
+def test_sk_group_k_and_coarse_groups():
+    """Per-column scales (group = K) and groups of four K blocks."""
+    M, K, N = 72, 2560, 512
+    for g in (K, 512):
+        A, Bq, S = make_inputs(M, K, N, g, seed=g)
+        w4.w4a16_set_forced_plan(_plan(4, 4, 3))
+        desc = w4.w4a16_describe(M, K, N, g)
+        say("sk group", g, desc)
+        C = run_gemm(A, Bq, S, g)
+        _, C64 = oracle.gemm(A, Bq, S, g)
+        assert_gemm_close(C, C64, f"group {g} {desc}")
+
+
+def test_sk_one_hot_rows_are_exact():
+    """A row that is e_k picks weight row k exactly (every other product is an
+    exact zero), through partial tiles and padding: the reduction adds exact
+    zeros in any order."""
+    M, K, N, g = 40, 1280, 320, 128
+    _, Bq, S = make_inputs(M, K, N, g, seed=3)
+    A = np.zeros((M, K), dtype=np.float16)
+    ks = np.random.default_rng(4).integers(0, K, size=M)
+    A[np.arange(M), ks] = 1.0
+    W = oracle.dequant(Bq, S, g)
+    for mb, ns, wm in VARIANTS:
+        w4.w4a16_set_forced_plan(_plan(mb, ns, 4, wm))
+        say("sk one-hot", mb, ns, wm)
+        C = run_gemm(A, Bq, S, g)
+        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, ns, wm)
+
+
+def test_sk_deterministic_and_counters_reset():
+    """Repeats are bit-identical on a shared workspace, whose counter header
+    is all zero after every call."""
+    import torch
+    M, K, N, g = 96, 4096, 2048, 128
+    A, Bq, S = make_inputs(M, K, N, g, seed=5)
+    w4.w4a16_set_forced_plan(_plan(4, 4, 7))
+    desc = w4.w4a16_describe(M, K, N, g)
+    need = w4.w4a16_workspace_bytes(M, K, N, g)
+    assert need > 65536, desc
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    Bp = repack_on_device(dev(Bq), K, N)
+    say("sk determinism", desc)
+    first = run_gemm(A, Bq, S, g, workspace=ws, Bp=Bp)
+    for i in range(8):
+        again = run_gemm(A, Bq, S, g, workspace=ws, Bp=Bp)
+        assert np.array_equal(first.view(np.uint16), again.view(np.uint16)), i
+        assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+    _, C64 = oracle.gemm(A, Bq, S, g)
+    assert_gemm_close(first, C64, desc)
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_sk_fused_epilogue(act):
+    """Bias and ReLU / SiLU in the stream-K output stage, whole and shared
+    tiles alike."""
+    M, K, N, g = 45, 3584, 208, 128
+    A, Bq, S = make_inputs(M, K, N, g, seed=9)
+    bias = make_bias(N, seed=10)
+    _, Y64, Z64 = oracle.gemm_fused(A, Bq, S, g, bias, act)
+    for grid, (mb, ns, wm) in ((1, (4, 4, 1)), (5, (4, 4, 1)), (5, (2, 4, 2))):
+        w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm))
+        desc = w4.w4a16_describe(M, K, N, g)
+        say("sk fused", act, desc)
+        C = run_gemm_fused(A, Bq, S, g, bias, act)
+        assert_epilogue_close(C, Z64, Y64, f"act {act} {desc}")
+
+
+def test_heuristic_picks_stream_k_only_on_large_layers():
+    """The stream-K kernel takes 9..16 rows on a layer with many K blocks per
+    compute unit; other batches and small layers keep the whole-tile
+    kernels, and the forced plan "tile -1" gives the plan the heuristic
+    makes without it."""
+    K, N = 18432, 73728
+    for M in (9, 16):
+        assert w4.w4a16_describe(M, K, N, 128).startswith("gemm_sk_kernel<1,4,6,1>"), M
+    for M in (1, 8, 17, 32, 64, 128):
+        assert not w4.w4a16_describe(M, K, N, 128).startswith("gemm_sk_kernel<"), M
+    assert not w4.w4a16_describe(16, 4096, 4096, 128).startswith("gemm_sk_kernel<")
+    w4.w4a16_set_forced_plan("0,0,0,0,0,-1")
+    desc = w4.w4a16_describe(16, K, N, 128)
+    assert not desc.startswith("gemm_sk_kernel<"), desc
+    M = 64
+    A, Bq, S = make_inputs(M, 2048, 4096, 128, seed=8)
+    _, C64 = oracle.gemm(A, Bq, S, 128)
+    say("tile -1", w4.w4a16_describe(M, 2048, 4096, 128))
+    assert_gemm_close(run_gemm(A, Bq, S, 128), C64, "tile -1")

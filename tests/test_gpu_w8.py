@@ -77,7 +77,7 @@ def test_dequant8_all_codes_against_every_scale():
                           oracle.dequant8(Bq8, S, K).view(np.uint16))
 
 
-# the plans' kernels (as w4a16_describe prints them), one shape each
+# the plans' kernels (as w8a16_describe prints them), one shape each
 W8_CASES = [
     (1, 4096, 4096, "gemm_kernel<1,1,8,2>"),
     (1, 4096, 12288, "gemm_kernel<1,1,4,2>"),
@@ -98,7 +98,7 @@ W8_CASES = [
 
 @pytest.mark.parametrize("M,K,N,kernel", W8_CASES)
 def test_gemm8_matches_oracle(M, K, N, kernel):
-    desc = w4.w4a16_describe(M, K, N, 128)
+    desc = w4.w8a16_describe(M, K, N, 128)
     assert desc.startswith(kernel + " "), desc
     A, _, S = make_inputs(M, K, N, 128, seed=M + N)
     Bq8 = _words8(K, N, M * 7 + N)
@@ -119,7 +119,7 @@ def test_gemm8_forced_plans_split_k(monkeypatch, plan):
     A, _, S = make_inputs(M, K, N, group, seed=5)
     Bq8 = _words8(K, N, 9)
     w4.w4a16_set_forced_plan(plan)
-    desc = w4.w4a16_describe(M, K, N, group)
+    desc = w4.w8a16_describe(M, K, N, group)
     assert "splits=1 " not in desc, desc
     say("gemm8 forced", plan, desc)
     C = run_gemm8(A, Bq8, S, group)
@@ -153,10 +153,10 @@ def test_gemm8_deterministic_split_k():
     M, K, N = 16, 4096, 12288
     A, _, S = make_inputs(M, K, N, 128, seed=8)
     Bq8 = _words8(K, N, 10)
-    desc = w4.w4a16_describe(M, K, N, 128)
+    desc = w4.w8a16_describe(M, K, N, 128)
     assert "splits=1 " not in desc, desc
     Bp = repack8_on_device(dev(Bq8), K, N)
-    ws = w4.alloc_workspace(M, K, N, 128)
+    ws = w4.alloc_workspace8(M, K, N, 128)
     say("gemm8 determinism", desc)
     first = run_gemm8(A, Bq8, S, 128, workspace=ws, Bp=Bp)
     for i in range(8):

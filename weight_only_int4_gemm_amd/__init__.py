@@ -17,6 +17,8 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
     w8a16_gemm(A, Bpacked, scales, C, M, K, N, group, workspace, stream=None)
     w8a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
     w8a16_packed_bytes(K, N)
+    w8a16_workspace_bytes(M, K, N, group)
+    w8a16_describe(M, K, N, group)
     w4a16_sparse24_repack(Bq, mask, Bpacked, K, N, stream=None)
     w4a16_sparse24_gemm(A, Bpacked, scales, C, M, K, N, group, workspace,
                         stream=None)
@@ -44,10 +46,12 @@ __all__ = [
     "W4A16_ACT_NONE", "W4A16_ACT_RELU", "W4A16_ACT_SILU",
     "w4a16_gemm_awq", "w4a16_dequant_awq_debug", "W4A16_DTYPE_F16", "W4A16_DTYPE_BF16",
     "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug", "w8a16_packed_bytes",
+    "w8a16_workspace_bytes", "w8a16_describe", "alloc_workspace8",
     "w4a16_sparse24_repack", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_workspace_bytes", "w4a16_sparse24_describe",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
-    "w4a16_status_string", "w4a16_describe", "w4a16_set_forced_plan", "EXPORTED_SYMBOLS",
+    "w4a16_status_string", "w4a16_describe", "w4a16_set_forced_plan",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,7 +72,7 @@ EXPORTED_SYMBOLS = (
     "w8a16_packed_bytes", "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_repack", "w4a16_sparse24_workspace_bytes",
     "w4a16_sparse24_describe", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
-    "w4a16_set_forced_plan",
+    "w4a16_set_forced_plan", "w8a16_workspace_bytes", "w8a16_describe",
 )
 
 
@@ -123,6 +127,10 @@ def load():
     lib.w8a16_packed_bytes.restype = sz
     lib.w8a16_repack.argtypes = [vp, vp, i, i, vp]
     lib.w8a16_repack.restype = i
+    lib.w8a16_workspace_bytes.argtypes = [i, i, i, i]
+    lib.w8a16_workspace_bytes.restype = sz
+    lib.w8a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
+    lib.w8a16_describe.restype = i
     lib.w8a16_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp]
     lib.w8a16_gemm.restype = i
     lib.w8a16_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
@@ -351,6 +359,16 @@ def w8a16_packed_bytes(K: int, N: int) -> int:
     return load().w8a16_packed_bytes(int(K), int(N))
 
 
+def w8a16_workspace_bytes(M: int, K: int, N: int, group: int) -> int:
+    return load().w8a16_workspace_bytes(int(M), int(K), int(N), int(group))
+
+
+def w8a16_describe(M: int, K: int, N: int, group: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check("w8a16_describe", load().w8a16_describe(int(M), int(K), int(N), int(group), buf, 256))
+    return buf.value.decode()
+
+
 def w8a16_repack(Bq8, Bpacked, K: int, N: int, stream=None) -> None:
     import torch
     _expect(Bq8, torch.int32, "Bq8")
@@ -370,7 +388,7 @@ def w8a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
     _expect(scales, torch.float16, "scales")
     _expect(C, torch.float16, "C")
     _need_gemm(M, K, N, group, A, Bpacked, w8a16_packed_bytes(K, N), scales, C, workspace,
-               w4a16_workspace_bytes(M, K, N, group))
+               w8a16_workspace_bytes(M, K, N, group))
     _check("w8a16_gemm", load().w8a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
                                            int(M), int(K), int(N), int(group),
                                            _ptr(workspace), _stream(stream)))
@@ -463,6 +481,15 @@ def alloc_workspace(M: int, K: int, N: int, group: int, device=None):
     """A zero-filled workspace of ``w4a16_workspace_bytes`` bytes, or None."""
     import torch
     nbytes = w4a16_workspace_bytes(M, K, N, group)
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+def alloc_workspace8(M: int, K: int, N: int, group: int, device=None):
+    """A zero-filled workspace of ``w8a16_workspace_bytes`` bytes, or None."""
+    import torch
+    nbytes = w8a16_workspace_bytes(M, K, N, group)
     if nbytes == 0:
         return None
     return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 PROBES_LIB = os.path.join(PKG, "libw4a16_probes.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm_lds.hip", "repack.hip", "dequant.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm_lds.hip", "gemm_sk.hip", "gemm_sk_fmt.hip", "repack.hip", "dequant.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -80,6 +80,45 @@ def build(verbose: bool = False) -> str:
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, pobj])
     os.replace(tmp, PROBES_LIB)
     return LIB
+
+
+# Host-side AddressSanitizer build: the same sources and device code, with
+# the host half of every file instrumented.  It is a test build for the
+# argument checks and planner (tests/test_host_sanitizer.py loads it into a
+# process with the sanitizer runtime preloaded); kernels are never launched
+# from it.
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libw4a16_asan.so")
+ASAN_HOST_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer "
+                   "-Xarch_host -g").split()
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that matches hipcc, for LD_PRELOAD."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/*/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang AddressSanitizer runtime not found under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def build_host_asan() -> str:
+    hipcc = _hipcc()
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(ASAN_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([hipcc, *HIPCC_FLAGS, *ASAN_HOST_FLAGS, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
+    jobs = min(len(cmds), int(os.environ.get("MAX_JOBS", "8")) or 1, 16)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(_run, cmds))
+    tmp = ASAN_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_HOST_FLAGS[:2], "-o", tmp,
+          *objs])
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
 
 
 if __name__ == "__main__":

@@ -65,6 +65,7 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q, int fmt) {
+  if (q.tile == 4) return fmt <= kFmtBf16Zp && sk_is_compiled(q.mb, q.nb, q.depth, q.wm);
   if (fmt == kFmtSp24) {
     if (q.tile == 2) return lds_sp_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth);
     return q.tile == 0 && q.wm == 1 && sp_is_compiled(q.mb, q.nb, q.wk, q.depth);
@@ -81,7 +82,9 @@ bool variant_is_compiled(const Plan& q, int fmt) {
 // text is "mb,nb,wk,splits[,depth[,tile[,unused[,wm]]]]": a field <= 0 keeps
 // the heuristic's value; tile is 0 (the default) for the streaming kernel,
 // 2 for the LDS kernel with 16 x 16 blocks, 3 for the LDS kernel with
-// 32 x 32 blocks.  The override feeds the same kernels, and
+// 32 x 32 blocks, 4 for the stream-K kernel (splits = its grid), and -1
+// for the plan the heuristic makes when it does not pick the stream-K
+// kernel (the other fields are then ignored).  The override feeds the same kernels, and
 // w4a16_workspace_bytes sees it as well, so sizes agree as long as it is
 // not changed between the two calls.
 struct ForcedPlan {
@@ -100,7 +103,7 @@ bool parse_forced_plan(const char* text, ForcedPlan* out) {
   if (std::sscanf(text, "%d,%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
                   &unused, &wm) < 4)
     return false;
-  if (tile != 0 && tile != 2 && tile != 3) return false;
+  if (tile != -1 && tile != 0 && tile != 2 && tile != 3 && tile != 4) return false;
   *out = ForcedPlan{true, mb, nb, wk, splits, depth, tile, wm};
   return true;
 }
@@ -119,7 +122,7 @@ void seed_forced_from_env() {
   });
 }
 
-void apply_forced_plan(Plan* p, int KB, int fmt) {
+void apply_forced_plan(Plan* p, const Plan& base, int KB, int fmt) {
   seed_forced_from_env();
   if (!g_force_any.load(std::memory_order_acquire)) return;
   ForcedPlan f;
@@ -128,12 +131,19 @@ void apply_forced_plan(Plan* p, int KB, int fmt) {
     f = g_force;
   }
   if (!f.set) return;
-  Plan q = *p;
+  if (f.tile == -1) {  // the heuristic's plan without the stream-K kernel
+    *p = base;
+    return;
+  }
+  // fields left open come from the heuristic's plan of the forced family
+  Plan q = (f.tile == 4) == (p->tile == 4) ? *p : base;
   q.tile = f.tile;
   if (f.mb > 0) q.mb = f.mb;
   if (f.nb > 0) q.nb = f.nb;
   if (f.wk > 0) q.wk = f.wk;
-  if (f.splits > 0) q.splits = f.splits > KB ? KB : f.splits;
+  if (f.splits > 0) q.splits = (f.tile == 4 || f.splits <= KB) ? f.splits : KB;
+  if (q.tile != 4 && q.splits < 1) q.splits = 1;  // the stream-K plan's grid is set later
+  if (q.tile == 4 && f.splits <= 0) q.splits = 0;  // stream-K: the heuristic grid
   if (f.depth > 0) q.depth = f.depth;
   q.wm = f.wm > 0 ? f.wm : 1;
   if (!variant_is_compiled(q, fmt)) {
@@ -159,7 +169,14 @@ int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len)
   const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan p = make_plan(M, K, N, group, cus, fmt);
-  if (p.tile >= 2)
+  if (p.tile == 4)
+    std::snprintf(buf, len,
+                  "gemm_sk_kernel<%d,%d,%d,%d> grid=%dx1x1 block=%d tiles=%dx%d splits=%d "
+                  "workspace=%zu",
+                  p.mb, p.nb, p.depth, p.wm, p.splits, 64 * kSkWavesPerGroup * p.wm, p.tiles_n,
+                  p.tiles_m,
+                  p.splits, p.workspace_bytes);
+  else if (p.tile >= 2)
     std::snprintf(buf, len,
                   "gemm_lds_kernel<%d,%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
                   "workspace=%zu",
@@ -205,6 +222,22 @@ size_t workspace_fmt(int M, int K, int N, int group, int fmt) {
 // wider wave tiles: 4096 x 12288 at M = 128: 26.6 -> 21.1 us); and the K
 // split there is twice the dense one below a full wave of workgroups and
 // none above it.
+// Whether the stream-K kernel takes a call, and with how many waves along M
+// (0: not taken).  Measured against the plans above (graph replay over
+// rotating weight copies), it is ahead only for 9 to 16 rows on a layer
+// that gives every compute unit many K blocks of 256 columns (18432 x 73728
+// at M = 16: 164.7 against 168.8 us).  At 32 to 128 rows there the LDS
+// kernel is level or ahead (180 / 236 / 380 us against 183 / 239 / 388 us at
+// M = 32 / 64 / 128), two waves per SIMD are slower than one, and on the
+// Llama-2-7B layers the stream-K fix-up and prologue cost 15-20 us more than
+// a grid of whole tiles.
+static int stream_k_wm(int M, int KB, int N, int cus, int fmt) {
+  if (fmt > kFmtBf16Zp || M <= 8 || M > 16) return 0;
+  const int64_t blocks = (int64_t)((N + 255) / 256) * KB;  // 256-column K blocks
+  if (blocks < (int64_t)48 * cus) return 0;
+  return 1;
+}
+
 Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   (void)group;
   Plan p{};
@@ -284,8 +317,9 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   }
   auto shape = [&](Plan& q) {
     const int f = q.tile == 3 ? 32 : 16;
+    if (q.tile == 4) q.wk = kSkWavesPerGroup;
     q.tm = f * q.mb * q.wm;
-    q.tn = f * q.nb * (q.tile ? q.wk : 1);  // tile and LDS kernels split N over waves
+    q.tn = f * q.nb * (q.tile ? q.wk : 1);  // LDS and stream-K kernels split N over waves
     q.tiles_n = (N + q.tn - 1) / q.tn;
     q.tiles_m = (M + q.tm - 1) / q.tm;
   };
@@ -342,9 +376,41 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   if (want > cap) want = cap;
   if (want > 64) want = 64;
   p.splits = (int)(want < 1 ? 1 : want);
-  apply_forced_plan(&p, KB, fmt);
+  const Plan base = p;  // the plan without the stream-K kernel
+  const int sk_wm = stream_k_wm(M, KB, N, cus, fmt);
+  if (sk_wm > 0) {
+    // stream-K kernel: wm x 4 waves of 16*mb x 64, every compute unit an
+    // equal share of the (tile, K block) iterations
+    p.tile = 4;
+    p.wm = sk_wm;
+    p.wk = kSkWavesPerGroup;
+    p.nb = 4;
+    const int rows = (M + sk_wm - 1) / sk_wm;  // rows per wave
+    p.mb = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : 8;
+    p.depth = sk_wm == 1 ? (p.mb == 8 ? 3 : p.mb == 4 ? 4 : 6) : (p.mb == 4 ? 3 : p.mb == 2 ? 4 : 6);
+    p.splits = 0;  // the stream-K grid is set below
+  }
+  apply_forced_plan(&p, base, KB, fmt);
   shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
+  if (p.tile == 4 && !variant_is_compiled(p, fmt)) return Plan{};  // not reached: plans name compiled variants
+  if (p.tile == 4) {
+    // Stream-K grid: one workgroup per compute unit, each with at least
+    // kSkMinIters iterations (fewer workgroups for small problems), never
+    // more workgroups than iterations.  With more tiles than the counter
+    // header can count (one counter per tile and wave), every workgroup
+    // takes whole tiles.
+    const int64_t units = ftiles * ((KB + p.depth - 1) / p.depth);  // of depth K blocks
+    int64_t g = p.splits > 0 ? p.splits : cus;
+    if (p.splits <= 0 && g * kSkMinIters > units * p.depth)
+      g = (units * p.depth + kSkMinIters - 1) / kSkMinIters;
+    if (g > units) g = units;
+    if (g < 1) g = 1;
+    if (ftiles * kSkWavesPerGroup * p.wm > kMaxSplitTiles) g = ftiles;
+    p.splits = (int)g;
+    p.workspace_bytes = sk_workspace_bytes(p.splits, p.tm, p.tn, (int)ftiles, KB, p.depth);
+    return p;
+  }
   if (ftiles > kMaxSplitTiles) p.splits = 1;  // the counter header holds one per tile
   p.workspace_bytes = 0;
   if (p.splits > 1) {
@@ -482,7 +548,8 @@ int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* sca
       (bias && overlap(C, cbytes, bias, (size_t)N * 2)) ||
       (zeros && overlap(C, cbytes, zeros, (size_t)(K / group) * N)))
     return W4A16_ERR_SHAPE;
-  const int cus = current_cus(nullptr);
+  int dev = -1;
+  const int cus = current_cus(&dev);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan plan = make_plan(M, K, N, group, cus, fmt);
   if (plan.workspace_bytes > 0) {
@@ -558,6 +625,14 @@ int w8a16_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales, uint16_
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return W4A16_ERR_LAUNCH;
   return W4A16_OK;
+}
+
+size_t w8a16_workspace_bytes(int M, int K, int N, int group) {
+  return workspace_fmt(M, K, N, group, kFmtW8);
+}
+
+int w8a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
+  return describe_fmt(M, K, N, group, kFmtW8, buf, len);
 }
 
 int w8a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales, uint16_t* C,

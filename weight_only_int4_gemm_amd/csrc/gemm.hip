@@ -468,6 +468,8 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
   // and for any gb as long as kb, gb < 2^16 (K < 2^23 is checked).
   const uint64_t gb = (uint64_t)(group / kBlockK);
   const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
+  if (p.tile == 4)
+    return launch_sk(p, A, Bp, S, C, M, K, N, gmagic, ep, wf, workspace, stream);
   if (p.tile >= 2)
     return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, ep, wf, workspace, stream);
   if (p.tile) return hipErrorInvalidValue;

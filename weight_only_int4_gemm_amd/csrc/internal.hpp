@@ -11,7 +11,9 @@ namespace w4a16 {
 //  tile   0: the streaming kernel (small batches), 2: the LDS kernel
 //         (every operand through LDS stages) with 16 x 16 matrix blocks,
 //         3: the LDS kernel with 32 x 32 blocks (mb and nb then count
-//         32-row / 32-column blocks)
+//         32-row / 32-column blocks), 4: the stream-K kernel (gemm_sk.hip:
+//         four waves of 16*mb x 16*nb, `splits` workgroups each running an
+//         equal share of the (tile, K block) iterations)
 //  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
 //  nb     16-column blocks per wave
 //  wk     waves per workgroup (LDS kernel: waves along N).  Streaming
@@ -56,6 +58,8 @@ bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
 bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns);
+bool sk_is_compiled(int mb, int nb, int ns, int wm);
+size_t sk_workspace_bytes(int wgs, int tm, int tn, int tiles, int KB, int ns);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
                          hipStream_t stream);
@@ -68,6 +72,9 @@ hipError_t launch_dequant(const uint32_t* Bp, const uint16_t* S, uint16_t* W,
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
                       Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream);
+hipError_t launch_sk(const Plan& p, const uint16_t* A, const uint32_t* Bp, const uint16_t* S,
+                     uint16_t* C, int M, int K, int N, uint64_t gmagic, Epilogue ep,
+                     WeightFormat wf, void* workspace, hipStream_t stream);
 hipError_t launch_gemm(const Plan& plan, const uint16_t* A, const uint32_t* Bp,
                        const uint16_t* S, uint16_t* C, int M, int K, int N,
                        int group, Epilogue ep, WeightFormat wf, void* workspace,
@@ -85,6 +92,10 @@ hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8
 // zero, and a workspace zero-filled once serves calls of any shape in turn.
 // Plans split K only when the output has at most kMaxSplitTiles tiles.
 constexpr int kMaxSplitTiles = 16384;
+// The stream-K kernel: waves per workgroup (each with its own counter per
+// tile) and the fewest iterations a workgroup is given.
+constexpr int kSkWavesPerGroup = 4;
+constexpr int kSkMinIters = 8;
 constexpr size_t kCounterHeaderBytes = (size_t)kMaxSplitTiles * sizeof(unsigned);
 
 }  // namespace w4a16

@@ -4,7 +4,7 @@
 //  * w4a16_probe_read: a plain read of a device buffer with 16-byte
 //    non-temporal loads, every byte once -- the HBM rate a weight stream
 //    can reach.
-//  * w4a16_probe_mfma: independent v_mfma_f32_16x16x32_f16 chains on
+//  * w4a16_probe_mfma: sixteen independent v_mfma_f32_16x16x32_f16 chains on
 //    register operands in every wave of a full grid -- the FP16 matrix rate
 //    with no memory traffic.
 // Neither is part of the GEMM; bench.py times them with HIP events.
@@ -47,10 +47,11 @@ __global__ __launch_bounds__(kReadThreads) void read_kernel(const uint4_vt* __re
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
-constexpr int kMfmaChains = 8;
+constexpr int kMfmaChains = 16;
 
-// kMfmaChains independent accumulators per wave, `iters` rounds; operands
-// are built from the lane index so the compiler cannot fold them.
+// kMfmaChains independent accumulators per wave (enough to cover the
+// instruction's latency), `iters` rounds; operands are built from the lane
+// index so the compiler cannot fold them.
 __global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink) {
   half8_vt a, b;
 #pragma unroll
@@ -58,10 +59,14 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict_
     a[i] = (_Float16)(float)((threadIdx.x + i) & 7);
     b[i] = (_Float16)(float)((threadIdx.x * 3 + i) & 7);
   }
+  // The first round starts from an inline zero accumulator: a zero-filled
+  // array carried into the loop would have the compiler copy the
+  // accumulators between registers on every trip.
   float4_vt acc[kMfmaChains];
 #pragma unroll
-  for (int c = 0; c < kMfmaChains; ++c) acc[c] = float4_vt{0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < iters; ++it) {
+  for (int c = 0; c < kMfmaChains; ++c)
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, float4_vt{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  for (int it = 1; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < kMfmaChains; ++c)
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
