@@ -51,7 +51,8 @@ enum w4a16_status {
     W4A16_ERR_SHAPE = -2,     /* M, K or N out of range or not a multiple    */
     W4A16_ERR_GROUP = -3,     /* group not a multiple of 128 dividing K      */
     W4A16_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned            */
-    W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed      */
+    W4A16_ERR_WORKSPACE = -5, /* workspace NULL although one is needed, or  */
+                              /* (noalloc) more than its scratch holds     */
     W4A16_ERR_LAUNCH = -6,    /* the kernel launch failed                    */
     W4A16_ERR_DEVICE = -7,    /* no usable current HIP device                */
     W4A16_ERR_EPILOGUE = -8,  /* unknown activation for w4a16_gemm_fused     */
@@ -182,6 +183,30 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group);
 int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked,
                const uint16_t* scales, uint16_t* C, int M, int K, int N,
                int group, void* workspace, void* stream);
+
+/*
+ * w4a16_gemm_noalloc -- w4a16_gemm for callers that cannot allocate memory
+ * (code under HIP-graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same plan and kernels, with the split-K partials and
+ * counters in a scratch array the library holds on each device (a static
+ * device array of W4A16_NOALLOC_SCRATCH_BYTES, 64 MiB, kept until the
+ * process ends) instead of a caller's workspace.
+ *
+ * A, Bpacked, scales, C, M, K, N, group, stream, numerics and errors: as
+ * w4a16_gemm.  No allocation, free, memset or synchronisation happens; the
+ * first call on a device takes the scratch's address and clears its
+ * counters with a small kernel on `stream`.
+ * Limit: a shape whose plan needs more split-K scratch than
+ * W4A16_NOALLOC_SCRATCH_BYTES (w4a16_workspace_bytes(M, K, N, group) above
+ * it) returns W4A16_ERR_WORKSPACE and launches nothing.
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents: calls that overlap in time on one device (other
+ * streams, other threads) race and must not be issued; calls ordered on one
+ * stream, or synchronised, are safe.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int w4a16_gemm_noalloc(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                       uint16_t* C, int M, int K, int N, int group, void* stream);
 
 /*
  * w4a16_gemm_fused -- C = act(A . dequant(Bpacked, scales) + bias).

@@ -96,3 +96,5 @@ def test_poisoned_workspace_is_a_documented_precondition():
     assert "Every call leaves the counters at zero again" in doc
     assert "header of 32-bit arrival counters" in doc
     assert "must not share a workspace" in doc
+    noalloc = _doc_of("int w4a16_gemm_noalloc")
+    assert "clears its counters" in noalloc

@@ -6,6 +6,7 @@ stream.  The functions carry the C interface's names (include/w4a16.h):
 
     w4a16_repack(Bq, Bpacked, K, N, stream=None)
     w4a16_gemm(A, Bpacked, scales, C, M, K, N, group, workspace, stream=None)
+    w4a16_gemm_noalloc(A, Bpacked, scales, C, M, K, N, group, stream=None)
     w4a16_gemm_fused(A, Bpacked, scales, bias, activation, C, M, K, N, group,
                      workspace, stream=None)
     w4a16_dequant_debug(Bpacked, scales, W, K, N, group, stream=None)
@@ -50,8 +51,8 @@ __all__ = [
     "w4a16_sparse24_repack", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_workspace_bytes", "w4a16_sparse24_describe",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
-    "w4a16_status_string", "w4a16_describe", "w4a16_set_forced_plan",
-    "EXPORTED_SYMBOLS",
+    "w4a16_status_string", "w4a16_describe", "w4a16_set_forced_plan", "w4a16_gemm_noalloc",
+    "W4A16_NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +65,7 @@ W4A16_ACT_RELU = 1
 W4A16_ACT_SILU = 2
 W4A16_DTYPE_F16 = 0
 W4A16_DTYPE_BF16 = 1
+W4A16_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 EXPORTED_SYMBOLS = (
     "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
@@ -72,7 +74,7 @@ EXPORTED_SYMBOLS = (
     "w8a16_packed_bytes", "w8a16_repack", "w8a16_gemm", "w8a16_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_repack", "w4a16_sparse24_workspace_bytes",
     "w4a16_sparse24_describe", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
-    "w4a16_set_forced_plan", "w8a16_workspace_bytes", "w8a16_describe",
+    "w4a16_set_forced_plan", "w4a16_gemm_noalloc", "w8a16_workspace_bytes", "w8a16_describe",
 )
 
 
@@ -151,6 +153,8 @@ def load():
     lib.w4a16_sparse24_gemm.restype = i
     lib.w4a16_sparse24_dequant_debug.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.w4a16_sparse24_dequant_debug.restype = i
+    lib.w4a16_gemm_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    lib.w4a16_gemm_noalloc.restype = i
     lib.w4a16_set_forced_plan.argtypes = [ctypes.c_char_p]
     lib.w4a16_set_forced_plan.restype = i
     _lib = lib
@@ -297,6 +301,20 @@ def w4a16_gemm(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
     _check("w4a16_gemm", load().w4a16_gemm(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C),
                                            int(M), int(K), int(N), int(group),
                                            _ptr(workspace), _stream(stream)))
+
+
+def w4a16_gemm_noalloc(A, Bpacked, scales, C, M: int, K: int, N: int, group: int,
+                       stream=None) -> None:
+    """w4a16_gemm with the library's own per-device scratch: no workspace."""
+    import torch
+    _expect(A, torch.float16, "A")
+    _expect(Bpacked, torch.int32, "Bpacked")
+    _expect(scales, torch.float16, "scales")
+    _expect(C, torch.float16, "C")
+    _need_gemm(M, K, N, group, A, Bpacked, w4a16_packed_bytes(K, N), scales, C, None, 0)
+    _check("w4a16_gemm_noalloc",
+           load().w4a16_gemm_noalloc(_ptr(A), _ptr(Bpacked), _ptr(scales), _ptr(C), int(M),
+                                     int(K), int(N), int(group), _stream(stream)))
 
 
 def w4a16_gemm_fused(A, Bpacked, scales, bias, activation: int, C, M: int, K: int, N: int,

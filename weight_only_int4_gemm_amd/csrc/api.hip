@@ -521,13 +521,54 @@ int w4a16_dequant_awq_debug(const uint32_t* Bpacked, const uint16_t* scales,
 
 namespace {
 
+// ---- The allocation-free variant (w4a16_gemm_noalloc) -------------------
+// Its split-K partials and arrival counters live in this file-scope device
+// array instead of a caller's workspace.  Each device the library runs on
+// holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in: kernels get the device address
+// taken with hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)W4A16_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > kCounterHeaderBytes, "the scratch holds the counter header");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Zero n 32-bit words (the counter header at set-up).  A kernel rather
+// than a memset, so that a first call under HIP-graph capture records an
+// ordinary kernel node.
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The scratch of the current device `dev`; on the first call for a device,
+// take its address and clear its counters (on `stream`, ahead of the call's
+// own kernels).
+int scratch_of(int dev, hipStream_t stream, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return W4A16_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return W4A16_ERR_DEVICE;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((kMaxSplitTiles + 255) / 256), dim3(256), 0,
+                       stream, static_cast<uint32_t*>(p), kMaxSplitTiles);
+    if (hipGetLastError() != hipSuccess) return W4A16_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4A16_OK;
+}
+
 // The GEMM behind every entry point: argument checks, then the plan and the
 // launch.  fmt is a weight format of format.hpp (0: FP16, 1: FP16 with zero
 // points, 2: BF16, 3: BF16 with zero points, 4: 8-bit codes, 5: 2:4-sparse
 // codes).
 int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
                  const uint8_t* zeros, const uint16_t* bias, int activation, uint16_t* C,
-                 int M, int K, int N, int group, int fmt, void* workspace, void* stream) {
+                 int M, int K, int N, int group, int fmt, void* workspace, void* stream,
+                 bool use_scratch = false) {
   if (M < 0) return W4A16_ERR_SHAPE;
   int rc = check_kn(K, N, true);
   if (rc != W4A16_OK) return rc;
@@ -552,6 +593,14 @@ int gemm_checked(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* sca
   const int cus = current_cus(&dev);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan plan = make_plan(M, K, N, group, cus, fmt);
+  if (use_scratch) {
+    workspace = nullptr;
+    if (plan.workspace_bytes > kScratchBytes) return W4A16_ERR_WORKSPACE;
+    if (plan.workspace_bytes > 0) {
+      rc = scratch_of(dev, static_cast<hipStream_t>(stream), &workspace);
+      if (rc != W4A16_OK) return rc;
+    }
+  }
   if (plan.workspace_bytes > 0) {
     if (!workspace) return W4A16_ERR_WORKSPACE;
     if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
@@ -592,6 +641,12 @@ int w4a16_gemm(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scale
                void* stream) {
   return gemm_checked(A, Bpacked, scales, nullptr, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
                       0, workspace, stream);
+}
+
+int w4a16_gemm_noalloc(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
+                       uint16_t* C, int M, int K, int N, int group, void* stream) {
+  return gemm_checked(A, Bpacked, scales, nullptr, nullptr, W4A16_ACT_NONE, C, M, K, N, group,
+                      0, nullptr, stream, /*use_scratch=*/true);
 }
 
 size_t w8a16_packed_bytes(int K, int N) {
