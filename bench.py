@@ -35,6 +35,12 @@ to the value recorded with the counters:
     rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-graph --no-secondary --no-probes --no-clocks --copy-probe
     python3 bench.py --pmc-summary OUT/fetch OUT/write profiles/pmc_traffic_large_layer_sweep.json
 
+The kernel durations come from a trace of the same workload, summarised by
+``--trace-summary``:
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/kt -o run -- python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-graph --no-secondary --no-probes --no-clocks
+    python3 bench.py --trace-summary OUT/kt/run_kernel_stats.csv profiles/kernel_trace_large_layer_sweep.md
+
 ``--configs-report OUT.md`` instead times every workload shape one GEMM at a
 time (the single 4096 x 4096 layer, the Llama-2-7B layers, the 18432 x 73728
 batch sweep, the 8192 x 28672 prefill layer and the deep-K layers with group
@@ -74,6 +80,12 @@ REPEATS = 5          # timed regions of exactly --steps steps; the median is rep
 PROBE_READ_BYTES = 2 * 2**30    # the stream-read ceiling: a 2 GiB buffer read once per launch
 PROBE_MFMA_ITERS = 2048
 PROBE_MFMA_BLOCKS = 1024         # four waves per SIMD
+# the kernel-trace run behind profiles/kernel_trace_large_layer_sweep.md
+TRACE_RUN_FLAGS = ("--steps 10 --warmup 2 --no-cpu-baseline --no-graph --no-secondary --no-probes "
+                   "--no-clocks")
+# the counter runs behind roofline.traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
+PMC_RUN_FLAGS = ("--steps 2 --warmup 1 --no-cpu-baseline --no-graph --no-secondary --no-probes "
+                 "--no-clocks --copy-probe")
 
 # The workloads.  "sweep" is the one the metric is quoted on: the large
 # single layer at every batch size from 1 to 128.
@@ -155,6 +167,8 @@ def parse():
     ap.add_argument("--pmc-kernels", nargs="+", metavar=("OUT", "DIR"),
                     help="summarise rocprofv3 --pmc runs (one DIR each) into OUT (JSON): "
                          "per GEMM kernel and counter, the value per dispatch")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="write a rocprofv3 kernel-stats table as markdown")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script into a traffic file and exit")
@@ -258,14 +272,12 @@ def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
             "hbm_bytes_per_dispatch": (f * (fetch_scale or 1) + w * (write_scale or 1)) * 1024,
         }
     summary = {
-        "what": "HBM bytes per dispatch of each GEMM kernel over the Llama-2-7B W4A16 step "
-                "(bench.py workload), from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled "
-                "by what the counter reads for a device copy of known size",
+        "what": "HBM bytes per dispatch of each GEMM kernel of bench.py's default workload "
+                f"({WORKLOADS['sweep']['workload']}), from rocprofv3 FETCH_SIZE and WRITE_SIZE, "
+                "each scaled by what the counter reads for a device copy of known size",
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py --steps 3 "
-            "--warmup 1 --no-cpu-baseline --no-graph --copy-probe",
-            "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py --steps 3 "
-            "--warmup 1 --no-cpu-baseline --no-graph --copy-probe",
+            f"rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py {PMC_RUN_FLAGS}",
+            f"rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py {PMC_RUN_FLAGS}",
             "python3 bench.py --pmc-summary OUT/fetch OUT/write " + os.path.relpath(out_path, ROOT),
         ],
         "kernel_source_hash": kernel_source_hash(),
@@ -278,6 +290,50 @@ def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
         json.dump(summary, f, indent=1)
         f.write("\n")
     print(json.dumps(summary, indent=1))
+
+
+def trace_summary(stats_csv: str, out_path: str) -> None:
+    """A rocprofv3 --kernel-trace --stats kernel table as markdown: calls,
+    average, min and max duration and share of GPU time per kernel."""
+    import csv
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((_short_kernel_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]),
+                         float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[1] * r[2])
+    wl = WORKLOADS["sweep"]
+    lines = [
+        "# Kernel trace: bench.py default workload",
+        "",
+        f"Workload: {wl['workload']}.",
+        "",
+        "Command (from the repository root on the GPU box; `OUT` a scratch directory), then the "
+        "summary:",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+        f"-d OUT/kt -o run -- python3 $REPO/bench.py {TRACE_RUN_FLAGS}",
+        "python3 bench.py --trace-summary OUT/kt/run_kernel_stats.csv "
+        + os.path.relpath(out_path, ROOT),
+        "```",
+        "",
+        "The calls are the warm-up steps (at least half a second of them), five timed regions of "
+        "10 steps, then each GEMM launched back to back between two HIP events (bench.py's "
+        "per-launch durations).  The averages are the kernels' own durations and should agree "
+        "with bench.py's `roofline.avg_launch_us` for the dominant kernel.",
+        "",
+        f"Kernel source hash (bench.py `kernel_source_hash`): `{kernel_source_hash()}`",
+        "",
+        "| kernel | calls | average us | min us | max us | share of GPU time |",
+        "|---|---|---|---|---|---|",
+    ]
+    for name, calls, avg, mn, mx, pct in rows:
+        lines.append(f"| `{name}` | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} "
+                     f"| {pct:.1f}% |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def pmc_kernels(out_path: str, run_dirs) -> None:
@@ -1174,6 +1230,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
     if args.pmc_kernels:
         pmc_kernels(args.pmc_kernels[0], args.pmc_kernels[1:])

@@ -92,11 +92,32 @@ size_t w4a16_packed_bytes(int K, int N);
  * W4A16_ERR_DEVICE.  Launches nothing. */
 int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len);
 
+/* Weight formats, named by the entry point that takes them. */
+enum w4a16_format {
+    W4A16_FORMAT_F16 = 0,      /* w4a16_gemm, w4a16_gemm_fused              */
+    W4A16_FORMAT_F16_ZP = 1,   /* w4a16_gemm_awq: FP16 with zero points     */
+    W4A16_FORMAT_BF16 = 2,     /* w4a16_gemm_awq: BF16                      */
+    W4A16_FORMAT_BF16_ZP = 3,  /* w4a16_gemm_awq: BF16 with zero points     */
+    W4A16_FORMAT_W8 = 4,       /* w8a16_gemm                                */
+    W4A16_FORMAT_SPARSE24 = 5  /* w4a16_sparse24_gemm                       */
+};
+
+/* The line w4a16_describe would write for a call of weight format `format`
+ * on a device with `cus` compute units, computed without querying any
+ * device (for planning tools and tests on a machine without a GPU).
+ * Returns as w4a16_describe, with W4A16_ERR_DTYPE for an unknown format and
+ * W4A16_ERR_DEVICE for cus <= 0.  Follows the forced plan like
+ * w4a16_describe. */
+int w4a16_plan_describe(int M, int K, int N, int group, int format, int cus, char* buf,
+                        size_t len);
+
 /* Tuning and testing only: replace the plan heuristic of every later call
  * in this process with the text spec
  *   "mb,nb,wk,splits[,depth[,tile[,unused[,wm]]]]"
  * (a field <= 0 keeps the heuristic's value; tile 0 is the streaming
- * kernel, 2 the LDS kernel with 16 x 16 blocks, 3 with 32 x 32 blocks).  A
+ * kernel, 2 the LDS kernel with 16 x 16 blocks, 3 with 32 x 32 blocks, 4 the
+ * stream-K kernel (wk = its waves along N, splits = its grid), -1 the plan
+ * the heuristic makes without the stream-K kernel).  A
  * spec naming a variant that is not compiled leaves the heuristic's plan in
  * place.  NULL or "" restores the heuristic.  The environment variable
  * W4A16_FORCE_PLAN, read once when the library first plans a call, seeds the

@@ -17,8 +17,9 @@ from tests.tolerance import assert_epilogue_close, assert_gemm_close
 
 pytestmark = pytest.mark.gpu
 
-# compiled variants (16*mb rows per wave, pipeline depth ns, wm waves along M)
-VARIANTS = [(8, 3, 1), (4, 4, 1), (2, 6, 1), (1, 6, 1), (4, 3, 2), (2, 4, 2), (1, 6, 2)]
+# compiled variants (16*mb rows per wave, pipeline depth ns, wm x wn waves)
+VARIANTS = [(8, 3, 1, 4), (4, 4, 1, 4), (2, 6, 1, 4), (1, 6, 1, 4), (4, 3, 2, 4), (2, 4, 2, 4),
+            (1, 6, 2, 4), (1, 4, 1, 8), (2, 3, 1, 8), (4, 3, 1, 8)]
 
 
 @pytest.fixture(autouse=True)
@@ -28,45 +29,49 @@ def _no_forced_plan():
     w4.w4a16_set_forced_plan(None)
 
 
-def _plan(mb, ns, grid, wm=1):
-    return f"{mb},4,4,{grid},{ns},4,0,{wm}"
+def _plan(mb, ns, grid, wm=1, wn=4):
+    return f"{mb},4,{wn},{grid},{ns},4,0,{wm}"
 
 
-def _name(mb, ns, wm):
-    return f"gemm_sk_kernel<{mb},4,{ns},{wm}>"
+def _name(mb, ns, wm, wn=4):
+    return f"gemm_sk_kernel<{mb},4,{ns},{wm},{wn}>"
 
 
-@pytest.mark.parametrize("mb,ns,wm", VARIANTS)
+@pytest.mark.parametrize("mb,ns,wm,wn", VARIANTS)
 @pytest.mark.parametrize("grid", [1, 3, 7, 0])
-def test_sk_forced_grids_agree(mb, ns, wm, grid):
+def test_sk_forced_grids_agree(mb, ns, wm, wn, grid):
     """M = 45 and N = 208 leave ragged row and column tiles; K = 3584 is 28
     K blocks (padded to a multiple of ns where needed); grids of 3 and 7
     workgroups cut tiles in the middle."""
     M, K, N, g = 45, 3584, 208, 128
     A, Bq, S = make_inputs(M, K, N, g, seed=11)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm, wn))
     desc = w4.w4a16_describe(M, K, N, g)
-    assert desc.startswith(_name(mb, ns, wm)), desc
-    say("sk forced", mb, ns, wm, grid, desc)
+    assert desc.startswith(_name(mb, ns, wm, wn)), desc
+    say("sk forced", mb, ns, wm, wn, grid, desc)
     C = run_gemm(A, Bq, S, g)
     _, C64 = oracle.gemm(A, Bq, S, g)
     assert_gemm_close(C, C64, desc)
 
 
-@pytest.mark.parametrize("M,K,N,mb,ns,wm", [(200, 4096, 1024, 8, 3, 1), (64, 3840, 768, 2, 4, 2),
-                                            (16, 2048, 4160, 1, 6, 1), (130, 1152, 2048, 4, 3, 2)])
-def test_sk_default_and_split_grids(M, K, N, mb, ns, wm):
+@pytest.mark.parametrize("M,K,N,mb,ns,wm,wn", [(200, 4096, 1024, 8, 3, 1, 4),
+                                               (64, 3840, 768, 2, 4, 2, 4),
+                                               (16, 2048, 4160, 1, 6, 1, 4),
+                                               (130, 1152, 2048, 4, 3, 2, 4),
+                                               (40, 2048, 4160, 2, 3, 1, 8),
+                                               (16, 1536, 1536, 1, 4, 1, 8)])
+def test_sk_default_and_split_grids(M, K, N, mb, ns, wm, wn):
     """Several column and row tiles; the default grid (one workgroup per
     compute unit, at least eight K blocks each) and a 5-workgroup grid whose
     runs end inside tiles."""
     A, Bq, S = make_inputs(M, K, N, 128, seed=M + N)
     _, C64 = oracle.gemm(A, Bq, S, 128)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, 0, wm))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 0, wm, wn))
     desc = w4.w4a16_describe(M, K, N, 128)
-    assert desc.startswith(_name(mb, ns, wm)), desc
+    assert desc.startswith(_name(mb, ns, wm, wn)), desc
     say("sk default grid", M, K, N, desc)
     assert_gemm_close(run_gemm(A, Bq, S, 128), C64, desc)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, 5, wm))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 5, wm, wn))
     desc5 = w4.w4a16_describe(M, K, N, 128)
     assert "workspace=0" not in desc5, desc5
     say("sk grid 5", M, K, N, desc5)
@@ -96,11 +101,11 @@ def test_sk_one_hot_rows_are_exact():
     ks = np.random.default_rng(4).integers(0, K, size=M)
     A[np.arange(M), ks] = 1.0
     W = oracle.dequant(Bq, S, g)
-    for mb, ns, wm in VARIANTS:
-        w4.w4a16_set_forced_plan(_plan(mb, ns, 4, wm))
-        say("sk one-hot", mb, ns, wm)
+    for mb, ns, wm, wn in VARIANTS:
+        w4.w4a16_set_forced_plan(_plan(mb, ns, 4, wm, wn))
+        say("sk one-hot", mb, ns, wm, wn)
         C = run_gemm(A, Bq, S, g)
-        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, ns, wm)
+        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, ns, wm, wn)
 
 
 def test_sk_deterministic_and_counters_reset():
@@ -133,27 +138,20 @@ def test_sk_fused_epilogue(act):
     A, Bq, S = make_inputs(M, K, N, g, seed=9)
     bias = make_bias(N, seed=10)
     _, Y64, Z64 = oracle.gemm_fused(A, Bq, S, g, bias, act)
-    for grid, (mb, ns, wm) in ((1, (4, 4, 1)), (5, (4, 4, 1)), (5, (2, 4, 2))):
-        w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm))
+    for grid, (mb, ns, wm, wn) in ((1, (4, 4, 1, 4)), (5, (4, 4, 1, 4)), (5, (2, 4, 2, 4)),
+                                   (5, (2, 3, 1, 8))):
+        w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm, wn))
         desc = w4.w4a16_describe(M, K, N, g)
         say("sk fused", act, desc)
         C = run_gemm_fused(A, Bq, S, g, bias, act)
         assert_epilogue_close(C, Z64, Y64, f"act {act} {desc}")
 
 
-def test_heuristic_picks_stream_k_only_on_large_layers():
-    """The stream-K kernel takes 9..16 rows on a layer with many K blocks per
-    compute unit; other batches and small layers keep the whole-tile
-    kernels, and the forced plan "tile -1" gives the plan the heuristic
-    makes without it."""
-    K, N = 18432, 73728
-    for M in (9, 16):
-        assert w4.w4a16_describe(M, K, N, 128).startswith("gemm_sk_kernel<1,4,6,1>"), M
-    for M in (1, 8, 17, 32, 64, 128):
-        assert not w4.w4a16_describe(M, K, N, 128).startswith("gemm_sk_kernel<"), M
-    assert not w4.w4a16_describe(16, 4096, 4096, 128).startswith("gemm_sk_kernel<")
+def test_forced_plan_without_stream_k():
+    """The forced plan "tile -1" gives the plan the heuristic makes without
+    the stream-K kernel, and it runs."""
     w4.w4a16_set_forced_plan("0,0,0,0,0,-1")
-    desc = w4.w4a16_describe(16, K, N, 128)
+    desc = w4.w4a16_describe(16, 18432, 73728, 128)
     assert not desc.startswith("gemm_sk_kernel<"), desc
     M = 64
     A, Bq, S = make_inputs(M, 2048, 4096, 128, seed=8)

@@ -51,7 +51,8 @@ __all__ = [
     "w4a16_sparse24_repack", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_workspace_bytes", "w4a16_sparse24_describe",
     "w4a16_workspace_bytes", "w4a16_packed_bytes", "w4a16_layout_version",
-    "w4a16_status_string", "w4a16_describe", "w4a16_set_forced_plan", "w4a16_gemm_noalloc",
+    "w4a16_status_string", "w4a16_describe", "w4a16_plan_describe", "w4a16_set_forced_plan",
+    "w4a16_gemm_noalloc",
     "W4A16_NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
 ]
 
@@ -75,6 +76,7 @@ EXPORTED_SYMBOLS = (
     "w4a16_sparse24_packed_bytes", "w4a16_sparse24_repack", "w4a16_sparse24_workspace_bytes",
     "w4a16_sparse24_describe", "w4a16_sparse24_gemm", "w4a16_sparse24_dequant_debug",
     "w4a16_set_forced_plan", "w4a16_gemm_noalloc", "w8a16_workspace_bytes", "w8a16_describe",
+    "w4a16_plan_describe",
 )
 
 
@@ -141,6 +143,8 @@ def load():
     lib.w4a16_dequant_debug.restype = i
     lib.w4a16_describe.argtypes = [i, i, i, i, ctypes.c_char_p, sz]
     lib.w4a16_describe.restype = i
+    lib.w4a16_plan_describe.argtypes = [i, i, i, i, i, i, ctypes.c_char_p, sz]
+    lib.w4a16_plan_describe.restype = i
     lib.w4a16_sparse24_packed_bytes.argtypes = [i, i]
     lib.w4a16_sparse24_packed_bytes.restype = sz
     lib.w4a16_sparse24_repack.argtypes = [vp, vp, vp, i, i, vp]
@@ -268,6 +272,20 @@ def w4a16_workspace_bytes(M: int, K: int, N: int, group: int) -> int:
 def w4a16_describe(M: int, K: int, N: int, group: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check("w4a16_describe", load().w4a16_describe(int(M), int(K), int(N), int(group), buf, 256))
+    return buf.value.decode()
+
+
+# weight formats of w4a16_plan_describe (enum w4a16_format)
+W4A16_FORMAT_F16, W4A16_FORMAT_F16_ZP, W4A16_FORMAT_BF16, W4A16_FORMAT_BF16_ZP = 0, 1, 2, 3
+W4A16_FORMAT_W8, W4A16_FORMAT_SPARSE24 = 4, 5
+
+
+def w4a16_plan_describe(M: int, K: int, N: int, group: int, fmt: int, cus: int) -> str:
+    """The plan of a call of weight format ``fmt`` on a device with ``cus``
+    compute units, computed without a device."""
+    buf = ctypes.create_string_buffer(256)
+    _check("w4a16_plan_describe", load().w4a16_plan_describe(int(M), int(K), int(N), int(group),
+                                                             int(fmt), int(cus), buf, 256))
     return buf.value.decode()
 
 

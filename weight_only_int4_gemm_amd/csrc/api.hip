@@ -65,7 +65,7 @@ int check_group(int K, int group) {
 }
 
 bool variant_is_compiled(const Plan& q, int fmt) {
-  if (q.tile == 4) return fmt <= kFmtBf16Zp && sk_is_compiled(q.mb, q.nb, q.depth, q.wm);
+  if (q.tile == 4) return fmt <= kFmtBf16Zp && sk_is_compiled(q.mb, q.nb, q.depth, q.wm, q.wk);
   if (fmt == kFmtSp24) {
     if (q.tile == 2) return lds_sp_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth);
     return q.tile == 0 && q.wm == 1 && sp_is_compiled(q.mb, q.nb, q.wk, q.depth);
@@ -157,8 +157,9 @@ void apply_forced_plan(Plan* p, const Plan& base, int KB, int fmt) {
   *p = q;
 }
 
-// The plan of one call as one line of text (w4a16_describe).
-int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len) {
+// The plan of one call on a device with `cus` compute units as one line of
+// text (w4a16_describe, w4a16_plan_describe).
+int describe_plan(int M, int K, int N, int group, int fmt, int cus, char* buf, size_t len) {
   if (!buf || len == 0) return W4A16_ERR_NULL;
   buf[0] = 0;
   if (M <= 0 || N == 0) return W4A16_ERR_SHAPE;
@@ -166,14 +167,13 @@ int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len)
   if (rc != W4A16_OK) return rc;
   rc = check_group(K, group);
   if (rc != W4A16_OK) return rc;
-  const int cus = current_cus(nullptr);
   if (cus <= 0) return W4A16_ERR_DEVICE;
   const Plan p = make_plan(M, K, N, group, cus, fmt);
   if (p.tile == 4)
     std::snprintf(buf, len,
-                  "gemm_sk_kernel<%d,%d,%d,%d> grid=%dx1x1 block=%d tiles=%dx%d splits=%d "
+                  "gemm_sk_kernel<%d,%d,%d,%d,%d> grid=%dx1x1 block=%d tiles=%dx%d splits=%d "
                   "workspace=%zu",
-                  p.mb, p.nb, p.depth, p.wm, p.splits, 64 * kSkWavesPerGroup * p.wm, p.tiles_n,
+                  p.mb, p.nb, p.depth, p.wm, p.wk, p.splits, 64 * p.wk * p.wm, p.tiles_n,
                   p.tiles_m,
                   p.splits, p.workspace_bytes);
   else if (p.tile >= 2)
@@ -188,6 +188,17 @@ int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len)
                   p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
                   p.splits, p.workspace_bytes);
   return W4A16_OK;
+}
+
+int describe_fmt(int M, int K, int N, int group, int fmt, char* buf, size_t len) {
+  if (!buf || len == 0) return W4A16_ERR_NULL;
+  buf[0] = 0;
+  if (M <= 0 || N == 0) return W4A16_ERR_SHAPE;
+  int rc = check_kn(K, N, false);
+  if (rc != W4A16_OK) return rc;
+  rc = check_group(K, group);
+  if (rc != W4A16_OK) return rc;
+  return describe_plan(M, K, N, group, fmt, current_cus(nullptr), buf, len);
 }
 
 size_t workspace_fmt(int M, int K, int N, int group, int fmt) {
@@ -222,20 +233,29 @@ size_t workspace_fmt(int M, int K, int N, int group, int fmt) {
 // wider wave tiles: 4096 x 12288 at M = 128: 26.6 -> 21.1 us); and the K
 // split there is twice the dense one below a full wave of workgroups and
 // none above it.
-// Whether the stream-K kernel takes a call, and with how many waves along M
-// (0: not taken).  Measured against the plans above (graph replay over
-// rotating weight copies), it is ahead only for 9 to 16 rows on a layer
-// that gives every compute unit many K blocks of 256 columns (18432 x 73728
-// at M = 16: 164.7 against 168.8 us).  At 32 to 128 rows there the LDS
-// kernel is level or ahead (180 / 236 / 380 us against 183 / 239 / 388 us at
-// M = 32 / 64 / 128), two waves per SIMD are slower than one, and on the
-// Llama-2-7B layers the stream-K fix-up and prologue cost 15-20 us more than
-// a grid of whole tiles.
-static int stream_k_wm(int M, int KB, int N, int cus, int fmt) {
-  if (fmt > kFmtBf16Zp || M <= 8 || M > 16) return 0;
+// Whether the stream-K kernel takes a call: the 4-bit dense formats from 9
+// to 64 rows, on a layer that gives every compute unit many K blocks of 256
+// columns, as 16*mb x 512 tiles of eight waves (two per SIMD, each with its
+// own 64 columns, so no weight is unpacked twice).  Measured against the
+// whole-tile plans by graph replay over rotating weight copies, on the
+// 18432 x 73728 layer: 144-154 against 152-161 us at M = 16, 160 against
+// 176-185 us at M = 32, 211 against 232-234 us at M = 64.  At M = 128 the
+// LDS kernel's 128 x 256 tiles stay ahead (368 against 394 us).  On smaller
+// layers the fix-up and the pipeline fill cost 10-20 us that a grid of whole
+// tiles does not pay: 8192 x 28672, 28672 x 8192 and the Llama-2-7B layers
+// at M = 16..64 ran 1.16-2.9x slower.
+static bool stream_k_plan(int M, int KB, int N, int cus, int fmt, Plan* p) {
+  if (fmt > kFmtBf16Zp || M <= 8 || M > 64) return false;
   const int64_t blocks = (int64_t)((N + 255) / 256) * KB;  // 256-column K blocks
-  if (blocks < (int64_t)48 * cus) return 0;
-  return 1;
+  if (blocks < (int64_t)48 * cus) return false;
+  p->tile = 4;
+  p->wm = 1;
+  p->wk = 8;  // waves along N
+  p->nb = 4;
+  p->mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  p->depth = p->mb == 1 ? 4 : 3;  // as many stages as fit in LDS
+  p->splits = 0;                  // the stream-K grid is set below
+  return true;
 }
 
 Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
@@ -317,7 +337,6 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   }
   auto shape = [&](Plan& q) {
     const int f = q.tile == 3 ? 32 : 16;
-    if (q.tile == 4) q.wk = kSkWavesPerGroup;
     q.tm = f * q.mb * q.wm;
     q.tn = f * q.nb * (q.tile ? q.wk : 1);  // LDS and stream-K kernels split N over waves
     q.tiles_n = (N + q.tn - 1) / q.tn;
@@ -377,19 +396,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   if (want > 64) want = 64;
   p.splits = (int)(want < 1 ? 1 : want);
   const Plan base = p;  // the plan without the stream-K kernel
-  const int sk_wm = stream_k_wm(M, KB, N, cus, fmt);
-  if (sk_wm > 0) {
-    // stream-K kernel: wm x 4 waves of 16*mb x 64, every compute unit an
-    // equal share of the (tile, K block) iterations
-    p.tile = 4;
-    p.wm = sk_wm;
-    p.wk = kSkWavesPerGroup;
-    p.nb = 4;
-    const int rows = (M + sk_wm - 1) / sk_wm;  // rows per wave
-    p.mb = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : 8;
-    p.depth = sk_wm == 1 ? (p.mb == 8 ? 3 : p.mb == 4 ? 4 : 6) : (p.mb == 4 ? 3 : p.mb == 2 ? 4 : 6);
-    p.splits = 0;  // the stream-K grid is set below
-  }
+  stream_k_plan(M, KB, N, cus, fmt, &p);
   apply_forced_plan(&p, base, KB, fmt);
   shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
@@ -406,7 +413,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
       g = (units * p.depth + kSkMinIters - 1) / kSkMinIters;
     if (g > units) g = units;
     if (g < 1) g = 1;
-    if (ftiles * kSkWavesPerGroup * p.wm > kMaxSplitTiles) g = ftiles;
+    if (ftiles * p.wk * p.wm > kMaxSplitTiles) g = ftiles;
     p.splits = (int)g;
     p.workspace_bytes = sk_workspace_bytes(p.splits, p.tm, p.tn, (int)ftiles, KB, p.depth);
     return p;
@@ -467,6 +474,14 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group) {
 
 int w4a16_describe(int M, int K, int N, int group, char* buf, size_t len) {
   return describe_fmt(M, K, N, group, kFmtF16, buf, len);
+}
+
+int w4a16_plan_describe(int M, int K, int N, int group, int format, int cus, char* buf,
+                        size_t len) {
+  if (!buf || len == 0) return W4A16_ERR_NULL;
+  buf[0] = 0;
+  if (format < kFmtF16 || format > kFmtSp24) return W4A16_ERR_DTYPE;
+  return describe_plan(M, K, N, group, format, cus, buf, len);
 }
 
 int w4a16_repack(const uint32_t* Bq, uint32_t* Bpacked, int K, int N, void* stream) {

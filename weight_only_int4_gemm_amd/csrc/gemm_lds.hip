@@ -31,11 +31,16 @@
 //    wave reads its fragments with one conflict-free 16-byte read per block;
 //  * scales: the tile's 16*NB*WN FP16 scales of this K block's group.
 //
+// With 16 x 16 blocks the weights are the matrix instruction's first
+// operand and the activations its second, so a lane's four accumulators are
+// four consecutive output columns of one row and the output stage stores
+// 8 bytes per lane and block (tile_common.hpp).
+//
 // 2:4-sparse weights (format 5): a code block is 768 bytes (layout.hpp),
 // brought in by one 16-byte direct load on lanes 0..47; a wave reads its
 // two code words (8 bytes) and its position word from LDS and runs two
 // sparse 16x16x64 matrix instructions per K block and 16 x 16 output block
-// (format.hpp, smma16), whose results are C transposed.
+// (format.hpp, smma16), whose results are likewise C transposed.
 #include <type_traits>
 
 #include "layout.hpp"
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   const int n16_last = N / kBlockN - 1;
   const int wrow0 = row0 + wm * F * MB;  // this wave's tile
   const int wcol0 = col0 + wn * F * NB;
-  LaneBias<NB, F, EPI> bias;
+  typename std::conditional<F == 16, LaneBias4<NB, EPI>, LaneBias<NB, F, EPI>>::type bias;
   bias.load(ep, wcol0, N);
 
   // Code pieces this wave loads: piece (wave + WAVES * i) % (BLOCKS * PPB)
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          if constexpr (F == 16) acc[mb][nb] = mma16<FMT>(cur[mb], bcur[nb], acc[mb][nb]);
+          if constexpr (F == 16) acc[mb][nb] = mma16<FMT>(bcur[nb], cur[mb], acc[mb][nb]);
         }
     }
   };
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   if constexpr (F == 16)
-    store_output_tile<MB, NB, WAVES, EPI, FMT, SP>(acc, C, M, N, wrow0, wcol0, split, splits,
+    store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, splits,
                                                counters, partials,
                                                reinterpret_cast<int*>(&st0.s[0]), ep, bias);
   else
@@ -479,7 +484,7 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
   X(4, 1, 1, 8, 3, 32) X(2, 1, 1, 8, 3, 32) X(4, 1, 1, 4, 3, 32) X(2, 2, 1, 4, 3, 32)       \
   X(4, 4, 2, 4, 3, 16) X(2, 4, 4, 2, 3, 16) X(4, 2, 2, 4, 3, 16) X(2, 2, 4, 2, 3, 16)       \
   X(2, 2, 2, 4, 3, 16) X(2, 4, 2, 4, 3, 16) X(4, 4, 2, 2, 3, 16) X(2, 4, 2, 2, 3, 16)       \
-  X(1, 2, 4, 2, 3, 32) X(1, 4, 4, 2, 3, 32) X(2, 2, 2, 4, 3, 32)
+  X(1, 2, 4, 2, 3, 32) X(1, 4, 4, 2, 3, 32) X(2, 2, 2, 4, 3, 32) X(4, 4, 1, 8, 3, 16)
 
 // Variants compiled for the other formats too (16 x 16 blocks): the ones
 // the plans pick.

@@ -65,7 +65,6 @@ namespace {
 
 typedef _Float16 half4_sk_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSkColWaves = kSkWavesPerGroup;  // waves along N
 
 // Logical run of this workgroup: runs g, g + 1, ... on one XCD when the
 // grid is a multiple of the 8 XCDs (block b runs on XCD b % 8).
@@ -92,13 +91,13 @@ __device__ __forceinline__ int sk_run_of(int64_t x, int64_t U, int64_t G) {
 // FMT: the weight format (format.hpp), 0 to 3: FP16 or BF16, with or
 // without zero points.  A, S and C hold raw 16-bit values; Z the zero points
 // uint8[K/group][N] of formats 1 and 3.  The fused output stage is FP16 only.
-// WM: waves along M.  The workgroup is WM x 4 waves, one or two per SIMD;
-// wave (wm, wn) owns rows 16*MB*wm .. +16*MB and columns 16*NB*wn .. +16*NB
-// of the tile, and each code block of the tile is loaded once and read by
-// the WM waves of its column.
-template <int MB, int NB, int NS, int WM, bool EPI, int FMT>
-__global__ __launch_bounds__(64 * kSkColWaves * WM)
-__attribute__((amdgpu_waves_per_eu(WM, WM))) void
+// WM x WN waves (WN = 4 or 8): one or two per SIMD.  Wave (wm, wn) owns
+// rows 16*MB*wm .. +16*MB and columns 16*NB*wn .. +16*NB of the tile, and
+// each code block of the tile is loaded once and read by the WM waves of
+// its column.
+template <int MB, int NB, int NS, int WM, int WN, bool EPI, int FMT>
+__global__ __launch_bounds__(64 * WN * WM)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void
 gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
                const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
                uint64_t group_magic, int tiles_n, int tiles_m, unsigned* __restrict__ counters,
@@ -106,16 +105,20 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   static_assert(FMT >= 0 && FMT <= 3, "the 4-bit dense formats");
   static_assert(!EPI || FMT == kFmtF16, "the fused epilogue is FP16 only");
   constexpr bool ZP = Format<FMT>::kZp;
-  constexpr int WN = kSkColWaves;
+  static_assert(WN == 4 || WN == 8, "one or two wave columns per SIMD");
   constexpr int WAVES = WN * WM;
   constexpr int TM = 16 * MB * WM;         // rows of the tile
   constexpr int TNW = 16 * NB;             // columns of one wave
   constexpr int TN = WN * TNW;             // columns of the tile
   constexpr int APIECES = TM * 16;         // 16-byte pieces of one stage's activations
-  constexpr int ALOADS = APIECES / 64 / WAVES;  // = MB activation wave-loads per wave
+  constexpr int ACHUNKS = APIECES / 64;         // 1 KiB wave-loads of activations
+  // activation loads per wave; with fewer chunks than waves some chunks are
+  // loaded twice (same bytes to the same place), so every wave issues the
+  // same number of loads
+  constexpr int ALOADS = (ACHUNKS + WAVES - 1) / WAVES;
   constexpr int CLOADS = WN * NB / WAVES;       // code blocks each wave loads
   static_assert(NB == 4, "a wave's 64 scales: one 2-byte direct load, one 16-byte read");
-  static_assert(ALOADS == MB && CLOADS * WAVES == WN * NB, "every wave loads an equal share");
+  static_assert(CLOADS * WAVES == WN * NB, "every wave loads an equal share of the codes");
   constexpr int LOADS = ALOADS + CLOADS + 1 + (ZP ? 1 : 0);  // direct loads per wave per stage
   static_assert(NS >= 2 && (NS - 1) * LOADS < 64, "vmcnt range");
   struct StagePlain {
@@ -186,10 +189,10 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const int tn = ld_tn;
     const int tm = ld_tm;
     const int kb = ld_kb < KB ? ld_kb : KB - 1;  // padding iterations re-read the last block
-    // activations: chunk c = wave + WAVES * q holds rows 4c .. 4c + 3
+    // activations: chunk c = (wave + WAVES * q) % ACHUNKS holds rows 4c .. 4c + 3
 #pragma unroll
     for (int q = 0; q < ALOADS; ++q) {
-      const int chunk = wave + WAVES * q;
+      const int chunk = (wave + WAVES * q) % ACHUNKS;
       const int r = 4 * chunk + (lane >> 4);
       const int gr0 = tm * TM + r;
       const int gr = gr0 < M ? gr0 : M - 1;  // rows past M: never stored
@@ -486,13 +489,13 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 // ---------------------------------------------------------------------------
 // host side
 
-// Compiled variants (MB, NB, NS, WM): MB row blocks per wave, NS stages, WM
-// waves along M.
-#define W4A16_SK_VARIANTS(X)                                                        \
-  X(8, 4, 3, 1) X(4, 4, 4, 1) X(2, 4, 6, 1) X(1, 4, 6, 1) X(4, 4, 3, 2) X(2, 4, 4, 2) \
-      X(1, 4, 6, 2)
+// Compiled variants (MB, NB, NS, WM, WN): MB row blocks per wave, NS
+// stages, WM x WN waves.
+#define W4A16_SK_VARIANTS(X)                                                                \
+  X(8, 4, 3, 1, 4) X(4, 4, 4, 1, 4) X(2, 4, 6, 1, 4) X(1, 4, 6, 1, 4) X(4, 4, 3, 2, 4)       \
+      X(2, 4, 4, 2, 4) X(1, 4, 6, 2, 4) X(1, 4, 4, 1, 8) X(2, 4, 3, 1, 8) X(4, 4, 3, 1, 8)
 
-template <int MB, int NB, int NS, int WM, int FMT>
+template <int MB, int NB, int NS, int WM, int WN, int FMT>
 hipError_t launch_sk_one(const Plan& p, const uint16_t* A, const uint32_t* Bp, const uint16_t* S,
                          uint16_t* C, int M, int K, int N, uint64_t gmagic, Epilogue ep,
                          const uint8_t* Z, void* workspace, hipStream_t stream) {
@@ -502,20 +505,20 @@ hipError_t launch_sk_one(const Plan& p, const uint16_t* A, const uint32_t* Bp, c
     counters = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterHeaderBytes);
   }
-  const dim3 grid(p.splits), block(64 * kSkColWaves * WM);
+  const dim3 grid(p.splits), block(64 * WN * WM);
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
   if constexpr (FMT == kFmtF16) {
     if (epilogue_needed(ep)) {
-      hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WM, true, FMT>), grid, block, 0, stream, a, Bp, s,
+      hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WM, WN, true, FMT>), grid, block, 0, stream, a, Bp, s,
                          c, M, K, N, gmagic, p.tiles_n, p.tiles_m, counters, partials, ep, Z);
       return hipGetLastError();
     }
   } else {
     if (epilogue_needed(ep)) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WM, false, FMT>), grid, block, 0, stream, a, Bp, s, c,
+  hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WM, WN, false, FMT>), grid, block, 0, stream, a, Bp, s, c,
                      M, K, N, gmagic, p.tiles_n, p.tiles_m, counters, partials, ep, Z);
   return hipGetLastError();
 }
@@ -524,10 +527,10 @@ template <int FMT>
 hipError_t launch_sk_fmt(const Plan& p, const uint16_t* A, const uint32_t* Bp, const uint16_t* S,
                          uint16_t* C, int M, int K, int N, uint64_t gmagic, Epilogue ep,
                          const uint8_t* Z, void* workspace, hipStream_t stream) {
-#define W4A16_SKCASE(MB_, NB_, NS_, WM_)                                                 \
-  if (p.mb == MB_ && p.nb == NB_ && p.depth == NS_ && p.wm == WM_)                       \
-    return launch_sk_one<MB_, NB_, NS_, WM_, FMT>(p, A, Bp, S, C, M, K, N, gmagic, ep, Z,  \
-                                                  workspace, stream);
+#define W4A16_SKCASE(MB_, NB_, NS_, WM_, WN_)                                                 \
+  if (p.mb == MB_ && p.nb == NB_ && p.depth == NS_ && p.wm == WM_ && p.wk == WN_)             \
+    return launch_sk_one<MB_, NB_, NS_, WM_, WN_, FMT>(p, A, Bp, S, C, M, K, N, gmagic, ep, Z, \
+                                                       workspace, stream);
   W4A16_SK_VARIANTS(W4A16_SKCASE)
 #undef W4A16_SKCASE
   return hipErrorInvalidValue;

@@ -58,7 +58,7 @@ bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
 bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns);
-bool sk_is_compiled(int mb, int nb, int ns, int wm);
+bool sk_is_compiled(int mb, int nb, int ns, int wm, int wn);
 size_t sk_workspace_bytes(int wgs, int tm, int tn, int tiles, int KB, int ns);
 
 hipError_t launch_repack(const uint32_t* Bq, uint32_t* Bp, int K, int N,
@@ -92,9 +92,7 @@ hipError_t launch_dequant_fmt(const uint32_t* Bp, const uint16_t* S, const uint8
 // zero, and a workspace zero-filled once serves calls of any shape in turn.
 // Plans split K only when the output has at most kMaxSplitTiles tiles.
 constexpr int kMaxSplitTiles = 16384;
-// The stream-K kernel: waves per workgroup (each with its own counter per
-// tile) and the fewest iterations a workgroup is given.
-constexpr int kSkWavesPerGroup = 4;
+// The stream-K kernel: the fewest iterations a workgroup is given.
 constexpr int kSkMinIters = 8;
 constexpr size_t kCounterHeaderBytes = (size_t)kMaxSplitTiles * sizeof(unsigned);
 

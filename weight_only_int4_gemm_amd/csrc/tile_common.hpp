@@ -70,10 +70,35 @@ struct LaneBias {
   }
 };
 
+typedef _Float16 half4_tc_t __attribute__((ext_vector_type(4)));
+
+// The bias for transposed 16 x 16 blocks: lane l stores columns
+// wcol0 + 16 nb + 4 (l / 16) .. +3 of its NB column blocks, loaded as one
+// 8-byte vector per block at kernel start (same reasoning as LaneBias).
+template <int NB, bool EPI>
+struct LaneBias4 {
+  half4_tc_t v[NB];
+  __device__ __forceinline__ void load(const Epilogue& ep, int wcol0, int N) {
+    if constexpr (EPI) {
+      const int c = wcol0 + 4 * (int)((threadIdx.x & 63) >> 4);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        v[nb] = (ep.bias && c + 16 * nb < N)
+                    ? *reinterpret_cast<const half4_tc_t*>(ep.bias + c + 16 * nb)
+                    : half4_tc_t{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ float at(int nb, int e) const {
+    if constexpr (EPI) return (float)v[nb][e];
+    return 0.f;
+  }
+};
+
 // Write a workgroup's output tile.  Each of its WAVES waves owns a
 // 16*MB x 16*NB block of it starting at row wrow0, column wcol0; acc[mb][nb]
-// holds, in lane l, rows 4*(l/16) .. +3 of column l % 16 of the 16x16 block
-// (mb, nb) of that wave tile.
+// holds block (mb, nb) of that wave tile transposed (the weights are the
+// matrix instruction's first operand): lane l has row l % 16 and columns
+// 4*(l/16) .. +3, stored as one 8-byte vector.
 //
 // With splits > 1: publish the partial tile with device-coherent stores,
 // wait for them, count the arrival; the last workgroup of the tile adds the
@@ -83,55 +108,35 @@ struct LaneBias {
 // that sums finds its own fragments at the same places.  `flag` is an int in
 // LDS no wave touches any more.  The epilogue is applied to the final sums
 // only; FMT sets the output type (FP16, or BF16 for formats 2 and 3).
-// TRANS: acc[mb][nb] holds the block transposed (the sparse instruction's
-// result): lane l has row l % 16, columns 4*(l/16) .. +3, stored as one
-// 8-byte vector.
-template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16, bool TRANS = false>
+template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
                                                   int wrow0, int wcol0, int split, int splits,
                                                   unsigned* __restrict__ counters,
                                                   float* __restrict__ partials, int* flag,
                                                   const Epilogue& ep,
-                                                  const LaneBias<NB, 16, EPI>& bias) {
+                                                  const LaneBias4<NB, EPI>& bias) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col_base = wcol0 + (lane & 15);
   auto write_c = [&]() {
-    if constexpr (TRANS) {
-      static_assert(!EPI, "no fused epilogue on the transposed path");
-      typedef _Float16 half4_vt __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int gr = wrow0 + mb * 16 + (lane & 15);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          // N is a multiple of 16: four columns from a multiple of 4 fit
-          const int gc = wcol0 + nb * 16 + (lane >> 4) * 4;
-          if (gr < M && gc < N) {
-            half4_vt h;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) h[i] = out16<FMT>(acc[mb][nb][i]);
-            *reinterpret_cast<half4_vt*>(C + (int64_t)gr * N + gc) = h;
-          }
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int gr = wrow0 + mb * 16 + (lane & 15);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int gc = col_base + nb * 16;
-        if (gc >= N) continue;
-        const float b = bias[nb];
+        // N is a multiple of 16: four columns from a multiple of 4 fit
+        const int gc = wcol0 + nb * 16 + (lane >> 4) * 4;
+        if (gr < M && gc < N) {
+          half4_tc_t h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int gr = wrow0 + mb * 16 + (lane >> 4) * 4 + i;
-          const float x = acc[mb][nb][i];
-          if (gr < M) C[(int64_t)gr * N + gc] = out16<FMT>(EPI ? epilogue_apply(ep, x, b) : x);
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[mb][nb][e];
+            h[e] = out16<FMT>(EPI ? epilogue_apply(ep, x, bias.at(nb, e)) : x);
+          }
+          *reinterpret_cast<half4_tc_t*>(C + (int64_t)gr * N + gc) = h;
         }
       }
+    }
   };
   if (splits == 1) {
     write_c();
