@@ -115,9 +115,9 @@ int w4a16_plan_describe(int M, int K, int N, int group, int format, int cus, cha
  * in this process with the text spec
  *   "mb,nb,wk,splits[,depth[,tile[,unused[,wm]]]]"
  * (a field <= 0 keeps the heuristic's value; tile 0 is the streaming
- * kernel, 2 the LDS kernel with 16 x 16 blocks, 3 with 32 x 32 blocks, 4 the
- * stream-K kernel (wk = its waves along N, splits = its grid), -1 the plan
- * the heuristic makes without the stream-K kernel).  A
+ * kernel, 2 the LDS kernel, 4 the stream-K kernel (wk = its waves along N,
+ * splits = its grid), -1 the plan the heuristic makes without the stream-K
+ * kernel).  A
  * spec naming a variant that is not compiled leaves the heuristic's plan in
  * place.  NULL or "" restores the heuristic.  The environment variable
  * W4A16_FORCE_PLAN, read once when the library first plans a call, seeds the
@@ -271,9 +271,8 @@ int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked,
  *         W4A16_ERR_DTYPE.
  * The other arguments, layouts, alignment, workspace and errors are those
  * of w4a16_gemm (same plan and workspace size).  With dtype F16 and zeros
- * NULL this is w4a16_gemm.  The BF16 and zero-point kernels are compiled
- * for the variants the library's plans choose; a plan forced outside them
- * (a tuning override) returns W4A16_ERR_LAUNCH.  No fused epilogue here.
+ * NULL this is w4a16_gemm.  Every format is compiled for the same kernel
+ * variants (the ones the library's plans choose).  No fused epilogue here.
  */
 int w4a16_gemm_awq(const uint16_t* A, const uint32_t* Bpacked, const uint16_t* scales,
                    const uint8_t* zeros, uint16_t* C, int M, int K, int N, int group,

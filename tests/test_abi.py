@@ -242,10 +242,11 @@ def test_forced_plan_setter(lib):
     assert lib.w4a16_set_forced_plan(b"1,2,4,1") == OK
     assert lib.w4a16_set_forced_plan(b"1,2,4,1,2,0,0,1") == OK
     assert lib.w4a16_set_forced_plan(b"4,1,8,2,3,2") == OK
-    assert lib.w4a16_set_forced_plan(b"2,4,4,0,4,4,0,2") == OK  # stream-K, two waves along M
+    assert lib.w4a16_set_forced_plan(b"2,4,8,0,3,4") == OK      # stream-K, eight waves
     assert lib.w4a16_set_forced_plan(b"0,0,0,0,0,-1") == OK     # the plan without stream-K
     assert lib.w4a16_set_forced_plan(b"1,2") == ERR_SHAPE        # fewer than four fields
     assert lib.w4a16_set_forced_plan(b"1,2,4,1,2,1") == ERR_SHAPE  # no tile kernel 1
+    assert lib.w4a16_set_forced_plan(b"4,1,8,1,3,3") == ERR_SHAPE  # nor 3 (removed)
     assert lib.w4a16_set_forced_plan(b"x") == ERR_SHAPE
     assert lib.w4a16_set_forced_plan(None) == OK
     assert lib.w4a16_set_forced_plan(b"") == OK

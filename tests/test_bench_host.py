@@ -22,14 +22,16 @@ def test_kernel_names_from_profiler_output():
         "_ZN5w4a1611gemm_kernelILi1ELi4ELi4ELi2EEEvPKDF16_": "gemm_kernel<1,4,4,2>",
         "_ZN5w4a1613repack_kernelEPKjPjii": "repack_kernel",
         # the fused-epilogue switch (a bool template argument) is dropped
-        "_ZN5w4a1615gemm_lds_kernelILi4ELi2ELi2ELi4ELi3ELi16ELb1EEEvPKDF16_PKjS2_PDF16_iiimiPjPf"
-        "NS_8EpilogueE": "gemm_lds_kernel<4,2,2,4,3,16>",
-        "void w4a16::gemm_lds_kernel<4, 1, 1, 8, 3, 16, false>(_Float16 const*)":
-            "gemm_lds_kernel<4,1,1,8,3,16>",
+        "_ZN5w4a1615gemm_lds_kernelILi4ELi2ELi2ELi4ELi3ELb1EEEvPKDF16_PKjS2_PDF16_iiimiPjPf"
+        "NS_8EpilogueE": "gemm_lds_kernel<4,2,2,4,3>",
+        "void w4a16::gemm_lds_kernel<4, 1, 1, 8, 3, false>(_Float16 const*)":
+            "gemm_lds_kernel<4,1,1,8,3>",
         # and so is the weight format after it
-        "_ZN5w4a1615gemm_lds_kernelILi4ELi1ELi1ELi8ELi3ELi16ELb0ELi2EEEvPKDF16_PKjS2_PDF16_"
-        "iiimiPjPfNS_8EpilogueEPKh": "gemm_lds_kernel<4,1,1,8,3,16>",
+        "_ZN5w4a1615gemm_lds_kernelILi4ELi1ELi1ELi8ELi3ELb0ELi2EEEvPKDF16_PKjS2_PDF16_"
+        "iiimiPjPfNS_8EpilogueEPKh": "gemm_lds_kernel<4,1,1,8,3>",
         "void w4a16::gemm_kernel<1, 1, 8, 2, false, 3>(_Float16 const*)": "gemm_kernel<1,1,8,2>",
+        "_ZN5w4a1614gemm_sk_kernelILi2ELi4ELi3ELi8ELb0ELi0EEEvPKDF16_PKjS2_PDF16_iiimiiPjPf":
+            "gemm_sk_kernel<2,4,3,8>",
     }
     for raw, short in cases.items():
         assert bench._short_kernel_name(raw) == short
@@ -85,7 +87,7 @@ def _fake_pmc_db(path, rows):
 
 
 def test_pmc_kernels_summary(tmp_path):
-    k = "_ZN5w4a1615gemm_lds_kernelILi8ELi2ELi1ELi8ELi3ELi16ELb0ELi0EEEvPKDF16_"
+    k = "_ZN5w4a1615gemm_lds_kernelILi8ELi2ELi1ELi8ELi3ELb0ELi0EEEvPKDF16_"
     # two dispatches of one GEMM kernel and one of another kernel (ignored)
     rows = []
     for d, busy, gui in ((1, 1024 * 500.0, 8 * 1000.0), (2, 1024 * 700.0, 8 * 1000.0)):
@@ -96,8 +98,8 @@ def test_pmc_kernels_summary(tmp_path):
     out = tmp_path / "out.json"
     bench.pmc_kernels(str(out), [str(tmp_path / "run_a")])
     summ = json.loads(out.read_text())
-    e = summ["runs"]["run_a"]["kernels"]["gemm_lds_kernel<8,2,1,8,3,16>"]
-    assert list(summ["runs"]["run_a"]["kernels"]) == ["gemm_lds_kernel<8,2,1,8,3,16>"]
+    e = summ["runs"]["run_a"]["kernels"]["gemm_lds_kernel<8,2,1,8,3>"]
+    assert list(summ["runs"]["run_a"]["kernels"]) == ["gemm_lds_kernel<8,2,1,8,3>"]
     assert e["GRBM_GUI_ACTIVE"]["dispatches"] == 2
     assert e["SQ_VALU_MFMA_BUSY_CYCLES"]["sum_per_dispatch"] == 1024 * 600.0
     # busy cycles over (one XCD's active cycles x 1024 SIMDs): 600 / 1000

@@ -108,13 +108,13 @@ AWQ_CASES = [
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,4>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),
-    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4,16>"),
-    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4,16>"),
-    (45, 1024, 208, "gemm_lds_kernel<4,1,1,8,3,16>"),
-    (128, 1024, 1024, "gemm_lds_kernel<4,1,1,8,3,16>"),
-    (128, 512, 36864, "gemm_lds_kernel<4,2,2,4,3,16>"),
-    (128, 256, 65536, "gemm_lds_kernel<8,2,1,8,3,16>"),
-    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3,16>"),
+    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4>"),
+    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4>"),
+    (45, 1024, 208, "gemm_lds_kernel<4,1,1,8,3>"),
+    (128, 1024, 1024, "gemm_lds_kernel<4,1,1,8,3>"),
+    (128, 512, 36864, "gemm_lds_kernel<4,2,2,4,3>"),
+    (128, 256, 65536, "gemm_lds_kernel<8,2,1,8,3>"),
+    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3>"),
 ]
 SAMPLE_COLS_ABOVE = 16384   # wider layers are checked on sampled columns
 
@@ -136,10 +136,9 @@ def test_awq_gemm_matches_oracle(fmt, dtype, zp, M, K, N, kernel):
 
 
 @pytest.mark.parametrize("fmt,dtype,zp", FORMATS)
-@pytest.mark.parametrize("plan", ["1,4,4,5,4", "1,2,8,3,2", "1,2,8,4,4,2", "2,2,8,2,4,2",
-                                  "4,1,8,3,3,2", "4,2,4,2,3,2,0,2", "8,2,8,2,3,2",
-                                  "8,4,4,3,3,4", "4,4,4,5,4,4", "2,4,4,4,6,4", "1,4,4,7,6,4",
-                                  "4,4,4,5,3,4,0,2", "2,4,4,4,4,4,0,2", "1,4,4,7,6,4,0,2"])
+@pytest.mark.parametrize("plan", ["1,4,4,5,4", "1,2,8,3,2", "1,1,4,2,2", "1,2,8,4,4,2",
+                                  "2,2,8,2,4,2", "4,1,8,3,3,2", "4,2,4,2,3,2,0,2",
+                                  "8,2,8,2,3,2", "1,4,8,5,4,4", "2,4,8,4,3,4", "4,4,8,3,3,4"])
 def test_awq_forced_plans_split_k(monkeypatch, fmt, dtype, zp, plan):
     """The compiled variants with split-K (forced; for the stream-K kernel,
     grids that share tiles between workgroups), M = 45 ragged rows, N = 208
@@ -202,18 +201,17 @@ def test_awq_split_k_deterministic():
         assert np.array_equal(first, again), f"run {i}"
 
 
-def test_awq_plan_outside_the_compiled_variants_is_rejected(monkeypatch):
-    """A forced plan with no BF16 build fails loudly; FP16 runs it."""
-    import torch
+def test_awq_forced_plan_outside_the_compiled_variants_is_ignored(monkeypatch):
+    """A forced plan naming a variant compiled for no dense format (here a
+    2:4-only LDS tile) leaves the heuristic's plan in place, for FP16 and
+    BF16 alike, and the call runs it."""
     M, K, N = 45, 1024, 208
-    A, Bq, S, Z = make_inputs_awq(M, K, N, 128, seed=3, bf16=True)
+    heur = w4.w4a16_describe(M, K, N, 128)
     w4.w4a16_set_forced_plan("4,2,4,1,3,2")
-    assert w4.w4a16_describe(M, K, N, 128).startswith("gemm_lds_kernel<4,2,1,4,3,16>")
-    say("awq rejected plan")
-    with pytest.raises(w4.W4A16Error) as e:
-        run_gemm_awq(A, Bq, S, Z, 128, 1)
-    assert e.value.name == "W4A16_ERR_LAUNCH"
-    A16, Bq16, S16, _ = make_inputs_awq(M, K, N, 128, seed=3)
-    C = run_gemm_awq(A16, Bq16, S16, None, 128, 0)
-    _, C64 = oracle.gemm_awq(A16, Bq16, S16, None, 128, 0)
-    _check(C, C64, 0, "fp16 forced")
+    assert w4.w4a16_describe(M, K, N, 128) == heur
+    say("awq ignored plan", heur)
+    for dtype in (1, 0):
+        A, Bq, S, Z = make_inputs_awq(M, K, N, 128, seed=3, bf16=bool(dtype))
+        C = run_gemm_awq(A, Bq, S, Z, 128, dtype)
+        _, C64 = oracle.gemm_awq(A, Bq, S, Z, 128, dtype)
+        _check(C, C64, dtype, f"dtype {dtype} ignored plan")

@@ -48,11 +48,10 @@ def _check(C, C64, bias, act, what):
 
 # One variant of each kernel family, with and without split-K; M = 45 and
 # N = 208 leave ragged row and column tiles.
-FUSED_PLANS = ["1,2,4,1,2", "1,4,4,7,2",            # streaming kernel
-               "4,1,8,1,3,2", "8,2,8,2,3,2", "1,4,8,1,4,2",   # LDS kernel, 16 x 16
-               "4,1,8,1,3,3", "4,1,8,3,3,3"]        # LDS kernel, 32 x 32
-KERNEL_OF_TILE = {0: "gemm_kernel", 2: "gemm_lds_kernel",
-                  3: "gemm_lds_kernel"}
+FUSED_PLANS = ["1,2,8,1,2", "1,4,4,7,2", "1,4,4,3,4",                  # streaming kernel
+               "4,1,8,1,3,2", "8,2,8,2,3,2", "1,2,8,1,4,2", "4,2,4,3,3,2,0,2",  # LDS kernel
+               "2,4,8,0,3,4", "1,4,8,5,4,4"]                                  # stream-K kernel
+KERNEL_OF_TILE = {0: "gemm_kernel", 2: "gemm_lds_kernel", 4: "gemm_sk_kernel"}
 
 
 @pytest.mark.parametrize("plan", FUSED_PLANS)

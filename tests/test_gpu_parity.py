@@ -142,22 +142,15 @@ def test_gemm_matches_oracle(M, K, N, group):
     assert_gemm_close(C, C64, f"M={M} K={K} N={N} g={group}")
 
 
-STREAM_PLANS = ["1,1,4,1,2", "1,1,8,3,4", "1,2,4,2,2", "1,2,8,1,4", "1,4,4,7,2", "1,4,8,2,2",
-                "2,2,4,3,2", "2,4,4,1,2", "4,2,4,5,1", "4,4,4,1,1", "8,2,4,2,1", "8,4,4,1,1"]
-LDS_PLANS = ["4,2,2,1,3,2", "4,2,4,3,3,2", "4,2,4,1,4,2", "4,2,4,6,4,2", "4,4,4,2,3,2",
-             "8,1,4,3,3,2", "8,2,4,1,2,2", "8,2,4,5,3,2", "8,4,4,2,2,2", "8,4,4,1,3,2",
-             "4,1,8,2,3,2", "4,2,8,1,3,2", "8,1,8,3,3,2", "8,2,8,1,3,2",
-             "1,4,4,2,4,2", "1,8,4,1,4,2", "1,2,8,4,4,2", "1,4,8,1,4,2", "2,4,4,3,4,2",
-             "2,2,8,8,4,2", "2,4,8,1,3,2"]
-# LDS kernel with 32 x 32 matrix blocks (mb, nb count 32-row / 32-column blocks)
-LDS32_PLANS = ["4,1,8,1,3,3", "4,1,8,3,3,3", "2,1,8,3,3,3", "4,1,4,1,3,3", "2,2,4,5,3,3"]
-# LDS kernel with a grid of wave tiles: the eighth field is the number of
-# waves along M (mb, nb count each wave's row / column blocks)
-LDS_GRID_PLANS = ["4,4,4,1,3,2,0,2", "2,4,2,3,3,2,0,4", "4,2,4,1,3,2,0,2", "2,2,2,2,3,2,0,4",
-                  "2,2,4,5,3,2,0,2", "2,4,4,1,3,2,0,2", "4,4,2,2,3,2,0,2", "2,4,2,1,3,2,0,2",
-                  "1,2,2,1,3,3,0,4", "1,4,2,3,3,3,0,4", "2,2,4,1,3,3,0,2"]
-KERNEL_OF_TILE = {0: "gemm_kernel", 2: "gemm_lds_kernel",
-                  3: "gemm_lds_kernel"}
+# Every compiled variant, with and without K splits (fields: mb, nb, wk,
+# splits, depth[, tile, unused, wm]; tile 0 the streaming kernel, 2 the LDS
+# kernel, whose eighth field is the number of waves along M).
+STREAM_PLANS = ["1,1,4,1,2", "1,1,4,3,2", "1,1,8,1,2", "1,1,8,5,2", "1,2,8,1,2", "1,2,8,4,2",
+                "1,4,4,1,2", "1,4,4,7,2", "1,4,4,1,4", "1,4,4,2,4"]
+LDS_PLANS = ["1,2,8,1,4,2", "1,2,8,4,4,2", "2,2,8,1,4,2", "2,2,8,8,4,2", "4,1,8,1,3,2",
+             "4,1,8,2,3,2", "4,1,8,6,3,2", "8,2,8,1,3,2", "8,2,8,3,3,2"]
+LDS_GRID_PLANS = ["4,2,4,1,3,2,0,2", "4,2,4,5,3,2,0,2"]
+KERNEL_OF_TILE = {0: "gemm_kernel", 2: "gemm_lds_kernel"}
 
 
 def _forced_plan_case(monkeypatch, plan, group):
@@ -170,26 +163,26 @@ def _forced_plan_case(monkeypatch, plan, group):
     fields = [int(x) for x in plan.split(",")]
     kernel = KERNEL_OF_TILE[fields[5] if len(fields) > 5 else 0]
     assert desc.startswith(kernel + "<"), desc   # the forced variant is the one that runs
-    if len(fields) > 5 and fields[5] >= 2:
+    mb, nb, wk, splits, depth = fields[:5]
+    if len(fields) > 5 and fields[5] == 2:
         wm = fields[7] if len(fields) > 7 else 1
-        mb, nb, wk, splits, depth = fields[:5]
-        f = 32 if fields[5] == 3 else 16
-        assert desc.startswith(f"{kernel}<{mb},{nb},{wm},{wk},{depth},{f}>"), desc
-        assert f"splits={min(splits, K // 128)} " in desc, desc
+        assert desc.startswith(f"{kernel}<{mb},{nb},{wm},{wk},{depth}>"), desc
+    else:
+        assert desc.startswith(f"{kernel}<{mb},{nb},{wk},{depth}>"), desc
+    assert f"splits={min(splits, K // 128)} " in desc, desc
     say("forced plan", plan, "group", group, desc)
     C = run_gemm(A, Bq, S, group)
     assert_gemm_close(C, C64, f"plan {plan} group {group}")
 
 
-@pytest.mark.parametrize("plan", STREAM_PLANS + LDS_PLANS + LDS32_PLANS +
-                         LDS_GRID_PLANS)
+@pytest.mark.parametrize("plan", STREAM_PLANS + LDS_PLANS + LDS_GRID_PLANS)
 def test_gemm_forced_plans_agree(monkeypatch, plan):
     """Every compiled variant and split count gives the oracle's answer."""
     _forced_plan_case(monkeypatch, plan, 128)
 
 
-@pytest.mark.parametrize("plan", ["1,2,4,3,2", "4,2,4,3,3,2", "8,4,4,2,2,2",
-                                  "4,1,8,2,3,3", "2,4,2,2,3,2,0,4", "1,2,2,2,3,3,0,4"])
+@pytest.mark.parametrize("plan", ["1,2,8,3,2", "1,4,4,2,4", "2,2,8,3,4,2", "8,2,8,2,3,2",
+                                  "4,2,4,2,3,2,0,2"])
 def test_gemm_forced_plans_coarse_groups(monkeypatch, plan):
     """A scale group of four K blocks (512): each K block finds its group row."""
     _forced_plan_case(monkeypatch, plan, 512)

@@ -1,4 +1,4 @@
-"""The stream-K kernel (gemm_sk.hip) against the oracle: every compiled
+"""The stream-K kernel (gemm_sk.hpp) against the oracle: every compiled
 variant, grids that cut tiles between workgroups anywhere (so partial tiles
 go through the workspace and the last arriver adds them in K order), tile
 padding when the K blocks are not a multiple of the pipeline depth, ragged
@@ -17,9 +17,8 @@ from tests.tolerance import assert_epilogue_close, assert_gemm_close
 
 pytestmark = pytest.mark.gpu
 
-# compiled variants (16*mb rows per wave, pipeline depth ns, wm x wn waves)
-VARIANTS = [(8, 3, 1, 4), (4, 4, 1, 4), (2, 6, 1, 4), (1, 6, 1, 4), (4, 3, 2, 4), (2, 4, 2, 4),
-            (1, 6, 2, 4), (1, 4, 1, 8), (2, 3, 1, 8), (4, 3, 1, 8)]
+# compiled variants: 16*mb rows, pipeline depth ns, eight waves of 64 columns
+VARIANTS = [(1, 4), (2, 3), (4, 3)]
 
 
 @pytest.fixture(autouse=True)
@@ -29,49 +28,46 @@ def _no_forced_plan():
     w4.w4a16_set_forced_plan(None)
 
 
-def _plan(mb, ns, grid, wm=1, wn=4):
-    return f"{mb},4,{wn},{grid},{ns},4,0,{wm}"
+def _plan(mb, ns, grid):
+    return f"{mb},4,8,{grid},{ns},4"
 
 
-def _name(mb, ns, wm, wn=4):
-    return f"gemm_sk_kernel<{mb},4,{ns},{wm},{wn}>"
+def _name(mb, ns):
+    return f"gemm_sk_kernel<{mb},4,{ns},8>"
 
 
-@pytest.mark.parametrize("mb,ns,wm,wn", VARIANTS)
+@pytest.mark.parametrize("mb,ns", VARIANTS)
 @pytest.mark.parametrize("grid", [1, 3, 7, 0])
-def test_sk_forced_grids_agree(mb, ns, wm, wn, grid):
+def test_sk_forced_grids_agree(mb, ns, grid):
     """M = 45 and N = 208 leave ragged row and column tiles; K = 3584 is 28
     K blocks (padded to a multiple of ns where needed); grids of 3 and 7
     workgroups cut tiles in the middle."""
     M, K, N, g = 45, 3584, 208, 128
     A, Bq, S = make_inputs(M, K, N, g, seed=11)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm, wn))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, grid))
     desc = w4.w4a16_describe(M, K, N, g)
-    assert desc.startswith(_name(mb, ns, wm, wn)), desc
-    say("sk forced", mb, ns, wm, wn, grid, desc)
+    assert desc.startswith(_name(mb, ns)), desc
+    say("sk forced", mb, ns, grid, desc)
     C = run_gemm(A, Bq, S, g)
     _, C64 = oracle.gemm(A, Bq, S, g)
     assert_gemm_close(C, C64, desc)
 
 
-@pytest.mark.parametrize("M,K,N,mb,ns,wm,wn", [(200, 4096, 1024, 8, 3, 1, 4),
-                                               (64, 3840, 768, 2, 4, 2, 4),
-                                               (16, 2048, 4160, 1, 6, 1, 4),
-                                               (130, 1152, 2048, 4, 3, 2, 4),
-                                               (40, 2048, 4160, 2, 3, 1, 8),
-                                               (16, 1536, 1536, 1, 4, 1, 8)])
-def test_sk_default_and_split_grids(M, K, N, mb, ns, wm, wn):
+@pytest.mark.parametrize("M,K,N,mb,ns", [(16, 2048, 4160, 1, 4), (40, 2048, 4160, 2, 3),
+                                         (64, 3840, 768, 4, 3), (130, 1152, 2048, 4, 3),
+                                         (16, 1536, 1536, 1, 4)])
+def test_sk_default_and_split_grids(M, K, N, mb, ns):
     """Several column and row tiles; the default grid (one workgroup per
     compute unit, at least eight K blocks each) and a 5-workgroup grid whose
     runs end inside tiles."""
     A, Bq, S = make_inputs(M, K, N, 128, seed=M + N)
     _, C64 = oracle.gemm(A, Bq, S, 128)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, 0, wm, wn))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 0))
     desc = w4.w4a16_describe(M, K, N, 128)
-    assert desc.startswith(_name(mb, ns, wm, wn)), desc
+    assert desc.startswith(_name(mb, ns)), desc
     say("sk default grid", M, K, N, desc)
     assert_gemm_close(run_gemm(A, Bq, S, 128), C64, desc)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, 5, wm, wn))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 5))
     desc5 = w4.w4a16_describe(M, K, N, 128)
     assert "workspace=0" not in desc5, desc5
     say("sk grid 5", M, K, N, desc5)
@@ -83,7 +79,7 @@ def test_sk_group_k_and_coarse_groups():
     M, K, N = 72, 2560, 512
     for g in (K, 512):
         A, Bq, S = make_inputs(M, K, N, g, seed=g)
-        w4.w4a16_set_forced_plan(_plan(4, 4, 3))
+        w4.w4a16_set_forced_plan(_plan(4, 3, 3))
         desc = w4.w4a16_describe(M, K, N, g)
         say("sk group", g, desc)
         C = run_gemm(A, Bq, S, g)
@@ -101,11 +97,11 @@ def test_sk_one_hot_rows_are_exact():
     ks = np.random.default_rng(4).integers(0, K, size=M)
     A[np.arange(M), ks] = 1.0
     W = oracle.dequant(Bq, S, g)
-    for mb, ns, wm, wn in VARIANTS:
-        w4.w4a16_set_forced_plan(_plan(mb, ns, 4, wm, wn))
-        say("sk one-hot", mb, ns, wm, wn)
+    for mb, ns in VARIANTS:
+        w4.w4a16_set_forced_plan(_plan(mb, ns, 4))
+        say("sk one-hot", mb, ns)
         C = run_gemm(A, Bq, S, g)
-        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, ns, wm, wn)
+        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, ns)
 
 
 def test_sk_deterministic_and_counters_reset():
@@ -114,7 +110,7 @@ def test_sk_deterministic_and_counters_reset():
     import torch
     M, K, N, g = 96, 4096, 2048, 128
     A, Bq, S = make_inputs(M, K, N, g, seed=5)
-    w4.w4a16_set_forced_plan(_plan(4, 4, 7))
+    w4.w4a16_set_forced_plan(_plan(4, 3, 7))
     desc = w4.w4a16_describe(M, K, N, g)
     need = w4.w4a16_workspace_bytes(M, K, N, g)
     assert need > 65536, desc
@@ -138,9 +134,8 @@ def test_sk_fused_epilogue(act):
     A, Bq, S = make_inputs(M, K, N, g, seed=9)
     bias = make_bias(N, seed=10)
     _, Y64, Z64 = oracle.gemm_fused(A, Bq, S, g, bias, act)
-    for grid, (mb, ns, wm, wn) in ((1, (4, 4, 1, 4)), (5, (4, 4, 1, 4)), (5, (2, 4, 2, 4)),
-                                   (5, (2, 3, 1, 8))):
-        w4.w4a16_set_forced_plan(_plan(mb, ns, grid, wm, wn))
+    for grid, (mb, ns) in ((1, (2, 3)), (5, (2, 3)), (5, (1, 4)), (7, (4, 3))):
+        w4.w4a16_set_forced_plan(_plan(mb, ns, grid))
         desc = w4.w4a16_describe(M, K, N, g)
         say("sk fused", act, desc)
         C = run_gemm_fused(A, Bq, S, g, bias, act)

@@ -100,13 +100,13 @@ SP_CASES = [
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,2>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),
-    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4,16>"),
-    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4,16>"),
-    (45, 1024, 208, "gemm_lds_kernel<4,2,1,4,3,16>"),
-    (128, 1024, 1024, "gemm_lds_kernel<4,2,1,4,3,16>"),
-    (128, 512, 36864, "gemm_lds_kernel<4,2,1,4,3,16>"),
-    (128, 256, 65536, "gemm_lds_kernel<4,2,1,4,3,16>"),
-    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3,16>"),
+    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4>"),
+    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4>"),
+    (45, 1024, 208, "gemm_lds_kernel<4,2,1,4,3>"),
+    (128, 1024, 1024, "gemm_lds_kernel<4,2,1,4,3>"),
+    (128, 512, 36864, "gemm_lds_kernel<4,2,1,4,3>"),
+    (128, 256, 65536, "gemm_lds_kernel<4,2,1,4,3>"),
+    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3>"),
 ]
 
 
@@ -126,13 +126,10 @@ def test_gemm_sp24_matches_oracle(M, K, N, kernel):
     assert_gemm_close(C if cols is None else C[:, cols], C64, f"M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("plan", ["1,1,8,3,2", "1,2,8,4,2", "1,4,8,2,2", "1,1,4,5,2",
-                                  "1,4,4,3,4", "1,4,4,2,2", "2,2,4,3,2", "2,4,4,2,2",
-                                  "4,2,4,3,1", "4,4,4,2,1", "8,2,4,4,1",
-                                  "1,2,8,4,4,2", "2,2,8,2,4,2", "4,1,8,3,3,2",
-                                  "4,2,4,2,3,2,0,2", "8,2,8,2,3,2", "4,2,4,2,3,2",
-                                  "4,2,8,3,3,2", "8,1,8,2,3,2", "2,2,4,4,3,2,0,2",
-                                  "2,4,4,2,4,2", "8,4,4,2,3,2"])
+# every 2:4 variant the library compiles, each with a K split
+@pytest.mark.parametrize("plan", ["1,1,8,3,2", "1,2,8,4,2", "1,1,4,5,2", "1,4,4,2,2",
+                                  "1,2,8,4,4,2", "2,2,8,2,4,2", "8,2,8,2,3,2", "4,2,4,2,3,2",
+                                  "4,2,4,3,3,2"])
 def test_gemm_sp24_forced_plans_split_k(monkeypatch, plan):
     M, K, N, group = 45, 3584, 208, 512
     A, Bq, S = make_inputs(M, K, N, group, seed=5)
@@ -141,7 +138,7 @@ def test_gemm_sp24_forced_plans_split_k(monkeypatch, plan):
     desc = w4.w4a16_sparse24_describe(M, K, N, group)
     f = [int(x) for x in plan.split(",")] + [0, 0, 0]
     mb, nb, wk, depth, tile, wm = f[0], f[1], f[2], f[4], f[5], f[7] or 1
-    want = (f"gemm_lds_kernel<{mb},{nb},{wm},{wk},{depth},16>" if tile == 2
+    want = (f"gemm_lds_kernel<{mb},{nb},{wm},{wk},{depth}>" if tile == 2
             else f"gemm_kernel<{mb},{nb},{wk},{depth}>")
     assert desc.startswith(want), desc
     assert "splits=1 " not in desc, desc

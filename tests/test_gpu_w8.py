@@ -86,13 +86,13 @@ W8_CASES = [
     (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,4>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),
-    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4,16>"),
-    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4,16>"),
-    (45, 1024, 208, "gemm_lds_kernel<4,1,1,8,3,16>"),
-    (128, 1024, 1024, "gemm_lds_kernel<4,1,1,8,3,16>"),
-    (128, 512, 36864, "gemm_lds_kernel<4,2,2,4,3,16>"),
-    (128, 256, 65536, "gemm_lds_kernel<8,2,1,8,3,16>"),
-    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3,16>"),
+    (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4>"),
+    (32, 1024, 4096, "gemm_lds_kernel<2,2,1,8,4>"),
+    (45, 1024, 208, "gemm_lds_kernel<4,1,1,8,3>"),
+    (128, 1024, 1024, "gemm_lds_kernel<4,1,1,8,3>"),
+    (128, 512, 36864, "gemm_lds_kernel<4,2,2,4,3>"),
+    (128, 256, 65536, "gemm_lds_kernel<8,2,1,8,3>"),
+    (300, 512, 512, "gemm_lds_kernel<8,2,1,8,3>"),
 ]
 
 

@@ -1,13 +1,19 @@
 """The plan heuristic on the CPU (w4a16_plan_describe takes the compute-unit
 count as an argument, so no device is needed): which kernel each batch and
-layer size gets."""
+layer size gets, and that every compiled kernel instantiation is one some
+plan picks (none is dead weight in the library)."""
 
 from __future__ import annotations
+
+import os
+import re
 
 import pytest
 
 import weight_only_int4_gemm_amd as w4
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "weight_only_int4_gemm_amd", "csrc")
 CUS = 256  # MI355X
 
 F16, F16ZP, BF16, BF16ZP, W8, SP24 = range(6)
@@ -19,8 +25,8 @@ def plan(M, K, N, fmt=F16, group=128):
 
 def test_stream_k_takes_9_to_64_rows_on_large_layers():
     K, N = 18432, 73728
-    for M, name in ((9, "1,4,4,1,8"), (16, "1,4,4,1,8"), (17, "2,4,3,1,8"), (32, "2,4,3,1,8"),
-                    (33, "4,4,3,1,8"), (64, "4,4,3,1,8")):
+    for M, name in ((9, "1,4,4,8"), (16, "1,4,4,8"), (17, "2,4,3,8"), (32, "2,4,3,8"),
+                    (33, "4,4,3,8"), (64, "4,4,3,8")):
         for fmt in (F16, F16ZP, BF16, BF16ZP):
             assert plan(M, K, N, fmt).startswith(f"gemm_sk_kernel<{name}>"), (M, fmt)
         assert not plan(M, K, N, W8).startswith("gemm_sk_kernel<"), M
@@ -40,3 +46,69 @@ def test_plan_describe_checks_its_arguments():
         w4.w4a16_plan_describe(16, 4096, 4096, 128, F16, 0)    # no compute units
     with pytest.raises(w4.W4A16Error):
         w4.w4a16_plan_describe(16, 4000, 4096, 128, F16, CUS)  # K not a multiple of 128
+
+
+def _macro_tuples(path, name):
+    """The X(...) argument tuples of a variant-list macro (following one
+    level of macros it includes)."""
+    src = open(path).read()
+    m = re.search(r"#define " + name + r"\(X\)(.*?)(?:\n\n|\n(?=[^ \\]))", src, re.S)
+    assert m, name
+    body = m.group(1)
+    out = [tuple(int(x) for x in t.split(",")) for t in re.findall(r"X\(([\d, ]+)\)", body)]
+    for inner in re.findall(r"(W4A16_\w+_VARIANTS)\(X\)", body):
+        out += _macro_tuples(path, inner)
+    return out
+
+
+def compiled_variants():
+    """{(kernel, format): [template tuple as w4a16_describe prints it]}."""
+    g, l, k = (os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_lds.hip", "gemm_sk.hpp"))
+    out = {}
+    for fmt in (F16, F16ZP, BF16, BF16ZP, W8):
+        for t in _macro_tuples(g, "W4A16_VARIANTS"):
+            out.setdefault(("gemm_kernel", fmt), set()).add(t)
+    for t in _macro_tuples(g, "W4A16_SP_VARIANTS"):
+        out.setdefault(("gemm_kernel", SP24), set()).add(t)
+    for fmt in (F16, F16ZP, BF16, BF16ZP, W8):
+        for t in _macro_tuples(l, "W4A16_LDS_VARIANTS"):
+            out.setdefault(("gemm_lds_kernel", fmt), set()).add(t)
+    for t in _macro_tuples(l, "W4A16_LDS_SP_VARIANTS"):
+        out.setdefault(("gemm_lds_kernel", SP24), set()).add(t)
+    for fmt in (F16, F16ZP, BF16, BF16ZP):
+        for t in _macro_tuples(k, "W4A16_SK_VARIANTS"):
+            # printed as <mb,nb,depth,wn>, the macro's own order
+            out.setdefault(("gemm_sk_kernel", fmt), set()).add(t)
+    return out
+
+
+MS = [1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128, 129, 192, 256, 512,
+      1024, 2048, 4096]
+KS = [128, 256, 512, 1024, 2048, 3584, 4096, 8192, 11008, 13824, 18432, 28672]
+NS = [16, 64, 208, 512, 1024, 2048, 4096, 5120, 8192, 12288, 14336, 22016, 28672, 36864,
+      65536, 73728]
+
+
+def reachable_variants():
+    seen = {}
+    for fmt in range(6):
+        for M in MS:
+            for K in KS:
+                for N in NS:
+                    for group in ((128, K) if fmt != SP24 else (128,)):
+                        d = plan(M, K, N, fmt, group)
+                        name, args = re.match(r"(\w+)<([\d,]+)>", d).groups()
+                        seen.setdefault((name, fmt), set()).add(
+                            tuple(int(x) for x in args.split(",")))
+    return seen
+
+
+def test_every_compiled_variant_is_one_a_plan_picks():
+    compiled = compiled_variants()
+    seen = reachable_variants()
+    dead = {key: sorted(v - seen.get(key, set())) for key, v in compiled.items()}
+    dead = {k: v for k, v in dead.items() if v}
+    assert not dead, f"compiled but never planned: {dead}"
+    missing = {key: sorted(v - compiled.get(key, set())) for key, v in seen.items()}
+    missing = {k: v for k, v in missing.items() if v}
+    assert not missing, f"planned but not compiled: {missing}"

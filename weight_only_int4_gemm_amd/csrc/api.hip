@@ -70,8 +70,7 @@ bool variant_is_compiled(const Plan& q, int fmt) {
     if (q.tile == 2) return lds_sp_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth);
     return q.tile == 0 && q.wm == 1 && sp_is_compiled(q.mb, q.nb, q.wk, q.depth);
   }
-  if (q.tile >= 2)
-    return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth, q.tile == 3 ? 32 : 16);
+  if (q.tile == 2) return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth);
   if (q.wm != 1 || q.tile != 0) return false;
   return plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
 }
@@ -81,10 +80,9 @@ bool variant_is_compiled(const Plan& q, int fmt) {
 // library first plans a call, and replaced by w4a16_set_forced_plan.  The
 // text is "mb,nb,wk,splits[,depth[,tile[,unused[,wm]]]]": a field <= 0 keeps
 // the heuristic's value; tile is 0 (the default) for the streaming kernel,
-// 2 for the LDS kernel with 16 x 16 blocks, 3 for the LDS kernel with
-// 32 x 32 blocks, 4 for the stream-K kernel (splits = its grid), and -1
-// for the plan the heuristic makes when it does not pick the stream-K
-// kernel (the other fields are then ignored).  The override feeds the same kernels, and
+// 2 for the LDS kernel, 4 for the stream-K kernel (wk = its waves along N,
+// splits = its grid), and -1 for the plan the heuristic makes when it does
+// not pick the stream-K kernel (the other fields are then ignored).  The override feeds the same kernels, and
 // w4a16_workspace_bytes sees it as well, so sizes agree as long as it is
 // not changed between the two calls.
 struct ForcedPlan {
@@ -103,7 +101,7 @@ bool parse_forced_plan(const char* text, ForcedPlan* out) {
   if (std::sscanf(text, "%d,%d,%d,%d,%d,%d,%d,%d", &mb, &nb, &wk, &splits, &depth, &tile,
                   &unused, &wm) < 4)
     return false;
-  if (tile != -1 && tile != 0 && tile != 2 && tile != 3 && tile != 4) return false;
+  if (tile != -1 && tile != 0 && tile != 2 && tile != 4) return false;
   *out = ForcedPlan{true, mb, nb, wk, splits, depth, tile, wm};
   return true;
 }
@@ -171,16 +169,16 @@ int describe_plan(int M, int K, int N, int group, int fmt, int cus, char* buf, s
   const Plan p = make_plan(M, K, N, group, cus, fmt);
   if (p.tile == 4)
     std::snprintf(buf, len,
-                  "gemm_sk_kernel<%d,%d,%d,%d,%d> grid=%dx1x1 block=%d tiles=%dx%d splits=%d "
+                  "gemm_sk_kernel<%d,%d,%d,%d> grid=%dx1x1 block=%d tiles=%dx%d splits=%d "
                   "workspace=%zu",
-                  p.mb, p.nb, p.depth, p.wm, p.wk, p.splits, 64 * p.wk * p.wm, p.tiles_n,
+                  p.mb, p.nb, p.depth, p.wk, p.splits, 64 * p.wk, p.tiles_n,
                   p.tiles_m,
                   p.splits, p.workspace_bytes);
-  else if (p.tile >= 2)
+  else if (p.tile == 2)
     std::snprintf(buf, len,
-                  "gemm_lds_kernel<%d,%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
+                  "gemm_lds_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
                   "workspace=%zu",
-                  p.mb, p.nb, p.wm, p.wk, p.depth, p.tile == 3 ? 32 : 16, p.tiles_n, p.tiles_m,
+                  p.mb, p.nb, p.wm, p.wk, p.depth, p.tiles_n, p.tiles_m,
                   p.splits, 64 * p.wm * p.wk, p.splits, p.workspace_bytes);
   else
     std::snprintf(buf, len,
@@ -336,9 +334,8 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     p.depth = 3;
   }
   auto shape = [&](Plan& q) {
-    const int f = q.tile == 3 ? 32 : 16;
-    q.tm = f * q.mb * q.wm;
-    q.tn = f * q.nb * (q.tile ? q.wk : 1);  // LDS and stream-K kernels split N over waves
+    q.tm = 16 * q.mb * q.wm;
+    q.tn = 16 * q.nb * (q.tile ? q.wk : 1);  // LDS and stream-K kernels split N over waves
     q.tiles_n = (N + q.tn - 1) / q.tn;
     q.tiles_m = (M + q.tm - 1) / q.tm;
   };

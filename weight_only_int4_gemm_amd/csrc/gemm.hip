@@ -426,23 +426,13 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
   return hipGetLastError();
 }
 
-// Compiled variants (MB, NB, WK, D).
-#define W4A16_VARIANTS(X)                                                        \
-  X(1, 1, 4, 2) X(1, 1, 4, 4) X(1, 1, 8, 2) X(1, 1, 8, 4) X(1, 1, 16, 2)         \
-  X(1, 1, 16, 4) X(1, 2, 4, 2) X(1, 2, 4, 4) X(1, 2, 8, 2) X(1, 2, 8, 4)         \
-  X(1, 2, 16, 2) X(1, 4, 4, 2) X(1, 4, 4, 4) X(1, 4, 8, 2) X(1, 4, 16, 2)        \
-  X(2, 2, 4, 2) X(2, 2, 8, 2) X(2, 4, 4, 2) X(2, 4, 8, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) \
-  X(8, 2, 4, 1) X(8, 4, 4, 1)
+// Compiled variants (MB, NB, WK, D): the plans' ones, for the formats 0 to
+// 4 (FP16 and BF16 with or without zero points, 8-bit codes).
+#define W4A16_VARIANTS(X) X(1, 1, 4, 2) X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 4, 2) X(1, 4, 4, 4)
 
-// Variants compiled for the other formats too: the ones the plans pick.
-#define W4A16_FMT_VARIANTS(X) \
-  X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 8, 2) X(1, 1, 4, 2) X(1, 4, 4, 4) X(1, 4, 4, 2)
-
-// Variants compiled for 2:4-sparse weights: the plans' small-batch ones and
-// wider row tiles for larger batches.
-#define W4A16_SP_VARIANTS(X)                                                  \
-  X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 8, 2) X(1, 1, 4, 2) X(1, 4, 4, 4) X(1, 4, 4, 2) \
-  X(2, 2, 4, 2) X(2, 4, 4, 2) X(4, 2, 4, 1) X(4, 4, 4, 1) X(8, 2, 4, 1)
+// Variants compiled for 2:4-sparse weights (the plans keep two K blocks in
+// flight).
+#define W4A16_SP_VARIANTS(X) X(1, 1, 4, 2) X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 4, 2)
 
 bool sp_is_compiled(int mb, int nb, int wk, int depth) {
 #define W4A16_SMATCH(MB_, NB_, WK_, D_) \
@@ -470,20 +460,14 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
   const uint64_t gmagic = (((uint64_t)1 << 32) + gb - 1) / gb;
   if (p.tile == 4)
     return launch_sk(p, A, Bp, S, C, M, K, N, gmagic, ep, wf, workspace, stream);
-  if (p.tile >= 2)
+  if (p.tile == 2)
     return launch_lds(p, A, Bp, S, C, M, K, N, gmagic, ep, wf, workspace, stream);
   if (p.tile) return hipErrorInvalidValue;
-  if (wf.fmt == kFmtF16) {
-#define W4A16_CASE(MB_, NB_, WK_, D_)                                               \
-  if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                   \
-    return launch_one<MB_, NB_, WK_, D_, kFmtF16>(p, A, Bp, S, C, M, K, N, gmagic, ep, \
-                                                  nullptr, workspace, stream);
-    W4A16_VARIANTS(W4A16_CASE)
-#undef W4A16_CASE
-    return hipErrorInvalidValue;
-  }
-#define W4A16_FCASE(MB_, NB_, WK_, D_)                                                    \
+#define W4A16_CASE(MB_, NB_, WK_, D_)                                                     \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_) {                       \
+    if (wf.fmt == kFmtF16)                                                                \
+      return launch_one<MB_, NB_, WK_, D_, kFmtF16>(p, A, Bp, S, C, M, K, N, gmagic, ep,   \
+                                                    nullptr, workspace, stream);          \
     if (wf.fmt == kFmtF16Zp)                                                              \
       return launch_one<MB_, NB_, WK_, D_, kFmtF16Zp>(p, A, Bp, S, C, M, K, N, gmagic, ep, \
                                                       wf.zeros, workspace, stream);       \
@@ -497,8 +481,10 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
       return launch_one<MB_, NB_, WK_, D_, kFmtW8>(p, A, Bp, S, C, M, K, N, gmagic, ep,    \
                                                    nullptr, workspace, stream);           \
   }
-  W4A16_FMT_VARIANTS(W4A16_FCASE)
-#undef W4A16_FCASE
+  if (wf.fmt != kFmtSp24) {
+    W4A16_VARIANTS(W4A16_CASE)
+  }
+#undef W4A16_CASE
   if (wf.fmt == kFmtSp24) {
 #define W4A16_SCASE(MB_, NB_, WK_, D_)                                                      \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                           \

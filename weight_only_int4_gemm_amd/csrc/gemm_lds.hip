@@ -49,33 +49,27 @@
 
 namespace w4a16 {
 
-// F is the edge of the matrix instruction's output block: 16 for
-// v_mfma_f32_16x16x32_f16, 32 for v_mfma_f32_32x32x16_f16 (MB and NB count
-// F-row and F-column blocks).  The 32 x 32 form does twice the work per
-// instruction at the same operand size and issues at the full rate, where
-// the 16 x 16 form sustains about 80% of it; it reads the same packed layout
-// (the lane-to-word map below).
+// MB and NB count the 16-row and 16-column blocks of a wave's tile (the
+// output block of v_mfma_f32_16x16x32_f16).
 //
-// FMT is the weight format (format.hpp): formats other than 0 (zero points,
-// BF16) use the 16 x 16 blocks and no fused epilogue; their zero points are
-// one more part of each stage, loaded like the scales.
-template <int MB, int NB, int WM, int WN, int NS, int F, bool EPI, int FMT>
+// FMT is the weight format (format.hpp): formats other than 0 have no fused
+// epilogue; their zero points are one more part of each stage, loaded like
+// the scales.
+template <int MB, int NB, int WM, int WN, int NS, bool EPI, int FMT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
     uint64_t group_magic, int splits, unsigned* __restrict__ counters,
     float* __restrict__ partials, Epilogue ep, const uint8_t* __restrict__ Z) {
-  static_assert(F == 16 || F == 32, "16 x 16 or 32 x 32 blocks");
-  static_assert(FMT == kFmtF16 || (F == 16 && !EPI), "formats 1-5: 16 x 16 blocks, no epilogue");
+  static_assert(FMT == kFmtF16 || !EPI, "formats 1-5: no fused epilogue");
   constexpr bool ZP = Format<FMT>::kZp;
   constexpr bool SP = Format<FMT>::kSp;
   constexpr int BLOCK_PIECES = SP ? 48 : 64;     // 16-byte pieces of one code block
   constexpr int PPB = Format<FMT>::kW8 ? 2 : 1;  // 1 KiB pieces per code block and K block
   constexpr int WAVES = WM * WN;
-  constexpr int TM = F * MB * WM;
-  constexpr int TN = F * NB * WN;
-  constexpr int NB16 = NB * F / 16;            // 16-column code blocks per wave
-  constexpr int BLOCKS = NB16 * WN;            // 16-column code blocks of the tile
+  constexpr int TM = 16 * MB * WM;
+  constexpr int TN = 16 * NB * WN;
+  constexpr int BLOCKS = NB * WN;              // 16-column code blocks of the tile
   constexpr int APIECES = TM * 16;             // 16-byte pieces of activations
   constexpr int ACHUNKS = APIECES / 64;        // 1 KiB wave-loads of activations
   // direct loads per wave of activation chunks and of code blocks; with
@@ -123,9 +117,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   const int row0 = tile_m * TM;
   const int col0 = tile_n * TN;
   const int n16_last = N / kBlockN - 1;
-  const int wrow0 = row0 + wm * F * MB;  // this wave's tile
-  const int wcol0 = col0 + wn * F * NB;
-  typename std::conditional<F == 16, LaneBias4<NB, EPI>, LaneBias<NB, F, EPI>>::type bias;
+  const int wrow0 = row0 + wm * 16 * MB;  // this wave's tile
+  const int wcol0 = col0 + wn * 16 * NB;
+  LaneBias4<NB, EPI> bias;
   bias.load(ep, wcol0, N);
 
   // Code pieces this wave loads: piece (wave + WAVES * i) % (BLOCKS * PPB)
@@ -202,14 +196,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     }
   };
 
-  typedef typename std::conditional<F == 16, float4_t, float16_t>::type acc_t;
-  acc_t acc[MB][NB];
+  float4_t acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < F * F / 64; ++i) acc[mb][nb][i] = 0.f;  // F*F/64 values per lane
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   // ---- 16 x 16 blocks: four 32-deep slices per K block -------------------
   // Lane l takes activation row l % 16, in-features 8(l/16) .. +7 of the
@@ -271,74 +262,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          if constexpr (F == 16) acc[mb][nb] = mma16<FMT>(bcur[nb], cur[mb], acc[mb][nb]);
+          acc[mb][nb] = mma16<FMT>(bcur[nb], cur[mb], acc[mb][nb]);
         }
     }
   };
 
-  // ---- 32 x 32 blocks: eight 16-deep slices per K block ------------------
-  // Lane l takes activation row l % 32, in-features 8(l/32) .. +7 of the
-  // slice, and for column c = l % 32 the eight codes of those in-features.
-  // In the packed layout (16-column blocks, lane l' holding column l' % 16
-  // and in-features 32j + 8(l'/16) .. +7 in its word j) these are word s/2
-  // of lane (l % 16) + 16 (2 (s % 2) + l / 32) of block c / 16: even slices
-  // take the four words of one lane, odd slices of another.
-  auto read_a32 = [&](const Stage& sg, int s, half8_t* a) {
-    const int r32 = lane & 31;
-    const int piece = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = (wm * MB + mb) * 32 + r32;
-      a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + (piece ^ (r & 15))]);
-    }
-  };
-  auto compute32 = [&](const Stage& sg) {
-    uint4 we[NB], wo[NB];  // words of the even and of the odd slices
-    half2_t s2[NB];
-    const _Float16* sh = reinterpret_cast<const _Float16*>(sg.s);
-    const int c32 = lane & 31;
-    const int le = l16 + 16 * (lane >> 5);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int blk = 64 * (wn * NB16 + 2 * nb + (c32 >> 4));
-      we[nb] = sg.b[blk + le];
-      wo[nb] = sg.b[blk + le + 32];
-      const _Float16 sc = sh[wn * 32 * NB + nb * 32 + c32];
-      s2[nb] = half2_t{sc, sc};
-    }
-    auto unpack_slice = [&](int s, half8_t* bf) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint4& w = (s & 1) ? wo[nb] : we[nb];
-        const int j = s >> 1;
-        const uint32_t word = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
-        bf[nb] = unpack_scale(word, s2[nb]);
-      }
-    };
-    half8_t a0[MB], a1[MB];
-    half8_t b0[NB], b1[NB];
-    read_a32(sg, 0, a0);
-    unpack_slice(0, b0);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t* cur = (s & 1) ? a1 : a0;
-      half8_t* nxt = (s & 1) ? a0 : a1;
-      half8_t* bcur = (s & 1) ? b1 : b0;
-      half8_t* bnxt = (s & 1) ? b0 : b1;
-      if (s < 7) {
-        read_a32(sg, s + 1, nxt);
-        unpack_slice(s + 1, bnxt);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if constexpr (F == 32)
-            acc[mb][nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[mb], bcur[nb], acc[mb][nb], 0, 0, 0);
-        }
-    }
-  };
   // ---- 2:4-sparse codes: two 64-deep sparse steps per K block ------------
   // Step t multiplies the weights' compressed code word t (transposed: rows
   // are output columns) by the activation fragments of 32-deep slices 2t
@@ -372,23 +300,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (F == 16) acc[mb][nb] = smma16(b0[nb], a0[mb], a1[mb], pos[nb], acc[mb][nb]);
+        acc[mb][nb] = smma16(b0[nb], a0[mb], a1[mb], pos[nb], acc[mb][nb]);
       }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (F == 16)
-          acc[mb][nb] = smma16(b1[nb], a2[mb], a3[mb], pos[nb] >> 16, acc[mb][nb]);
+        acc[mb][nb] = smma16(b1[nb], a2[mb], a3[mb], pos[nb] >> 16, acc[mb][nb]);
       }
   };
   auto compute = [&](const Stage& sg) {
     if constexpr (SP)
       compute_sp(sg);
-    else if constexpr (F == 16)
-      compute16(sg);
     else
-      compute32(sg);
+      compute16(sg);
   };
 
   // The pipeline: step t consumes stage t % NS; before it, once every wave
@@ -408,7 +333,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // from four waves stalls each wave for hundreds of cycles).  So the
   // step's loads are spread between its matrix instructions: one load
   // after every MFMA_PER_LOAD of them.
-  constexpr int NMFMA = (SP ? 2 : F == 16 ? 4 : 8) * MB * NB;
+  constexpr int NMFMA = (SP ? 2 : 4) * MB * NB;
   constexpr int MFMA_PER_LOAD = NMFMA / (LOADS + 1) > 0 ? NMFMA / (LOADS + 1) : 1;
   auto step = [&](int u, int kb) {  // u = t % NS
     stage_barrier<(NS - 2) * LOADS>();
@@ -433,17 +358,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  if constexpr (F == 16)
-    store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, splits,
-                                               counters, partials,
-                                               reinterpret_cast<int*>(&st0.s[0]), ep, bias);
-  else
-    store_output_tile32<MB, NB, WAVES, EPI>(acc, C, M, N, wrow0, wcol0, split, splits,
-                                            counters, partials, reinterpret_cast<int*>(&st0.s[0]),
-                                            ep, bias);
+  store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, splits, counters,
+                                             partials, reinterpret_cast<int*>(&st0.s[0]), ep,
+                                             bias);
 }
 
-template <int MB, int NB, int WM, int WN, int NS, int F, int FMT>
+template <int MB, int NB, int WM, int WN, int NS, int FMT>
 static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                                  const uint16_t* S, uint16_t* C, int M, int K, int N,
                                  uint64_t gmagic, Epilogue ep, const uint8_t* Z, void* workspace,
@@ -460,7 +380,7 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
   auto c = reinterpret_cast<_Float16*>(C);
   if constexpr (FMT == kFmtF16) {
     if (epilogue_needed(ep)) {
-      hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, true, FMT>), grid, block, 0,
+      hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, true, FMT>), grid, block, 0,
                          stream, a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep,
                          Z);
       return hipGetLastError();
@@ -468,43 +388,30 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
   } else {
     if (epilogue_needed(ep)) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, F, false, FMT>), grid, block, 0,
-                     stream, a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
+  hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, false, FMT>), grid, block, 0, stream,
+                     a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
   return hipGetLastError();
 }
 
-// Compiled variants (MB, NB, WM, WN, NS, F).  WM = 1: every wave spans the
-// tile's rows; WM > 1: a grid of WM x WN wave tiles.
-#define W4A16_LDS_VARIANTS(X)                                                              \
-  X(4, 2, 1, 2, 3, 16) X(4, 2, 1, 4, 3, 16) X(4, 2, 1, 4, 4, 16) X(4, 4, 1, 4, 3, 16)       \
-  X(8, 1, 1, 4, 3, 16) X(8, 2, 1, 4, 2, 16) X(8, 2, 1, 4, 3, 16) X(8, 4, 1, 4, 2, 16)       \
-  X(8, 4, 1, 4, 3, 16) X(4, 1, 1, 8, 3, 16) X(4, 2, 1, 8, 3, 16) X(8, 1, 1, 8, 3, 16)       \
-  X(8, 2, 1, 8, 3, 16) X(1, 4, 1, 4, 4, 16) X(1, 8, 1, 4, 4, 16) X(1, 2, 1, 8, 4, 16)       \
-  X(1, 4, 1, 8, 4, 16) X(2, 4, 1, 4, 4, 16) X(2, 2, 1, 8, 4, 16) X(2, 4, 1, 8, 3, 16)       \
-  X(4, 1, 1, 8, 3, 32) X(2, 1, 1, 8, 3, 32) X(4, 1, 1, 4, 3, 32) X(2, 2, 1, 4, 3, 32)       \
-  X(4, 4, 2, 4, 3, 16) X(2, 4, 4, 2, 3, 16) X(4, 2, 2, 4, 3, 16) X(2, 2, 4, 2, 3, 16)       \
-  X(2, 2, 2, 4, 3, 16) X(2, 4, 2, 4, 3, 16) X(4, 4, 2, 2, 3, 16) X(2, 4, 2, 2, 3, 16)       \
-  X(1, 2, 4, 2, 3, 32) X(1, 4, 4, 2, 3, 32) X(2, 2, 2, 4, 3, 32) X(4, 4, 1, 8, 3, 16)
-
-// Variants compiled for the other formats too (16 x 16 blocks): the ones
-// the plans pick.
-#define W4A16_LDS_FMT_VARIANTS(X)                                                     \
+// Compiled variants (MB, NB, WM, WN, NS): the plans' tiles, for the formats
+// 0 to 4 (FP16 and BF16 with or without zero points, 8-bit codes).  WM = 1:
+// every wave spans the tile's rows; WM > 1: a grid of WM x WN wave tiles.
+#define W4A16_LDS_VARIANTS(X) \
   X(1, 2, 1, 8, 4) X(2, 2, 1, 8, 4) X(4, 1, 1, 8, 3) X(8, 2, 1, 8, 3) X(4, 2, 2, 4, 3)
 
-bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f) {
-#define W4A16_LMATCH(MB_, NB_, WM_, WN_, NS_, F_) \
-  if (mb == MB_ && nb == NB_ && wm == WM_ && wn == WN_ && ns == NS_ && f == F_) return true;
+bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns) {
+#define W4A16_LMATCH(MB_, NB_, WM_, WN_, NS_) \
+  if (mb == MB_ && nb == NB_ && wm == WM_ && wn == WN_ && ns == NS_) return true;
   W4A16_LDS_VARIANTS(W4A16_LMATCH)
 #undef W4A16_LMATCH
   return false;
 }
 
-// Variants compiled for 2:4-sparse codes: the plans' ones and wider wave
-// tiles (with half the matrix instructions per activation fragment, wider
-// column blocks per wave keep more of them in flight).
-#define W4A16_LDS_SP_VARIANTS(X)                                                       \
-  W4A16_LDS_FMT_VARIANTS(X) X(4, 2, 1, 4, 3) X(4, 2, 1, 8, 3) X(8, 1, 1, 8, 3)          \
-  X(2, 2, 2, 4, 3) X(2, 4, 1, 4, 4) X(8, 4, 1, 4, 3)
+// Variants compiled for 2:4-sparse codes: the plans' tiles (with half the
+// matrix instructions per activation fragment, 32 < M <= 128 takes four
+// waves of 64 x 32 rather than eight of 64 x 16).
+#define W4A16_LDS_SP_VARIANTS(X) \
+  X(1, 2, 1, 8, 4) X(2, 2, 1, 8, 4) X(8, 2, 1, 8, 3) X(4, 2, 1, 4, 3)
 
 bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns) {
 #define W4A16_LSMATCH(MB_, NB_, WM_, WN_, NS_) \
@@ -527,46 +434,35 @@ constexpr int w8_stages(int mb, int nb, int wm, int wn, int ns) {
 hipError_t launch_lds(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                       const uint16_t* S, uint16_t* C, int M, int K, int N, uint64_t gmagic,
                       Epilogue ep, WeightFormat wf, void* workspace, hipStream_t stream) {
-  const int f = p.tile == 3 ? 32 : 16;
-  if (wf.fmt == kFmtF16) {
-#define W4A16_LCASE(MB_, NB_, WM_, WN_, NS_, F_)                                             \
-  if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_ && f == F_) \
-    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, F_, kFmtF16>(p, A, Bp, S, C, M, K, N,      \
-                                                                gmagic, ep, nullptr,         \
-                                                                workspace, stream);
-    W4A16_LDS_VARIANTS(W4A16_LCASE)
-#undef W4A16_LCASE
-    return hipErrorInvalidValue;
-  }
-  if (f != 16) return hipErrorInvalidValue;
   if (wf.fmt == kFmtSp24) {
-#define W4A16_LSCASE(MB_, NB_, WM_, WN_, NS_)                                                 \
-  if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_)             \
-    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtSp24>(p, A, Bp, S, C, M, K, N,     \
-                                                                 gmagic, ep, nullptr,         \
-                                                                 workspace, stream);
+#define W4A16_LSCASE(MB_, NB_, WM_, WN_, NS_)                                                  \
+  if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_)              \
+    return launch_lds_one<MB_, NB_, WM_, WN_, NS_, kFmtSp24>(p, A, Bp, S, C, M, K, N, gmagic, \
+                                                             ep, nullptr, workspace, stream);
     W4A16_LDS_SP_VARIANTS(W4A16_LSCASE)
 #undef W4A16_LSCASE
     return hipErrorInvalidValue;
   }
-#define W4A16_LFCASE(MB_, NB_, WM_, WN_, NS_)                                                 \
+#define W4A16_LCASE(MB_, NB_, WM_, WN_, NS_)                                                  \
   if (p.mb == MB_ && p.nb == NB_ && p.wm == WM_ && p.wk == WN_ && p.depth == NS_) {           \
+    if (wf.fmt == kFmtF16)                                                                    \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, kFmtF16>(p, A, Bp, S, C, M, K, N, gmagic, \
+                                                              ep, nullptr, workspace, stream); \
     if (wf.fmt == kFmtF16Zp)                                                                  \
-      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtF16Zp>(                          \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, kFmtF16Zp>(                              \
           p, A, Bp, S, C, M, K, N, gmagic, ep, wf.zeros, workspace, stream);                  \
     if (wf.fmt == kFmtBf16)                                                                   \
-      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtBf16>(                           \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, kFmtBf16>(                               \
           p, A, Bp, S, C, M, K, N, gmagic, ep, nullptr, workspace, stream);                   \
     if (wf.fmt == kFmtBf16Zp)                                                                 \
-      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, 16, kFmtBf16Zp>(                         \
+      return launch_lds_one<MB_, NB_, WM_, WN_, NS_, kFmtBf16Zp>(                             \
           p, A, Bp, S, C, M, K, N, gmagic, ep, wf.zeros, workspace, stream);                  \
     if (wf.fmt == kFmtW8)                                                                     \
-      return launch_lds_one<MB_, NB_, WM_, WN_, w8_stages(MB_, NB_, WM_, WN_, NS_), 16,       \
-                            kFmtW8>(p, A, Bp, S, C, M, K, N, gmagic, ep, nullptr, workspace,  \
-                                    stream);                                                  \
+      return launch_lds_one<MB_, NB_, WM_, WN_, w8_stages(MB_, NB_, WM_, WN_, NS_), kFmtW8>(  \
+          p, A, Bp, S, C, M, K, N, gmagic, ep, nullptr, workspace, stream);                   \
   }
-  W4A16_LDS_FMT_VARIANTS(W4A16_LFCASE)
-#undef W4A16_LFCASE
+  W4A16_LDS_VARIANTS(W4A16_LCASE)
+#undef W4A16_LCASE
   return hipErrorInvalidValue;
 }
 

@@ -6,8 +6,8 @@
 namespace w4a16 {
 
 bool sk_is_compiled(int mb, int nb, int ns, int wm, int wn) {
-#define W4A16_SKMATCH(MB_, NB_, NS_, WM_, WN_) \
-  if (mb == MB_ && nb == NB_ && ns == NS_ && wm == WM_ && wn == WN_) return true;
+#define W4A16_SKMATCH(MB_, NB_, NS_, WN_) \
+  if (mb == MB_ && nb == NB_ && ns == NS_ && wm == 1 && wn == WN_) return true;
   W4A16_SK_VARIANTS(W4A16_SKMATCH)
 #undef W4A16_SKMATCH
   return false;

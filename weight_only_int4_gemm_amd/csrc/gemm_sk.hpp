@@ -1,8 +1,8 @@
-// The stream-K W4A16 GEMM for 16 rows and more: C = A . dequant(Bpacked).
+// The stream-K W4A16 GEMM (9 to 64 rows on large layers): C = A . dequant(Bpacked).
 // (The kernel template; gemm_sk.hip and gemm_sk_fmt.hip instantiate it for
 // the FP16 format and for the formats with zero points or BF16.)
 //
-// Work decomposition.  The output is cut into tiles of 16*MB rows x 64*NB
+// Work decomposition.  The output is cut into tiles of 16*MB rows x 16*NB*WN
 // columns; a tile's K dimension into 128-deep K blocks.  The (tile, K block)
 // iterations, tile-major and K-minor (row tiles of one column tile next to
 // each other), are dealt out in G equal contiguous runs, one per workgroup,
@@ -19,15 +19,15 @@
 // (blocks are dealt to the 8 XCDs in turn), where row tiles of one column
 // tile share their codes in the XCD's L2.
 //
-// Inside a workgroup: WM x 4 waves, one or two per SIMD.  Wave (wm, wn)
-// owns the tile's columns 16*NB*wn .. +16*NB and rows 16*MB*wm .. +16*MB.
-// Per K block a pipeline stage in LDS holds the tile's activations and
-// codes (each wave loads an equal share) and the scales (each wave those of
-// its own columns), all brought in by the direct global -> LDS load NS - 1
-// K blocks ahead ("Quant Marlin kernel", "The architecture", top row:
-// asynchronous copies of the next tiles into shared memory while the
-// current one is multiplied).  With two waves per SIMD one wave's LDS reads
-// and unpacking run while the other's matrix instructions do.
+// Inside a workgroup: WN waves, one or two per SIMD.  Wave w owns the
+// tile's columns 16*NB*w .. +16*NB and every row.  Per K block a pipeline
+// stage in LDS holds the tile's activations and codes (each wave loads an
+// equal share) and the scales (each wave those of its own columns), all
+// brought in by the direct global -> LDS load NS - 1 K blocks ahead ("Quant
+// Marlin kernel", "The architecture", top row: asynchronous copies of the
+// next tiles into shared memory while the current one is multiplied).  With
+// two waves per SIMD one wave's LDS reads and unpacking run while the
+// other's matrix instructions do, and no weight is unpacked twice.
 //
 // Per 32-deep slice a wave reads MB activation fragments from LDS, unpacks
 // NB code words (unpack.hpp) and issues MB x NB matrix instructions.  The
@@ -91,13 +91,9 @@ __device__ __forceinline__ int sk_run_of(int64_t x, int64_t U, int64_t G) {
 // FMT: the weight format (format.hpp), 0 to 3: FP16 or BF16, with or
 // without zero points.  A, S and C hold raw 16-bit values; Z the zero points
 // uint8[K/group][N] of formats 1 and 3.  The fused output stage is FP16 only.
-// WM x WN waves (WN = 4 or 8): one or two per SIMD.  Wave (wm, wn) owns
-// rows 16*MB*wm .. +16*MB and columns 16*NB*wn .. +16*NB of the tile, and
-// each code block of the tile is loaded once and read by the WM waves of
-// its column.
-template <int MB, int NB, int NS, int WM, int WN, bool EPI, int FMT>
-__global__ __launch_bounds__(64 * WN * WM)
-__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void
+// WN waves (4 or 8): one or two per SIMD.
+template <int MB, int NB, int NS, int WN, bool EPI, int FMT>
+__global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(WN / 4, WN / 4))) void
 gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
                const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
                uint64_t group_magic, int tiles_n, int tiles_m, unsigned* __restrict__ counters,
@@ -105,9 +101,9 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   static_assert(FMT >= 0 && FMT <= 3, "the 4-bit dense formats");
   static_assert(!EPI || FMT == kFmtF16, "the fused epilogue is FP16 only");
   constexpr bool ZP = Format<FMT>::kZp;
-  static_assert(WN == 4 || WN == 8, "one or two wave columns per SIMD");
-  constexpr int WAVES = WN * WM;
-  constexpr int TM = 16 * MB * WM;         // rows of the tile
+  static_assert(WN == 4 || WN == 8, "one or two waves per SIMD");
+  constexpr int WAVES = WN;
+  constexpr int TM = 16 * MB;              // rows of the tile
   constexpr int TNW = 16 * NB;             // columns of one wave
   constexpr int TN = WN * TNW;             // columns of the tile
   constexpr int APIECES = TM * 16;         // 16-byte pieces of one stage's activations
@@ -116,9 +112,8 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   // loaded twice (same bytes to the same place), so every wave issues the
   // same number of loads
   constexpr int ALOADS = (ACHUNKS + WAVES - 1) / WAVES;
-  constexpr int CLOADS = WN * NB / WAVES;       // code blocks each wave loads
+  constexpr int CLOADS = NB;                    // code blocks each wave loads: its own
   static_assert(NB == 4, "a wave's 64 scales: one 2-byte direct load, one 16-byte read");
-  static_assert(CLOADS * WAVES == WN * NB, "every wave loads an equal share of the codes");
   constexpr int LOADS = ALOADS + CLOADS + 1 + (ZP ? 1 : 0);  // direct loads per wave per stage
   static_assert(NS >= 2 && (NS - 1) * LOADS < 64, "vmcnt range");
   struct StagePlain {
@@ -156,8 +151,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN;  // this wave's row and column in the tile's wave grid
-  const int wn = wave - wm * WN;
+  const int wn = wave;  // this wave's column block of the tile
   const int l16 = lane & 15;
   const int G = gridDim.x;
   const int run = sk_run_index(G);
@@ -213,8 +207,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     // direct load puts lane L's value in 32-bit word L of the destination.
     // Lane L loads column 16 (L % 4) + L / 4, so the four scales lane l
     // uses (columns 16 nb + l % 16, nb = 0..3) are words 4 (l % 16) .. +3:
-    // one read.  (With WM = 2 both waves of a column load them: the same
-    // bytes to the same words.)
+    // one read.
     {
       const int c0 = tn * TN + wn * TNW + 16 * (lane & 3) + (lane >> 2);
       const int c = c0 <= N - 1 ? c0 : N - 1;
@@ -249,7 +242,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const int lg = lane >> 4;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int r = (wm * MB + mb) * 16 + l16;
+      const int r = mb * 16 + l16;
       a[mb] = __builtin_bit_cast(half8_t, sg.a[r * 16 + ((4 * j + lg) ^ (r & 15))]);
     }
   };
@@ -301,7 +294,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   auto finish_tile = [&](int tile, bool whole) {
     const int tn = tile / tiles_m;
     const int tm = tile - tn * tiles_m;
-    const int row0 = tm * TM + wm * 16 * MB;
+    const int row0 = tm * TM;
     const int col0 = tn * TN + wn * TNW;
     // fused output stage: the bias of the four columns this lane stores in
     // each column block, loaded together up front
@@ -489,13 +482,11 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 // ---------------------------------------------------------------------------
 // host side
 
-// Compiled variants (MB, NB, NS, WM, WN): MB row blocks per wave, NS
-// stages, WM x WN waves.
-#define W4A16_SK_VARIANTS(X)                                                                \
-  X(8, 4, 3, 1, 4) X(4, 4, 4, 1, 4) X(2, 4, 6, 1, 4) X(1, 4, 6, 1, 4) X(4, 4, 3, 2, 4)       \
-      X(2, 4, 4, 2, 4) X(1, 4, 6, 2, 4) X(1, 4, 4, 1, 8) X(2, 4, 3, 1, 8) X(4, 4, 3, 1, 8)
+// Compiled variants (MB, NB, NS, WN): the plans' ones (MB row blocks, NS
+// stages, WN waves).
+#define W4A16_SK_VARIANTS(X) X(1, 4, 4, 8) X(2, 4, 3, 8) X(4, 4, 3, 8)
 
-template <int MB, int NB, int NS, int WM, int WN, int FMT>
+template <int MB, int NB, int NS, int WN, int FMT>
 hipError_t launch_sk_one(const Plan& p, const uint16_t* A, const uint32_t* Bp, const uint16_t* S,
                          uint16_t* C, int M, int K, int N, uint64_t gmagic, Epilogue ep,
                          const uint8_t* Z, void* workspace, hipStream_t stream) {
@@ -505,20 +496,20 @@ hipError_t launch_sk_one(const Plan& p, const uint16_t* A, const uint32_t* Bp, c
     counters = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterHeaderBytes);
   }
-  const dim3 grid(p.splits), block(64 * WN * WM);
+  const dim3 grid(p.splits), block(64 * WN);
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
   if constexpr (FMT == kFmtF16) {
     if (epilogue_needed(ep)) {
-      hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WM, WN, true, FMT>), grid, block, 0, stream, a, Bp, s,
+      hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WN, true, FMT>), grid, block, 0, stream, a, Bp, s,
                          c, M, K, N, gmagic, p.tiles_n, p.tiles_m, counters, partials, ep, Z);
       return hipGetLastError();
     }
   } else {
     if (epilogue_needed(ep)) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WM, WN, false, FMT>), grid, block, 0, stream, a, Bp, s, c,
+  hipLaunchKernelGGL((gemm_sk_kernel<MB, NB, NS, WN, false, FMT>), grid, block, 0, stream, a, Bp, s, c,
                      M, K, N, gmagic, p.tiles_n, p.tiles_m, counters, partials, ep, Z);
   return hipGetLastError();
 }
@@ -527,10 +518,10 @@ template <int FMT>
 hipError_t launch_sk_fmt(const Plan& p, const uint16_t* A, const uint32_t* Bp, const uint16_t* S,
                          uint16_t* C, int M, int K, int N, uint64_t gmagic, Epilogue ep,
                          const uint8_t* Z, void* workspace, hipStream_t stream) {
-#define W4A16_SKCASE(MB_, NB_, NS_, WM_, WN_)                                                 \
-  if (p.mb == MB_ && p.nb == NB_ && p.depth == NS_ && p.wm == WM_ && p.wk == WN_)             \
-    return launch_sk_one<MB_, NB_, NS_, WM_, WN_, FMT>(p, A, Bp, S, C, M, K, N, gmagic, ep, Z, \
-                                                       workspace, stream);
+#define W4A16_SKCASE(MB_, NB_, NS_, WN_)                                                     \
+  if (p.mb == MB_ && p.nb == NB_ && p.depth == NS_ && p.wm == 1 && p.wk == WN_)               \
+    return launch_sk_one<MB_, NB_, NS_, WN_, FMT>(p, A, Bp, S, C, M, K, N, gmagic, ep, Z,      \
+                                                  workspace, stream);
   W4A16_SK_VARIANTS(W4A16_SKCASE)
 #undef W4A16_SKCASE
   return hipErrorInvalidValue;

@@ -9,25 +9,23 @@ namespace w4a16 {
 
 // How one w4a16_gemm call is cut into work.
 //  tile   0: the streaming kernel (small batches), 2: the LDS kernel
-//         (every operand through LDS stages) with 16 x 16 matrix blocks,
-//         3: the LDS kernel with 32 x 32 blocks (mb and nb then count
-//         32-row / 32-column blocks), 4: the stream-K kernel (gemm_sk.hip:
-//         four waves of 16*mb x 16*nb, `splits` workgroups each running an
-//         equal share of the (tile, K block) iterations)
-//  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb rows)
+//         (every operand through LDS stages), 4: the stream-K kernel
+//         (gemm_sk.hpp: wk waves of 16*mb x 16*nb, `splits` workgroups each
+//         running an equal share of the (tile, K block) iterations)
+//  mb     16-row blocks per wave (the workgroup's M tile is 16 * mb * wm)
 //  nb     16-column blocks per wave
-//  wk     waves per workgroup (LDS kernel: waves along N).  Streaming
-//         kernel: they split the workgroup's K range (every wk-th 128-deep
-//         K block each) and their sums are added in wave order through LDS;
-//         the N tile is 16 * nb.  LDS kernel: they split the N tile, which
-//         is 16 * nb * wk.
-//  wm     LDS kernel: waves along M (1 elsewhere); the M tile is
-//         16 * mb * wm (32 * ... with 32 x 32 blocks), the workgroup
+//  wk     waves per workgroup (LDS and stream-K kernels: waves along N).
+//         Streaming kernel: they split the workgroup's K range (every wk-th
+//         128-deep K block each) and their sums are added in wave order
+//         through LDS; the N tile is 16 * nb.  LDS and stream-K kernels:
+//         they split the N tile, which is 16 * nb * wk.
+//  wm     LDS kernel: waves along M (1 elsewhere); the workgroup has
 //         wm * wk waves
 //  splits K ranges per output tile, one workgroup each; their FP32
 //         partials go through the workspace and are added in split order
-//  depth  streaming kernel: K blocks each wave keeps in flight; LDS
-//         kernel: stages of activations, codes and scales
+//         (stream-K kernel: the number of workgroups)
+//  depth  streaming kernel: K blocks each wave keeps in flight; LDS and
+//         stream-K kernels: stages of activations, codes and scales
 struct Plan {
   int tile, mb, nb, wk, splits, depth, wm;
   int tm, tn;              // output tile of one workgroup
@@ -56,7 +54,7 @@ struct WeightFormat {
 Plan make_plan(int M, int K, int N, int group, int cus, int fmt = 0);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
-bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns, int f);
+bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns);
 bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns);
 bool sk_is_compiled(int mb, int nb, int ns, int wm, int wn);
 size_t sk_workspace_bytes(int wgs, int tm, int tn, int tiles, int KB, int ns);

@@ -9,7 +9,6 @@
 
 namespace w4a16 {
 
-typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* global_ptr_t;
 
@@ -46,35 +45,16 @@ __device__ __forceinline__ void stage_barrier() {
   keep_load_order();
 }
 
-// The bias of the columns this lane stores, loaded as raw FP16 at kernel
-// start (fused epilogue only) so that the load's latency hides behind the
-// main loop; it is converted where the output stage uses it.  The count-
-// based waits of the pipelines stay correct: this load is older than every
-// stage load, and loads complete in order.
-// `wcol0` is the first column of the wave's own tile; lane l stores column
-// l % F of each of its NB column blocks (wcol0 + F * nb + l % F).
-template <int NB, int F, bool EPI>
-struct LaneBias {
-  _Float16 v[NB];
-  __device__ __forceinline__ void load(const Epilogue& ep, int wcol0, int N) {
-    if constexpr (EPI) {
-      const int c = wcol0 + (int)(threadIdx.x & (F - 1));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        v[nb] = (ep.bias && c + F * nb < N) ? ep.bias[c + F * nb] : (_Float16)0.f;
-    }
-  }
-  __device__ __forceinline__ float operator[](int nb) const {
-    if constexpr (EPI) return (float)v[nb];
-    return 0.f;
-  }
-};
 
 typedef _Float16 half4_tc_t __attribute__((ext_vector_type(4)));
 
-// The bias for transposed 16 x 16 blocks: lane l stores columns
-// wcol0 + 16 nb + 4 (l / 16) .. +3 of its NB column blocks, loaded as one
-// 8-byte vector per block at kernel start (same reasoning as LaneBias).
+// The bias of the columns this lane stores (fused epilogue only), loaded as
+// raw FP16 at kernel start so that the load's latency hides behind the main
+// loop; it is converted where the output stage uses it.  The count-based
+// waits of the pipelines stay correct: this load is older than every stage
+// load, and loads complete in order.  With transposed 16 x 16 blocks lane l
+// stores columns wcol0 + 16 nb + 4 (l / 16) .. +3 of its NB column blocks:
+// one 8-byte vector per block.
 template <int NB, bool EPI>
 struct LaneBias4 {
   half4_tc_t v[NB];
@@ -180,91 +160,5 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
     __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The same for 32 x 32 blocks (v_mfma_f32_32x32x16_f16): acc[mb][nb] holds,
-// in lane l, column l % 32 of the block and rows 8q + 4(l/32) + i in element
-// 4q + i (q, i = 0..3) of the wave tile starting at (wrow0, wcol0).  A
-// partial is kept in fragment order (wave, row block, column block, q, lane,
-// four values).
-template <int MB, int NB, int WAVES, bool EPI>
-__device__ __forceinline__ void store_output_tile32(float16_t (&acc)[MB][NB],
-                                                    _Float16* __restrict__ C, int M, int N,
-                                                    int wrow0, int wcol0, int split, int splits,
-                                                    unsigned* __restrict__ counters,
-                                                    float* __restrict__ partials, int* flag,
-                                                    const Epilogue& ep,
-                                                    const LaneBias<NB, 32, EPI>& bias) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col_base = wcol0 + (lane & 31);
-  const int row_lane = 4 * (lane >> 5);
-  auto write_c = [&]() {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int gc = col_base + nb * 32;
-        if (gc >= N) continue;
-        const float b = bias[nb];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int gr = wrow0 + mb * 32 + 8 * q + row_lane + i;
-            const float x = acc[mb][nb][4 * q + i];
-            if (gr < M) C[(int64_t)gr * N + gc] = (_Float16)(EPI ? epilogue_apply(ep, x, b) : x);
-          }
-      }
-  };
-  if (splits == 1) {
-    write_c();
-    return;
-  }
-
-  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-  constexpr int TE = WAVES * MB * NB * 1024;  // elements of the tile
-  const float* tile_base = partials + (int64_t)tile * splits * TE;
-  const int frag0 = wave * MB * NB * 4 * 64 + lane;
-  auto quad = [&](const float16_t& v, int q) {
-    return float4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-  };
-  {
-    const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          store_coherent(mine, frag0 + ((mb * NB + nb) * 4 + q) * 64, quad(acc[mb][nb], q));
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = prev == (unsigned)(splits - 1);
-  }
-  __syncthreads();
-  if (!*flag) return;
-
-  // Sum in split order 0, 1, ... into the (now free) accumulators.
-  for (int s = 0; s < splits; ++s) {
-    const __amdgpu_buffer_rsrc_t ps = coherent_rsrc(tile_base + (int64_t)s * TE);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4_t x = load_coherent(ps, frag0 + ((mb * NB + nb) * 4 + q) * 64);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[mb][nb][4 * q + i] = s == 0 ? x[i] : acc[mb][nb][4 * q + i] + x[i];
-        }
-  }
-  write_c();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 }  // namespace w4a16
