@@ -17,8 +17,9 @@ from tests.tolerance import assert_epilogue_close, assert_gemm_close
 
 pytestmark = pytest.mark.gpu
 
-# compiled variants: 16*mb rows, pipeline depth ns, eight waves of 64 columns
-VARIANTS = [(1, 4), (2, 3), (4, 3)]
+# compiled variants: 16*mb rows, 16*nb columns per wave, pipeline depth ns,
+# eight waves
+VARIANTS = [(1, 4, 4), (2, 4, 3), (4, 4, 3), (8, 2, 3)]
 
 
 @pytest.fixture(autouse=True)
@@ -28,46 +29,47 @@ def _no_forced_plan():
     w4.w4a16_set_forced_plan(None)
 
 
-def _plan(mb, ns, grid):
-    return f"{mb},4,8,{grid},{ns},4"
+def _plan(mb, ns, grid, nb=4):
+    return f"{mb},{nb},8,{grid},{ns},4"
 
 
-def _name(mb, ns):
-    return f"gemm_sk_kernel<{mb},4,{ns},8>"
+def _name(mb, ns, nb=4):
+    return f"gemm_sk_kernel<{mb},{nb},{ns},8>"
 
 
-@pytest.mark.parametrize("mb,ns", VARIANTS)
+@pytest.mark.parametrize("mb,nb,ns", VARIANTS)
 @pytest.mark.parametrize("grid", [1, 3, 7, 0])
-def test_sk_forced_grids_agree(mb, ns, grid):
+def test_sk_forced_grids_agree(mb, nb, ns, grid):
     """M = 45 and N = 208 leave ragged row and column tiles; K = 3584 is 28
     K blocks (padded to a multiple of ns where needed); grids of 3 and 7
     workgroups cut tiles in the middle."""
     M, K, N, g = 45, 3584, 208, 128
     A, Bq, S = make_inputs(M, K, N, g, seed=11)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, grid))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, grid, nb))
     desc = w4.w4a16_describe(M, K, N, g)
-    assert desc.startswith(_name(mb, ns)), desc
-    say("sk forced", mb, ns, grid, desc)
+    assert desc.startswith(_name(mb, ns, nb)), desc
+    say("sk forced", mb, nb, ns, grid, desc)
     C = run_gemm(A, Bq, S, g)
     _, C64 = oracle.gemm(A, Bq, S, g)
     assert_gemm_close(C, C64, desc)
 
 
-@pytest.mark.parametrize("M,K,N,mb,ns", [(16, 2048, 4160, 1, 4), (40, 2048, 4160, 2, 3),
-                                         (64, 3840, 768, 4, 3), (130, 1152, 2048, 4, 3),
-                                         (16, 1536, 1536, 1, 4)])
-def test_sk_default_and_split_grids(M, K, N, mb, ns):
+@pytest.mark.parametrize("M,K,N,mb,nb,ns", [(16, 2048, 4160, 1, 4, 4), (40, 2048, 4160, 2, 4, 3),
+                                            (64, 3840, 768, 4, 4, 3), (130, 1152, 2048, 4, 4, 3),
+                                            (16, 1536, 1536, 1, 4, 4), (200, 4096, 1024, 8, 2, 3),
+                                            (300, 1152, 2096, 8, 2, 3)])
+def test_sk_default_and_split_grids(M, K, N, mb, nb, ns):
     """Several column and row tiles; the default grid (one workgroup per
     compute unit, at least eight K blocks each) and a 5-workgroup grid whose
     runs end inside tiles."""
     A, Bq, S = make_inputs(M, K, N, 128, seed=M + N)
     _, C64 = oracle.gemm(A, Bq, S, 128)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, 0))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 0, nb))
     desc = w4.w4a16_describe(M, K, N, 128)
-    assert desc.startswith(_name(mb, ns)), desc
+    assert desc.startswith(_name(mb, ns, nb)), desc
     say("sk default grid", M, K, N, desc)
     assert_gemm_close(run_gemm(A, Bq, S, 128), C64, desc)
-    w4.w4a16_set_forced_plan(_plan(mb, ns, 5))
+    w4.w4a16_set_forced_plan(_plan(mb, ns, 5, nb))
     desc5 = w4.w4a16_describe(M, K, N, 128)
     assert "workspace=0" not in desc5, desc5
     say("sk grid 5", M, K, N, desc5)
@@ -97,11 +99,11 @@ def test_sk_one_hot_rows_are_exact():
     ks = np.random.default_rng(4).integers(0, K, size=M)
     A[np.arange(M), ks] = 1.0
     W = oracle.dequant(Bq, S, g)
-    for mb, ns in VARIANTS:
-        w4.w4a16_set_forced_plan(_plan(mb, ns, 4))
-        say("sk one-hot", mb, ns)
+    for mb, nb, ns in VARIANTS:
+        w4.w4a16_set_forced_plan(_plan(mb, ns, 4, nb))
+        say("sk one-hot", mb, nb, ns)
         C = run_gemm(A, Bq, S, g)
-        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, ns)
+        assert np.array_equal(C.astype(np.float64), W[ks].astype(np.float64)), (mb, nb, ns)
 
 
 def test_sk_deterministic_and_counters_reset():
@@ -134,8 +136,9 @@ def test_sk_fused_epilogue(act):
     A, Bq, S = make_inputs(M, K, N, g, seed=9)
     bias = make_bias(N, seed=10)
     _, Y64, Z64 = oracle.gemm_fused(A, Bq, S, g, bias, act)
-    for grid, (mb, ns) in ((1, (2, 3)), (5, (2, 3)), (5, (1, 4)), (7, (4, 3))):
-        w4.w4a16_set_forced_plan(_plan(mb, ns, grid))
+    for grid, (mb, nb, ns) in ((1, (2, 4, 3)), (5, (2, 4, 3)), (5, (1, 4, 4)), (7, (4, 4, 3)),
+                               (3, (8, 2, 3))):
+        w4.w4a16_set_forced_plan(_plan(mb, ns, grid, nb))
         desc = w4.w4a16_describe(M, K, N, g)
         say("sk fused", act, desc)
         C = run_gemm_fused(A, Bq, S, g, bias, act)

@@ -23,7 +23,7 @@ def plan(M, K, N, fmt=F16, group=128):
     return w4.w4a16_plan_describe(M, K, N, group, fmt, CUS)
 
 
-def test_stream_k_takes_9_to_64_rows_on_large_layers():
+def test_stream_k_takes_9_to_128_rows_on_large_layers():
     K, N = 18432, 73728
     for M, name in ((9, "1,4,4,8"), (16, "1,4,4,8"), (17, "2,4,3,8"), (32, "2,4,3,8"),
                     (33, "4,4,3,8"), (64, "4,4,3,8")):
@@ -31,12 +31,21 @@ def test_stream_k_takes_9_to_64_rows_on_large_layers():
             assert plan(M, K, N, fmt).startswith(f"gemm_sk_kernel<{name}>"), (M, fmt)
         assert not plan(M, K, N, W8).startswith("gemm_sk_kernel<"), M
         assert not plan(M, K, N, SP24).startswith("gemm_sk_kernel<"), M
-    for M in (1, 8, 65, 128, 1024):
+    for M in (65, 96, 128):
+        for fmt in (F16, F16ZP, BF16, BF16ZP):
+            assert plan(M, K, N, fmt).startswith("gemm_sk_kernel<8,2,3,8>"), (M, fmt)
+    assert plan(128, 28672, 8192).startswith("gemm_sk_kernel<8,2,3,8>")
+    for M in (1, 8, 129, 1024):
         assert not plan(M, K, N).startswith("gemm_sk_kernel<"), M
     for K2, N2 in ((4096, 4096), (4096, 12288), (4096, 22016), (11008, 4096), (8192, 28672),
                    (28672, 8192), (13824, 5120)):
         for M in (16, 32, 64):
             assert not plan(M, K2, N2).startswith("gemm_sk_kernel<"), (M, K2, N2)
+    for K2, N2 in ((4096, 4096), (4096, 12288), (4096, 22016), (11008, 4096), (8192, 28672),
+                   (13824, 5120)):
+        assert not plan(128, K2, N2).startswith("gemm_sk_kernel<"), (K2, N2)
+    for M in (512, 1024, 4096):
+        assert not plan(M, 8192, 28672).startswith("gemm_sk_kernel<"), M
 
 
 def test_plan_describe_checks_its_arguments():

@@ -231,28 +231,46 @@ size_t workspace_fmt(int M, int K, int N, int group, int fmt) {
 // wider wave tiles: 4096 x 12288 at M = 128: 26.6 -> 21.1 us); and the K
 // split there is twice the dense one below a full wave of workgroups and
 // none above it.
-// Whether the stream-K kernel takes a call: the 4-bit dense formats from 9
-// to 64 rows, on a layer that gives every compute unit many K blocks of 256
-// columns, as 16*mb x 512 tiles of eight waves (two per SIMD, each with its
-// own 64 columns, so no weight is unpacked twice).  Measured against the
-// whole-tile plans by graph replay over rotating weight copies, on the
-// 18432 x 73728 layer: 144-154 against 152-161 us at M = 16, 160 against
-// 176-185 us at M = 32, 211 against 232-234 us at M = 64.  At M = 128 the
-// LDS kernel's 128 x 256 tiles stay ahead (368 against 394 us).  On smaller
-// layers the fix-up and the pipeline fill cost 10-20 us that a grid of whole
-// tiles does not pay: 8192 x 28672, 28672 x 8192 and the Llama-2-7B layers
-// at M = 16..64 ran 1.16-2.9x slower.
-static bool stream_k_plan(int M, int KB, int N, int cus, int fmt, Plan* p) {
-  if (fmt > kFmtBf16Zp || M <= 8 || M > 64) return false;
-  const int64_t blocks = (int64_t)((N + 255) / 256) * KB;  // 256-column K blocks
-  if (blocks < (int64_t)48 * cus) return false;
-  p->tile = 4;
-  p->wm = 1;
-  p->wk = 8;  // waves along N
-  p->nb = 4;
-  p->mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-  p->depth = p->mb == 1 ? 4 : 3;  // as many stages as fit in LDS
-  p->splits = 0;                  // the stream-K grid is set below
+// Whether the stream-K kernel takes a call (4-bit dense formats only), and
+// its tile: eight waves (two per SIMD, each with its own columns, so no
+// weight is unpacked twice), every compute unit an equal share of the
+// (tile, K block) iterations.  Measured against the whole-tile plans by
+// graph replay over rotating weight copies:
+//  * 9 to 64 rows, on a layer with at least 48 K blocks of 256 columns per
+//    compute unit: 16*mb x 512 tiles.  18432 x 73728: 144-154 against
+//    152-161 us at M = 16, 160 against 176-185 us at M = 32, 211 against
+//    232-234 us at M = 64.  On smaller layers the fix-up and pipeline fill
+//    cost 10-20 us that a grid of whole tiles does not pay (8192 x 28672,
+//    28672 x 8192 and the Llama-2-7B layers: 1.16-2.9x slower).
+//  * 65 to 128 rows, where the LDS plan splits K and the layer gives at
+//    least 24 iterations of 128 x 256 tiles per compute unit: 128 x 256
+//    tiles (waves of 128 x 32, the LDS plan's own), with no partial tiles
+//    through the workspace and no last wave of workgroups half empty.
+//    18432 x 73728: 329-339 against 354-366 us at M = 65..128; 28672 x 8192
+//    at M = 128: 78-80 against 85-86 us.  Below that count (the Llama-2-7B
+//    layers: 1.3-2.9x slower) and in prefill, where the LDS plan needs no
+//    split (4-14% slower), the LDS kernel stays.
+static bool stream_k_plan(int M, int KB, int N, int cus, int fmt, const Plan& base, Plan* p) {
+  if (fmt > kFmtBf16Zp || M <= 8 || M > 128) return false;
+  Plan q = *p;
+  q.tile = 4;
+  q.wm = 1;
+  q.wk = 8;  // waves along N
+  q.splits = 0;  // the stream-K grid is set below
+  if (M <= 64) {
+    const int64_t blocks = (int64_t)((N + 255) / 256) * KB;  // 256-column K blocks
+    if (blocks < (int64_t)48 * cus) return false;
+    q.nb = 4;
+    q.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    q.depth = q.mb == 1 ? 4 : 3;  // as many stages as fit in LDS
+  } else {
+    const int64_t iters = (int64_t)((N + 255) / 256) * ((M + 127) / 128) * KB;
+    if (base.tile != 2 || base.splits <= 1 || iters < (int64_t)24 * cus) return false;
+    q.nb = 2;
+    q.mb = 8;
+    q.depth = 3;
+  }
+  *p = q;
   return true;
 }
 
@@ -393,7 +411,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   if (want > 64) want = 64;
   p.splits = (int)(want < 1 ? 1 : want);
   const Plan base = p;  // the plan without the stream-K kernel
-  stream_k_plan(M, KB, N, cus, fmt, &p);
+  stream_k_plan(M, KB, N, cus, fmt, base, &p);
   apply_forced_plan(&p, base, KB, fmt);
   shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;

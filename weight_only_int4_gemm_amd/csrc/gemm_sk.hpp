@@ -1,4 +1,4 @@
-// The stream-K W4A16 GEMM (9 to 64 rows on large layers): C = A . dequant(Bpacked).
+// The stream-K W4A16 GEMM (9 to 128 rows on large layers): C = A . dequant(Bpacked).
 // (The kernel template; gemm_sk.hip and gemm_sk_fmt.hip instantiate it for
 // the FP16 format and for the formats with zero points or BF16.)
 //
@@ -113,7 +113,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   // same number of loads
   constexpr int ALOADS = (ACHUNKS + WAVES - 1) / WAVES;
   constexpr int CLOADS = NB;                    // code blocks each wave loads: its own
-  static_assert(NB == 4, "a wave's 64 scales: one 2-byte direct load, one 16-byte read");
+  static_assert(NB == 2 || NB == 4, "a wave's scales: one 2-byte direct load, one vector read");
   constexpr int LOADS = ALOADS + CLOADS + 1 + (ZP ? 1 : 0);  // direct loads per wave per stage
   static_assert(NS >= 2 && (NS - 1) * LOADS < 64, "vmcnt range");
   struct StagePlain {
@@ -203,13 +203,14 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
       const uint32_t* src = Bp + block_word_offset(n16c, kb, K) + lane * kWordsPerLane;
       __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)&sg.b[64 * blk], 16, 0, 0);
     }
-    // the 64 scales of this wave's columns, one FP16 per lane; a 2-byte
+    // the scales of this wave's 16*NB columns, one FP16 per lane; a 2-byte
     // direct load puts lane L's value in 32-bit word L of the destination.
-    // Lane L loads column 16 (L % 4) + L / 4, so the four scales lane l
-    // uses (columns 16 nb + l % 16, nb = 0..3) are words 4 (l % 16) .. +3:
-    // one read.
+    // Lane L loads column 16 (L % NB) + (L / NB) % 16, so the NB scales
+    // lane l uses (columns 16 nb + l % 16) are words NB (l % 16) .. +NB-1:
+    // one read.  (With NB = 2 lanes 32..63 load the same columns again
+    // into words no lane reads.)
     {
-      const int c0 = tn * TN + wn * TNW + 16 * (lane & 3) + (lane >> 2);
+      const int c0 = tn * TN + wn * TNW + 16 * (lane % NB) + (lane / NB) % 16;
       const int c = c0 <= N - 1 ? c0 : N - 1;
       const _Float16* src = S + (int64_t)scale_row(kb) * N + c;
       __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)&sg.s[64 * wn], 2, 0, 0);
@@ -251,16 +252,34 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   auto read_codes = [&](const Stage& sg, bool pad) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) cw[nb] = sg.b[64 * (wn * NB + nb) + lane];
-    const uint4 s4 = reinterpret_cast<const uint4*>(&sg.s[64 * wn])[l16];
     const uint32_t keep = pad ? 0u : 0xFFFFu;
-    const uint32_t w[4] = {s4.x & keep, s4.y & keep, s4.z & keep, s4.w & keep};
-    uint32_t zp[4] = {8u, 8u, 8u, 8u};
+    uint32_t w[NB];
+    uint32_t zp[NB];
+    if constexpr (NB == 4) {
+      const uint4 s4 = reinterpret_cast<const uint4*>(&sg.s[64 * wn])[l16];
+      w[0] = s4.x & keep;
+      w[1] = s4.y & keep;
+      w[2] = s4.z & keep;
+      w[3] = s4.w & keep;
+    } else {
+      const uint2 s2 = reinterpret_cast<const uint2*>(&sg.s[64 * wn])[l16];
+      w[0] = s2.x & keep;
+      w[1] = s2.y & keep;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) zp[nb] = 8u;
     if constexpr (ZP) {
-      const uint4 z4 = reinterpret_cast<const uint4*>(&sg.z[64 * wn])[l16];
-      zp[0] = z4.x & 0xFFu;
-      zp[1] = z4.y & 0xFFu;
-      zp[2] = z4.z & 0xFFu;
-      zp[3] = z4.w & 0xFFu;
+      if constexpr (NB == 4) {
+        const uint4 z4 = reinterpret_cast<const uint4*>(&sg.z[64 * wn])[l16];
+        zp[0] = z4.x & 0xFFu;
+        zp[1] = z4.y & 0xFFu;
+        zp[2] = z4.z & 0xFFu;
+        zp[3] = z4.w & 0xFFu;
+      } else {
+        const uint2 z2 = reinterpret_cast<const uint2*>(&sg.z[64 * wn])[l16];
+        zp[0] = z2.x & 0xFFu;
+        zp[1] = z2.y & 0xFFu;
+      }
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -484,7 +503,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 
 // Compiled variants (MB, NB, NS, WN): the plans' ones (MB row blocks, NS
 // stages, WN waves).
-#define W4A16_SK_VARIANTS(X) X(1, 4, 4, 8) X(2, 4, 3, 8) X(4, 4, 3, 8)
+#define W4A16_SK_VARIANTS(X) X(1, 4, 4, 8) X(2, 4, 3, 8) X(4, 4, 3, 8) X(8, 2, 3, 8)
 
 template <int MB, int NB, int NS, int WN, int FMT>
 hipError_t launch_sk_one(const Plan& p, const uint16_t* A, const uint32_t* Bp, const uint16_t* S,
