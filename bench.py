@@ -143,7 +143,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step (profiler runs)")
-    ap.add_argument("--cpu-sample-cols", type=int, default=4096,
+    ap.add_argument("--cpu-sample-cols", type=int, default=12288,
                     help="output columns per layer for the CPU oracle (0 = whole layers)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a one-dispatch elementwise copy (negation) "
