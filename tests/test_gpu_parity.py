@@ -395,3 +395,26 @@ def test_binding_refuses_buffers_too_small():
     W = torch.empty((K - 128, N), dtype=torch.float16, device="cuda")
     with pytest.raises(ValueError, match="W"):
         w4.w4a16_dequant_debug(Bp, S_d, W, K, N, g)
+
+
+def test_lds_tail_tiles_split():
+    """With more tiles than compute units and a partial last wave, the LDS
+    kernel runs the whole waves' tiles whole and splits only the remaining
+    ones in K: M = 300 and N = 28672 give 3 x 112 = 336 tiles of 128 x 256,
+    256 whole and 80 split.  Matches the oracle everywhere, repeats bit for
+    bit, and leaves the counters at zero."""
+    import torch
+    M, K, N, g = 300, 2048, 28672, 128
+    desc = w4.w4a16_describe(M, K, N, g)
+    assert desc.startswith("gemm_lds_kernel<") and "whole=256 " in desc, desc
+    assert "splits=1 " not in desc, desc
+    A, Bq, S = make_inputs(M, K, N, g, seed=30)
+    Bp = repack_on_device(dev(Bq), K, N)
+    ws = torch.zeros(w4.w4a16_workspace_bytes(M, K, N, g), dtype=torch.uint8, device="cuda")
+    say("lds tail split", desc)
+    first = run_gemm(A, Bq, S, g, workspace=ws, Bp=Bp)
+    again = run_gemm(A, Bq, S, g, workspace=ws, Bp=Bp)
+    assert np.array_equal(first.view(np.uint16), again.view(np.uint16))
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+    _, C64 = oracle.gemm(A, Bq, S, g)
+    assert_gemm_close(first, C64, desc)

@@ -48,6 +48,23 @@ def test_stream_k_takes_9_to_128_rows_on_large_layers():
         assert not plan(M, 8192, 28672).startswith("gemm_sk_kernel<"), M
 
 
+def test_lds_tail_split():
+    """More tiles than compute units and a last wave at most half full:
+    whole waves' tiles run whole, the rest are split in two along K."""
+    d = plan(1024, 8192, 28672)   # 8 x 112 = 896 tiles: 768 whole + 128 split 2 ways
+    assert d.startswith("gemm_lds_kernel<8,2,1,8,3>") and "whole=768 splits=2 " in d, d
+    assert "grid=1024x1x1" in d, d
+    d = plan(512, 8192, 28672)    # 448 tiles: the last wave three-quarters full, nothing split
+    assert "splits=1 " in d and "workspace=0" in d, d
+    d = plan(4096, 8192, 28672)   # 3584 tiles: 14 full waves, nothing split
+    assert "splits=1 " in d and "workspace=0" in d, d
+    w4.w4a16_set_forced_plan("8,2,8,1,3,2")   # a forced plan is taken as it is
+    try:
+        assert "splits=1 " in plan(1024, 8192, 28672)
+    finally:
+        w4.w4a16_set_forced_plan(None)
+
+
 def test_plan_describe_checks_its_arguments():
     with pytest.raises(w4.W4A16Error):
         w4.w4a16_plan_describe(16, 4096, 4096, 128, 6, CUS)    # no such format

@@ -120,18 +120,19 @@ void seed_forced_from_env() {
   });
 }
 
-void apply_forced_plan(Plan* p, const Plan& base, int KB, int fmt) {
+// Returns whether a forced plan replaced the heuristic's.
+bool apply_forced_plan(Plan* p, const Plan& base, int KB, int fmt) {
   seed_forced_from_env();
-  if (!g_force_any.load(std::memory_order_acquire)) return;
+  if (!g_force_any.load(std::memory_order_acquire)) return false;
   ForcedPlan f;
   {
     std::lock_guard<std::mutex> lock(g_force_mu);
     f = g_force;
   }
-  if (!f.set) return;
+  if (!f.set) return false;
   if (f.tile == -1) {  // the heuristic's plan without the stream-K kernel
     *p = base;
-    return;
+    return false;
   }
   // fields left open come from the heuristic's plan of the forced family
   Plan q = (f.tile == 4) == (p->tile == 4) ? *p : base;
@@ -151,8 +152,9 @@ void apply_forced_plan(Plan* p, const Plan& base, int KB, int fmt) {
       if (variant_is_compiled(q, fmt)) break;
     }
   }
-  if (!variant_is_compiled(q, fmt)) return;
+  if (!variant_is_compiled(q, fmt)) return false;
   *p = q;
+  return true;
 }
 
 // The plan of one call on a device with `cus` compute units as one line of
@@ -174,12 +176,15 @@ int describe_plan(int M, int K, int N, int group, int fmt, int cus, char* buf, s
                   p.mb, p.nb, p.depth, p.wk, p.splits, 64 * p.wk, p.tiles_n,
                   p.tiles_m,
                   p.splits, p.workspace_bytes);
-  else if (p.tile == 2)
+  else if (p.tile == 2) {
+    const int tiles = p.tiles_n * p.tiles_m;
+    const int head = p.splits > 1 ? p.head : tiles;
     std::snprintf(buf, len,
-                  "gemm_lds_kernel<%d,%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d "
-                  "workspace=%zu",
-                  p.mb, p.nb, p.wm, p.wk, p.depth, p.tiles_n, p.tiles_m,
-                  p.splits, 64 * p.wm * p.wk, p.splits, p.workspace_bytes);
+                  "gemm_lds_kernel<%d,%d,%d,%d,%d> grid=%dx1x1 block=%d tiles=%dx%d whole=%d "
+                  "splits=%d workspace=%zu",
+                  p.mb, p.nb, p.wm, p.wk, p.depth, head + (tiles - head) * p.splits,
+                  64 * p.wm * p.wk, p.tiles_n, p.tiles_m, head, p.splits, p.workspace_bytes);
+  }
   else
     std::snprintf(buf, len,
                   "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
@@ -412,9 +417,10 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   p.splits = (int)(want < 1 ? 1 : want);
   const Plan base = p;  // the plan without the stream-K kernel
   stream_k_plan(M, KB, N, cus, fmt, base, &p);
-  apply_forced_plan(&p, base, KB, fmt);
+  const bool forced = apply_forced_plan(&p, base, KB, fmt);
   shape(p);
   const int64_t ftiles = (int64_t)p.tiles_n * p.tiles_m;
+  p.head = 0;
   if (p.tile == 4 && !variant_is_compiled(p, fmt)) return Plan{};  // not reached: plans name compiled variants
   if (p.tile == 4) {
     // Stream-K grid: one workgroup per compute unit, each with at least
@@ -433,11 +439,29 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     p.workspace_bytes = sk_workspace_bytes(p.splits, p.tm, p.tn, (int)ftiles, KB, p.depth);
     return p;
   }
-  if (ftiles > kMaxSplitTiles) p.splits = 1;  // the counter header holds one per tile
+  if (p.tile == 2 && p.splits == 1 && !forced && ftiles > cus && KB >= 16) {
+    // LDS kernel with more tiles than compute units: when the last wave of
+    // workgroups would run at most half full, the whole waves' tiles run
+    // whole and the rest are split in two along K, so the last wave takes
+    // half a tile-time.  8192 x 28672 at M = 1024 (896 tiles on 256 CUs,
+    // the fourth wave half full): 417-420 against 436-439 us.  Splitting
+    // every tile writes and re-reads partials for all of them (6% slower
+    // there), and a four-way split of a three-quarter-full last wave
+    // (M = 512) measured 4-5% slower than none.
+    const int64_t head = ftiles / cus * cus, tail = ftiles - head;
+    if (tail > 0 && 2 * tail <= cus) {
+      p.splits = 2;
+      p.head = (int)head;
+    }
+  }
+  if (ftiles - p.head > kMaxSplitTiles) {  // the counter header holds one per split tile
+    p.splits = 1;
+    p.head = 0;
+  }
   p.workspace_bytes = 0;
   if (p.splits > 1) {
-    p.workspace_bytes = kCounterHeaderBytes +
-                        (size_t)ftiles * p.splits * p.tm * p.tn * sizeof(float);
+    p.workspace_bytes = kCounterHeaderBytes + (size_t)(ftiles - p.head) * p.splits * p.tm *
+                                                  p.tn * sizeof(float);
   }
   return p;
 }

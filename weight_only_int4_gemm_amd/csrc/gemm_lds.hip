@@ -59,7 +59,8 @@ template <int MB, int NB, int WM, int WN, int NS, bool EPI, int FMT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     const _Float16* __restrict__ S, _Float16* __restrict__ C, int M, int K, int N,
-    uint64_t group_magic, int splits, unsigned* __restrict__ counters,
+    uint64_t group_magic, int tiles_n, int head, int tail_tiles, int splits,
+    unsigned* __restrict__ counters,
     float* __restrict__ partials, Epilogue ep, const uint8_t* __restrict__ Z) {
   static_assert(FMT == kFmtF16 || !EPI, "formats 1-5: no fused epilogue");
   constexpr bool ZP = Format<FMT>::kZp;
@@ -107,12 +108,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN;  // this wave's row block and column block
   const int wn = wave % WN;
-  const int tile_n = blockIdx.x;
-  const int tile_m = blockIdx.y;
-  const int split = blockIdx.z;
+  // Workgroup -> (tile, K range): the first `head` workgroups take whole
+  // tiles; the remaining tail_tiles tiles are split `splits` ways, split
+  // by split (all their first K ranges, then all their second, ...).
+  // Tiles are numbered with the column tile fastest.
+  const int b = blockIdx.x;
+  int tile = b, split = 0, nsplit = 1;
+  if (b >= head) {
+    const int j = b - head;
+    split = j / tail_tiles;
+    tile = head + (j - split * tail_tiles);
+    nsplit = splits;
+  }
+  const int tile_m = tile / tiles_n;
+  const int tile_n = tile - tile_m * tiles_n;
   const int KB = K / kBlockK;
-  const int kb0 = (int)((int64_t)KB * split / splits);
-  const int kb1 = (int)((int64_t)KB * (split + 1) / splits);
+  const int kb0 = (int)((int64_t)KB * split / nsplit);
+  const int kb1 = (int)((int64_t)KB * (split + 1) / nsplit);
   const int l16 = lane & 15;
   const int row0 = tile_m * TM;
   const int col0 = tile_n * TN;
@@ -358,9 +370,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, splits, counters,
-                                             partials, reinterpret_cast<int*>(&st0.s[0]), ep,
-                                             bias);
+  store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, nsplit,
+                                             tile - head, counters, partials,
+                                             reinterpret_cast<int*>(&st0.s[0]), ep, bias);
 }
 
 template <int MB, int NB, int WM, int WN, int NS, int FMT>
@@ -374,22 +386,26 @@ static hipError_t launch_lds_one(const Plan& p, const uint16_t* A, const uint32_
     counters = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterHeaderBytes);
   }
-  const dim3 grid(p.tiles_n, p.tiles_m, p.splits), block(64 * WM * WN);
+  const int tiles = p.tiles_n * p.tiles_m;
+  const int head = p.splits > 1 ? p.head : tiles;
+  const int tail = tiles - head;
+  const dim3 grid(head + tail * p.splits), block(64 * WM * WN);
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
   if constexpr (FMT == kFmtF16) {
     if (epilogue_needed(ep)) {
       hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, true, FMT>), grid, block, 0,
-                         stream, a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep,
-                         Z);
+                         stream, a, Bp, s, c, M, K, N, gmagic, p.tiles_n, head, tail, p.splits,
+                         counters, partials, ep, Z);
       return hipGetLastError();
     }
   } else {
     if (epilogue_needed(ep)) return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL((gemm_lds_kernel<MB, NB, WM, WN, NS, false, FMT>), grid, block, 0, stream,
-                     a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
+                     a, Bp, s, c, M, K, N, gmagic, p.tiles_n, head, tail, p.splits, counters,
+                     partials, ep, Z);
   return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@ struct Plan {
   int tile, mb, nb, wk, splits, depth, wm;
   int tm, tn;              // output tile of one workgroup
   int tiles_n, tiles_m;
+  int head;                // LDS kernel with splits > 1: tiles run whole before the
+                           // split ones (0: every tile is split)
   size_t workspace_bytes;  // 0 when splits == 1
 };
 

@@ -80,7 +80,8 @@ struct LaneBias4 {
 // matrix instruction's first operand): lane l has row l % 16 and columns
 // 4*(l/16) .. +3, stored as one 8-byte vector.
 //
-// With splits > 1: publish the partial tile with device-coherent stores,
+// With splits > 1 (slot: the tile's index among the split tiles, for its
+// counter and partials): publish the partial tile with device-coherent stores,
 // wait for them, count the arrival; the last workgroup of the tile adds the
 // partials in split order and writes C.  A partial is kept in fragment
 // order -- wave, 16-row block, 16-column block, lane, four values -- so each
@@ -92,6 +93,7 @@ template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
                                                   int wrow0, int wcol0, int split, int splits,
+                                                  int slot,
                                                   unsigned* __restrict__ counters,
                                                   float* __restrict__ partials, int* flag,
                                                   const Epilogue& ep,
@@ -123,9 +125,8 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
     return;
   }
 
-  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
   constexpr int TE = WAVES * MB * NB * 256;  // elements of the tile
-  const float* tile_base = partials + (int64_t)tile * splits * TE;
+  const float* tile_base = partials + (int64_t)slot * splits * TE;
   const int frag0 = wave * MB * NB * 64 + lane;
   {
     const __amdgpu_buffer_rsrc_t mine = coherent_rsrc(tile_base + (int64_t)split * TE);
@@ -138,7 +139,7 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev =
-        __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counters + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = prev == (unsigned)(splits - 1);
   }
   __syncthreads();
@@ -157,7 +158,7 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
   }
   write_c();
   if (threadIdx.x == 0)
-    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(counters + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 
