@@ -156,3 +156,19 @@ def test_forced_plan_without_stream_k():
     _, C64 = oracle.gemm(A, Bq, S, 128)
     say("tile -1", w4.w4a16_describe(M, 2048, 4096, 128))
     assert_gemm_close(run_gemm(A, Bq, S, 128), C64, "tile -1")
+
+
+@pytest.mark.parametrize("mb,nb,ns", VARIANTS)
+@pytest.mark.parametrize("M,K,N", [(20, 128, 16), (100, 256, 48), (9, 384, 528), (128, 640, 1040)])
+def test_sk_small_k_and_narrow_n(mb, nb, ns, M, K, N):
+    """K blocks fewer than the pipeline stages (all but one iteration of a
+    tile is padding), a single 16-column block, and N one block past a tile
+    boundary, on the default and a 3-workgroup grid."""
+    A, Bq, S = make_inputs(M, K, N, 128, seed=M + K + N)
+    _, C64 = oracle.gemm(A, Bq, S, 128)
+    for grid in (0, 3):
+        w4.w4a16_set_forced_plan(_plan(mb, ns, grid, nb))
+        desc = w4.w4a16_describe(M, K, N, 128)
+        assert desc.startswith(_name(mb, ns, nb)), desc
+        say("sk small", M, K, N, desc)
+        assert_gemm_close(run_gemm(A, Bq, S, 128), C64, desc)
