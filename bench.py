@@ -239,7 +239,7 @@ def _pmc_values(run_dir: str, counter: str):
     return out
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
+def pmc_summary(fetch_dir: str, write_dir: str, out_path: str, workload: str = "sweep") -> None:
     fetch = _pmc_values(fetch_dir, "FETCH_SIZE")
     write = _pmc_values(write_dir, "WRITE_SIZE")
 
@@ -271,14 +271,18 @@ def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
             "write_kib_per_dispatch": w,
             "hbm_bytes_per_dispatch": (f * (fetch_scale or 1) + w * (write_scale or 1)) * 1024,
         }
+    wflag = "" if workload == "sweep" else f" --workload {workload}"
     summary = {
-        "what": "HBM bytes per dispatch of each GEMM kernel of bench.py's default workload "
-                f"({WORKLOADS['sweep']['workload']}), from rocprofv3 FETCH_SIZE and WRITE_SIZE, "
+        "what": f"HBM bytes per dispatch of each GEMM kernel of bench.py's {workload} workload "
+                f"({WORKLOADS[workload]['workload']}), from rocprofv3 FETCH_SIZE and WRITE_SIZE, "
                 "each scaled by what the counter reads for a device copy of known size",
         "commands": [
-            f"rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py {PMC_RUN_FLAGS}",
-            f"rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py {PMC_RUN_FLAGS}",
-            "python3 bench.py --pmc-summary OUT/fetch OUT/write " + os.path.relpath(out_path, ROOT),
+            f"rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run -- python3 bench.py{wflag} "
+            f"{PMC_RUN_FLAGS}",
+            f"rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run -- python3 bench.py{wflag} "
+            f"{PMC_RUN_FLAGS}",
+            f"python3 bench.py{wflag} --pmc-summary OUT/fetch OUT/write "
+            + os.path.relpath(out_path, ROOT),
         ],
         "kernel_source_hash": kernel_source_hash(),
         "copy_probe": {"kernel": copy_name, "bytes": COPY_PROBE_BYTES,
@@ -292,7 +296,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, out_path: str) -> None:
     print(json.dumps(summary, indent=1))
 
 
-def trace_summary(stats_csv: str, out_path: str) -> None:
+def trace_summary(stats_csv: str, out_path: str, workload: str = "sweep") -> None:
     """A rocprofv3 --kernel-trace --stats kernel table as markdown: calls,
     average, min and max duration and share of GPU time per kernel."""
     import csv
@@ -302,9 +306,11 @@ def trace_summary(stats_csv: str, out_path: str) -> None:
             rows.append((_short_kernel_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]),
                          float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
     rows.sort(key=lambda r: -r[1] * r[2])
-    wl = WORKLOADS["sweep"]
+    wl = WORKLOADS[workload]
+    wflag = "" if workload == "sweep" else f" --workload {workload}"
     lines = [
-        "# Kernel trace: bench.py default workload",
+        "# Kernel trace: bench.py " + ("default workload" if workload == "sweep"
+                                       else f"{workload} workload"),
         "",
         f"Workload: {wl['workload']}.",
         "",
@@ -313,8 +319,8 @@ def trace_summary(stats_csv: str, out_path: str) -> None:
         "",
         "```",
         "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-        f"-d OUT/kt -o run -- python3 $REPO/bench.py {TRACE_RUN_FLAGS}",
-        "python3 bench.py --trace-summary OUT/kt/run_kernel_stats.csv "
+        f"-d OUT/kt -o run -- python3 $REPO/bench.py{wflag} {TRACE_RUN_FLAGS}",
+        f"python3 bench.py{wflag} --trace-summary OUT/kt/run_kernel_stats.csv "
         + os.path.relpath(out_path, ROOT),
         "```",
         "",
@@ -1229,10 +1235,10 @@ def _clocks_under_load(run_step, first_step: int, torch, seconds: float = 2.0) -
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, workload=args.workload)
         return
     if args.trace_summary:
-        trace_summary(*args.trace_summary)
+        trace_summary(*args.trace_summary, workload=args.workload)
         return
     if args.pmc_kernels:
         pmc_kernels(args.pmc_kernels[0], args.pmc_kernels[1:])
