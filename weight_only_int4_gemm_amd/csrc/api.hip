@@ -187,9 +187,10 @@ int describe_plan(int M, int K, int N, int group, int fmt, int cus, char* buf, s
   }
   else
     std::snprintf(buf, len,
-                  "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu",
+                  "gemm_kernel<%d,%d,%d,%d> grid=%dx%dx%d block=%d splits=%d workspace=%zu%s",
                   p.mb, p.nb, p.wk, p.depth, p.tiles_n, p.tiles_m, p.splits, 64 * p.wk,
-                  p.splits, p.workspace_bytes);
+                  p.splits, p.workspace_bytes,
+                  activations_lds_bytes(p, M, K, fmt) ? " activations=lds" : "");
   return W4A16_OK;
 }
 

@@ -31,6 +31,13 @@
 // per 16-row block and 32-deep step).  Loads run one step ahead of the
 // matrix instructions: the codes of the next K block and the activations of
 // the next 32-deep step are in flight while the current ones are consumed.
+//
+// Batches of at most kAldsMaxRows rows (ALDS): the workgroup first copies
+// rows 0..M-1 of A over its K range into LDS (at most kAldsMaxBytes), once,
+// while the first code loads are in flight, and each step reads its
+// activation fragment from there.  A wave then issues two loads per K block
+// and column block (codes and scale) instead of six, and a ring slot holds
+// no activations.  Llama-2-7B qkv at M = 1: 8.5 against 9.5 us.
 #include "coherent.hpp"
 #include "epilogue.hpp"
 #include "format.hpp"
@@ -83,7 +90,7 @@ struct Slot<MB, NB, false, false, true> {
 // (BF16 without zero points: the compiler's own choice for the deepest
 // variant kept one wave per SIMD; the hint asks for the two it gets in the
 // other formats.)
-template <int MB, int NB, int WK, int D, bool EPI, int FMT>
+template <int MB, int NB, int WK, int D, bool EPI, int FMT, bool ALDS = false>
 __global__ __launch_bounds__(64 * WK)
 __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
@@ -95,6 +102,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   constexpr bool W8 = Format<FMT>::kW8;
   constexpr bool SP = Format<FMT>::kSp;
   typedef Slot<MB, NB, ZP, W8, SP> SlotT;
+  static_assert(!ALDS || (MB == 1 && !SP), "activations in LDS: one row block, dense codes");
+  // ALDS: rows 0..M-1 of the row tile over this workgroup's K range, row
+  // after row, krange halfs each (the launch sizes it)
+  extern __shared__ uint4 a_lds[];
   constexpr int TM = 16 * MB;
   constexpr int TN = 16 * NB;
   constexpr int LDT = TN + 4;  // padded LDS row (floats), keeps 16-byte alignment
@@ -148,6 +159,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
     const int r = tile_m * TM + mb * 16 + l16;
     arow[mb] = A + (int64_t)(r < M ? r : M - 1) * K + lk;
   }
+  // ALDS: halfs per LDS row, and this lane's row in LDS (rows past M read
+  // the last row, as above)
+  const int krange = (kb1 - kb0) * kBlockK;
+  const int arow_l = tile_m * TM + l16 < M ? l16 : M - 1 - tile_m * TM;
   const uint32_t* bcol[NB];
   const _Float16* scol[NB];
   const uint8_t* zcol[NB];
@@ -200,13 +215,23 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
       sl.s[nb] = half2_t{sc, sc};
       if constexpr (ZP) sl.z[nb] = zcol[nb][srow];
     }
+    if constexpr (!ALDS) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sl.a[mb][j] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
+        for (int j = 0; j < 4; ++j)
+          sl.a[mb][j] = *reinterpret_cast<const half8_t*>(arow[mb] + kb * kBlockK + 32 * j);
+    }
   };
-  auto compute = [&](const SlotT& sl) {
+  // kbc: the K block the slot holds
+  auto compute = [&](const SlotT& sl, int kbc) {
+    half8_t al[4] = {};
+    if constexpr (ALDS) {
+      const _Float16* base = reinterpret_cast<const _Float16*>(a_lds) + arow_l * krange +
+                             (kbc - kb0) * kBlockK + lk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = *reinterpret_cast<const half8_t*>(base + 32 * j);
+    }
     if constexpr (SP) {
       // two 64-deep sparse steps; the accumulators hold C transposed
 #pragma unroll
@@ -239,7 +264,12 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
             b = unpack_col<FMT>(w, make_col<FMT>(sl.s[nb], z));
           }
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mma16<FMT>(sl.a[mb][j], b, acc[mb][nb]);
+          for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (ALDS)
+              acc[mb][nb] = mma16<FMT>(al[j], b, acc[mb][nb]);
+            else
+              acc[mb][nb] = mma16<FMT>(sl.a[mb][j], b, acc[mb][nb]);
+          }
         }
       }
     }
@@ -251,21 +281,38 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   // keeps every load unconditional.
   const int first = kb0 + wave;
   const int nblk = first < kb1 ? (kb1 - first + WK - 1) / WK : 0;
+  const int last = first + (nblk > 0 ? nblk - 1 : 0) * WK;
+  SlotT slot[D];
   if (nblk > 0) {
-    const int last = first + (nblk - 1) * WK;
-    SlotT slot[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int kb = first + u * WK;
       load(slot[u], kb < last ? kb : last);
     }
+  }
+  if constexpr (ALDS) {
+    // Rows 0..M-1 of this row tile over K blocks [kb0, kb1) into LDS, 16
+    // bytes per thread and step, after the first code loads so that they
+    // overlap.  Every wave takes part and meets the barrier, including
+    // waves without K blocks.
+    const int rows = M - tile_m * TM < TM ? M - tile_m * TM : TM;
+    const int ppr = krange / 8;  // pieces per row
+    const int pieces = rows * ppr;
+    for (int v = threadIdx.x; v < pieces; v += blockDim.x) {
+      const int r = v / ppr, c = v - r * ppr;
+      a_lds[v] = *reinterpret_cast<const uint4*>(A + (int64_t)(tile_m * TM + r) * K +
+                                                  kb0 * kBlockK + c * 8);
+    }
+    __syncthreads();
+  }
+  if (nblk > 0) {
     // Full rounds: straight-line code, so the wait before each slot's use
     // counts exactly the D - 1 slots of loads issued after it.
     int t = 0;
     for (; t + D <= nblk; t += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
-        compute(slot[u]);
+        compute(slot[u], first + (t + u) * WK);
         const int kb = first + (t + u + D) * WK;
         load(slot[u], kb < last ? kb : last);
       }
@@ -273,7 +320,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
     // The last, partial round: compute only.
 #pragma unroll
     for (int u = 0; u < D - 1; ++u) {
-      if (t + u < nblk) compute(slot[u]);
+      if (t + u < nblk) compute(slot[u], first + (t + u) * WK);
     }
   }
 
@@ -397,6 +444,14 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
     __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+size_t activations_lds_bytes(const Plan& p, int M, int K, int fmt) {
+  if (p.tile != 0 || p.mb != 1 || fmt == kFmtSp24 || M < 1 || M > kAldsMaxRows) return 0;
+  // M rows over the longest K range of a split (one row tile: M < 16)
+  const int KB = K / kBlockK;
+  const size_t bytes = (size_t)M * ((KB + p.splits - 1) / p.splits) * kBlockK * 2;
+  return bytes <= kAldsMaxBytes ? bytes : 0;
+}
+
 template <int MB, int NB, int WK, int D, int FMT>
 static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* Bp,
                              const uint16_t* S, uint16_t* C, int M, int K, int N,
@@ -412,14 +467,31 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
   auto a = reinterpret_cast<const _Float16*>(A);
   auto s = reinterpret_cast<const _Float16*>(S);
   auto c = reinterpret_cast<_Float16*>(C);
+  constexpr bool kAldsVariant = MB == 1 && FMT != kFmtSp24;
+  const size_t alds = kAldsVariant ? activations_lds_bytes(p, M, K, FMT) : 0;
   if constexpr (FMT == kFmtF16) {
     if (epilogue_needed(ep)) {
+      if constexpr (kAldsVariant) {
+        if (alds) {
+          hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, true, FMT, true>), grid, block, alds,
+                             stream, a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials,
+                             ep, Z);
+          return hipGetLastError();
+        }
+      }
       hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, true, FMT>), grid, block, 0, stream, a, Bp,
                          s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
       return hipGetLastError();
     }
   } else {
     if (epilogue_needed(ep)) return hipErrorInvalidValue;
+  }
+  if constexpr (kAldsVariant) {
+    if (alds) {
+      hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, false, FMT, true>), grid, block, alds, stream,
+                         a, Bp, s, c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((gemm_kernel<MB, NB, WK, D, false, FMT>), grid, block, 0, stream, a, Bp, s,
                      c, M, K, N, gmagic, p.splits, counters, partials, ep, Z);

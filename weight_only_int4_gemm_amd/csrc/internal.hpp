@@ -54,6 +54,14 @@ struct WeightFormat {
 };
 
 Plan make_plan(int M, int K, int N, int group, int cus, int fmt = 0);
+
+// The streaming kernel with activations in LDS (gemm.hip): batches of at
+// most kAldsMaxRows rows whose rows over one workgroup's K range take at
+// most kAldsMaxBytes.  activations_lds_bytes: the LDS the launch of plan p
+// gives them, 0 when the call reads its activations from global memory.
+constexpr int kAldsMaxRows = 4;
+constexpr size_t kAldsMaxBytes = 32768;
+size_t activations_lds_bytes(const Plan& p, int M, int K, int fmt);
 bool plan_is_compiled(int mb, int nb, int wk, int depth);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns);
