@@ -90,14 +90,15 @@ __device__ __forceinline__ ColParams make_col(half2_t s2, uint32_t z) {
 // The exact integers q - z of one word, as four FP16 pairs in B-operand
 // order: unpack_scale's steps with the subtrahends 1024 + z (codes at bits
 // 0..3) and 64 + z (codes at bits 4..7).
+template <bool VIS = false>
 __device__ __forceinline__ Half8 codes_minus_zero(uint32_t word, half2_t zlo, half2_t zhi) {
 #pragma clang fp contract(off)
   const uint32_t w8 = word >> 8;
   Half8 raw;
-  raw.u[0] = and_or(word, 0x000F000Fu, 0x64006400u);
-  raw.u[1] = and_or(word, 0x00F000F0u, 0x54005400u);
-  raw.u[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
-  raw.u[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
+  raw.u[0] = and_or<VIS>(word, 0x000F000Fu, 0x64006400u);
+  raw.u[1] = and_or<VIS>(word, 0x00F000F0u, 0x54005400u);
+  raw.u[2] = and_or<VIS>(w8, 0x000F000Fu, 0x64006400u);
+  raw.u[3] = and_or<VIS>(w8, 0x00F000F0u, 0x54005400u);
   Half8 d;
   d.h2[0] = raw.h2[0] - zlo;  // exact
   d.h2[1] = raw.h2[1] - zhi;
@@ -107,10 +108,11 @@ __device__ __forceinline__ Half8 codes_minus_zero(uint32_t word, half2_t zlo, ha
 }
 
 // FP16 with a zero point: (q - z) * s, one rounding.
+template <bool VIS = false>
 __device__ __forceinline__ half8_t unpack_scale_zp(uint32_t word, half2_t scale2, half2_t zlo,
                                                    half2_t zhi) {
 #pragma clang fp contract(off)
-  Half8 out = codes_minus_zero(word, zlo, zhi);
+  Half8 out = codes_minus_zero<VIS>(word, zlo, zhi);
 #pragma unroll
   for (int i = 0; i < 4; ++i) out.h2[i] = out.h2[i] * scale2;
   return out.v;
@@ -118,10 +120,11 @@ __device__ __forceinline__ half8_t unpack_scale_zp(uint32_t word, half2_t scale2
 
 // BF16: eight weights bf16_rne((q - z) * s) in the B-operand order of the
 // 16x16x32 BF16 matrix instruction (the same order as FP16), as raw bits.
+template <bool VIS = false>
 __device__ __forceinline__ half8_t unpack_scale_bf16(uint32_t word, float s, half2_t zlo,
                                                      half2_t zhi) {
 #pragma clang fp contract(off)
-  const Half8 d = codes_minus_zero(word, zlo, zhi);
+  const Half8 d = codes_minus_zero<VIS>(word, zlo, zhi);
   Half8 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -131,14 +134,16 @@ __device__ __forceinline__ half8_t unpack_scale_bf16(uint32_t word, float s, hal
   return out.v;
 }
 
-template <int FMT>
+// VIS: the AND-OR steps in the form the compiler's scheduling groups see
+// (and_or in unpack.hpp).
+template <int FMT, bool VIS = false>
 __device__ __forceinline__ half8_t unpack_col(uint32_t word, const ColParams& p) {
   if constexpr (FMT == kFmtF16 || FMT == kFmtSp24)
-    return unpack_scale(word, p.s2);
+    return unpack_scale<VIS>(word, p.s2);
   else if constexpr (FMT == kFmtF16Zp)
-    return unpack_scale_zp(word, p.s2, p.zlo, p.zhi);
+    return unpack_scale_zp<VIS>(word, p.s2, p.zlo, p.zhi);
   else
-    return unpack_scale_bf16(word, p.s, p.zlo, p.zhi);
+    return unpack_scale_bf16<VIS>(word, p.s, p.zlo, p.zhi);
 }
 
 // 8-bit codes: the eight FP16 weights (q - 128) * s of one 32-deep step

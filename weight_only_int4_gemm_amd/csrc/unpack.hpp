@@ -51,22 +51,36 @@ union Half8 {
 // (x & mask) | magic as one instruction.  Left to itself the compiler emits
 // an AND and an OR with literal operands (two issue slots); the three-operand
 // form needs both constants in registers, which it then keeps across the loop.
+// VIS = false writes the instruction out; the compiler's scheduling groups
+// do not count it as a vector instruction then.  VIS = true hands the
+// compiler the constants as opaque register values and the plain expression,
+// from which it forms the same instruction, visible to those groups (the
+// LDS kernel's interleaved schedule relies on that; the other kernels were
+// measured slower with it).
+template <bool VIS = false>
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
-  return r;
+  if constexpr (VIS) {
+    asm("" : "+v"(mask));
+    asm("" : "+v"(magic));
+    return (x & mask) | magic;
+  } else {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
+    return r;
+  }
 }
 
+template <bool VIS = false>
 __device__ __forceinline__ half8_t unpack_scale(uint32_t word, half2_t scale2) {
 #pragma clang fp contract(off)
   const half2_t bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
   const half2_t bias_hi = {(_Float16)72.0f, (_Float16)72.0f};      //   64 + 8
   const uint32_t w8 = word >> 8;
   Half8 raw;
-  raw.u[0] = and_or(word, 0x000F000Fu, 0x64006400u);  // codes 0, 1: 1024 + q
-  raw.u[1] = and_or(word, 0x00F000F0u, 0x54005400u);  // codes 2, 3:   64 + q
-  raw.u[2] = and_or(w8, 0x000F000Fu, 0x64006400u);    // codes 4, 5
-  raw.u[3] = and_or(w8, 0x00F000F0u, 0x54005400u);    // codes 6, 7
+  raw.u[0] = and_or<VIS>(word, 0x000F000Fu, 0x64006400u);  // codes 0, 1: 1024 + q
+  raw.u[1] = and_or<VIS>(word, 0x00F000F0u, 0x54005400u);  // codes 2, 3:   64 + q
+  raw.u[2] = and_or<VIS>(w8, 0x000F000Fu, 0x64006400u);    // codes 4, 5
+  raw.u[3] = and_or<VIS>(w8, 0x00F000F0u, 0x54005400u);    // codes 6, 7
   Half8 out;
   out.h2[0] = (raw.h2[0] - bias_lo) * scale2;  // exact subtraction, one rounding
   out.h2[1] = (raw.h2[1] - bias_hi) * scale2;
