@@ -308,10 +308,16 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
       p.wk = 4;
       p.depth = KB >= 64 && KB < 96 ? 4 : 2;
     }
-  } else if (M <= 32) {
+  } else if (M <= 32 && !(fmt != kFmtSp24 && M > 16 && KB >= 32 && KB <= 112 &&
+                           (N + 255) / 256 <= cus / 8)) {
     // LDS kernel with 16- or 32-row tiles and 256 columns (eight waves of
     // 16 or 32 x 32): one activation tile in LDS serves every wave, where
-    // the streaming kernel would have each wave load its own copy
+    // the streaming kernel would have each wave load its own copy.  (17 to
+    // 32 rows on narrow layers, 4096 <= K <= 14336, dense codes, take the
+    // 64 x 128 tiles below:
+    // 4096 x 4096 at M = 32 10.5 against 11.5 us, 5120 x 5120 11.8 against
+    // 13.1 us, 4096 x 8192 11.9 against 12.5 us, 11008 x 4096 15.9 against
+    // 16.4 us; 4096 x 12288 and wider keep these, 12.9 against 15.3 us.)
     p.tile = 2;
     p.mb = M <= 16 ? 1 : 2;
     p.nb = 2;
@@ -377,6 +383,10 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     want = (sparse && M > 32 && M <= 128 ? 2 : 1) * cus / tiles;
     while (want & (want - 1)) want &= want - 1;
     cap = KB / 4 < 8 ? KB / 4 : 8;
+    // 64 x 128 tiles: at least eight K blocks per split (K = 4096: four
+    // splits, 10.5-11.8 us against 11.3-14.4 us with eight, on 4096 x 4096,
+    // 4096 x 6144, 4096 x 8192 and 5120 x 5120 at M = 24..48)
+    if (!sparse && p.mb == 4 && p.nb == 1 && p.wm == 1 && KB / 8 < cap) cap = KB / 8;
   } else if (p.tile && sparse && M > 32 && M <= 128) {
     want = 1;
     cap = 1;
