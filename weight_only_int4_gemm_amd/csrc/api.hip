@@ -383,10 +383,12 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     want = (sparse && M > 32 && M <= 128 ? 2 : 1) * cus / tiles;
     while (want & (want - 1)) want &= want - 1;
     cap = KB / 4 < 8 ? KB / 4 : 8;
-    // 64 x 128 tiles: at least eight K blocks per split (K = 4096: four
-    // splits, 10.5-11.8 us against 11.3-14.4 us with eight, on 4096 x 4096,
-    // 4096 x 6144, 4096 x 8192 and 5120 x 5120 at M = 24..48)
-    if (!sparse && p.mb == 4 && p.nb == 1 && p.wm == 1 && KB / 8 < cap) cap = KB / 8;
+    // from K = 4096 on, at least eight K blocks per split (K = 4096: four
+    // splits, not eight).  64 x 128 tiles: 10.5-11.8 us against 11.3-14.4 us
+    // with eight splits on 4096 x 4096, 4096 x 6144, 4096 x 8192 and
+    // 5120 x 5120 at M = 24..48; 16-row tiles on 4096 x 8192 at M = 8 / 16:
+    // 10.6 / 10.8 against 11.2 us.
+    if (!sparse && KB >= 32 && KB / 8 < cap) cap = KB / 8;
   } else if (p.tile && sparse && M > 32 && M <= 128) {
     want = 1;
     cap = 1;
