@@ -308,16 +308,17 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
       p.wk = 4;
       p.depth = KB >= 64 && KB < 96 ? 4 : 2;
     }
-  } else if (M <= 32 && !(fmt != kFmtSp24 && M > 16 && KB >= 32 && KB <= 112 &&
+  } else if (M <= 32 && !(fmt != kFmtSp24 && M > 16 && KB >= 32 && KB <= 64 &&
                            (N + 255) / 256 <= cus / 8)) {
     // LDS kernel with 16- or 32-row tiles and 256 columns (eight waves of
     // 16 or 32 x 32): one activation tile in LDS serves every wave, where
     // the streaming kernel would have each wave load its own copy.  (17 to
-    // 32 rows on narrow layers, 4096 <= K <= 14336, dense codes, take the
-    // 64 x 128 tiles below:
-    // 4096 x 4096 at M = 32 10.5 against 11.5 us, 5120 x 5120 11.8 against
-    // 13.1 us, 4096 x 8192 11.9 against 12.5 us, 11008 x 4096 15.9 against
-    // 16.4 us; 4096 x 12288 and wider keep these, 12.9 against 15.3 us.)
+    // 32 rows on narrow layers, 4096 <= K <= 8192, dense codes, take the
+    // 64 x 128 tiles below: 4096 x 4096 at M = 32 10.5 against 11.5 us,
+    // 5120 x 5120 11.8 against 13.1 us, 4096 x 8192 11.9 against 12.5 us.
+    // 4096 x 12288 and wider keep these, 12.9 against 15.3 us; so does
+    // deeper K, where the choice went both ways: 11008 x 4096 15.5 against
+    // 16.4 us, but 13824 x 5120 20.3 against 18.1 us.)
     p.tile = 2;
     p.mb = M <= 16 ? 1 : 2;
     p.nb = 2;
