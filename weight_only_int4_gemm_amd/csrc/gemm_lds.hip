@@ -67,12 +67,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   constexpr bool SP = Format<FMT>::kSp;
   constexpr int BLOCK_PIECES = SP ? 48 : 64;     // 16-byte pieces of one code block
   constexpr int PPB = Format<FMT>::kW8 ? 2 : 1;  // 1 KiB pieces per code block and K block
-  // Wave tiles of 128 rows (4-bit dense codes): the step's matrix
-  // instructions, fragment reads and unpacking are interleaved one by one
-  // (see step below).  Prefill 8192 x 28672 at M = 512 / 1024 / 4096: 1.2 /
-  // 2.2 / 1.7% faster on one box.  The 64-row tiles measured up to 4% slower
-  // with it (Llama-2-7B gate/up at M = 128) and keep the compiler's order.
-  constexpr bool kSched = !Format<FMT>::kSp && PPB == 1 && MB >= 8;
+  // Wave tiles of 128 rows, FP16 weights: the step's matrix instructions,
+  // fragment reads and unpacking are interleaved one by one (see step
+  // below).  Prefill 8192 x 28672 at M = 512 / 1024 / 4096: 1.2 / 2.2 / 1.7%
+  // faster on one box.  The 64-row tiles measured up to 4% slower with it
+  // (Llama-2-7B gate/up at M = 128), and so did the zero-point and BF16
+  // formats, whose unpacking takes more instructions than the pattern
+  // places (prefill at M = 1024: 4-8%); they keep the compiler's order.
+  constexpr bool kSched = FMT == kFmtF16 && MB >= 8;
   constexpr int WAVES = WM * WN;
   constexpr int TM = 16 * MB * WM;
   constexpr int TN = 16 * NB * WN;

@@ -109,8 +109,10 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   // matrix instruction on gfx950, and these tiles have 1.6 unpacking
   // instructions per matrix instruction.  18432 x 73728 at M = 128: 2% faster
   // (three rounds, one box); the 64-row tile measured 2.6% slower with it,
-  // and the smaller tiles keep the compiler's order as well.
-  constexpr bool kSched = MB >= 8;
+  // and the smaller tiles keep the compiler's order as well.  FP16 weights
+  // only: the zero-point and BF16 unpacking takes more instructions than
+  // the pattern places (the same pattern cost the LDS kernel 4-8% there).
+  constexpr bool kSched = FMT == kFmtF16 && MB >= 8;
   constexpr int TM = 16 * MB;              // rows of the tile
   constexpr int TNW = 16 * NB;             // columns of one wave
   constexpr int TN = WN * TNW;             // columns of the tile
