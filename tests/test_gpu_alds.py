@@ -1,6 +1,6 @@
 """The streaming kernel with its activations staged in LDS (batches of at
-most four rows whose rows over one workgroup's K range fit in 32 KiB; the
-plan description then ends in ``activations=lds``).
+most four rows whose rows over one workgroup's K range fit in 32 KiB, FP16
+activations; the plan description then ends in ``activations=lds``).
 
 The staged path must give the oracle's answer within the GEMM bound, be exact
 on one-hot rows, and produce exactly the bits of the same kernel variant
@@ -118,13 +118,15 @@ def test_staged_one_hot_rows_exact(M, K, N):
 @pytest.mark.parametrize("dtype,zp", [(0, True), (1, False), (1, True)])
 @pytest.mark.parametrize("M,K,N", [(1, 3584, 208), (3, 1024, 80)])
 def test_staged_zero_point_and_bf16_formats(dtype, zp, M, K, N):
+    """FP16 with zero points stages its activations; the BF16 formats keep
+    the global path (measured faster for them).  Both match the oracle."""
     A, Bq, S, Z = make_inputs_awq(M, K, N, 128, seed=M + N + dtype, bf16=dtype == 1)
     Z = Z if zp else None
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     fmt = (2 if dtype else 0) + (1 if zp else 0)   # the w4a16_format number
     desc = w4.w4a16_plan_describe(M, K, N, 128, fmt, cus)
-    assert STAGED in desc, desc
+    assert (STAGED in desc) == (dtype == 0), desc
     say("staged awq", dtype, zp, M, K, N, desc)
     C = run_gemm_awq(A, Bq, S, Z, 128, dtype)
     _, C64 = oracle.gemm_awq(A, Bq, S, Z, 128, dtype)

@@ -57,7 +57,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt = 0);
 
 // The streaming kernel with activations in LDS (gemm.hip): batches of at
 // most kAldsMaxRows rows whose rows over one workgroup's K range take at
-// most kAldsMaxBytes.  activations_lds_bytes: the LDS the launch of plan p
+// most kAldsMaxBytes, in the FP16-activation formats (0, 1 and 4).  activations_lds_bytes: the LDS the launch of plan p
 // gives them, 0 when the call reads its activations from global memory.
 constexpr int kAldsMaxRows = 4;
 constexpr size_t kAldsMaxBytes = 32768;
