@@ -48,6 +48,57 @@ def test_stream_k_takes_9_to_128_rows_on_large_layers():
         assert not plan(M, 8192, 28672).startswith("gemm_sk_kernel<"), M
 
 
+def test_narrow_layers_17_to_32_rows_take_64_row_tiles():
+    """17 to 32 rows on narrow layers (at most cus/8 column tiles of 256,
+    4096 <= K <= 8192, dense codes): 64 x 128 tiles; wider layers, deeper K,
+    2:4 codes and 16 rows keep the 32 x 256 (16 x 256) tiles."""
+    for M in (17, 24, 32):
+        for K, N in ((4096, 4096), (4096, 6144), (4096, 8192), (5120, 5120), (8192, 4096)):
+            for fmt in (F16, F16ZP, BF16, BF16ZP, W8):
+                assert plan(M, K, N, fmt).startswith("gemm_lds_kernel<4,1,1,8,3>"), (M, K, N, fmt)
+        for K, N in ((4096, 12288), (4096, 22016), (11008, 4096), (13824, 5120), (2048, 4096)):
+            assert plan(M, K, N).startswith("gemm_lds_kernel<2,2,1,8,4>"), (M, K, N)
+        assert not plan(M, 4096, 4096, SP24).startswith("gemm_lds_kernel<4,1,1,8,3>"), M
+    assert plan(16, 4096, 8192).startswith("gemm_lds_kernel<1,2,1,8,4>")
+
+
+def test_few_tiles_keep_eight_k_blocks_per_split():
+    """With fewer tiles than compute units the LDS kernel splits K, but from
+    K = 4096 on into ranges of at least eight K blocks (deep K keeps the cap
+    of eight splits; below K = 4096 the old cap of K/512)."""
+    def splits(d):
+        return int(re.search(r"splits=(\d+)", d).group(1))
+    assert splits(plan(32, 4096, 4096)) == 4          # 32 tiles: 8 wanted, 32/8 allowed
+    assert splits(plan(48, 4096, 4096)) == 4
+    assert splits(plan(16, 4096, 8192)) == 4
+    assert splits(plan(16, 6144, 8192)) == 6
+    assert splits(plan(32, 11008, 4096)) == 8         # deep enough: eight
+    assert splits(plan(32, 28672, 8192)) == 8
+    assert splits(plan(16, 2048, 8192)) == 4          # below K = 4096: K/512
+    for M, K, N in ((32, 4096, 4096), (16, 4096, 8192), (16, 6144, 8192), (48, 5120, 5120)):
+        d = plan(M, K, N)
+        assert (K // 128) // splits(d) >= 8, (M, K, N, d)
+
+
+def test_activations_in_lds_rule():
+    """The streaming kernel stages its activations in LDS exactly when the
+    batch has at most four rows, those rows over a workgroup's K range fit in
+    32 KiB, and the activations are FP16 (formats 0, 1 and 4)."""
+    staged = "activations=lds"
+    for fmt in (F16, F16ZP, W8):
+        assert staged in plan(1, 4096, 12288, fmt)
+        assert staged in plan(4, 4096, 4096, fmt)           # 4 x 4096 x 2 = 32 KiB
+        assert staged not in plan(4, 4224, 4096, fmt)       # 33 KiB
+        assert staged not in plan(5, 4096, 4096, fmt)
+        assert staged in plan(2, 16384, 64, fmt)            # split K: 43 blocks per range
+    for fmt in (BF16, BF16ZP, SP24):
+        for M in (1, 2, 4):
+            assert staged not in plan(M, 4096, 12288, fmt), (M, fmt)
+    assert staged not in plan(1, 18432, 73728)              # 36 KiB per row
+    for M in (16, 128, 1024):                               # other kernels never
+        assert staged not in plan(M, 4096, 4096), M
+
+
 def test_lds_tail_split():
     """More tiles than compute units and a last wave at most half full:
     whole waves' tiles run whole, the rest are split in two along K."""
