@@ -32,7 +32,8 @@
 // matrix instructions: the codes of the next K block and the activations of
 // the next 32-deep step are in flight while the current ones are consumed.
 //
-// Batches of at most kAldsMaxRows rows (ALDS): the workgroup first copies
+// Batches of at most kAldsMaxRows rows with FP16 activations (ALDS; the
+// rule is activations_lds_bytes): the workgroup first copies
 // rows 0..M-1 of A over its K range into LDS (at most kAldsMaxBytes), once,
 // while the first code loads are in flight, and each step reads its
 // activation fragment from there.  A wave then issues two loads per K block
