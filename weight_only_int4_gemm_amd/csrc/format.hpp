@@ -134,6 +134,17 @@ __device__ __forceinline__ half8_t unpack_scale_bf16(uint32_t word, float s, hal
   return out.v;
 }
 
+// The FP16 formats 0 and 1 unscaled: the exact integers q - z of one word
+// (z = 8 for format 0), for kernels that apply the scale to FP32 sums.
+template <int FMT, bool VIS = false>
+__device__ __forceinline__ half8_t unpack_col_codes(uint32_t word, const ColParams& p) {
+  static_assert(FMT == kFmtF16 || FMT == kFmtF16Zp, "FP16 formats with 4-bit codes");
+  if constexpr (FMT == kFmtF16)
+    return codes_minus_eight<VIS>(word).v;
+  else
+    return codes_minus_zero<VIS>(word, p.zlo, p.zhi).v;
+}
+
 // VIS: the AND-OR steps in the form the compiler's scheduling groups see
 // (and_or in unpack.hpp).
 template <int FMT, bool VIS = false>

@@ -103,6 +103,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   constexpr bool W8 = Format<FMT>::kW8;
   constexpr bool SP = Format<FMT>::kSp;
   typedef Slot<MB, NB, ZP, W8, SP> SlotT;
+  // FP16 formats 0 and 1: the scale is applied to FP32 sums (see compute)
+  // wherever a second column block or a second wave per SIMD covers the
+  // wait for those sums.
+  constexpr bool kPostScale = (FMT == kFmtF16 || FMT == kFmtF16Zp) && (NB > 1 || WK > 4);
   static_assert(!ALDS || (MB == 1 && !SP), "activations in LDS: one row block, dense codes");
   // ALDS: rows 0..M-1 of the row tile over this workgroup's K range, row
   // after row, krange halfs each (the launch sizes it)
@@ -245,6 +249,50 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
           for (int mb = 0; mb < MB; ++mb)
             acc[mb][nb] = smma16(w, sl.a[mb][2 * t], sl.a[mb][2 * t + 1], pos, acc[mb][nb]);
         }
+      }
+    } else if constexpr (kPostScale) {
+      // One group scale per lane and K block (the lane's column), so
+      //   sum_k a_k * (q_k - z) * s = s * sum_k a_k * (q_k - z):
+      // the four matrix instructions of a (row block, column block) take
+      // the exact integers q - z, and their FP32 sum is scaled with one
+      // multiply-add.  That drops the 4 packed multiplies per word (13 ->
+      // 9 unpacking instructions) for 4 multiply-adds per 16 x 16 block:
+      // the vector work, not HBM, limited this kernel (the 18432 x 73728
+      // layer at M = 1..8: 4-6% faster; 28672 x 8192 and 4096 x 22016 at
+      // M = 1: 7%).  The products are exact and the weights are never
+      // rounded to FP16, so the result is the definition's up to FP32
+      // summation order, closer to the float64 product than the rounded
+      // weights are.  With one column block and one wave per SIMD the
+      // multiply-adds wait for the matrix unit (4096 x 4096 at M = 16:
+      // 7.2 against 7.0 us), and that variant keeps the scaled weights.
+      float4_t blk[MB][NB];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t w = j == 0 ? sl.b[nb].x : j == 1 ? sl.b[nb].y
+                           : j == 2 ? sl.b[nb].z : sl.b[nb].w;
+          uint32_t z = 8;
+          if constexpr (ZP) z = sl.z[nb];
+          const half8_t b = unpack_col_codes<FMT>(w, make_col<FMT>(sl.s[nb], z));
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const half8_t a = ALDS ? al[j] : sl.a[mb][j];
+            if (j == 0)
+              blk[mb][nb] = mma16<FMT>(a, b, float4_t{0.f, 0.f, 0.f, 0.f});
+            else
+              blk[mb][nb] = mma16<FMT>(a, b, blk[mb][nb]);
+          }
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float s = (float)sl.s[nb].x;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[mb][nb][i] = __builtin_fmaf(blk[mb][nb][i], s, acc[mb][nb][i]);
       }
     } else {
 #pragma unroll

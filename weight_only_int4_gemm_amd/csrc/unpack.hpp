@@ -31,8 +31,9 @@
 // used.)
 //
 // Cost: 5 bit operations, 4 packed subtractions and 4 packed multiplies per
-// eight weights.  This is the one routine both the GEMM and the
-// dequantisation check use.
+// eight weights.  The dequantisation check and the LDS and stream-K GEMM
+// kernels run all of it; the streaming GEMM kernel runs its bit operations
+// and subtractions (codes_minus_eight) and scales the FP32 sums instead.
 #pragma once
 
 #include <stdint.h>
@@ -70,8 +71,11 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t m
   }
 }
 
+// The exact integers q - 8 of one word as four FP16 pairs, unscaled: the
+// first two steps of unpack_scale.  The streaming GEMM kernel multiplies
+// these and applies the scale to the FP32 sums instead.
 template <bool VIS = false>
-__device__ __forceinline__ half8_t unpack_scale(uint32_t word, half2_t scale2) {
+__device__ __forceinline__ Half8 codes_minus_eight(uint32_t word) {
 #pragma clang fp contract(off)
   const half2_t bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
   const half2_t bias_hi = {(_Float16)72.0f, (_Float16)72.0f};      //   64 + 8
@@ -81,11 +85,20 @@ __device__ __forceinline__ half8_t unpack_scale(uint32_t word, half2_t scale2) {
   raw.u[1] = and_or<VIS>(word, 0x00F000F0u, 0x54005400u);  // codes 2, 3:   64 + q
   raw.u[2] = and_or<VIS>(w8, 0x000F000Fu, 0x64006400u);    // codes 4, 5
   raw.u[3] = and_or<VIS>(w8, 0x00F000F0u, 0x54005400u);    // codes 6, 7
-  Half8 out;
-  out.h2[0] = (raw.h2[0] - bias_lo) * scale2;  // exact subtraction, one rounding
-  out.h2[1] = (raw.h2[1] - bias_hi) * scale2;
-  out.h2[2] = (raw.h2[2] - bias_lo) * scale2;
-  out.h2[3] = (raw.h2[3] - bias_hi) * scale2;
+  Half8 d;
+  d.h2[0] = raw.h2[0] - bias_lo;  // exact subtraction
+  d.h2[1] = raw.h2[1] - bias_hi;
+  d.h2[2] = raw.h2[2] - bias_lo;
+  d.h2[3] = raw.h2[3] - bias_hi;
+  return d;
+}
+
+template <bool VIS = false>
+__device__ __forceinline__ half8_t unpack_scale(uint32_t word, half2_t scale2) {
+#pragma clang fp contract(off)
+  Half8 out = codes_minus_eight<VIS>(word);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out.h2[i] = out.h2[i] * scale2;  // one rounding
   return out.v;
 }
 
