@@ -189,3 +189,24 @@ def test_every_compiled_variant_is_one_a_plan_picks():
     missing = {key: sorted(v - compiled.get(key, set())) for key, v in seen.items()}
     missing = {k: v for k, v in missing.items() if v}
     assert not missing, f"planned but not compiled: {missing}"
+
+
+def test_five_to_eight_rows_stream_on_wide_layers_in_fp16():
+    """FP16 formats at M = 5..8 on layers with N >= 8192: the streaming
+    kernel, unsplit, 64-column tiles of four waves from 1536 column blocks
+    and 32-column tiles of eight waves below; the other formats keep the
+    LDS kernel there."""
+    for K, N, name in ((8192, 28672, "1,4,4,2"), (4096, 22016, "1,2,8,2"),
+                       (4096, 12288, "1,2,8,2"), (28672, 8192, "1,2,8,2"),
+                       (18432, 73728, "1,4,4,2")):
+        for M in (5, 8):
+            for fmt in (F16, F16ZP):
+                d = plan(M, K, N, fmt)
+                assert d.startswith(f"gemm_kernel<{name}>") and " splits=1 " in d, (K, N, M, d)
+        for fmt in (BF16, W8):
+            d = plan(8, K, N, fmt)
+            assert d.startswith("gemm_kernel<1,4,4,2>" if N == 73728 else "gemm_lds_kernel<"), d
+    # unchanged: four rows and fewer, nine rows and more, narrow layers
+    assert plan(4, 28672, 8192).startswith("gemm_kernel<1,2,8,2>") and " splits=3 " in plan(4, 28672, 8192)
+    assert plan(9, 4096, 12288).startswith("gemm_lds_kernel<")
+    assert plan(8, 13824, 5120).startswith("gemm_kernel<1,4,4,2>") and " splits=8 " in plan(8, 13824, 5120)

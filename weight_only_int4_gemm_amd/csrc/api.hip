@@ -287,7 +287,10 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
   const int n16 = N / kBlockN;
   const int KB = K / kBlockK;
   if (cus <= 0) cus = 256;
-  if (M <= 4 || (M <= 16 && N < 8192) || (M <= 8 && n16 >= 8 * cus)) {
+  // FP16 formats: the streaming kernel scales its FP32 sums, which makes it
+  // the faster one at five to eight rows on every wide layer too
+  const bool scaled_sums = fmt == kFmtF16 || fmt == kFmtF16Zp;
+  if (M <= 4 || (M <= 16 && N < 8192) || (M <= 8 && (n16 >= 8 * cus || scaled_sums))) {
     // streaming kernel: activations straight from global memory (up to
     // M = 8 on very wide layers too: 18432 x 73728 at M = 8 took 128 us
     // against 145 us in the LDS kernel; at M = 16 the LDS kernel is ahead)
@@ -302,6 +305,16 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
       // at M = 1 keeps eight waves of 32 columns, 14.1 against 14.7 us)
       p.nb = n16 >= 8 * cus ? 4 : (n16 >= 4 * cus || KB >= 96) ? 2 : 1;
       p.wk = p.nb != 2 && n16 / p.nb >= 2 * cus ? 4 : 8;
+      p.depth = 2;
+    } else if (N >= 8192 && n16 < 8 * cus) {
+      // five to eight rows, FP16 formats, wide layers: 64-column tiles of
+      // four waves from 1536 column blocks, else 32-column tiles of eight
+      // waves, unsplit.  Measured at M = 8 against the LDS kernel's 16-row
+      // tiles (graph replay, same box): 8192 x 28672 25.7 against 30.3 us,
+      // 4096 x 22016 12.9 against 16.2 us, 4096 x 12288 9.3 against
+      // 11.1 us, 28672 x 8192 27.5 against 30.5 us (three K ranges: 30.7).
+      p.nb = n16 >= 6 * cus ? 4 : 2;
+      p.wk = p.nb == 4 ? 4 : 8;
       p.depth = 2;
     } else {
       p.nb = n16 >= 2 * cus || KB >= 64 ? 4 : 1;
@@ -414,7 +427,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
     // 13824 x 5120: 1.2-1.25x over unsplit 16-column tiles)
     want = 3;
     cap = KB / (2 * p.wk);
-  } else if (M > 4 && KB >= 96 && tiles < 2 * (int64_t)cus) {
+  } else if (M > 4 && KB >= 96 && N < 8192 && tiles < 2 * (int64_t)cus) {
     // streaming, five to sixteen rows, deep K: eight K ranges per 64-column
     // tile (13824 x 5120: 1.3x over the default below)
     want = 8;
