@@ -1,13 +1,14 @@
-"""Which product each streaming variant computes, for the FP16 formats 0
-and 1.
+"""Which product each kernel variant computes, for the FP16 formats 0 and 1.
 
 The streaming kernel applies the group scale to the FP32 sum of each 128-deep
 block wherever another column block or a second wave per SIMD covers the
-wait for that sum (more than one column block, or eight waves): its result
-is then the product with the exact weights (q - z) * s, never rounded to
-FP16.  The variant with one column block and four waves scales each weight
-in FP16 first, as the oracle's definition does.  Both are within the GEMM
-bound of the oracle; this test shows which one a variant computes.
+wait for that sum (more than one column block, or eight waves), and so does
+the stream-K kernel with 16-row tiles: the result is then the product with
+the exact weights (q - z) * s, never rounded to FP16.  The streaming variant
+with one column block and four waves, and the stream-K tiles of 32 rows or
+more, scale each weight in FP16 first, as the oracle's definition does.
+Both are within the GEMM bound of the oracle; this test shows which one a
+variant computes.
 
 With K in the thousands the two products round to different FP16 outputs
 in about 40% of places, while FP32 accumulation moves an output across a
@@ -51,14 +52,21 @@ def _match(C, ref64):
     return float(np.mean(C.view(np.uint16) == ref64.astype(np.float16).view(np.uint16)))
 
 
-# mb, nb, wk, splits, depth; True where the scale is applied to the sums
-PLANS = [("1,2,8,1,2", True), ("1,4,4,1,2", True), ("1,1,8,1,2", True),
-         ("1,4,4,3,2", True), ("1,1,4,1,2", False), ("1,1,4,2,2", False)]
+# forced plan (mb, nb, wk, splits, depth[, tile]), the kernel it names, and
+# whether that kernel applies the scale to the sums
+PLANS = [("1,2,8,1,2", "gemm_kernel<1,2,8,2>", True),
+         ("1,4,4,1,2", "gemm_kernel<1,4,4,2>", True),
+         ("1,1,8,1,2", "gemm_kernel<1,1,8,2>", True),
+         ("1,4,4,3,2", "gemm_kernel<1,4,4,2>", True),
+         ("1,1,4,1,2", "gemm_kernel<1,1,4,2>", False),
+         ("1,1,4,2,2", "gemm_kernel<1,1,4,2>", False),
+         ("1,4,8,0,4,4", "gemm_sk_kernel<1,4,4,8>", True),
+         ("2,4,8,0,3,4", "gemm_sk_kernel<2,4,3,8>", False)]
 
 
-@pytest.mark.parametrize("plan,post", PLANS)
+@pytest.mark.parametrize("plan,kernel,post", PLANS)
 @pytest.mark.parametrize("zp", [False, True])
-def test_streaming_variant_product(plan, post, zp):
+def test_variant_product(plan, kernel, post, zp):
     M, K, N, group = 3, 4096, 512, 128
     if zp:
         A, Bq, S, Z = make_inputs_awq(M, K, N, group, seed=41)
@@ -67,8 +75,7 @@ def test_streaming_variant_product(plan, post, zp):
         Z = None
     w4.w4a16_set_forced_plan(plan)
     desc = w4.w4a16_describe(M, K, N, group)
-    mb, nb, wk, splits, depth = (int(x) for x in plan.split(","))
-    assert desc.startswith(f"gemm_kernel<{mb},{nb},{wk},{depth}>"), desc
+    assert desc.startswith(kernel + " "), desc
     say("post-scale", plan, "zp" if zp else "f16", desc)
     C = run_gemm_awq(A, Bq, S, Z, group, 0) if zp else run_gemm(A, Bq, S, group)
 

@@ -113,6 +113,12 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   // only: the zero-point and BF16 unpacking takes more instructions than
   // the pattern places (the same pattern cost the LDS kernel 4-8% there).
   constexpr bool kSched = FMT == kFmtF16 && MB >= 8;
+  // One 16-row block, FP16 formats (kPost): the matrix instructions take the
+  // exact integers q - z, with the activations as their first operand (a
+  // lane's four sums are then four rows of its own column), and each K
+  // block's FP32 sums are scaled with one multiply-add per sum: 9 unpacking
+  // instructions per code word instead of 13.
+  constexpr bool kPost = MB == 1 && (FMT == kFmtF16 || FMT == kFmtF16Zp);
   constexpr int TM = 16 * MB;              // rows of the tile
   constexpr int TNW = 16 * NB;             // columns of one wave
   constexpr int TN = WN * TNW;             // columns of the tile
@@ -272,6 +278,8 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 
   // ---- per-wave registers ----
   float4_t acc[MB][NB];  // set by the first slice of every tile segment
+  float4_t blk[kPost ? NB : 1];     // kPost: the current K block's sums
+  half2_t s_blk[kPost ? NB : 1];    // kPost: its scales
   half8_t af[2][MB];  // activation fragments, two slices
   half8_t bf[2][NB];  // unpacked weights, two slices
   uint4 cw[NB];       // this K block's code words (one per slice)
@@ -327,10 +335,18 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const uint32_t w = j == 0 ? cw[nb].x : j == 1 ? cw[nb].y : j == 2 ? cw[nb].z : cw[nb].w;
-      b[nb] = unpack_col<FMT, kSched>(w, cp[nb]);
+      if constexpr (kPost)
+        b[nb] = unpack_col_codes<FMT>(w, cp[nb]);
+      else
+        b[nb] = unpack_col<FMT, kSched>(w, cp[nb]);
     }
   };
   auto mma = [&](const half8_t* a, const half8_t* b) {
+    if constexpr (kPost) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) blk[nb] = mma16<FMT>(a[0], b[nb], blk[nb]);
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -340,6 +356,11 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   // the first slice of a tile segment: the sums start from zero (an inline
   // constant operand, so no register is ever cleared)
   auto mma_first = [&](const half8_t* a, const half8_t* b) {
+    if constexpr (kPost) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) blk[nb] = mma16<FMT>(a[0], b[nb], float4_t{0.f, 0.f, 0.f, 0.f});
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -366,6 +387,28 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
       }
     }
     auto write_c = [&](int mb, int nb, const float4_t& x) {
+      if constexpr (kPost) {
+        // rows 4 (l / 16) .. +3 of column 16 nb + l % 16
+        const int gc = col0 + nb * 16 + l16;
+        if (gc >= N) return;
+        float bias = 0.f;
+        if constexpr (EPI) {
+          if (ep.bias) bias = (float)ep.bias[gc];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gr = row0 + (lane >> 4) * 4 + e;
+          if (gr < M) {
+            _Float16 h;
+            if constexpr (EPI)
+              h = (_Float16)epilogue_apply(ep, x[e], bias);
+            else
+              h = out16<FMT>(x[e]);
+            C[(int64_t)gr * N + gc] = h;
+          }
+        }
+        return;
+      }
       const int gr = row0 + mb * 16 + l16;
       const int gc = col0 + nb * 16 + (lane >> 4) * 4;  // N % 16 == 0: all four or none
       if (gr < M && gc < N) {
@@ -490,7 +533,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   auto step = [&](Stage& cur, Stage& nxt, bool pad_next, auto first, auto read_next) {
     read_a(cur, 1, af[1]);
     unpack(1, bf[1]);
-    if constexpr (decltype(first)::value)
+    if constexpr (decltype(first)::value || kPost)  // kPost: every K block's sums start at zero
       mma_first(af[0], bf[0]);
     else
       mma(af[0], bf[0]);
@@ -504,6 +547,10 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     mma(af[0], bf[0]);
     slice_order(std::integral_constant<int, 3>());
     stage_barrier<(NS - 2) * LOADS>();
+    if constexpr (kPost) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s_blk[nb] = cp[nb].s2;  // before the next block's
+    }
     if constexpr (decltype(read_next)::value) {
       read_codes(nxt, pad_next);
       read_a(nxt, 0, af[0]);
@@ -511,6 +558,18 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     load_stage(cur);
     mma(af[1], bf[1]);
     if constexpr (decltype(read_next)::value) unpack(0, bf[0]);
+    if constexpr (kPost) {
+      // the block's sums into the tile's, scaled (the next block's
+      // unpacking above covers the matrix unit's latency)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float s = (float)s_blk[nb][0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[0][nb][e] = decltype(first)::value ? blk[nb][e] * s
+                                                 : __builtin_fmaf(blk[nb][e], s, acc[0][nb][e]);
+      }
+    }
     if constexpr (kSched) {
       // after the barrier: the next block's code and scale reads first, then
       // per matrix instruction one fragment read, one direct load and the
