@@ -47,6 +47,9 @@
 // The weights are the matrix instruction's first operand and the
 // activations its second, so a lane's four accumulators are four
 // consecutive output columns of one row: each lane stores 8 bytes of FP16.
+// The 16-row tiles of the FP16 formats swap the operands and scale each K
+// block's sums instead of the weights (kPost below): a lane's four sums are
+// then four rows of its own column, stored as four 2-byte values.
 #pragma once
 
 #include <type_traits>
