@@ -447,7 +447,10 @@ def measured_ceilings(torch, dev):
             ts.append(e0.elapsed_time(e1) / 1e3)
         return float(np.median(ts))
 
-    read_blocks = 256 * 8
+    # Short-lived workgroups read fastest in this grid-stride form (one box,
+    # 2 GiB: 6.2 TB/s with 1024 or 2048 workgroups of 512, 6.6 with 4096,
+    # 7.0 with 8192): 8192 of them, four rounds of eight loads per thread.
+    read_blocks = 256 * 32
     t_read = timed(lambda: lib.w4a16_probe_read(buf.data_ptr(), PROBE_READ_BYTES,
                                                 sink.data_ptr(), read_blocks, sh))
     del buf
@@ -462,7 +465,7 @@ def measured_ceilings(torch, dev):
         "hbm_read_frac_of_peak": read_gbps / (roofline.HBM_PEAK_BYTES_PER_S / 1e9),
         "mfma_f16_tflops": mfma_tflops,
         "mfma_frac_of_peak": mfma_tflops / (roofline.MFMA_F16_PEAK_FLOPS / 1e12),
-        "probe": "2 GiB read once with 16-byte non-temporal loads (2048 workgroups of 512); "
+        "probe": "2 GiB read once with 16-byte non-temporal loads (8192 workgroups of 512); "
                  f"{PROBE_MFMA_ITERS} rounds of 16 independent v_mfma_f32_16x16x32_f16 per wave, "
                  f"{PROBE_MFMA_BLOCKS} workgroups of 4 waves; median of 5 launches each",
     }
