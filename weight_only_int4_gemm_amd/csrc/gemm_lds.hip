@@ -34,7 +34,10 @@
 // With 16 x 16 blocks the weights are the matrix instruction's first
 // operand and the activations its second, so a lane's four accumulators are
 // four consecutive output columns of one row and the output stage stores
-// 8 bytes per lane and block (tile_common.hpp).
+// 8 bytes per lane and block (tile_common.hpp).  The 16-row tiles of the
+// FP16 formats swap the operands and scale each K block's sums instead of
+// the weights (kPost below): a lane's four sums are four rows of its own
+// column.
 //
 // 2:4-sparse weights (format 5): a code block is 768 bytes (layout.hpp),
 // brought in by one 16-byte direct load on lanes 0..47; a wave reads its
@@ -75,6 +78,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // formats, whose unpacking takes more instructions than the pattern
   // places (prefill at M = 1024: 4-8%); they keep the compiler's order.
   constexpr bool kSched = FMT == kFmtF16 && MB >= 8;
+  // One 16-row block, FP16 formats with 4-bit codes (kPost): the matrix
+  // instructions take the exact integers q - z with the activations as their
+  // first operand (a lane's four sums are four rows of its own column), and
+  // each K block's FP32 sums are scaled with one multiply-add per sum
+  // instead of every weight: 9 unpacking instructions per code word, not 13.
+  constexpr bool kPost = MB == 1 && !SP && PPB == 1 && (FMT == kFmtF16 || FMT == kFmtF16Zp);
   constexpr int WAVES = WM * WN;
   constexpr int TM = 16 * MB * WM;
   constexpr int TN = 16 * NB * WN;
@@ -217,6 +226,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   };
 
   float4_t acc[MB][NB];
+  float4_t blk[kPost ? NB : 1];  // kPost: the current K block's sums
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -260,7 +270,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
         } else {
           const uint32_t word =
               j == 0 ? w[nb].x : j == 1 ? w[nb].y : j == 2 ? w[nb].z : w[nb].w;
-          bf[nb] = unpack_col<FMT, kSched>(word, cp[nb]);
+          if constexpr (kPost)
+            bf[nb] = unpack_col_codes<FMT>(word, cp[nb]);
+          else
+            bf[nb] = unpack_col<FMT, kSched>(word, cp[nb]);
         }
       }
     };
@@ -278,12 +291,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
         read_a(sg, j + 1, nxt);
         unpack_slice(j + 1, bnxt);
       }
+      if constexpr (kPost) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int nb = 0; nb < NB; ++nb)
+          blk[nb] = mma16<FMT>(cur[0], bcur[nb], j == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : blk[nb]);
+      } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          acc[mb][nb] = mma16<FMT>(bcur[nb], cur[mb], acc[mb][nb]);
-        }
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            acc[mb][nb] = mma16<FMT>(bcur[nb], cur[mb], acc[mb][nb]);
+          }
+      }
+    }
+    if constexpr (kPost) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float s = (float)cp[nb].s2[0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[0][nb][e] = __builtin_fmaf(blk[nb][e], s, acc[0][nb][e]);
+      }
     }
   };
 
@@ -400,7 +427,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // below or the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0);
 
-  store_output_tile<MB, NB, WAVES, EPI, FMT>(acc, C, M, N, wrow0, wcol0, split, nsplit,
+  store_output_tile<MB, NB, WAVES, EPI, FMT, kPost>(acc, C, M, N, wrow0, wcol0, split, nsplit,
                                              tile - head, counters, partials,
                                              reinterpret_cast<int*>(&st0.s[0]), ep, bias);
 }

@@ -86,10 +86,13 @@ struct LaneBias4 {
 // partials in split order and writes C.  A partial is kept in fragment
 // order -- wave, 16-row block, 16-column block, lane, four values -- so each
 // lane moves its four accumulators in one 16-byte access and the workgroup
-// that sums finds its own fragments at the same places.  `flag` is an int in
+// that sums finds its own fragments at the same places.  With COLS the
+// blocks are not transposed (the activations were the first operand): lane
+// l has rows 4*(l/16) .. +3 of column l % 16, stored as four 2-byte values.
+// `flag` is an int in
 // LDS no wave touches any more.  The epilogue is applied to the final sums
 // only; FMT sets the output type (FP16, or BF16 for formats 2 and 3).
-template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16>
+template <int MB, int NB, int WAVES, bool EPI, int FMT = kFmtF16, bool COLS = false>
 __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
                                                   _Float16* __restrict__ C, int M, int N,
                                                   int wrow0, int wcol0, int split, int splits,
@@ -101,6 +104,23 @@ __device__ __forceinline__ void store_output_tile(float4_t (&acc)[MB][NB],
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   auto write_c = [&]() {
+    if constexpr (COLS) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int gc = wcol0 + nb * 16 + (lane & 15);
+        if (gc >= N) continue;
+        const float b = (EPI && ep.bias) ? (float)ep.bias[gc] : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int gr = wrow0 + mb * 16 + (lane >> 4) * 4 + e;
+            const float x = acc[mb][nb][e];
+            if (gr < M) C[(int64_t)gr * N + gc] = out16<FMT>(EPI ? epilogue_apply(ep, x, b) : x);
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int gr = wrow0 + mb * 16 + (lane & 15);
