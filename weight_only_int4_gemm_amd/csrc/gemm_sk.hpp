@@ -47,7 +47,7 @@
 // The weights are the matrix instruction's first operand and the
 // activations its second, so a lane's four accumulators are four
 // consecutive output columns of one row: each lane stores 8 bytes of FP16.
-// The 16-row tiles of the FP16 formats swap the operands and scale each K
+// The 16- and 32-row tiles of the FP16 formats swap the operands and scale each K
 // block's sums instead of the weights (kPost below): a lane's four sums are
 // then four rows of its own column, stored as four 2-byte values.
 #pragma once
@@ -116,12 +116,12 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   // only: the zero-point and BF16 unpacking takes more instructions than
   // the pattern places (the same pattern cost the LDS kernel 4-8% there).
   constexpr bool kSched = FMT == kFmtF16 && MB >= 8;
-  // One 16-row block, FP16 formats (kPost): the matrix instructions take the
+  // One or two 16-row blocks, FP16 formats (kPost): the matrix instructions take the
   // exact integers q - z, with the activations as their first operand (a
   // lane's four sums are then four rows of its own column), and each K
   // block's FP32 sums are scaled with one multiply-add per sum: 9 unpacking
   // instructions per code word instead of 13.
-  constexpr bool kPost = MB == 1 && (FMT == kFmtF16 || FMT == kFmtF16Zp);
+  constexpr bool kPost = MB <= 2 && (FMT == kFmtF16 || FMT == kFmtF16Zp);
   constexpr int TM = 16 * MB;              // rows of the tile
   constexpr int TNW = 16 * NB;             // columns of one wave
   constexpr int TN = WN * TNW;             // columns of the tile
@@ -281,7 +281,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
 
   // ---- per-wave registers ----
   float4_t acc[MB][NB];  // set by the first slice of every tile segment
-  float4_t blk[kPost ? NB : 1];     // kPost: the current K block's sums
+  float4_t blk[kPost ? MB : 1][kPost ? NB : 1];  // kPost: the current K block's sums
   half2_t s_blk[kPost ? NB : 1];    // kPost: its scales
   half8_t af[2][MB];  // activation fragments, two slices
   half8_t bf[2][NB];  // unpacked weights, two slices
@@ -347,7 +347,9 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   auto mma = [&](const half8_t* a, const half8_t* b) {
     if constexpr (kPost) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) blk[nb] = mma16<FMT>(a[0], b[nb], blk[nb]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) blk[mb][nb] = mma16<FMT>(a[mb], b[nb], blk[mb][nb]);
       return;
     }
 #pragma unroll
@@ -361,7 +363,10 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
   auto mma_first = [&](const half8_t* a, const half8_t* b) {
     if constexpr (kPost) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) blk[nb] = mma16<FMT>(a[0], b[nb], float4_t{0.f, 0.f, 0.f, 0.f});
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          blk[mb][nb] = mma16<FMT>(a[mb], b[nb], float4_t{0.f, 0.f, 0.f, 0.f});
       return;
     }
 #pragma unroll
@@ -391,7 +396,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
     }
     auto write_c = [&](int mb, int nb, const float4_t& x) {
       if constexpr (kPost) {
-        // rows 4 (l / 16) .. +3 of column 16 nb + l % 16
+        // rows 16 mb + 4 (l / 16) .. +3 of column 16 nb + l % 16
         const int gc = col0 + nb * 16 + l16;
         if (gc >= N) return;
         float bias = 0.f;
@@ -400,7 +405,7 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int gr = row0 + (lane >> 4) * 4 + e;
+          const int gr = row0 + mb * 16 + (lane >> 4) * 4 + e;
           if (gr < M) {
             _Float16 h;
             if constexpr (EPI)
@@ -568,9 +573,12 @@ gemm_sk_kernel(const _Float16* __restrict__ A, const uint32_t* __restrict__ Bp,
       for (int nb = 0; nb < NB; ++nb) {
         const float s = (float)s_blk[nb][0];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[0][nb][e] = decltype(first)::value ? blk[nb][e] * s
-                                                 : __builtin_fmaf(blk[nb][e], s, acc[0][nb][e]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[mb][nb][e] = decltype(first)::value
+                                 ? blk[mb][nb][e] * s
+                                 : __builtin_fmaf(blk[mb][nb][e], s, acc[mb][nb][e]);
       }
     }
     if constexpr (kSched) {
