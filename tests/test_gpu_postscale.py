@@ -3,8 +3,7 @@
 The streaming kernel applies the group scale to the FP32 sum of each 128-deep
 block wherever another column block or a second wave per SIMD covers the
 wait for that sum (more than one column block, or eight waves), and so does
-the stream-K kernel with 16- and 32-row tiles and the LDS kernel with
-16-row tiles: the result is then the product with the exact weights
+the stream-K and LDS kernels with 16- and 32-row tiles: the result is then the product with the exact weights
 (q - z) * s, never rounded to FP16.  The streaming variant with one column
 block and four waves, and the larger tiles, scale each weight in FP16 first,
 as the oracle's definition does.
@@ -66,6 +65,7 @@ PLANS = [("1,2,8,1,2", "gemm_kernel<1,2,8,2>", True),
          ("4,4,8,0,3,4", "gemm_sk_kernel<4,4,3,8>", False),
          ("1,2,8,1,4,2", "gemm_lds_kernel<1,2,1,8,4>", True),
          ("1,2,8,4,4,2", "gemm_lds_kernel<1,2,1,8,4>", True),
+         ("2,2,8,1,4,2", "gemm_lds_kernel<2,2,1,8,4>", True),
          ("4,1,8,1,3,2", "gemm_lds_kernel<4,1,1,8,3>", False)]
 
 

@@ -34,8 +34,8 @@
 // With 16 x 16 blocks the weights are the matrix instruction's first
 // operand and the activations its second, so a lane's four accumulators are
 // four consecutive output columns of one row and the output stage stores
-// 8 bytes per lane and block (tile_common.hpp).  The 16-row tiles of the
-// FP16 formats swap the operands and scale each K block's sums instead of
+// 8 bytes per lane and block (tile_common.hpp).  The 16- and 32-row tiles of
+// the FP16 formats swap the operands and scale each K block's sums instead of
 // the weights (kPost below): a lane's four sums are four rows of its own
 // column.
 //
@@ -78,12 +78,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   // formats, whose unpacking takes more instructions than the pattern
   // places (prefill at M = 1024: 4-8%); they keep the compiler's order.
   constexpr bool kSched = FMT == kFmtF16 && MB >= 8;
-  // One 16-row block, FP16 formats with 4-bit codes (kPost): the matrix
+  // One or two 16-row blocks, FP16 formats with 4-bit codes (kPost): the matrix
   // instructions take the exact integers q - z with the activations as their
   // first operand (a lane's four sums are four rows of its own column), and
   // each K block's FP32 sums are scaled with one multiply-add per sum
   // instead of every weight: 9 unpacking instructions per code word, not 13.
-  constexpr bool kPost = MB == 1 && !SP && PPB == 1 && (FMT == kFmtF16 || FMT == kFmtF16Zp);
+  constexpr bool kPost = MB <= 2 && !SP && PPB == 1 && (FMT == kFmtF16 || FMT == kFmtF16Zp);
   constexpr int WAVES = WM * WN;
   constexpr int TM = 16 * MB * WM;
   constexpr int TN = 16 * NB * WN;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
   };
 
   float4_t acc[MB][NB];
-  float4_t blk[kPost ? NB : 1];  // kPost: the current K block's sums
+  float4_t blk[kPost ? MB : 1][kPost ? NB : 1];  // kPost: the current K block's sums
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -293,8 +293,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
       }
       if constexpr (kPost) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          blk[nb] = mma16<FMT>(cur[0], bcur[nb], j == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : blk[nb]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            blk[mb][nb] = mma16<FMT>(cur[mb], bcur[nb],
+                                     j == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : blk[mb][nb]);
       } else {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -309,7 +312,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(
       for (int nb = 0; nb < NB; ++nb) {
         const float s = (float)cp[nb].s2[0];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[0][nb][e] = __builtin_fmaf(blk[nb][e], s, acc[0][nb][e]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[mb][nb][e] = __builtin_fmaf(blk[mb][nb][e], s, acc[mb][nb][e]);
       }
     }
   };

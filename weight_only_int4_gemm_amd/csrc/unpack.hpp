@@ -31,9 +31,9 @@
 // used.)
 //
 // Cost: 5 bit operations, 4 packed subtractions and 4 packed multiplies per
-// eight weights.  The dequantisation check and the larger GEMM tiles run
-// all of it; the streaming kernel, the 16- and 32-row stream-K tiles and the
-// 16-row LDS tiles run its bit operations and subtractions
+// eight weights.  The dequantisation check and the GEMM tiles of 64 rows
+// or more run all of it; the streaming kernel and the 16- and 32-row tiles
+// of the stream-K and LDS kernels run its bit operations and subtractions
 // (codes_minus_eight) and scale the FP32 sums instead.
 #pragma once
 
