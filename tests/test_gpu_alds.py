@@ -61,7 +61,7 @@ def test_staged_activations_match_oracle(M, K, N, group, staged):
 # splits' K ranges differ in length (K = 3584: 28 K blocks) and some waves
 # own no K block (seven splits of four blocks for four waves; five splits of
 # five or six blocks for eight waves).
-STAGED_PLANS = ["1,1,4,1,2", "1,1,4,7,2", "1,1,8,1,2", "1,1,8,5,2", "1,2,8,1,2", "1,2,8,4,2",
+STAGED_PLANS = ["1,4,4,7,2", "1,1,8,1,2", "1,1,8,5,2", "1,2,8,1,2", "1,2,8,4,2",
                 "1,4,4,1,2", "1,4,4,3,2", "1,4,4,1,4", "1,4,4,6,4"]
 
 
@@ -148,7 +148,7 @@ def test_staged_eight_bit_weights(M, K, N):
     assert_gemm_close(C, C64, f"w8 M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("plan", [None, "1,1,4,7,2", "1,4,4,3,4"])
+@pytest.mark.parametrize("plan", [None, "1,1,8,7,2", "1,4,4,3,4"])
 @pytest.mark.parametrize("act", [w4.W4A16_ACT_NONE, w4.W4A16_ACT_SILU])
 def test_staged_fused_epilogue(plan, act):
     M, K, N, group = 3, 3584, 208, 128

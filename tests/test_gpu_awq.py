@@ -102,10 +102,10 @@ def test_awq_dequant_exhaustive_codes_zero_points_scales(fmt, dtype, zp):
 # (M, K, N, the plan's kernel and template arguments as w4a16_describe prints them)
 AWQ_CASES = [
     (1, 4096, 4096, "gemm_kernel<1,1,8,2>"),
-    (1, 4096, 12288, "gemm_kernel<1,1,4,2>"),
+    (1, 4096, 12288, "gemm_kernel<1,1,8,2>"),
     (1, 4096, 22016, "gemm_kernel<1,2,8,2>"),
     (1, 2048, 36864, "gemm_kernel<1,4,4,2>"),
-    (8, 1024, 1024, "gemm_kernel<1,1,4,2>"),
+    (8, 1024, 1024, "gemm_kernel<1,2,8,2>"),
     (8, 11008, 1024, "gemm_kernel<1,4,4,4>"),
     (8, 13824, 512, "gemm_kernel<1,4,4,2>"),
     (16, 1024, 8192, "gemm_lds_kernel<1,2,1,8,4>"),
@@ -136,7 +136,7 @@ def test_awq_gemm_matches_oracle(fmt, dtype, zp, M, K, N, kernel):
 
 
 @pytest.mark.parametrize("fmt,dtype,zp", FORMATS)
-@pytest.mark.parametrize("plan", ["1,4,4,5,4", "1,2,8,3,2", "1,1,4,2,2", "1,2,8,4,4,2",
+@pytest.mark.parametrize("plan", ["1,4,4,5,4", "1,2,8,3,2", "1,1,8,2,2", "1,2,8,4,4,2",
                                   "2,2,8,2,4,2", "4,1,8,3,3,2", "4,2,4,2,3,2,0,2",
                                   "8,2,8,2,3,2", "1,4,8,5,4,4", "2,4,8,4,3,4", "4,4,8,3,3,4"])
 def test_awq_forced_plans_split_k(monkeypatch, fmt, dtype, zp, plan):

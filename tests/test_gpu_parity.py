@@ -145,7 +145,7 @@ def test_gemm_matches_oracle(M, K, N, group):
 # Every compiled variant, with and without K splits (fields: mb, nb, wk,
 # splits, depth[, tile, unused, wm]; tile 0 the streaming kernel, 2 the LDS
 # kernel, whose eighth field is the number of waves along M).
-STREAM_PLANS = ["1,1,4,1,2", "1,1,4,3,2", "1,1,8,1,2", "1,1,8,5,2", "1,2,8,1,2", "1,2,8,4,2",
+STREAM_PLANS = ["1,1,8,1,2", "1,1,8,3,2", "1,1,8,5,2", "1,2,8,1,2", "1,2,8,4,2",
                 "1,4,4,1,2", "1,4,4,7,2", "1,4,4,1,4", "1,4,4,2,4"]
 LDS_PLANS = ["1,2,8,1,4,2", "1,2,8,4,4,2", "2,2,8,1,4,2", "2,2,8,8,4,2", "4,1,8,1,3,2",
              "4,1,8,2,3,2", "4,1,8,6,3,2", "8,2,8,1,3,2", "8,2,8,3,3,2"]
@@ -190,7 +190,7 @@ def test_gemm_forced_plans_coarse_groups(monkeypatch, plan):
 
 # Forced split-K plans for the workspace-reuse test: the streaming kernel
 # with 16-column tiles and the LDS kernel with 64 x 128 tiles, both split.
-REUSE_PLANS = ["1,1,4,2,2", "4,1,8,2,3,2"]
+REUSE_PLANS = ["1,1,8,2,2", "4,1,8,2,3,2"]
 
 
 @pytest.mark.parametrize("plan", REUSE_PLANS)
@@ -351,7 +351,7 @@ def test_workspace_aliasing_an_input_is_rejected():
     launch."""
     import ctypes
     import torch
-    w4.w4a16_set_forced_plan("1,1,4,2,2")
+    w4.w4a16_set_forced_plan("1,1,8,2,2")
     M, K, N, g = 16, 2048, 1024, 128
     A, Bq, S = make_inputs(M, K, N, g, seed=3)
     need = w4.w4a16_workspace_bytes(M, K, N, g)

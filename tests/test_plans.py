@@ -145,6 +145,9 @@ def compiled_variants():
     for fmt in (F16, F16ZP, BF16, BF16ZP, W8):
         for t in _macro_tuples(g, "W4A16_VARIANTS"):
             out.setdefault(("gemm_kernel", fmt), set()).add(t)
+    for fmt in (BF16, BF16ZP, W8):
+        for t in _macro_tuples(g, "W4A16_SCALED_WEIGHT_VARIANTS"):
+            out.setdefault(("gemm_kernel", fmt), set()).add(t)
     for t in _macro_tuples(g, "W4A16_SP_VARIANTS"):
         out.setdefault(("gemm_kernel", SP24), set()).add(t)
     for fmt in (F16, F16ZP, BF16, BF16ZP, W8):

@@ -49,7 +49,7 @@ def _both(M, K, N, g, seed):
 # LDS kernel and the stream-K kernel (five workgroups, so runs share tiles),
 # each passing partials through the scratch.
 CASES = [
-    ("1,1,4,2,2", (16, 2048, 4096), (3, 1024, 1024)),
+    ("1,1,8,2,2", (16, 2048, 4096), (3, 1024, 1024)),
     ("4,1,8,2,3,2", (96, 2048, 2048), (40, 1024, 512)),
     ("2,4,8,5,3,4", (64, 2048, 2048), (20, 1024, 512)),
     (None, (16, 11008, 4096), (1, 4096, 4096)),

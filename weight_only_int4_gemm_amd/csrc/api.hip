@@ -72,7 +72,7 @@ bool variant_is_compiled(const Plan& q, int fmt) {
   }
   if (q.tile == 2) return lds_is_compiled(q.mb, q.nb, q.wm, q.wk, q.depth);
   if (q.wm != 1 || q.tile != 0) return false;
-  return plan_is_compiled(q.mb, q.nb, q.wk, q.depth);
+  return plan_is_compiled(q.mb, q.nb, q.wk, q.depth, fmt);
 }
 
 // Test and tuning override of the plan heuristic: a process-wide setting,
@@ -302,9 +302,14 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
       // else eight (measured: 18432 x 73728 at M = 1..4 126-131 us against
       // 130-142 us with eight; 4096 x 12288 at M = 1 9.4 against 10.0 us;
       // but 11008 x 4096, 256 tiles, 9.6 against 8.3 us; and 4096 x 22016
-      // at M = 1 keeps eight waves of 32 columns, 14.1 against 14.7 us)
+      // at M = 1 keeps eight waves of 32 columns, 14.1 against 14.7 us).
+      // In the FP16 formats, whose 16-column tiles of eight waves scale the
+      // sums (four waves of them scale the weights), 16-column tiles take
+      // eight waves throughout: 4096 x 12288 at M = 1 / 2 / 4 7.9 / 8.3 / 9.0
+      // against 8.4 / 9.0 / 10.1 us, 4096 x 8192 at M = 1 / 4 6.5 / 7.4
+      // against 6.8 / 8.1 us, 5120 x 10240 at M = 1 8.8 against 9.5 us.
       p.nb = n16 >= 8 * cus ? 4 : (n16 >= 4 * cus || KB >= 96) ? 2 : 1;
-      p.wk = p.nb != 2 && n16 / p.nb >= 2 * cus ? 4 : 8;
+      p.wk = p.nb != 2 && !(p.nb == 1 && scaled_sums) && n16 / p.nb >= 2 * cus ? 4 : 8;
       p.depth = 2;
     } else if (N >= 8192 && n16 < 8 * cus) {
       // five to eight rows, FP16 formats, wide layers: 64-column tiles of
@@ -320,6 +325,16 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt) {
       p.nb = n16 >= 2 * cus || KB >= 64 ? 4 : 1;
       p.wk = 4;
       p.depth = KB >= 64 && KB < 96 ? 4 : 2;
+      if (p.nb == 1 && scaled_sums) {
+        // FP16 formats, narrow and shallow layers: 32-column tiles of eight
+        // waves (which scale the sums), split in two by the rule below when
+        // that still fits one workgroup per compute unit.  Same box:
+        // 4096 x 4096 at M = 8 / 12 / 16 6.3 / 6.5 / 6.8 against 6.4 / 6.7 /
+        // 7.0 us; 5120 x 5120 at M = 16 9.1 against 12.8 us (320 tiles of
+        // 16 columns left a second, mostly empty wave of workgroups).
+        p.nb = 2;
+        p.wk = 8;
+      }
     }
   } else if (M <= 32 && !(fmt != kFmtSp24 && M > 16 && KB >= 32 && KB <= 64 &&
                            (N + 255) / 256 <= cus / 8)) {

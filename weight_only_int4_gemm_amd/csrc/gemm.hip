@@ -103,10 +103,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
   constexpr bool W8 = Format<FMT>::kW8;
   constexpr bool SP = Format<FMT>::kSp;
   typedef Slot<MB, NB, ZP, W8, SP> SlotT;
-  // FP16 formats 0 and 1: the scale is applied to FP32 sums (see compute)
-  // wherever a second column block or a second wave per SIMD covers the
-  // wait for those sums.
-  constexpr bool kPostScale = (FMT == kFmtF16 || FMT == kFmtF16Zp) && (NB > 1 || WK > 4);
+  // FP16 formats 0 and 1: the scale is applied to FP32 sums (see compute).
+  // Every variant compiled for them has a second column block or a second
+  // wave per SIMD to cover the wait for those sums.
+  constexpr bool kPostScale = FMT == kFmtF16 || FMT == kFmtF16Zp;
   static_assert(!ALDS || (MB == 1 && !SP), "activations in LDS: one row block, dense codes");
   // ALDS: rows 0..M-1 of the row tile over this workgroup's K range, row
   // after row, krange halfs each (the launch sizes it)
@@ -263,8 +263,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kFmtBf16 ? 2 : 1))) void gemm_kernel(
       // rounded to FP16, so the result is the definition's up to FP32
       // summation order, closer to the float64 product than the rounded
       // weights are.  With one column block and one wave per SIMD the
-      // multiply-adds wait for the matrix unit (4096 x 4096 at M = 16:
-      // 7.2 against 7.0 us), and that variant keeps the scaled weights.
+      // multiply-adds would wait for the matrix unit (4096 x 4096 at
+      // M = 16: 7.2 against 7.0 us with the weights scaled): that variant
+      // is compiled only for the other formats, and the plans give FP16
+      // eight waves or wider tiles there.
       float4_t blk[MB][NB];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -573,8 +575,11 @@ static hipError_t launch_one(const Plan& p, const uint16_t* A, const uint32_t* B
 }
 
 // Compiled variants (MB, NB, WK, D): the plans' ones, for the formats 0 to
-// 4 (FP16 and BF16 with or without zero points, 8-bit codes).
-#define W4A16_VARIANTS(X) X(1, 1, 4, 2) X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 4, 2) X(1, 4, 4, 4)
+// 4 (FP16 and BF16 with or without zero points, 8-bit codes) ...
+#define W4A16_VARIANTS(X) X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 4, 2) X(1, 4, 4, 4)
+// ... and, for the formats that scale the weights (2 to 4), 16-column tiles
+// of four waves (the plans give the FP16 formats eight waves there).
+#define W4A16_SCALED_WEIGHT_VARIANTS(X) X(1, 1, 4, 2)
 
 // Variants compiled for 2:4-sparse weights (the plans keep two K blocks in
 // flight).
@@ -588,10 +593,13 @@ bool sp_is_compiled(int mb, int nb, int wk, int depth) {
   return false;
 }
 
-bool plan_is_compiled(int mb, int nb, int wk, int depth) {
+bool plan_is_compiled(int mb, int nb, int wk, int depth, int fmt) {
 #define W4A16_MATCH(MB_, NB_, WK_, D_) \
   if (mb == MB_ && nb == NB_ && wk == WK_ && depth == D_) return true;
   W4A16_VARIANTS(W4A16_MATCH)
+  if (fmt == kFmtBf16 || fmt == kFmtBf16Zp || fmt == kFmtW8) {
+    W4A16_SCALED_WEIGHT_VARIANTS(W4A16_MATCH)
+  }
 #undef W4A16_MATCH
   return false;
 }
@@ -631,6 +639,20 @@ hipError_t launch_gemm(const Plan& p, const uint16_t* A, const uint32_t* Bp,
     W4A16_VARIANTS(W4A16_CASE)
   }
 #undef W4A16_CASE
+#define W4A16_WCASE(MB_, NB_, WK_, D_)                                                    \
+  if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_) {                       \
+    if (wf.fmt == kFmtBf16)                                                               \
+      return launch_one<MB_, NB_, WK_, D_, kFmtBf16>(p, A, Bp, S, C, M, K, N, gmagic, ep,  \
+                                                     nullptr, workspace, stream);         \
+    if (wf.fmt == kFmtBf16Zp)                                                             \
+      return launch_one<MB_, NB_, WK_, D_, kFmtBf16Zp>(p, A, Bp, S, C, M, K, N, gmagic,   \
+                                                       ep, wf.zeros, workspace, stream);  \
+    if (wf.fmt == kFmtW8)                                                                 \
+      return launch_one<MB_, NB_, WK_, D_, kFmtW8>(p, A, Bp, S, C, M, K, N, gmagic, ep,    \
+                                                   nullptr, workspace, stream);           \
+  }
+  W4A16_SCALED_WEIGHT_VARIANTS(W4A16_WCASE)
+#undef W4A16_WCASE
   if (wf.fmt == kFmtSp24) {
 #define W4A16_SCASE(MB_, NB_, WK_, D_)                                                      \
   if (p.mb == MB_ && p.nb == NB_ && p.wk == WK_ && p.depth == D_)                           \

@@ -62,7 +62,7 @@ Plan make_plan(int M, int K, int N, int group, int cus, int fmt = 0);
 constexpr int kAldsMaxRows = 4;
 constexpr size_t kAldsMaxBytes = 32768;
 size_t activations_lds_bytes(const Plan& p, int M, int K, int fmt);
-bool plan_is_compiled(int mb, int nb, int wk, int depth);
+bool plan_is_compiled(int mb, int nb, int wk, int depth, int fmt);
 bool sp_is_compiled(int mb, int nb, int wk, int depth);
 bool lds_is_compiled(int mb, int nb, int wm, int wn, int ns);
 bool lds_sp_is_compiled(int mb, int nb, int wm, int wn, int ns);
