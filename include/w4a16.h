@@ -194,9 +194,13 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group);
  *           scale per output column).
  * workspace (device, read/write) see w4a16_workspace_bytes; may be NULL
  *           only when that returns 0 for this shape.
- * Numerics: each weight is rounded once to FP16 from the exact (q-8)*s,
- *           products accumulate in FP32, C is rounded once to FP16
- *           (round to nearest even; overflow gives +-inf).
+ * Numerics: products accumulate in FP32 and C is rounded once to FP16
+ *           (round to nearest even; overflow gives +-inf).  Kernel variants
+ *           whose tiles have 16 or 32 rows multiply the exact integers q-8
+ *           and apply the scale to each 128-deep block's FP32 sum, so no
+ *           weight is rounded; those with 64 rows or more round each weight
+ *           once to FP16 from the exact (q-8)*s.  Both are the product up to
+ *           rounding; w4a16_describe names the variant a shape gets.
  * Errors:   W4A16_ERR_NULL, _SHAPE, _GROUP, _ALIGN, _WORKSPACE, _DEVICE,
  *           _LAUNCH.  C must not overlap A, Bpacked, scales or workspace,
  *           and the workspace none of the inputs.
@@ -262,7 +266,9 @@ int w4a16_gemm_fused(const uint16_t* A, const uint32_t* Bpacked,
  *   w[k][n] = rnd((q[k][n] - z[k/group][n]) * s[k/group][n])
  * with rnd the rounding (to nearest even) to the 16-bit type `dtype`, and
  * z = 8 when `zeros` is NULL.  A, scales and C hold `dtype` values; the sum
- * is FP32 and rounded once to `dtype`.
+ * is FP32 and rounded once to `dtype`.  With FP16 the tiles of 16 or 32
+ * rows skip rnd, as in w4a16_gemm: they scale the FP32 sums of the exact
+ * (q - z) per 128-deep block.
  *
  * zeros   (device, read) uint8 [K/group][N] row-major, the zero point of
  *         each group and column (AWQ uses 0..15; any byte value gives the
@@ -395,9 +401,11 @@ int w4a16_sparse24_dequant_debug(const uint32_t* Bpacked, const uint16_t* scales
 /*
  * w4a16_dequant_debug -- W = dequant(Bpacked, scales), written out.
  *
- * Uses the same device unpack-and-scale routine as w4a16_gemm, so it shows
- * bit for bit the FP16 weights the GEMM multiplies ("Quant Marlin kernel"
- * explainer, middle row: codes to FP16, times the group scale).
+ * Uses the same device unpack-and-scale routine as w4a16_gemm's tiles of 64
+ * rows or more, so it shows bit for bit the FP16 weights they multiply
+ * ("Quant Marlin kernel" explainer, middle row: codes to FP16, times the
+ * group scale); the smaller tiles take the routine's exact integers q - 8
+ * and scale their sums instead.
  *
  * Bpacked (device, read)  output of w4a16_repack for (K, N).
  * scales  (device, read)  FP16 [K/group][N].
