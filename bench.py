@@ -524,8 +524,15 @@ def _time_calls(calls, launches: int, repeats: int) -> float:
     calls (cycling over ``calls``), from HIP events on the current stream."""
     import numpy as np
     import torch
-    for i in range(max(5, len(calls))):
+    # the same calls for at least 0.2 s first: the host work that prepares a
+    # shape's inputs leaves the GPU idle long enough for its clocks to drop
+    t0 = time.perf_counter()
+    i = 0
+    while i < max(5, len(calls)) or time.perf_counter() - t0 < 0.2:
         calls[i % len(calls)]()
+        i += 1
+        if i % 32 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     times = []
     for _ in range(repeats):
@@ -663,7 +670,8 @@ def configs_report(out_path: str, repeats: int = 3, launches: int = 20) -> None:
         f"Kernel source hash: `{kernel_source_hash()}`. Per call: hipEvents around "
         f"{launches} back-to-back launches cycling over enough copies of the packed weights "
         f"to exceed 512 MB (so weights come from HBM, not the Infinity Cache), median of "
-        f"{repeats} repeats; the time includes launch gaps. Inputs: seeded synthetic data "
+        f"{repeats} repeats, after at least 0.2 s of the same calls; the time includes launch "
+        "gaps. Inputs: seeded synthetic data "
         "(weights seed 0, activations seed M). Roofline: HBM 8 TB/s, dense FP16 MFMA "
         "2.5 PFLOP/s; `frac` is the bound's time over the measured time. `FP16 us` is "
         "torch.matmul (hipBLASLt) on the same weights dequantised to FP16, timed the same "
